@@ -1,0 +1,217 @@
+"""Throughput of the ftx BERT encoder forward on one MI355X.
+
+Default workload: BERT-base, 12 layers, 12 heads x 64, fp16 (fp32 accumulation), sequence
+length 32, batch 512, no padding; weights N(0, 0.02), input N(0, 1), seeded, synthetic.
+A step is one full forward (all 12 layers) of the batch, inputs already in device memory.
+
+Prints ONE JSON line: sequences/s (value), ms per step, TFLOP/s and its fraction of the
+dense fp16 MFMA peak, the roofline of the dominant kernel measured with HIP events on the
+forward's stream, and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sequences/sec + TFLOPS (% MFMA peak), 12-layer BERT-base fp16, seq 32/128"
+PEAK_MFMA_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6, "fp32": 157.3}
+PEAK_HBM_GBS = 8000.0
+DTYPE_TAG = {"fp16": "f16", "bf16": "bf16", "fp32": "f32"}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="bert_base_fp16_s32")
+    p.add_argument("--batch", type=int, default=None)
+    p.add_argument("--unfused", action="store_true", help="standalone bias+split and bias+GELU kernels")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-kernel-times", action="store_true")
+    return p.parse_args()
+
+
+def step_work(shape, step: str):
+    """Algorithmic work of ONE launch of a step class: (flops, bytes).
+    Bytes are the minimum HBM traffic (each operand read once, result written once)."""
+    T, S, H, F, B = shape.tokens, shape.seq_len, shape.hidden, shape.ffn, shape.batch
+    e = 4 if shape.dtype == "fp32" else 2
+    if step == "qkv_gemm":
+        return 2.0 * T * 3 * H * H, (T * H + 3 * H * H + 3 * T * H) * e
+    if step == "attn_out_gemm":
+        return 2.0 * T * H * H, (T * H + H * H + T * H) * e
+    if step == "ffn1_gemm":
+        return 2.0 * T * F * H, (T * H + F * H + T * F) * e
+    if step == "ffn2_gemm":
+        return 2.0 * T * H * F, (T * F + H * F + T * H) * e
+    if step == "attention":
+        return 4.0 * B * S * S * H, 4 * T * H * e
+    if step in ("ln1", "ln2"):
+        return 0.0, 3 * T * H * e
+    if step == "bias_gelu":
+        return 0.0, 2 * T * F * e
+    if step == "bias_qkv_split":
+        return 0.0, 2 * 3 * T * H * e
+    raise KeyError(step)
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(case, target_s: float):
+    """The fp64 oracle, as it stands, on the first n sequences of the same workload."""
+    import oracle
+    layers = list(case.layers())
+    n = 1
+    t0 = time.perf_counter()
+    oracle.encoder_rows(case.x, layers, case.lens, case.shape.head_num, list(range(n)))
+    one = time.perf_counter() - t0
+    n = int(max(1, min(case.shape.batch, target_s / max(one, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.encoder_rows(case.x, layers, case.lens, case.shape.head_num, list(range(n)))
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "sequences/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"first {n} of {case.shape.batch} sequences, all {case.shape.num_layers} layers, "
+                      f"numpy float64 ({dt:.1f} s)",
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py runs on one GPU only: this encoder forward shards by data parallelism "
+              f"with no collective, and no multi-GPU run is part of this build (asked: --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synthetic_inputs as si
+    from transformer_encoder_bert_amd import ftx
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wl = si.WORKLOADS[args.workload]
+    batch = args.batch or max(wl.batches)
+    case = si.make_case(wl, batch)
+    shape = case.shape
+    dt = shape.dtype
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    def up(a):
+        h = si.host_array(a, dt)
+        if dt == "bf16":
+            return torch.from_numpy(h.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(h).to(dev)
+
+    enc = ftx.Encoder(shape.batch, shape.seq_len, shape.head_num, shape.size_per_head,
+                      shape.num_layers, dt)
+    for l, w in enumerate(case.layers()):
+        enc.set_weights(l, {k: up(w[k]) for k in si.WEIGHT_NAMES})
+    if args.unfused:
+        enc.set_option(ftx.FTX_OPT_FUSED_EPILOGUES, 0)
+    x = up(case.x)
+    lens = None if case.lens is None else torch.from_numpy(case.lens).to(dev)
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        enc.forward(x, lens, out)
+    torch.cuda.synchronize()
+
+    # timed region: K forwards between a synchronize on each side
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        enc.forward(x, lens, out)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = 1e3 * wall / args.steps
+    seqs = shape.batch / (ms_per_step * 1e-3)
+    flops = shape.flops()
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC, "value": seqs, "unit": "sequences/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_TAG[dt], "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.description}", "global_batch": shape.batch,
+                   "seq_len": shape.seq_len, "layers": shape.num_layers,
+                   "heads": shape.head_num, "size_per_head": shape.size_per_head,
+                   "parallelism": "none (1 GPU)",
+                   "epilogues": "standalone" if args.unfused else "fused"},
+        "tflops": tflops, "frac_mfma_peak": tflops / PEAK_MFMA_TFLOPS[dt],
+        "gpu_event_ms_per_step": gpu_ms / args.steps,
+        "roofline": None, "cpu_baseline": None,
+    }
+
+    if not args.no_kernel_times:
+        # the same K forwards again, with a HIP event pair around every launch on `stream`
+        enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)
+        enc.kernel_times()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            enc.forward(x, lens, out)
+        torch.cuda.synchronize()
+        timed_wall = time.perf_counter() - t0
+        times = enc.kernel_times()
+        enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 0)
+        kernels = {}
+        for name, (ms, cnt) in times.items():
+            if cnt == 0:
+                continue
+            avg = ms / cnt
+            fl, by = step_work(shape, name)
+            kernels[name] = {"avg_us": 1e3 * avg, "launches": cnt, "share": 0.0,
+                             "tflops": fl / (avg * 1e-3) / 1e12 if fl else None,
+                             "gbs_algorithmic": by / (avg * 1e-3) / 1e9}
+        total = sum(v["avg_us"] * v["launches"] for v in kernels.values())
+        for v in kernels.values():
+            v["share"] = v["avg_us"] * v["launches"] / total
+        dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
+        fl, by = step_work(shape, dom)
+        avg_s = kernels[dom]["avg_us"] * 1e-6
+        if fl > 0 and dom != "attention":
+            achieved, peak, unit, bound = fl / avg_s / 1e12, PEAK_MFMA_TFLOPS[dt], "TFLOP/s", "mfma"
+        else:
+            achieved, peak, unit, bound = by / avg_s / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+        result["roofline"] = {"kernel": dom, "bound": bound, "achieved": achieved, "peak": peak,
+                              "unit": unit, "frac": achieved / peak, "traffic": None,
+                              "work_per_launch": fl if bound == "mfma" else by,
+                              "avg_launch_us": kernels[dom]["avg_us"]}
+        result["kernels"] = kernels
+        result["ms_per_step_with_kernel_events"] = 1e3 * timed_wall / args.steps
+
+    enc.close()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,151 @@
+/*
+ * ftx.h -- C ABI of the ftx BERT-style Transformer encoder forward for AMD MI355X (gfx950).
+ *
+ * What it computes.  The forward pass of a multi-layer BERT-style Transformer encoder,
+ * the part the Faster Transformer article ("有钱任性：英伟达训练80亿参数量GPT-2，1475块V100
+ * 53分钟训练BERT", cloud.tencent.com/developer/article/1490359) describes in its section
+ * "什么是 Faster Transformer": a forward-only encoder whose network structure is fixed by
+ * the attention head count and the size of each head, called with a batch size and a
+ * maximum sentence length, in an FP16 or an FP32 compute mode, behind a C++ API.  Each
+ * layer (section "Faster Transformer 优化原理") is matrix multiplies plus element-wise
+ * work on their results: bias add, SoftMax, GELU and Layer Normalization.
+ *
+ * The layer, per sequence b with valid length len_b (post-LayerNorm form):
+ *   Q = X Wq + bq, K = X Wk + bk, V = X Wv + bv        head h = columns h*d .. h*d+d-1
+ *   P = softmax over keys j < len_b of (Q_h K_h^T / sqrt(d)); keys j >= len_b get 0
+ *   C = P V (heads merged back)
+ *   Y1 = LN(X + C Wo + bo; gamma1, beta1)
+ *   X' = LN(Y1 + gelu(Y1 W1 + b1) W2 + b2; gamma2, beta2)
+ * with LN(z) = gamma (z - mean) / sqrt(var + FTX_LN_EPSILON) + beta (biased variance),
+ * gelu(u) = u/2 (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))), and FFN width 4 * hidden.
+ * Every query row, padded or not, is computed; the output covers all B x S positions.
+ *
+ * Precision.  FTX_FP32: fp32 storage and arithmetic.  FTX_FP16 / FTX_BF16: storage in the
+ * 16-bit format, every matrix product accumulated in fp32, softmax and LayerNorm
+ * statistics in fp32; activations between kernels are stored in the 16-bit format.
+ *
+ * Conventions.
+ *  - All tensors are row-major.  All tensor pointers are DEVICE pointers on the device
+ *    that was current at ftx_encoder_create.  Weights are [in][out] (y = x W + b).
+ *  - Every function returns ftx_status; no C++ exception crosses this boundary.
+ *    ftx_last_error() returns a text description of the last failure on this thread.
+ *  - A handle is not thread-safe and its forwards must not overlap in time (they share
+ *    the handle's workspace).  Different handles are independent.
+ */
+#ifndef FTX_H_
+#define FTX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FTX_LN_EPSILON 1e-6f
+#define FTX_MAX_SEQ_LEN 512
+#define FTX_MAX_HIDDEN 4096
+
+typedef struct ftx_encoder ftx_encoder; /* opaque; owned by the library */
+
+typedef enum { FTX_FP32 = 0, FTX_FP16 = 1, FTX_BF16 = 2 } ftx_dtype;
+
+typedef enum {
+  FTX_OK = 0,
+  FTX_ERR_INVALID_ARG = 1,   /* NULL / misaligned / aliased pointer, value out of range */
+  FTX_ERR_UNSUPPORTED = 2,   /* a valid value this build does not implement */
+  FTX_ERR_OUT_OF_MEMORY = 3, /* device allocation failed */
+  FTX_ERR_DEVICE = 4,        /* a HIP runtime call failed (no device, launch failure...) */
+  FTX_ERR_NOT_READY = 5      /* forward called before every layer's weights were set */
+} ftx_status;
+
+/* One layer's weights, every tensor in the handle's dtype, device pointers.
+ * H = head_num * size_per_head, F = 4 H. */
+typedef struct {
+  const void *w_q, *b_q;             /* [H][H], [H] */
+  const void *w_k, *b_k;             /* [H][H], [H] */
+  const void *w_v, *b_v;             /* [H][H], [H] */
+  const void *w_o, *b_o;             /* [H][H], [H] */
+  const void *ln1_gamma, *ln1_beta;  /* [H], [H] */
+  const void *w_ffn1, *b_ffn1;       /* [H][F], [F] */
+  const void *w_ffn2, *b_ffn2;       /* [F][H], [H] */
+  const void *ln2_gamma, *ln2_beta;  /* [H], [H] */
+} ftx_layer_weights;
+
+/* Create an encoder for a fixed shape: the four runtime parameters of the article's
+ * section "什么是 Faster Transformer" (head count, size per head, batch size, maximum
+ * sentence length) plus the layer count and the storage dtype.
+ *   batch_size >= 1; seq_len in [32, FTX_MAX_SEQ_LEN] and a multiple of 32;
+ *   size_per_head in {32, 64}; head_num >= 1 with head_num*size_per_head <= FTX_MAX_HIDDEN;
+ *   num_layers >= 1; out != NULL (host pointer; receives the handle).
+ * Non-positive values, an unknown dtype or out == NULL -> FTX_ERR_INVALID_ARG (no HIP call
+ * is made).  Positive values outside the supported set -> FTX_ERR_UNSUPPORTED.
+ * Allocates the workspace and the weight storage on the current device (hipMalloc):
+ * about (10 B S H + L (12 H^2 + 13 H)) elements. */
+ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int size_per_head,
+                              int num_layers, ftx_dtype dtype, ftx_encoder **out);
+
+/* Copy one layer's weights into the handle (repacking them for the kernels: Wq|Wk|Wv
+ * fused and every matrix stored transposed, [out][in]).  The copies are enqueued on
+ * `stream` (a hipStream_t; NULL = the default stream), which is then synchronized, so
+ * the caller may free its buffers on return.  layer in [0, num_layers); w != NULL and
+ * every pointer in it non-NULL, else FTX_ERR_INVALID_ARG. */
+ftx_status ftx_set_weights(ftx_encoder *enc, int layer, const ftx_layer_weights *w,
+                           void *stream);
+
+/* Run the L-layer forward on `stream` (asynchronous: returns once enqueued).
+ *   input    [B][S][H] device, 16-byte aligned, left unmodified;
+ *   seq_lens [B] int32 device valid lengths, or NULL for "no padding".  Values are
+ *            clamped to [1, S] on the device (the host cannot read them);
+ *   output   [B][S][H] device, 16-byte aligned, must not overlap input.
+ * The caller keeps input, seq_lens and output alive until the stream passes the call.
+ * FTX_ERR_NOT_READY if some layer has no weights. */
+ftx_status ftx_forward(ftx_encoder *enc, const void *input, const int32_t *seq_lens,
+                       void *output, void *stream);
+
+/* Free the handle and its device memory (synchronizes the device first).  NULL -> FTX_OK. */
+ftx_status ftx_destroy(ftx_encoder *enc);
+
+/* Static text for a status code. */
+const char *ftx_status_string(ftx_status status);
+
+/* Description of the most recent failure on the calling thread ("" if none). */
+const char *ftx_last_error(void);
+
+/* ---------------------------------------------------------------------------------
+ * Options of a handle.
+ *   FTX_OPT_FUSED_EPILOGUES (default 1): 1 = bias+QKV split and bias+GELU run inside the
+ *     projection kernels' epilogues (7 launches per layer); 0 = they run as standalone
+ *     element-wise kernels after plain projections (9 launches per layer).  Same result
+ *     up to rounding order.
+ *   FTX_OPT_KERNEL_TIMING (default 0): 1 = every forward records a HIP event pair around
+ *     each launch, on the forward's stream, and accumulates per-step durations that
+ *     ftx_kernel_times() returns.
+ * Unknown option -> FTX_ERR_INVALID_ARG. */
+typedef enum { FTX_OPT_FUSED_EPILOGUES = 0, FTX_OPT_KERNEL_TIMING = 1 } ftx_option;
+ftx_status ftx_set_option(ftx_encoder *enc, ftx_option option, int value);
+
+/* Step classes of the per-step timing. */
+typedef enum {
+  FTX_STEP_QKV_GEMM = 0,        /* a1 (+a2 when fused) */
+  FTX_STEP_BIAS_QKV_SPLIT = 1,  /* a2 standalone */
+  FTX_STEP_ATTENTION = 2,       /* a3-a6 fused */
+  FTX_STEP_ATTN_OUT_GEMM = 3,   /* a7 */
+  FTX_STEP_LN1 = 4,             /* a8 */
+  FTX_STEP_FFN1_GEMM = 5,       /* a9 (+a10 when fused) */
+  FTX_STEP_BIAS_GELU = 6,       /* a10 standalone */
+  FTX_STEP_FFN2_GEMM = 7,       /* a11 */
+  FTX_STEP_LN2 = 8,             /* a12 */
+  FTX_NUM_STEPS = 9
+} ftx_step;
+
+/* Synchronize the events recorded since the last call and return, per step class, the
+ * summed duration in milliseconds (ms[FTX_NUM_STEPS]) and the number of launches
+ * (counts[FTX_NUM_STEPS]); then reset.  Either array may be NULL. */
+ftx_status ftx_kernel_times(ftx_encoder *enc, double *ms, int64_t *counts);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FTX_H_ */

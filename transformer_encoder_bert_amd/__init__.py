@@ -1,0 +1,8 @@
+"""ftx: forward pass of a BERT-style Transformer encoder on AMD MI355X (gfx950).
+
+The compute path is libftx.so (hand-written HIP kernels behind a C ABI, see
+include/ftx.h); ``transformer_encoder_bert_amd.ftx`` is its ctypes binding.  Importing
+this package does not load the library; the binding loads it on first use and raises
+if it has not been built.
+"""
+__all__ = ["ftx"]

@@ -1,0 +1,236 @@
+// Fused multi-head self-attention of the encoder layer on CDNA4 matrix cores.
+//
+// Source: the Faster Transformer article (cloud.tencent.com/developer/article/1490359),
+// section "Faster Transformer 优化原理": per layer, the batched Q K^T and P V matrix
+// multiplies with a SoftMax kernel between them (two SoftMax versions chosen by shape,
+// row sums by register shuffle, sums kept in float), plus the transposes around them.
+// Here the whole chain for one (sequence, head, 32-query block) runs in one wavefront:
+//
+//   S^T = K Q^T       v_mfma 32x32 tiles, keys on rows, the wave's 32 queries on columns;
+//                     a lane then holds 16 of the 32 keys of one query per tile;
+//   mask, scale       keys j >= len_b get -inf; scores scaled by 1/sqrt(d) inside exp2;
+//   softmax           row max and sum: the lane's own values, then one cross-lane step
+//                     (lane ^ 32) -- the wave64 form of the shuffle row reduction; fp32;
+//   C^T = V^T P^T     the probabilities stay in registers and are fed, converted to the
+//                     storage type, straight into the next MFMA as its B operand; V is
+//                     read from the per-head transposed layout V^T[d][S];
+//   merge heads       the result is stored at ctx[b*S + i][h*d + e] directly.
+//
+// Key tiles are processed in chunks of up to 4 (128 keys) with the running-max
+// rescaling of the streaming softmax, so S = 512 uses the same kernel; for S <= 128 the
+// loop runs once.  Key tiles entirely beyond len_b are skipped: their probabilities are
+// exactly 0, so skipping them changes nothing.  Every query row, padded or not, is
+// computed.
+
+#include <math.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace ftx {
+
+template <typename T> struct AttnMfma;
+
+template <> struct AttnMfma<f16> {
+  static constexpr int VEC = 8;
+  typedef f16x8 frag;
+  __device__ static __forceinline__ void mma(const frag& a, const frag& b, f32x16& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct AttnMfma<bf16> {
+  static constexpr int VEC = 8;
+  typedef bf16x8 frag;
+  __device__ static __forceinline__ void mma(const frag& a, const frag& b, f32x16& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct AttnMfma<float> {
+  static constexpr int VEC = 4;  // one 16-byte fragment feeds four 32x32x2 steps
+  typedef f32x4 frag;
+  __device__ static __forceinline__ void mma(const frag& a, const frag& b, f32x16& c) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], c, 0, 0, 0);
+  }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ q,
+                                                        const T* __restrict__ k,
+                                                        const T* __restrict__ vt,
+                                                        const int32_t* __restrict__ lens,
+                                                        T* __restrict__ ctx, int B, int S, int nh,
+                                                        float scale_log2e) {
+  typedef AttnMfma<T> MF;
+  typedef typename MF::frag frag;
+  typedef typename VecT<T, 4>::type v4;
+  constexpr int VEC = MF::VEC;
+  constexpr int KF = 2 * VEC;   // d consumed per fragment pair
+  constexpr int NQF = D / KF;   // fragments along d
+  constexpr int DT = D / 32;    // 32-row tiles of the transposed output along d
+  constexpr int CH = 4;         // key tiles per softmax chunk
+  constexpr int WPB = 4;        // waves per block
+
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int lr = lane % 32, g = lane / 32;
+  const int qblocks = S / 32;
+  const int ntasks = B * nh * qblocks;
+  // hand each XCD a contiguous range of tasks so the waves reading one head's K and V
+  // share that XCD's L2
+  const int nblk = gridDim.x;
+  int blk = blockIdx.x;
+  if (nblk % 8 == 0) blk = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
+  const int task = blk * WPB + wave;
+  if (task >= ntasks) return;
+  const int bh = task / qblocks, qb = task % qblocks;
+  const int b = bh / nh, h = bh % nh;
+  int len = lens ? lens[b] : S;
+  len = min(max(len, 1), S);
+  const int nkt = (len + 31) / 32;
+
+  frag qf[NQF];
+  {
+    const T* qp = q + ((size_t)bh * S + qb * 32 + lr) * D + g * VEC;
+#pragma unroll
+    for (int f = 0; f < NQF; ++f) qf[f] = *(const frag*)(qp + f * KF);
+  }
+  const T* kbase = k + (size_t)bh * S * D + g * VEC;
+  const T* vbase = vt + (size_t)bh * D * S;
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int c0 = 0; c0 < nkt; c0 += CH) {
+    f32x16 sc[CH];
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
+      const int kt = c0 + t;
+      if (kt < nkt) {
+        const T* kr = kbase + (size_t)(kt * 32 + lr) * D;
+#pragma unroll
+        for (int f = 0; f < NQF; ++f) MF::mma(*(const frag*)(kr + f * KF), qf[f], sc[t]);
+      }
+    }
+    // mask and chunk maximum (key of register r: tile*32 + 8*(r/4) + 4*g + r%4)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < CH; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = (c0 + t) * 32 + 8 * (r / 4) + 4 * g + (r % 4);
+        if (key >= len) sc[t][r] = -INFINITY;
+        mx = fmaxf(mx, sc[t][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);  // finite: the first chunk holds key 0 < len
+    const float alpha = exp2f((m_run - m_new) * scale_log2e);
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < CH; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2f((sc[t][r] - m_new) * scale_log2e);
+        sc[t][r] = p;
+        psum += p;
+      }
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+
+    // context: o[dt] += V^T[dt tile][keys] * P^T[keys][queries]
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      const int kt = c0 + t;
+      if (kt >= nkt) continue;
+      if constexpr (VEC == 8) {
+        // MFMA u consumes P registers 8u..8u+7 = keys kt*32 + 16u + {0..3, 8..11} + 4g
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          frag pf;
+#pragma unroll
+          for (int s = 0; s < 8; ++s) pf[s] = from_f32<T>(sc[t][8 * u + s]);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const T* vr = vbase + (size_t)(dt * 32 + lr) * S + kt * 32 + 16 * u + 4 * g;
+            const v4 lo = *(const v4*)(vr);
+            const v4 hi = *(const v4*)(vr + 8);
+            frag vf;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              vf[s] = lo[s];
+              vf[s + 4] = hi[s];
+            }
+            MF::mma(vf, pf, o[dt]);
+          }
+        }
+      } else {
+        // fp32: call u consumes registers 4u..4u+3 = keys kt*32 + 8u + 4g + {0..3}
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          frag pf;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) pf[s] = sc[t][4 * u + s];
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const T* vr = vbase + (size_t)(dt * 32 + lr) * S + kt * 32 + 8 * u + 4 * g;
+            MF::mma(*(const frag*)vr, pf, o[dt]);
+          }
+        }
+      }
+    }
+  }
+
+  // normalise and store with heads merged: ctx[b*S + query][h*D + dd]
+  const float inv = 1.0f / l_run;
+  const int H = nh * D;
+  T* out = ctx + ((size_t)b * S + qb * 32 + lr) * H + h * D + 4 * g;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      v4 vv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vv[e] = from_f32<T>(o[dt][4 * rr + e] * inv);
+      *(v4*)(out + dt * 32 + 8 * rr) = vv;
+    }
+}
+
+template <typename T>
+static hipError_t attn_launch(int B, int S, int nh, int d, const void* q, const void* k,
+                              const void* vt, const int32_t* lens, void* ctx, hipStream_t s) {
+  const int ntasks = B * nh * (S / 32);
+  const int blocks = (ntasks + 3) / 4;
+  const float scale_log2e = (float)(1.4426950408889634 / sqrt((double)d));
+  if (d == 64)
+    attention_kernel<T, 64><<<blocks, 256, 0, s>>>((const T*)q, (const T*)k, (const T*)vt, lens,
+                                                   (T*)ctx, B, S, nh, scale_log2e);
+  else if (d == 32)
+    attention_kernel<T, 32><<<blocks, 256, 0, s>>>((const T*)q, (const T*)k, (const T*)vt, lens,
+                                                   (T*)ctx, B, S, nh, scale_log2e);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(ftx_dtype dt, int B, int S, int nh, int d, const void* q,
+                            const void* k, const void* vt, const int32_t* lens, void* ctx,
+                            hipStream_t s) {
+  switch (dt) {
+    case FTX_FP32: return attn_launch<float>(B, S, nh, d, q, k, vt, lens, ctx, s);
+    case FTX_FP16: return attn_launch<f16>(B, S, nh, d, q, k, vt, lens, ctx, s);
+    case FTX_BF16: return attn_launch<bf16>(B, S, nh, d, q, k, vt, lens, ctx, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ftx

@@ -1,0 +1,268 @@
+// Element-wise and row-reduction kernels of the encoder layer: bias + residual + LayerNorm,
+// bias + GELU, bias + Q/K/V head split, and the weight transpose used when weights are set.
+//
+// Source: the Faster Transformer article (cloud.tencent.com/developer/article/1490359),
+// section "Faster Transformer 优化原理": everything except the matrix multiplies is fused
+// into a few custom kernels that work element-wise on the matrix-multiply results; 16-bit
+// data are moved as packed pairs and promoted to float for the SoftMax / LayerNorm sums;
+// row sums use register shuffles; 1/sqrt becomes rsqrt and pow(x, 3) becomes x*x*x.
+// Here: 64-lane wavefronts, 8- or 16-byte vector accesses, fp32 statistics, and a
+// two-pass (mean, then centred sum of squares) variance held entirely in registers.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace ftx {
+
+// ------------------------------------------------------------------------------------
+// bias + residual + LayerNorm: y = gamma * (z - mean) * rsqrt(var + eps) + beta,
+// z = x + a + bias.  LPR lanes own one row; each lane holds MAXV 4-element vectors,
+// vector v of a lane sits at column 4 * (v * LPR + sub) so that a wave's loads of one v
+// are contiguous.  EXACT: every lane owns exactly MAXV vectors (cols == 4 * LPR * MAXV).
+template <typename T, int LPR, int MAXV, bool EXACT>
+__global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
+                                                        const T* __restrict__ a,
+                                                        const T* __restrict__ bias,
+                                                        const T* __restrict__ gamma,
+                                                        const T* __restrict__ beta,
+                                                        T* y, int rows, int cols) {
+  typedef typename VecT<T, 4>::type v4;
+  constexpr int RPW = kWave / LPR;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int row = (blockIdx.x * (blockDim.x / kWave) + wave) * RPW + lane / LPR;
+  const int sub = lane % LPR;
+  if (row >= rows) return;  // whole LPR-lane groups leave together
+  const int nvec = cols / 4;
+  const size_t base = (size_t)row * cols;
+
+  float z[MAXV][4];
+  float sum = 0.f;
+#pragma unroll
+  for (int v = 0; v < MAXV; ++v) {
+    const int vi = v * LPR + sub;
+    if (EXACT || vi < nvec) {
+      const v4 xv = *(const v4*)(x + base + 4 * vi);
+      const v4 av = *(const v4*)(a + base + 4 * vi);
+      const v4 bv = *(const v4*)(bias + 4 * vi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        z[v][e] = to_f32(xv[e]) + to_f32(av[e]) + to_f32(bv[e]);
+        sum += z[v][e];
+      }
+    }
+  }
+  const float inv_n = 1.0f / (float)cols;
+  const float mean = group_sum<LPR>(sum) * inv_n;
+  float sq = 0.f;
+#pragma unroll
+  for (int v = 0; v < MAXV; ++v) {
+    const int vi = v * LPR + sub;
+    if (EXACT || vi < nvec) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float c = z[v][e] - mean;
+        sq += c * c;
+      }
+    }
+  }
+  const float var = group_sum<LPR>(sq) * inv_n;
+  const float rs = rsqrtf(var + FTX_LN_EPSILON);
+#pragma unroll
+  for (int v = 0; v < MAXV; ++v) {
+    const int vi = v * LPR + sub;
+    if (EXACT || vi < nvec) {
+      const v4 gv = *(const v4*)(gamma + 4 * vi);
+      const v4 btv = *(const v4*)(beta + 4 * vi);
+      v4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(to_f32(gv[e]) * ((z[v][e] - mean) * rs) + to_f32(btv[e]));
+      *(v4*)(y + base + 4 * vi) = o;
+    }
+  }
+}
+
+template <typename T, int LPR, int MAXV, bool EXACT>
+static hipError_t ln_launch(int rows, int cols, const void* x, const void* a, const void* bias,
+                            const void* gamma, const void* beta, void* y, hipStream_t s) {
+  constexpr int rows_per_block = (256 / kWave) * (kWave / LPR);
+  const int grid = (rows + rows_per_block - 1) / rows_per_block;
+  layernorm_kernel<T, LPR, MAXV, EXACT><<<grid, 256, 0, s>>>(
+      (const T*)x, (const T*)a, (const T*)bias, (const T*)gamma, (const T*)beta, (T*)y, rows, cols);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t ln_dispatch(int rows, int cols, const void* x, const void* a, const void* bias,
+                              const void* gamma, const void* beta, void* y, hipStream_t s) {
+  switch (cols) {  // exact register tilings for the common hidden sizes
+    case 128: return ln_launch<T, 32, 1, true>(rows, cols, x, a, bias, gamma, beta, y, s);
+    case 256: return ln_launch<T, 64, 1, true>(rows, cols, x, a, bias, gamma, beta, y, s);
+    case 384: return ln_launch<T, 32, 3, true>(rows, cols, x, a, bias, gamma, beta, y, s);
+    case 512: return ln_launch<T, 64, 2, true>(rows, cols, x, a, bias, gamma, beta, y, s);
+    case 768: return ln_launch<T, 64, 3, true>(rows, cols, x, a, bias, gamma, beta, y, s);
+    case 1024: return ln_launch<T, 64, 4, true>(rows, cols, x, a, bias, gamma, beta, y, s);
+    default: break;
+  }
+  if (cols <= 4 * 16 * 4)  // small rows: a quarter wave per row
+    return ln_launch<T, 16, 4, false>(rows, cols, x, a, bias, gamma, beta, y, s);
+  return ln_launch<T, 64, 16, false>(rows, cols, x, a, bias, gamma, beta, y, s);
+}
+
+hipError_t launch_bias_residual_layernorm(ftx_dtype dt, int rows, int cols, const void* x,
+                                          const void* a, const void* bias, const void* gamma,
+                                          const void* beta, void* y, hipStream_t s) {
+  switch (dt) {
+    case FTX_FP32: return ln_dispatch<float>(rows, cols, x, a, bias, gamma, beta, y, s);
+    case FTX_FP16: return ln_dispatch<f16>(rows, cols, x, a, bias, gamma, beta, y, s);
+    case FTX_BF16: return ln_dispatch<bf16>(rows, cols, x, a, bias, gamma, beta, y, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------------------------------
+// bias + GELU over [rows][cols], 16-byte vectors, grid-stride.
+template <typename T>
+__global__ __launch_bounds__(256) void bias_gelu_kernel(const T* u, const T* __restrict__ bias,
+                                                        T* g, int64_t nvec, int cols) {
+  typedef typename Vec16<T>::type vec;
+  constexpr int N = Vec16<T>::N;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nvec;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int col = (int)((i * N) % cols);
+    const vec uv = *(const vec*)(u + i * N);
+    const vec bv = *(const vec*)(bias + col);
+    vec o;
+#pragma unroll
+    for (int e = 0; e < N; ++e) o[e] = from_f32<T>(gelu_tanh(to_f32(uv[e]) + to_f32(bv[e])));
+    *(vec*)(g + i * N) = o;
+  }
+}
+
+template <typename T>
+static hipError_t gelu_launch(int rows, int cols, const void* u, const void* bias, void* g,
+                              hipStream_t s) {
+  const int64_t nvec = (int64_t)rows * cols / Vec16<T>::N;
+  int64_t blocks = (nvec + 255) / 256;
+  const int64_t cap = 256 * 16;  // 16 waves' worth of blocks per CU is plenty
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  bias_gelu_kernel<T><<<(int)blocks, 256, 0, s>>>((const T*)u, (const T*)bias, (T*)g, nvec, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_gelu(ftx_dtype dt, int rows, int cols, const void* u, const void* bias,
+                            void* g, hipStream_t s) {
+  switch (dt) {
+    case FTX_FP32: return gelu_launch<float>(rows, cols, u, bias, g, s);
+    case FTX_FP16: return gelu_launch<f16>(rows, cols, u, bias, g, s);
+    case FTX_BF16: return gelu_launch<bf16>(rows, cols, u, bias, g, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------------------------------
+// bias + head split: qkv [T][3H] -> q, k [B][n][S][D], vt [B][n][D][S].
+// Block = 32 tokens of one (which, head); V goes through LDS to be written along tokens.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bias_qkv_split_kernel(const T* __restrict__ qkv,
+                                                             const T* __restrict__ bias,
+                                                             T* __restrict__ q, T* __restrict__ k,
+                                                             T* __restrict__ vt, int S, int nh) {
+  typedef typename Vec16<T>::type vec;
+  constexpr int N = Vec16<T>::N;
+  constexpr int CPR = D / N;  // 16-byte chunks per head row
+  __shared__ T tile[32][D + N];
+  const int H = nh * D;
+  const int which = blockIdx.y / nh, h = blockIdx.y % nh;
+  const int t0 = blockIdx.x * 32;
+  const int b = t0 / S, s0 = t0 % S;
+  const size_t head = (size_t)b * nh + h;
+  for (int c = threadIdx.x; c < 32 * CPR; c += blockDim.x) {
+    const int r = c / CPR, cc = (c % CPR) * N;
+    const int col = which * H + h * D + cc;
+    const vec iv = *(const vec*)(qkv + (size_t)(t0 + r) * 3 * H + col);
+    const vec bv = *(const vec*)(bias + col);
+    vec o;
+#pragma unroll
+    for (int e = 0; e < N; ++e) o[e] = from_f32<T>(to_f32(iv[e]) + to_f32(bv[e]));
+    if (which < 2) {
+      T* dst = (which == 0 ? q : k) + (head * S + s0 + r) * D + cc;
+      *(vec*)dst = o;
+    } else {
+      *(vec*)&tile[r][cc] = o;
+    }
+  }
+  if (which == 2) {  // uniform across the block
+    __syncthreads();
+    constexpr int TCH = 32 / N;  // chunks along the 32 tokens
+    for (int c = threadIdx.x; c < D * TCH; c += blockDim.x) {
+      const int dd = c / TCH, sc = (c % TCH) * N;
+      vec o;
+#pragma unroll
+      for (int e = 0; e < N; ++e) o[e] = tile[sc + e][dd];
+      *(vec*)(vt + (head * D + dd) * S + s0 + sc) = o;
+    }
+  }
+}
+
+template <typename T>
+static hipError_t split_launch(int B, int S, int nh, int d, const void* qkv, const void* b_qkv,
+                               void* q, void* k, void* vt, hipStream_t s) {
+  dim3 grid((unsigned)(B * S / 32), (unsigned)(3 * nh));
+  if (d == 64)
+    bias_qkv_split_kernel<T, 64><<<grid, 256, 0, s>>>((const T*)qkv, (const T*)b_qkv, (T*)q, (T*)k, (T*)vt, S, nh);
+  else if (d == 32)
+    bias_qkv_split_kernel<T, 32><<<grid, 256, 0, s>>>((const T*)qkv, (const T*)b_qkv, (T*)q, (T*)k, (T*)vt, S, nh);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_qkv_split(ftx_dtype dt, int B, int S, int nh, int d, const void* qkv,
+                                 const void* b_qkv, void* q, void* k, void* vt, hipStream_t s) {
+  switch (dt) {
+    case FTX_FP32: return split_launch<float>(B, S, nh, d, qkv, b_qkv, q, k, vt, s);
+    case FTX_FP16: return split_launch<f16>(B, S, nh, d, qkv, b_qkv, q, k, vt, s);
+    case FTX_BF16: return split_launch<bf16>(B, S, nh, d, qkv, b_qkv, q, k, vt, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------------------------------
+// Transpose out[cols][rows] = in[rows][cols], 32x32 tiles through LDS, element accesses
+// (no alignment assumption).
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, T* __restrict__ out,
+                                                        int rows, int cols) {
+  __shared__ T tile[32][33];
+  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+  const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;  // 32 x 8
+  for (int i = ty; i < 32; i += 8) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < rows && c < cols) tile[i][tx] = in[(size_t)r * cols + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8) {
+    const int c = c0 + i, r = r0 + tx;
+    if (r < rows && c < cols) out[(size_t)c * rows + r] = tile[tx][i];
+  }
+}
+
+template <typename T>
+static hipError_t transpose_launch(int rows, int cols, const void* in, void* out, hipStream_t s) {
+  dim3 grid((unsigned)((cols + 31) / 32), (unsigned)((rows + 31) / 32));
+  transpose_kernel<T><<<grid, 256, 0, s>>>((const T*)in, (T*)out, rows, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(ftx_dtype dt, int rows, int cols, const void* in, void* out,
+                            hipStream_t s) {
+  switch (dt) {
+    case FTX_FP32: return transpose_launch<float>(rows, cols, in, out, s);
+    case FTX_FP16: return transpose_launch<f16>(rows, cols, in, out, s);
+    case FTX_BF16: return transpose_launch<bf16>(rows, cols, in, out, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ftx

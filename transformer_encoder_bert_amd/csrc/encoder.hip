@@ -1,0 +1,521 @@
+// The C ABI of ftx: encoder handle, weight repacking, the per-layer launch sequence, and
+// the step-level entry points.  Host code; every computation happens in the kernels of
+// gemm.hip, attention.hip and elementwise.hip.
+//
+// Source: the Faster Transformer article (cloud.tencent.com/developer/article/1490359),
+// section "什么是 Faster Transformer" (an encoder created for head count, size per head,
+// batch size and maximum sentence length, FP16/FP32 modes, a C++ API) and section
+// "Faster Transformer 优化原理" (one layer = matrix multiplies plus a few fused custom
+// kernels; launch configuration chosen per shape).
+
+#include <hip/hip_runtime.h>
+
+#include <initializer_list>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "ftx.h"
+#include "ftx_steps.h"
+#include "launch.h"
+
+using namespace ftx;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ftx_status fail(ftx_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+ftx_status hip_fail(hipError_t e, const char* what) {
+  if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
+    return fail(FTX_ERR_OUT_OF_MEMORY, std::string(what) + ": " + hipGetErrorString(e));
+  return fail(FTX_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define FTX_HIP(call)                                   \
+  do {                                                  \
+    hipError_t e_ = (call);                             \
+    if (e_ != hipSuccess) return hip_fail(e_, #call);   \
+  } while (0)
+
+size_t dtype_size(ftx_dtype dt) { return dt == FTX_FP32 ? 4 : 2; }
+bool dtype_ok(int dt) { return dt == FTX_FP32 || dt == FTX_FP16 || dt == FTX_BF16; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// True if `p` points into device memory (or managed memory) of the HIP runtime.  Kernels
+// given a host pointer would fault, so every entry point checks its tensor pointers.
+bool is_device_ptr(const void* p) {
+  if (!p) return false;
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged;
+}
+
+bool all_device(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && !is_device_ptr(p)) return false;
+  return true;
+}
+
+// Shape checks shared by create and the step entry points.
+ftx_status check_shape(int B, int S, int nh, int d) {
+  if (B < 1 || S < 1 || nh < 1 || d < 1) return fail(FTX_ERR_INVALID_ARG, "shape values must be >= 1");
+  if (d != 32 && d != 64) return fail(FTX_ERR_UNSUPPORTED, "size_per_head must be 32 or 64");
+  if (S % 32 != 0 || S > FTX_MAX_SEQ_LEN)
+    return fail(FTX_ERR_UNSUPPORTED, "seq_len must be a multiple of 32 in [32, 512]");
+  if ((long)nh * d > FTX_MAX_HIDDEN) return fail(FTX_ERR_UNSUPPORTED, "hidden size above 4096");
+  // 32-bit element indices inside kernels: the largest tensor is [B*S][4H]
+  if ((long long)B * S * 4 * nh * d >= (1LL << 31))
+    return fail(FTX_ERR_UNSUPPORTED, "batch * seq_len * 4 * hidden must stay below 2^31");
+  return FTX_OK;
+}
+
+struct LayerW {
+  void* w_qkv_t;  // [3H][H]
+  void* b_qkv;    // [3H]
+  void* w_o_t;    // [H][H]
+  void* b_o;
+  void* ln1_g;
+  void* ln1_b;
+  void* w1_t;     // [F][H]
+  void* b1;       // [F]
+  void* w2_t;     // [H][F]
+  void* b2;
+  void* ln2_g;
+  void* ln2_b;
+};
+
+}  // namespace
+
+struct ftx_encoder {
+  int B, S, nh, d, L, H, F, T;
+  ftx_dtype dt;
+  size_t es;
+  int device;
+  void* weights = nullptr;
+  void* ws = nullptr;
+  std::vector<LayerW> layers;
+  std::vector<char> ready;
+  // workspace views
+  void *q, *k, *vt, *ctx, *abuf, *y1, *u;
+  int fused = 1;
+  int timing = 0;
+  struct Mark {
+    hipEvent_t start, stop;
+    int step;
+  };
+  std::vector<Mark> marks;      // recorded, not yet read
+  std::vector<hipEvent_t> pool; // free events
+};
+
+namespace {
+
+ftx_status take_event(ftx_encoder* e, hipEvent_t* ev) {
+  if (!e->pool.empty()) {
+    *ev = e->pool.back();
+    e->pool.pop_back();
+    return FTX_OK;
+  }
+  FTX_HIP(hipEventCreate(ev));
+  return FTX_OK;
+}
+
+// Launch wrapper: optional event pair on the launch stream around one step.
+template <typename F>
+ftx_status run_step(ftx_encoder* e, int step, hipStream_t s, F&& launch) {
+  ftx_encoder::Mark m{nullptr, nullptr, step};
+  if (e->timing) {
+    ftx_status st = take_event(e, &m.start);
+    if (st != FTX_OK) return st;
+    if ((st = take_event(e, &m.stop)) != FTX_OK) return st;
+    FTX_HIP(hipEventRecord(m.start, s));
+  }
+  hipError_t err = launch();
+  if (err != hipSuccess) return hip_fail(err, "kernel launch");
+  if (e->timing) {
+    FTX_HIP(hipEventRecord(m.stop, s));
+    e->marks.push_back(m);
+  }
+  return FTX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ftx_status_string(ftx_status s) {
+  switch (s) {
+    case FTX_OK: return "ok";
+    case FTX_ERR_INVALID_ARG: return "invalid argument";
+    case FTX_ERR_UNSUPPORTED: return "unsupported";
+    case FTX_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case FTX_ERR_DEVICE: return "device error";
+    case FTX_ERR_NOT_READY: return "weights not set";
+  }
+  return "unknown status";
+}
+
+const char* ftx_last_error(void) { return g_last_error.c_str(); }
+
+ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int size_per_head,
+                              int num_layers, ftx_dtype dtype, ftx_encoder** out) {
+  g_last_error.clear();
+  if (!out) return fail(FTX_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
+  if (num_layers < 1) return fail(FTX_ERR_INVALID_ARG, "num_layers must be >= 1");
+  ftx_status st = check_shape(batch_size, seq_len, head_num, size_per_head);
+  if (st != FTX_OK) return st;
+
+  int dev = 0;
+  FTX_HIP(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  FTX_HIP(hipGetDeviceProperties(&prop, dev));
+  if (std::string(prop.gcnArchName).rfind("gfx950", 0) != 0)
+    return fail(FTX_ERR_UNSUPPORTED, std::string("built for gfx950, device is ") + prop.gcnArchName);
+
+  ftx_encoder* e = new (std::nothrow) ftx_encoder();
+  if (!e) return fail(FTX_ERR_OUT_OF_MEMORY, "host allocation");
+  e->B = batch_size;
+  e->S = seq_len;
+  e->nh = head_num;
+  e->d = size_per_head;
+  e->L = num_layers;
+  e->H = head_num * size_per_head;
+  e->F = 4 * e->H;
+  e->T = batch_size * seq_len;
+  e->dt = dtype;
+  e->es = dtype_size(dtype);
+  e->device = dev;
+
+  const size_t H = e->H, F = e->F, T = e->T, es = e->es;
+  // weights: per layer 3H*H + 3H + H*H + H + 2H + F*H + F + H*F + H + 2H elements, each
+  // tensor padded to 256 bytes
+  auto pad = [](size_t bytes) { return (bytes + 255) / 256 * 256; };
+  const size_t per_layer = pad(3 * H * H * es) + pad(3 * H * es) + pad(H * H * es) + 5 * pad(H * es) +
+                           pad(F * H * es) + pad(F * es) + pad(H * F * es) + pad(H * es);
+  hipError_t err = hipMalloc(&e->weights, per_layer * e->L);
+  if (err != hipSuccess) {
+    delete e;
+    return hip_fail(err, "hipMalloc(weights)");
+  }
+  const size_t TH = pad(T * H * es);
+  const size_t ws_bytes = 3 * TH /*q,k,vt*/ + TH /*ctx*/ + TH /*abuf*/ + TH /*y1*/ + pad(T * F * es) /*u*/;
+  err = hipMalloc(&e->ws, ws_bytes);
+  if (err != hipSuccess) {
+    hipFree(e->weights);
+    delete e;
+    return hip_fail(err, "hipMalloc(workspace)");
+  }
+  char* w = (char*)e->weights;
+  e->layers.resize(e->L);
+  for (int l = 0; l < e->L; ++l) {
+    LayerW& lw = e->layers[l];
+    auto take = [&](size_t bytes) { void* p = w; w += pad(bytes); return p; };
+    lw.w_qkv_t = take(3 * H * H * es);
+    lw.b_qkv = take(3 * H * es);
+    lw.w_o_t = take(H * H * es);
+    lw.b_o = take(H * es);
+    lw.ln1_g = take(H * es);
+    lw.ln1_b = take(H * es);
+    lw.w1_t = take(F * H * es);
+    lw.b1 = take(F * es);
+    lw.w2_t = take(H * F * es);
+    lw.b2 = take(H * es);
+    lw.ln2_g = take(H * es);
+    lw.ln2_b = take(H * es);
+  }
+  e->ready.assign(e->L, 0);
+  char* p = (char*)e->ws;
+  e->q = p; p += TH;
+  e->k = p; p += TH;
+  e->vt = p; p += TH;
+  e->ctx = p; p += TH;
+  e->abuf = p; p += TH;
+  e->y1 = p; p += TH;
+  e->u = p;
+  *out = e;
+  return FTX_OK;
+}
+
+ftx_status ftx_set_weights(ftx_encoder* e, int layer, const ftx_layer_weights* w, void* stream) {
+  g_last_error.clear();
+  if (!e) return fail(FTX_ERR_INVALID_ARG, "encoder is NULL");
+  if (!w) return fail(FTX_ERR_INVALID_ARG, "weights struct is NULL");
+  if (layer < 0 || layer >= e->L) return fail(FTX_ERR_INVALID_ARG, "layer out of range");
+  const void* ptrs[] = {w->w_q, w->b_q, w->w_k, w->b_k, w->w_v, w->b_v, w->w_o, w->b_o,
+                        w->ln1_gamma, w->ln1_beta, w->w_ffn1, w->b_ffn1, w->w_ffn2, w->b_ffn2,
+                        w->ln2_gamma, w->ln2_beta};
+  for (const void* p : ptrs)
+    if (!p) return fail(FTX_ERR_INVALID_ARG, "a weight pointer is NULL");
+  for (const void* p : ptrs)
+    if (!is_device_ptr(p)) return fail(FTX_ERR_INVALID_ARG, "a weight pointer is not device memory");
+  hipStream_t s = (hipStream_t)stream;
+  FTX_HIP(hipSetDevice(e->device));
+  const size_t H = e->H, F = e->F, es = e->es;
+  LayerW& lw = e->layers[layer];
+  char* qkv = (char*)lw.w_qkv_t;
+  FTX_HIP(launch_transpose(e->dt, e->H, e->H, w->w_q, qkv, s));
+  FTX_HIP(launch_transpose(e->dt, e->H, e->H, w->w_k, qkv + H * H * es, s));
+  FTX_HIP(launch_transpose(e->dt, e->H, e->H, w->w_v, qkv + 2 * H * H * es, s));
+  FTX_HIP(launch_transpose(e->dt, e->H, e->H, w->w_o, lw.w_o_t, s));
+  FTX_HIP(launch_transpose(e->dt, e->H, e->F, w->w_ffn1, lw.w1_t, s));
+  FTX_HIP(launch_transpose(e->dt, e->F, e->H, w->w_ffn2, lw.w2_t, s));
+  char* bqkv = (char*)lw.b_qkv;
+  FTX_HIP(hipMemcpyAsync(bqkv, w->b_q, H * es, hipMemcpyDeviceToDevice, s));
+  FTX_HIP(hipMemcpyAsync(bqkv + H * es, w->b_k, H * es, hipMemcpyDeviceToDevice, s));
+  FTX_HIP(hipMemcpyAsync(bqkv + 2 * H * es, w->b_v, H * es, hipMemcpyDeviceToDevice, s));
+  FTX_HIP(hipMemcpyAsync(lw.b_o, w->b_o, H * es, hipMemcpyDeviceToDevice, s));
+  FTX_HIP(hipMemcpyAsync(lw.ln1_g, w->ln1_gamma, H * es, hipMemcpyDeviceToDevice, s));
+  FTX_HIP(hipMemcpyAsync(lw.ln1_b, w->ln1_beta, H * es, hipMemcpyDeviceToDevice, s));
+  FTX_HIP(hipMemcpyAsync(lw.b1, w->b_ffn1, F * es, hipMemcpyDeviceToDevice, s));
+  FTX_HIP(hipMemcpyAsync(lw.b2, w->b_ffn2, H * es, hipMemcpyDeviceToDevice, s));
+  FTX_HIP(hipMemcpyAsync(lw.ln2_g, w->ln2_gamma, H * es, hipMemcpyDeviceToDevice, s));
+  FTX_HIP(hipMemcpyAsync(lw.ln2_b, w->ln2_beta, H * es, hipMemcpyDeviceToDevice, s));
+  FTX_HIP(hipStreamSynchronize(s));
+  e->ready[layer] = 1;
+  return FTX_OK;
+}
+
+ftx_status ftx_forward(ftx_encoder* e, const void* input, const int32_t* seq_lens, void* output,
+                       void* stream) {
+  g_last_error.clear();
+  if (!e) return fail(FTX_ERR_INVALID_ARG, "encoder is NULL");
+  if (!input || !output) return fail(FTX_ERR_INVALID_ARG, "input or output is NULL");
+  if (!aligned16(input) || !aligned16(output))
+    return fail(FTX_ERR_INVALID_ARG, "input and output must be 16-byte aligned");
+  const size_t bytes = (size_t)e->T * e->H * e->es;
+  if (overlap(input, bytes, output, bytes)) return fail(FTX_ERR_INVALID_ARG, "output overlaps input");
+  for (int l = 0; l < e->L; ++l)
+    if (!e->ready[l]) return fail(FTX_ERR_NOT_READY, "layer " + std::to_string(l) + " has no weights");
+  if (!all_device({input, output, seq_lens}))
+    return fail(FTX_ERR_INVALID_ARG, "input, output and seq_lens must be device memory");
+  hipStream_t s = (hipStream_t)stream;
+  FTX_HIP(hipSetDevice(e->device));
+  const ftx_dtype dt = e->dt;
+  const int B = e->B, S = e->S, nh = e->nh, d = e->d, H = e->H, F = e->F, T = e->T;
+  for (int l = 0; l < e->L; ++l) {
+    const LayerW& w = e->layers[l];
+    const void* x = (l == 0) ? input : output;  // the stack's state lives in `output`
+    ftx_status st;
+    if (e->fused) {
+      st = run_step(e, FTX_STEP_QKV_GEMM, s, [&] {
+        return launch_qkv_projection(dt, B, S, nh, d, x, w.w_qkv_t, w.b_qkv, e->q, e->k, e->vt, s);
+      });
+    } else {
+      st = run_step(e, FTX_STEP_QKV_GEMM, s, [&] {
+        return launch_linear(dt, T, 3 * H, H, x, w.w_qkv_t, nullptr, false, e->u, s);
+      });
+      if (st != FTX_OK) return st;
+      st = run_step(e, FTX_STEP_BIAS_QKV_SPLIT, s, [&] {
+        return launch_bias_qkv_split(dt, B, S, nh, d, e->u, w.b_qkv, e->q, e->k, e->vt, s);
+      });
+    }
+    if (st != FTX_OK) return st;
+    st = run_step(e, FTX_STEP_ATTENTION, s, [&] {
+      return launch_attention(dt, B, S, nh, d, e->q, e->k, e->vt, seq_lens, e->ctx, s);
+    });
+    if (st != FTX_OK) return st;
+    st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
+      return launch_linear(dt, T, H, H, e->ctx, w.w_o_t, nullptr, false, e->abuf, s);
+    });
+    if (st != FTX_OK) return st;
+    st = run_step(e, FTX_STEP_LN1, s, [&] {
+      return launch_bias_residual_layernorm(dt, T, H, x, e->abuf, w.b_o, w.ln1_g, w.ln1_b, e->y1, s);
+    });
+    if (st != FTX_OK) return st;
+    if (e->fused) {
+      st = run_step(e, FTX_STEP_FFN1_GEMM, s, [&] {
+        return launch_linear(dt, T, F, H, e->y1, w.w1_t, w.b1, true, e->u, s);
+      });
+    } else {
+      st = run_step(e, FTX_STEP_FFN1_GEMM, s, [&] {
+        return launch_linear(dt, T, F, H, e->y1, w.w1_t, nullptr, false, e->u, s);
+      });
+      if (st != FTX_OK) return st;
+      st = run_step(e, FTX_STEP_BIAS_GELU, s, [&] {
+        return launch_bias_gelu(dt, T, F, e->u, w.b1, e->u, s);
+      });
+    }
+    if (st != FTX_OK) return st;
+    st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
+      return launch_linear(dt, T, H, F, e->u, w.w2_t, nullptr, false, e->abuf, s);
+    });
+    if (st != FTX_OK) return st;
+    st = run_step(e, FTX_STEP_LN2, s, [&] {
+      return launch_bias_residual_layernorm(dt, T, H, e->y1, e->abuf, w.b2, w.ln2_g, w.ln2_b, output, s);
+    });
+    if (st != FTX_OK) return st;
+  }
+  return FTX_OK;
+}
+
+ftx_status ftx_destroy(ftx_encoder* e) {
+  g_last_error.clear();
+  if (!e) return FTX_OK;
+  hipSetDevice(e->device);
+  hipDeviceSynchronize();
+  for (auto& m : e->marks) {
+    hipEventDestroy(m.start);
+    hipEventDestroy(m.stop);
+  }
+  for (auto ev : e->pool) hipEventDestroy(ev);
+  hipFree(e->weights);
+  hipFree(e->ws);
+  delete e;
+  return FTX_OK;
+}
+
+ftx_status ftx_set_option(ftx_encoder* e, ftx_option option, int value) {
+  g_last_error.clear();
+  if (!e) return fail(FTX_ERR_INVALID_ARG, "encoder is NULL");
+  switch (option) {
+    case FTX_OPT_FUSED_EPILOGUES: e->fused = value ? 1 : 0; return FTX_OK;
+    case FTX_OPT_KERNEL_TIMING: e->timing = value ? 1 : 0; return FTX_OK;
+  }
+  return fail(FTX_ERR_INVALID_ARG, "unknown option");
+}
+
+ftx_status ftx_kernel_times(ftx_encoder* e, double* ms, int64_t* counts) {
+  g_last_error.clear();
+  if (!e) return fail(FTX_ERR_INVALID_ARG, "encoder is NULL");
+  double acc[FTX_NUM_STEPS] = {0};
+  int64_t cnt[FTX_NUM_STEPS] = {0};
+  for (auto& m : e->marks) {
+    FTX_HIP(hipEventSynchronize(m.stop));
+    float t = 0.f;
+    FTX_HIP(hipEventElapsedTime(&t, m.start, m.stop));
+    acc[m.step] += t;
+    cnt[m.step] += 1;
+    e->pool.push_back(m.start);
+    e->pool.push_back(m.stop);
+  }
+  e->marks.clear();
+  for (int i = 0; i < FTX_NUM_STEPS; ++i) {
+    if (ms) ms[i] = acc[i];
+    if (counts) counts[i] = cnt[i];
+  }
+  return FTX_OK;
+}
+
+// ------------------------------------------------------------------------ step entry points
+
+ftx_status ftx_step_linear(ftx_dtype dtype, int M, int N, int K, const void* a, const void* w_t,
+                           const void* bias, int gelu, void* c, void* stream) {
+  g_last_error.clear();
+  if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
+  if (M < 1 || N < 8 || K < 8 || N % 8 || K % 8)
+    return fail(FTX_ERR_INVALID_ARG, "need M >= 1 and N, K positive multiples of 8");
+  if ((long long)M * N >= (1LL << 31) || (long long)M * K >= (1LL << 31) || (long long)N * K >= (1LL << 31))
+    return fail(FTX_ERR_UNSUPPORTED, "operand above 2^31 elements");
+  if (!a || !w_t || !c) return fail(FTX_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(a) || !aligned16(w_t) || !aligned16(c)) return fail(FTX_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const size_t es = dtype_size(dtype);
+  if (overlap(a, (size_t)M * K * es, c, (size_t)M * N * es) || overlap(w_t, (size_t)N * K * es, c, (size_t)M * N * es))
+    return fail(FTX_ERR_INVALID_ARG, "output overlaps an input");
+  if (!all_device({a, w_t, bias, c})) return fail(FTX_ERR_INVALID_ARG, "pointers must be device memory");
+  hipError_t err = launch_linear(dtype, M, N, K, a, w_t, bias, gelu != 0, c, (hipStream_t)stream);
+  return err == hipSuccess ? FTX_OK : hip_fail(err, "linear launch");
+}
+
+ftx_status ftx_step_qkv_projection(ftx_dtype dtype, int B, int S, int n, int d, const void* x,
+                                   const void* w_qkv_t, const void* b_qkv, void* q, void* k,
+                                   void* v_t, void* stream) {
+  g_last_error.clear();
+  if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
+  ftx_status st = check_shape(B, S, n, d);
+  if (st != FTX_OK) return st;
+  if (!x || !w_qkv_t || !b_qkv || !q || !k || !v_t) return fail(FTX_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(x) || !aligned16(w_qkv_t) || !aligned16(q) || !aligned16(k) || !aligned16(v_t))
+    return fail(FTX_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (!all_device({x, w_qkv_t, b_qkv, q, k, v_t})) return fail(FTX_ERR_INVALID_ARG, "pointers must be device memory");
+  hipError_t err = launch_qkv_projection(dtype, B, S, n, d, x, w_qkv_t, b_qkv, q, k, v_t, (hipStream_t)stream);
+  return err == hipSuccess ? FTX_OK : hip_fail(err, "qkv projection launch");
+}
+
+ftx_status ftx_step_bias_qkv_split(ftx_dtype dtype, int B, int S, int n, int d, const void* qkv,
+                                   const void* b_qkv, void* q, void* k, void* v_t, void* stream) {
+  g_last_error.clear();
+  if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
+  ftx_status st = check_shape(B, S, n, d);
+  if (st != FTX_OK) return st;
+  if (!qkv || !b_qkv || !q || !k || !v_t) return fail(FTX_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(qkv) || !aligned16(b_qkv) || !aligned16(q) || !aligned16(k) || !aligned16(v_t))
+    return fail(FTX_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (!all_device({qkv, b_qkv, q, k, v_t})) return fail(FTX_ERR_INVALID_ARG, "pointers must be device memory");
+  hipError_t err = launch_bias_qkv_split(dtype, B, S, n, d, qkv, b_qkv, q, k, v_t, (hipStream_t)stream);
+  return err == hipSuccess ? FTX_OK : hip_fail(err, "bias qkv split launch");
+}
+
+ftx_status ftx_step_attention(ftx_dtype dtype, int B, int S, int n, int d, const void* q,
+                              const void* k, const void* v_t, const int32_t* seq_lens, void* ctx,
+                              void* stream) {
+  g_last_error.clear();
+  if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
+  ftx_status st = check_shape(B, S, n, d);
+  if (st != FTX_OK) return st;
+  if (!q || !k || !v_t || !ctx) return fail(FTX_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v_t) || !aligned16(ctx))
+    return fail(FTX_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (!all_device({q, k, v_t, seq_lens, ctx})) return fail(FTX_ERR_INVALID_ARG, "pointers must be device memory");
+  hipError_t err = launch_attention(dtype, B, S, n, d, q, k, v_t, seq_lens, ctx, (hipStream_t)stream);
+  return err == hipSuccess ? FTX_OK : hip_fail(err, "attention launch");
+}
+
+ftx_status ftx_step_bias_residual_layernorm(ftx_dtype dtype, int rows, int cols, const void* x,
+                                            const void* a, const void* bias, const void* gamma,
+                                            const void* beta, void* y, void* stream) {
+  g_last_error.clear();
+  if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
+  if (rows < 1 || cols < 4 || cols % 4) return fail(FTX_ERR_INVALID_ARG, "need rows >= 1, cols a positive multiple of 4");
+  if (cols > kMaxLayerNormCols) return fail(FTX_ERR_UNSUPPORTED, "cols above 4096");
+  if ((long long)rows * cols >= (1LL << 31)) return fail(FTX_ERR_UNSUPPORTED, "tensor above 2^31 elements");
+  if (!x || !a || !bias || !gamma || !beta || !y) return fail(FTX_ERR_INVALID_ARG, "NULL pointer");
+  const size_t align = dtype_size(dtype) * 4;  // 4-element vector accesses
+  for (const void* p : {x, a, bias, gamma, beta, (const void*)y})
+    if ((uintptr_t)p % align) return fail(FTX_ERR_INVALID_ARG, "pointers must be aligned to 4 elements");
+  if (!all_device({x, a, bias, gamma, beta, y})) return fail(FTX_ERR_INVALID_ARG, "pointers must be device memory");
+  hipError_t err = launch_bias_residual_layernorm(dtype, rows, cols, x, a, bias, gamma, beta, y, (hipStream_t)stream);
+  return err == hipSuccess ? FTX_OK : hip_fail(err, "layernorm launch");
+}
+
+ftx_status ftx_step_bias_gelu(ftx_dtype dtype, int rows, int cols, const void* u, const void* bias,
+                              void* g, void* stream) {
+  g_last_error.clear();
+  if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
+  if (rows < 1 || cols < 8 || cols % 8) return fail(FTX_ERR_INVALID_ARG, "need rows >= 1, cols a positive multiple of 8");
+  if ((long long)rows * cols >= (1LL << 31)) return fail(FTX_ERR_UNSUPPORTED, "tensor above 2^31 elements");
+  if (!u || !bias || !g) return fail(FTX_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(u) || !aligned16(bias) || !aligned16(g)) return fail(FTX_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (!all_device({u, bias, g})) return fail(FTX_ERR_INVALID_ARG, "pointers must be device memory");
+  hipError_t err = launch_bias_gelu(dtype, rows, cols, u, bias, g, (hipStream_t)stream);
+  return err == hipSuccess ? FTX_OK : hip_fail(err, "bias gelu launch");
+}
+
+ftx_status ftx_step_transpose(ftx_dtype dtype, int rows, int cols, const void* in, void* out,
+                              void* stream) {
+  g_last_error.clear();
+  if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
+  if (rows < 1 || cols < 1) return fail(FTX_ERR_INVALID_ARG, "need rows, cols >= 1");
+  if ((long long)rows * cols >= (1LL << 31)) return fail(FTX_ERR_UNSUPPORTED, "tensor above 2^31 elements");
+  if (!in || !out) return fail(FTX_ERR_INVALID_ARG, "NULL pointer");
+  const size_t bytes = (size_t)rows * cols * dtype_size(dtype);
+  if (overlap(in, bytes, out, bytes)) return fail(FTX_ERR_INVALID_ARG, "output overlaps input");
+  if (!all_device({in, out})) return fail(FTX_ERR_INVALID_ARG, "pointers must be device memory");
+  hipError_t err = launch_transpose(dtype, rows, cols, in, out, (hipStream_t)stream);
+  return err == hipSuccess ? FTX_OK : hip_fail(err, "transpose launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// Host-side launchers of the ftx kernels.  Arguments are validated by the C entry points
+// before these are called; each launcher enqueues one kernel and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "ftx.h"
+
+namespace ftx {
+
+hipError_t launch_linear(ftx_dtype dt, int M, int N, int K, const void* a, const void* w_t,
+                         const void* bias, bool gelu, void* c, hipStream_t s);
+
+hipError_t launch_qkv_projection(ftx_dtype dt, int B, int S, int nh, int d, const void* x,
+                                 const void* w_qkv_t, const void* b_qkv, void* q, void* k,
+                                 void* vt, hipStream_t s);
+
+hipError_t launch_bias_qkv_split(ftx_dtype dt, int B, int S, int nh, int d, const void* qkv,
+                                 const void* b_qkv, void* q, void* k, void* vt, hipStream_t s);
+
+hipError_t launch_attention(ftx_dtype dt, int B, int S, int nh, int d, const void* q,
+                            const void* k, const void* vt, const int32_t* lens, void* ctx,
+                            hipStream_t s);
+
+hipError_t launch_bias_residual_layernorm(ftx_dtype dt, int rows, int cols, const void* x,
+                                          const void* a, const void* bias, const void* gamma,
+                                          const void* beta, void* y, hipStream_t s);
+
+hipError_t launch_bias_gelu(ftx_dtype dt, int rows, int cols, const void* u, const void* bias,
+                            void* g, hipStream_t s);
+
+hipError_t launch_transpose(ftx_dtype dt, int rows, int cols, const void* in, void* out,
+                            hipStream_t s);
+
+// Largest LayerNorm row this build handles (4-element vectors, <= 16 per lane of a wave).
+constexpr int kMaxLayerNormCols = 4096;
+
+}  // namespace ftx
