@@ -39,6 +39,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-kernel-times", action="store_true")
+    p.add_argument("--copy-calib-mb", type=int, default=0,
+                   help="before the forwards, run a plain device copy kernel (torch.neg, fp16) over "
+                        "this many MiB three times, so a counter run also sees a kernel of known traffic")
     return p.parse_args()
 
 
@@ -134,6 +137,16 @@ def main():
     lens = None if case.lens is None else torch.from_numpy(case.lens).to(dev)
     out = torch.empty_like(x)
     stream = torch.cuda.current_stream()
+
+    if args.copy_calib_mb > 0:
+        n = args.copy_calib_mb * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)  # reads and writes exactly n * 2 bytes
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         enc.forward(x, lens, out)

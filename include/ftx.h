@@ -22,7 +22,11 @@
  *
  * Precision.  FTX_FP32: fp32 storage and arithmetic.  FTX_FP16 / FTX_BF16: storage in the
  * 16-bit format, every matrix product accumulated in fp32, softmax and LayerNorm
- * statistics in fp32; activations between kernels are stored in the 16-bit format.
+ * statistics in fp32; activations between kernels are stored in the 16-bit format, except
+ * that FTX_BF16 keeps what enters a LayerNorm un-normalised in fp32 -- the residual Y1 (the
+ * first LayerNorm's output, added back before the second) and the attention-output and
+ * FFN-output projections -- because bf16's rounding of those (up to 7.8e-3 at |v| in
+ * [2, 4)) reaches the layer output almost unattenuated.
  *
  * Conventions.
  *  - All tensors are row-major.  All tensor pointers are DEVICE pointers on the device
@@ -81,7 +85,7 @@ typedef struct {
  * Non-positive values, an unknown dtype or out == NULL -> FTX_ERR_INVALID_ARG (no HIP call
  * is made).  Positive values outside the supported set -> FTX_ERR_UNSUPPORTED.
  * Allocates the workspace and the weight storage on the current device (hipMalloc):
- * about (10 B S H + L (12 H^2 + 13 H)) elements. */
+ * about (10 B S H + L (12 H^2 + 13 H)) elements (plus 2 B S H fp32 values for FTX_BF16). */
 ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int size_per_head,
                               int num_layers, ftx_dtype dtype, ftx_encoder **out);
 

@@ -3,11 +3,11 @@
 Bars (max over all B x S x H outputs):
 * fp32: |gpu - oracle| / max(|oracle|, 1) <= 1e-4;
 * fp16: |gpu - oracle| <= 1e-2 per layer and <= 5e-2 after the whole stack;
-* bf16: |gpu - oracle| <= 1e-2 + 2^-7 |oracle| per layer and <= 5e-2 + 2^-7 |oracle| per
+* bf16: |gpu - oracle| <= 1e-2 + 2^-8 |oracle| per layer and <= 5e-2 + 2^-8 |oracle| per
   stack.  The bare 1e-2 is below bf16's own rounding of outputs |y| >= 4 (half an ulp
-  there is 2^-8 * 4 = 1.6e-2); two relative rounding units 2 * 2^-8 are added: the
-  output's rounding and that of the residual Y1, which the 16-bit mode stores in bf16 and
-  the second LayerNorm passes to the output with gain ~1.
+  there is 2^-9 * 4 = 7.8e-3, one ulp 1.6e-2), so one ulp of the output, 2^-8 |oracle|, is
+  added.  (The library keeps the residual Y1 in fp32 in bf16 mode; with Y1 stored in bf16
+  an exact fp64 model of the storage roundings already exceeds this bar.)
 Per layer means: a one-layer handle fed the oracle's previous-layer output rounded to the
 storage format, compared with the oracle's layer on that same input.
 """
@@ -35,11 +35,11 @@ def _gpu(request):
 
 
 def layer_tol(dtype):
-    return {"fp32": (0.0, 0.0), "fp16": (1e-2, 0.0), "bf16": (1e-2, 2.0 ** -7)}[dtype]
+    return {"fp32": (0.0, 0.0), "fp16": (1e-2, 0.0), "bf16": (1e-2, 2.0 ** -8)}[dtype]
 
 
 def stack_tol(dtype):
-    return {"fp32": (0.0, 0.0), "fp16": (5e-2, 0.0), "bf16": (5e-2, 2.0 ** -7)}[dtype]
+    return {"fp32": (0.0, 0.0), "fp16": (5e-2, 0.0), "bf16": (5e-2, 2.0 ** -8)}[dtype]
 
 
 def check(g, o, dtype, tol, what):

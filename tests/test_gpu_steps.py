@@ -60,6 +60,9 @@ LINEAR_SHAPES = [
     (257, 136, 200),     # ragged, several 64x64 tiles
     (1024, 768, 768),    # 128x128 tiles
     (2048, 3072, 768),   # FFN-in shape family
+    (4096, 2312, 768),   # 256x192 tiles with a ragged N tail
+    (16416, 768, 768),   # 256x128 tiles with a ragged M tail
+    (16384, 3072, 768),  # 256x256 tiles (BERT-base FFN-in at batch 512)
 ]
 
 
@@ -85,7 +88,8 @@ def test_linear(dtype, M, N, K, epi):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("B,S,n,d", [(1, 32, 4, 32), (2, 64, 3, 64), (3, 128, 2, 32), (1, 512, 2, 64)])
+@pytest.mark.parametrize("B,S,n,d", [(1, 32, 4, 32), (2, 64, 3, 64), (3, 128, 2, 32), (1, 512, 2, 64),
+                                     (64, 128, 12, 64)])
 def test_qkv_projection(dtype, B, S, n, d):
     H = n * d
     rng = np.random.default_rng(B + S + n + d)

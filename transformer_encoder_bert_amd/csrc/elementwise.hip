@@ -19,14 +19,18 @@ namespace ftx {
 // z = x + a + bias.  LPR lanes own one row; each lane holds MAXV 4-element vectors,
 // vector v of a lane sits at column 4 * (v * LPR + sub) so that a wave's loads of one v
 // are contiguous.  EXACT: every lane owns exactly MAXV vectors (cols == 4 * LPR * MAXV).
-template <typename T, int LPR, int MAXV, bool EXACT>
-__global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
-                                                        const T* __restrict__ a,
+// TX and TA are the types of the residual x and the branch a (T, or float when the
+// residual stream is kept in fp32); yf, when non-null, receives an fp32 copy of y.
+template <typename T, typename TX, typename TA, int LPR, int MAXV, bool EXACT>
+__global__ __launch_bounds__(256) void layernorm_kernel(const TX* __restrict__ x,
+                                                        const TA* __restrict__ a,
                                                         const T* __restrict__ bias,
                                                         const T* __restrict__ gamma,
                                                         const T* __restrict__ beta,
-                                                        T* y, int rows, int cols) {
+                                                        T* y, float* yf, int rows, int cols) {
   typedef typename VecT<T, 4>::type v4;
+  typedef typename VecT<TX, 4>::type x4;
+  typedef typename VecT<TA, 4>::type a4;
   constexpr int RPW = kWave / LPR;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int row = (blockIdx.x * (blockDim.x / kWave) + wave) * RPW + lane / LPR;
@@ -41,8 +45,8 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
   for (int v = 0; v < MAXV; ++v) {
     const int vi = v * LPR + sub;
     if (EXACT || vi < nvec) {
-      const v4 xv = *(const v4*)(x + base + 4 * vi);
-      const v4 av = *(const v4*)(a + base + 4 * vi);
+      const x4 xv = *(const x4*)(x + base + 4 * vi);
+      const a4 av = *(const a4*)(a + base + 4 * vi);
       const v4 bv = *(const v4*)(bias + 4 * vi);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -73,48 +77,73 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
     if (EXACT || vi < nvec) {
       const v4 gv = *(const v4*)(gamma + 4 * vi);
       const v4 btv = *(const v4*)(beta + 4 * vi);
+      f32x4 of;
       v4 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(to_f32(gv[e]) * ((z[v][e] - mean) * rs) + to_f32(btv[e]));
+      for (int e = 0; e < 4; ++e) {
+        of[e] = to_f32(gv[e]) * ((z[v][e] - mean) * rs) + to_f32(btv[e]);
+        o[e] = from_f32<T>(of[e]);
+      }
       *(v4*)(y + base + 4 * vi) = o;
+      if (yf) *(f32x4*)(yf + base + 4 * vi) = of;
     }
   }
 }
 
-template <typename T, int LPR, int MAXV, bool EXACT>
+template <typename T, typename TX, typename TA, int LPR, int MAXV, bool EXACT>
 static hipError_t ln_launch(int rows, int cols, const void* x, const void* a, const void* bias,
-                            const void* gamma, const void* beta, void* y, hipStream_t s) {
+                            const void* gamma, const void* beta, void* y, float* yf,
+                            hipStream_t s) {
   constexpr int rows_per_block = (256 / kWave) * (kWave / LPR);
   const int grid = (rows + rows_per_block - 1) / rows_per_block;
-  layernorm_kernel<T, LPR, MAXV, EXACT><<<grid, 256, 0, s>>>(
-      (const T*)x, (const T*)a, (const T*)bias, (const T*)gamma, (const T*)beta, (T*)y, rows, cols);
+  layernorm_kernel<T, TX, TA, LPR, MAXV, EXACT><<<grid, 256, 0, s>>>(
+      (const TX*)x, (const TA*)a, (const T*)bias, (const T*)gamma, (const T*)beta, (T*)y, yf,
+      rows, cols);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, typename TX, typename TA>
 static hipError_t ln_dispatch(int rows, int cols, const void* x, const void* a, const void* bias,
-                              const void* gamma, const void* beta, void* y, hipStream_t s) {
+                              const void* gamma, const void* beta, void* y, float* yf,
+                              hipStream_t s) {
   switch (cols) {  // exact register tilings for the common hidden sizes
-    case 128: return ln_launch<T, 32, 1, true>(rows, cols, x, a, bias, gamma, beta, y, s);
-    case 256: return ln_launch<T, 64, 1, true>(rows, cols, x, a, bias, gamma, beta, y, s);
-    case 384: return ln_launch<T, 32, 3, true>(rows, cols, x, a, bias, gamma, beta, y, s);
-    case 512: return ln_launch<T, 64, 2, true>(rows, cols, x, a, bias, gamma, beta, y, s);
-    case 768: return ln_launch<T, 64, 3, true>(rows, cols, x, a, bias, gamma, beta, y, s);
-    case 1024: return ln_launch<T, 64, 4, true>(rows, cols, x, a, bias, gamma, beta, y, s);
+    case 128: return ln_launch<T, TX, TA, 32, 1, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+    case 256: return ln_launch<T, TX, TA, 64, 1, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+    case 384: return ln_launch<T, TX, TA, 32, 3, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+    case 512: return ln_launch<T, TX, TA, 64, 2, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+    case 768: return ln_launch<T, TX, TA, 64, 3, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+    case 1024: return ln_launch<T, TX, TA, 64, 4, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
     default: break;
   }
   if (cols <= 4 * 16 * 4)  // small rows: a quarter wave per row
-    return ln_launch<T, 16, 4, false>(rows, cols, x, a, bias, gamma, beta, y, s);
-  return ln_launch<T, 64, 16, false>(rows, cols, x, a, bias, gamma, beta, y, s);
+    return ln_launch<T, TX, TA, 16, 4, false>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+  return ln_launch<T, TX, TA, 64, 16, false>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
 }
 
 hipError_t launch_bias_residual_layernorm(ftx_dtype dt, int rows, int cols, const void* x,
                                           const void* a, const void* bias, const void* gamma,
                                           const void* beta, void* y, hipStream_t s) {
   switch (dt) {
-    case FTX_FP32: return ln_dispatch<float>(rows, cols, x, a, bias, gamma, beta, y, s);
-    case FTX_FP16: return ln_dispatch<f16>(rows, cols, x, a, bias, gamma, beta, y, s);
-    case FTX_BF16: return ln_dispatch<bf16>(rows, cols, x, a, bias, gamma, beta, y, s);
+    case FTX_FP32: return ln_dispatch<float, float, float>(rows, cols, x, a, bias, gamma, beta, y, nullptr, s);
+    case FTX_FP16: return ln_dispatch<f16, f16, f16>(rows, cols, x, a, bias, gamma, beta, y, nullptr, s);
+    case FTX_BF16: return ln_dispatch<bf16, bf16, bf16>(rows, cols, x, a, bias, gamma, beta, y, nullptr, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bias_residual_layernorm_f32res(ftx_dtype dt, int rows, int cols,
+                                                 const void* x, bool x_f32, const float* a,
+                                                 const void* bias, const void* gamma,
+                                                 const void* beta, void* y, float* yf,
+                                                 hipStream_t s) {
+  switch (dt) {
+    case FTX_FP32: return hipErrorInvalidValue;  // fp32 mode has no separate residual copy
+    case FTX_FP16:
+      return x_f32 ? ln_dispatch<f16, float, float>(rows, cols, x, a, bias, gamma, beta, y, yf, s)
+                   : ln_dispatch<f16, f16, float>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+    case FTX_BF16:
+      return x_f32 ? ln_dispatch<bf16, float, float>(rows, cols, x, a, bias, gamma, beta, y, yf, s)
+                   : ln_dispatch<bf16, bf16, float>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
   }
   return hipErrorInvalidValue;
 }

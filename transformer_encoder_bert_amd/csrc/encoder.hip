@@ -110,6 +110,7 @@ struct ftx_encoder {
   std::vector<char> ready;
   // workspace views
   void *q, *k, *vt, *ctx, *abuf, *y1, *u;
+  float* y1f = nullptr;  // fp32 copy of Y1, the residual of the second LayerNorm (bf16 only)
   int fused = 1;
   int timing = 0;
   struct Mark {
@@ -212,7 +213,13 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
     return hip_fail(err, "hipMalloc(weights)");
   }
   const size_t TH = pad(T * H * es);
-  const size_t ws_bytes = 3 * TH /*q,k,vt*/ + TH /*ctx*/ + TH /*abuf*/ + TH /*y1*/ + pad(T * F * es) /*u*/;
+  // bf16 keeps what enters a LayerNorm un-normalised in fp32: the residual Y1 and the two
+  // projection outputs added to a residual (C Wo, G W2).  Half an ulp of bf16 at |v| in
+  // [2, 4) is 7.8e-3, and the LayerNorms pass such errors to the output with gain ~gamma.
+  const bool f32res = dtype == FTX_BF16;
+  const size_t TA = f32res ? pad(T * H * 4) : TH;  // abuf
+  const size_t ws_bytes = 3 * TH /*q,k,vt*/ + TH /*ctx*/ + TA /*abuf*/ + TH /*y1*/ +
+                          pad(T * F * es) /*u*/ + (f32res ? pad(T * H * 4) : 0) /*y1f*/;
   err = hipMalloc(&e->ws, ws_bytes);
   if (err != hipSuccess) {
     hipFree(e->weights);
@@ -243,9 +250,10 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
   e->k = p; p += TH;
   e->vt = p; p += TH;
   e->ctx = p; p += TH;
-  e->abuf = p; p += TH;
+  e->abuf = p; p += TA;
   e->y1 = p; p += TH;
-  e->u = p;
+  e->u = p; p += pad(T * F * es);
+  if (f32res) e->y1f = (float*)p;
   *out = e;
   return FTX_OK;
 }
@@ -329,10 +337,13 @@ ftx_status ftx_forward(ftx_encoder* e, const void* input, const int32_t* seq_len
     });
     if (st != FTX_OK) return st;
     st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
-      return launch_linear(dt, T, H, H, e->ctx, w.w_o_t, nullptr, false, e->abuf, s);
+      return launch_linear(dt, T, H, H, e->ctx, w.w_o_t, nullptr, false, e->abuf, s, e->y1f != nullptr);
     });
     if (st != FTX_OK) return st;
     st = run_step(e, FTX_STEP_LN1, s, [&] {
+      if (e->y1f)
+        return launch_bias_residual_layernorm_f32res(dt, T, H, x, false, (const float*)e->abuf, w.b_o, w.ln1_g,
+                                                     w.ln1_b, e->y1, e->y1f, s);
       return launch_bias_residual_layernorm(dt, T, H, x, e->abuf, w.b_o, w.ln1_g, w.ln1_b, e->y1, s);
     });
     if (st != FTX_OK) return st;
@@ -351,10 +362,13 @@ ftx_status ftx_forward(ftx_encoder* e, const void* input, const int32_t* seq_len
     }
     if (st != FTX_OK) return st;
     st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
-      return launch_linear(dt, T, H, F, e->u, w.w2_t, nullptr, false, e->abuf, s);
+      return launch_linear(dt, T, H, F, e->u, w.w2_t, nullptr, false, e->abuf, s, e->y1f != nullptr);
     });
     if (st != FTX_OK) return st;
     st = run_step(e, FTX_STEP_LN2, s, [&] {
+      if (e->y1f)
+        return launch_bias_residual_layernorm_f32res(dt, T, H, e->y1f, true, (const float*)e->abuf, w.b2,
+                                                     w.ln2_g, w.ln2_b, output, nullptr, s);
       return launch_bias_residual_layernorm(dt, T, H, e->y1, e->abuf, w.b2, w.ln2_g, w.ln2_b, output, s);
     });
     if (st != FTX_OK) return st;

@@ -7,17 +7,21 @@
 //   C[M][N] = A[M][K] * W[K][N], W held transposed (Wt[N][K], K contiguous) so both
 //   operands are read along K with 16-byte loads;
 //   v_mfma_f32_32x32x16_{f16,bf16} (fp32 accumulate) or v_mfma_f32_32x32x2f32 for fp32;
-//   a block tile BM x BN staged through double-buffered, padded LDS, waves WM x WN each
+//   a block tile BM x BN staged through double-buffered, row-padded LDS (the next K slab
+//   is fetched into registers while the current one is multiplied), waves WM x WN each
 //   owning a (BM/WM) x (BN/WN) sub-tile of 32x32 accumulators;
 //   the bias, the tanh GELU and the Q/K/V head split are applied in the epilogue on the
 //   fp32 accumulators, so U never makes a round trip through memory before its GELU.
 //
 // MFMA operand layout used (32x32 output tile, 64 lanes, g = lane / 32):
-//   A fragment: lane holds row (lane % 32), VEC consecutive K values at K-offset g * VEC;
-//   B fragment: lane holds column (lane % 32), the same K offsets;
+//   first operand: lane holds row (lane % 32), VEC consecutive K values at K-offset g * VEC;
+//   second operand: lane holds column (lane % 32), the same K offsets;
 //   accumulator register r of a lane holds row 8*(r/4) + 4*g + (r%4), column lane % 32.
-// The K order inside a fragment only has to agree between A and B, which it does by
-// construction (both load K-contiguous runs at the same offsets).
+// The K order inside a fragment only has to agree between the operands, which it does by
+// construction (both load K-contiguous runs at the same offsets).  The waves compute C^T
+// tiles -- the weight fragment is the first operand, the activation fragment the second --
+// so the four consecutive accumulator rows a lane holds are four consecutive columns n of
+// one output row m; the epilogue regroups them through LDS into 16-byte row vectors.
 
 #include "device_common.h"
 #include "launch.h"
@@ -55,65 +59,121 @@ template <> struct Mfma<float> {
 };
 
 // ------------------------------------------------------------------------------- epilogues
-// apply(row0, col, g, acc, M, N): acc is the 32x32 accumulator tile whose first row is
-// row0 and whose column for this lane is col.
+// After the K loop every wave holds C^T tiles of 32x32 fp32 accumulators: register r of a
+// lane holds column nt + 8 (r / 4) + 4 g + r % 4 of output row m = mt + lane % 32.  The
+// epilogue object supplies
+//   bias4(n)             the bias of columns n .. n+3 (read before the K loop, so its
+//                        latency hides behind the matrix multiply; zeros if there is none);
+//   act(v)               the element-wise work after the bias (GELU or nothing);
+//   transposed(nt)       whether the tile of columns nt .. nt+31 is stored column-major;
+//   store(m, n, v)       a 16-byte vector of consecutive columns n.. of row m;
+//   store_t(n, m, v)     a 16-byte vector of consecutive rows m.. of column n;
+// and the kernel stages each tile through LDS (converted to the output type) so that both
+// kinds of store are 16 bytes per lane, 64 contiguous bytes per row.  N is a multiple of 8,
+// M of the QKV projection a multiple of 32, so no vector straddles the end of a row.
 
-template <typename T, bool GELU> struct EpiLinear {
-  T* c;
+// tanh-form GELU as u * sigmoid(2 y), y = sqrt(2/pi) (u + 0.044715 u^3) (the cube written
+// u*u*u), with one exp and the hardware reciprocal instead of a divide; large negative u
+// gives exp -> inf, rcp -> 0 and a result of -0.
+__device__ __forceinline__ float gelu_fast(float u) {
+  const float y = 0.7978845608028654f * (u + 0.044715f * u * u * u);
+  return u * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * y));
+}
+
+template <typename T, bool GELU, typename TO = T> struct EpiLinear {
+  typedef TO out_t;
+  typedef typename Vec16<TO>::type vec;
+  typedef typename VecT<T, 4>::type b4;
+  TO* c;
   const T* bias;  // may be null
-  __device__ __forceinline__ void apply(int row0, int col, int g, const f32x16& acc, int M,
-                                        int N) const {
-    if (col >= N) return;
-    const float bv = bias ? to_f32(bias[col]) : 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = row0 + 8 * (r / 4) + 4 * g + (r % 4);
-      if (row < M) {
-        float v = acc[r] + bv;
-        if (GELU) v = gelu_tanh(v);
-        c[(size_t)row * N + col] = from_f32<T>(v);
-      }
-    }
+  int M, N;
+  __device__ __forceinline__ b4 bias4(int n) const {
+    b4 v = {};
+    if (bias && n < N) v = *(const b4*)(bias + n);
+    return v;
   }
+  __device__ __forceinline__ float act(float v) const { return GELU ? gelu_fast(v) : v; }
+  __device__ __forceinline__ bool transposed(int) const { return false; }
+  __device__ __forceinline__ void store(int m, int n, const vec& v) const {
+    if (m < M && n < N) *(vec*)(c + (size_t)m * N + n) = v;
+  }
+  __device__ __forceinline__ void store_t(int, int, const vec&) const {}
 };
 
-// bias + head split: column col of [Q|K|V] -> (which, head, dd); rows of one 32-row tile
-// belong to one sequence because S is a multiple of 32.
+// bias + head split: a 32-column tile lies inside one of Q, K, V and inside one head (d is
+// 32 or 64 and H a multiple of 32); row m is token s = m % S of sequence b = m / S.
+// Q and K are written [B][n][S][d]; V transposed per head, [B][n][d][S], from tiles staged
+// column-major (32 consecutive tokens of one feature; S is a multiple of 32).
 template <typename T> struct EpiQKV {
+  typedef T out_t;
+  typedef typename Vec16<T>::type vec;
+  typedef typename VecT<T, 4>::type b4;
   T* q;
   T* k;
   T* vt;
   const T* bias;
-  int S, nh, d;
-  __device__ __forceinline__ void apply(int row0, int col, int g, const f32x16& acc, int M,
-                                        int N) const {
-    if (col >= N || row0 >= M) return;
+  int S, nh, d, M, N;
+  __device__ __forceinline__ b4 bias4(int n) const {
+    b4 v = {};
+    if (n < N) v = *(const b4*)(bias + n);
+    return v;
+  }
+  __device__ __forceinline__ float act(float v) const { return v; }
+  __device__ __forceinline__ bool transposed(int nt) const { return nt >= 2 * nh * d; }
+  __device__ __forceinline__ void store(int m, int n, const vec& v) const {
+    if (m >= M || n >= N) return;
     const int H = nh * d;
-    const int which = col / H;
-    const int rem = col - which * H;
-    const int h = rem / d;
-    const int dd = rem - h * d;
-    const int b = row0 / S;
-    const int s0 = row0 - b * S;
-    const size_t head = (size_t)b * nh + h;
-    const float bv = to_f32(bias[col]);
-    if (which < 2) {
-      T* dst = (which == 0 ? q : k) + (head * S + s0) * d + dd;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dst[(size_t)(8 * (r / 4) + 4 * g + (r % 4)) * d] = from_f32<T>(acc[r] + bv);
-    } else {
-      typedef typename VecT<T, 4>::type v4;
-      T* dst = vt + (head * d + dd) * S + s0;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        v4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(acc[4 * rr + e] + bv);
-        *(v4*)(dst + 8 * rr + 4 * g) = o;
-      }
-    }
+    const int which = n / H, rem = n - which * H;
+    const int h = rem / d, dd = rem - h * d;
+    const int b = m / S, s = m - b * S;
+    *(vec*)((which == 0 ? q : k) + (((size_t)b * nh + h) * S + s) * d + dd) = v;
+  }
+  __device__ __forceinline__ void store_t(int n, int m, const vec& v) const {
+    if (m >= M || n >= N) return;
+    const int rem = n - 2 * nh * d;
+    const int h = rem / d, dd = rem - h * d;
+    const int b = m / S, s = m - b * S;
+    *(vec*)(vt + (((size_t)b * nh + h) * d + dd) * S + s) = v;
   }
 };
+
+// Stage one C^T tile (columns nt.., rows mt..) through this wave's LDS scratch `ws`
+// (32 x (32 + pad) elements of the output type) and hand it to the epilogue as 16-byte
+// vectors.  Wave-private: LDS accesses of one wave complete in order.
+template <typename Epi>
+__device__ __forceinline__ void epilogue_tile(const Epi& epi, typename Epi::out_t* ws, int mt,
+                                              int nt, int lane, const f32x16& acc,
+                                              const typename Epi::b4 (&bq)[4]) {
+  typedef typename Epi::out_t TO;
+  typedef typename Epi::vec vec;
+  constexpr int EV = 16 / sizeof(TO);       // elements per 16-byte vector
+  constexpr int LDW = 32 + EV;              // padded LDS row
+  constexpr int CPR = 32 / EV;              // vectors per 32-element row
+  constexpr int RPP = kWave / CPR;          // rows per pass
+  const int lr = lane % 32, g = lane / 32;
+  const bool tr = epi.transposed(nt);
+  typedef typename VecT<TO, 4>::type t4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int nl = 8 * q + 4 * g;           // local column of register 4q
+    t4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = from_f32<TO>(epi.act(acc[4 * q + e] + to_f32(bq[q][e])));
+    if (tr) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ws[(nl + e) * LDW + lr] = o[e];  // LDS rows run along m
+    } else {
+      *(t4*)(ws + lr * LDW + nl) = o;
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 32 / RPP; ++p) {
+    const int row = p * RPP + lane / CPR, c = (lane % CPR) * EV;
+    const vec v = *(const vec*)(ws + row * LDW + c);
+    if (tr) epi.store_t(nt + row, mt + c, v);
+    else epi.store(mt + row, nt + c, v);
+  }
+}
 
 // ---------------------------------------------------------------------------------- kernel
 
@@ -129,7 +189,7 @@ template <typename T, int BM, int BN, int WM, int WN> struct GemmCfg {
   static constexpr int A_CH = BM * CPR / NT;
   static constexpr int B_CH = BN * CPR / NT;
   static constexpr int STAGE = (BM + BN) * LDS_STRIDE;  // elements per LDS buffer
-  static_assert(TM >= 1 && TN >= 1, "wave tile below 32x32");
+  static_assert(TM >= 1 && TN >= 1 && TM * WM * 32 == BM && TN * WN * 32 == BN, "wave tiling");
   static_assert(A_CH * NT == BM * CPR && B_CH * NT == BN * CPR, "tile not divisible");
 };
 
@@ -169,13 +229,20 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane % 32, g = lane / 32;
 
-  f32x16 acc[C::TM][C::TN];
+  f32x16 acc[C::TN][C::TM];
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i)
+  for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j)
+    for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
+
+  // this lane's bias vectors for its columns nt + 8 q + 4 g of each of its column tiles
+  typename Epi::b4 bq[C::TN][4];
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bq[j][q] = epi.bias4(n0 + (wn * C::TN + j) * 32 + 8 * q + 4 * g);
 
   frag ra[C::A_CH], rb[C::B_CH];
   const frag zero = {};
@@ -228,31 +295,65 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) b[j] = *(const frag*)(Bs + j * 32 * C::LDS_STRIDE + kk);
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i)
+      for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j) MF::mma(a[i], b[j], acc[i][j]);
+        for (int i = 0; i < C::TM; ++i) MF::mma(b[j], a[i], acc[j][i]);
     }
     if (kt + 1 < nk) sstore(cur ^ 1);
     __syncthreads();
   }
 
+  // the K loop ended with a barrier, so the LDS is free: each wave stages its tiles in its
+  // own slice of it
+  typedef typename Epi::out_t TO;
+  constexpr int SCRATCH = 32 * (32 + 16 / sizeof(TO));  // elements of TO per wave
+  static_assert(SCRATCH * sizeof(TO) * (C::NT / kWave) <= sizeof(smem), "epilogue scratch");
+  TO* ws = (TO*)smem + wave * SCRATCH;
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i)
+  for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j)
-      epi.apply(m0 + (wm * C::TM + i) * 32, n0 + (wn * C::TN + j) * 32 + lr, g, acc[i][j], M, N);
+    for (int i = 0; i < C::TM; ++i)
+      epilogue_tile(epi, ws, m0 + (wm * C::TM + i) * 32, n0 + (wn * C::TN + j) * 32, lane, acc[j][i],
+                    bq[j]);
 }
 
 // --------------------------------------------------------------------------- tile choice
+// The launch configuration is chosen per shape (the article tunes grid and block sizes to
+// the number of input rows, which ranges from tens at batch 1 to thousands at batch in the
+// hundreds).  Candidates, with the fraction of MFMA peak a full CU reaches in each
+// (measured on the BERT-base projections at 16384 rows), and how many blocks share a CU:
+//   256x256, 8 waves (4 x 2), 147 KB LDS: 0.34, 1 block per CU
+//   256x192, 8 waves (4 x 2), 129 KB LDS: 0.33, 1 block per CU
+//   256x128, 8 waves (4 x 2), 111 KB LDS: 0.30, 1 block per CU
+//   128x128, 4 waves (2 x 2),  74 KB LDS: 0.25, 2 blocks per CU
+//    64x64,  4 waves (2 x 2),  37 KB LDS: 0.12, 4 blocks per CU
+//    32x32,  1 wave,           18 KB LDS: 0.05, 8 blocks per CU
+// The modelled time of a launch is (rounds of blocks over the 256 CUs) x (one block's
+// time); the candidate with the least modelled time wins, so small batches get small
+// tiles that still spread over every CU.  fp32 (twice the register footprint per element)
+// uses the table without its two largest tiles.
 
-enum TileCfg { TILE_128x128 = 0, TILE_64x64 = 1, TILE_32x32 = 2 };
+enum TileCfg { TILE_256x256, TILE_256x192, TILE_256x128, TILE_128x128, TILE_64x64, TILE_32x32, TILE_COUNT };
 
-static TileCfg choose_tile(int M, int N) {
-  const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
-  if (t128 >= 512) return TILE_128x128;
-  const long t64 = (long)((M + 63) / 64) * ((N + 63) / 64);
-  if (t64 >= 256) return TILE_64x64;
-  return TILE_32x32;
+static TileCfg choose_tile(int M, int N, bool wide) {
+  struct Cand { int bm, bn, per_cu; double eff; };
+  static const Cand cand[TILE_COUNT] = {{256, 256, 1, 0.34}, {256, 192, 1, 0.33}, {256, 128, 1, 0.30},
+                                        {128, 128, 2, 0.25}, {64, 64, 4, 0.12},   {32, 32, 8, 0.05}};
+  constexpr int kCUs = 256;
+  int best = TILE_32x32;
+  double best_t = 1e300;
+  for (int c = wide ? 0 : TILE_256x128; c < TILE_COUNT; ++c) {
+    const Cand& x = cand[c];
+    const long tiles = (long)((M + x.bm - 1) / x.bm) * ((N + x.bn - 1) / x.bn);
+    const long rounds = (tiles + (long)kCUs * x.per_cu - 1) / ((long)kCUs * x.per_cu);
+    // a block's time: its tile's work at its efficiency, shared with the other blocks on the CU
+    const double t = (double)rounds * x.bm * x.bn * x.per_cu / x.eff;
+    if (t < best_t * 0.999) {
+      best_t = t;
+      best = c;
+    }
+  }
+  return (TileCfg)best;
 }
 
 template <typename T, int BM, int BN, int WM, int WN, typename Epi>
@@ -267,27 +368,40 @@ static hipError_t gemm_launch_cfg(int M, int N, int K, const void* a, const void
 template <typename T, typename Epi>
 static hipError_t gemm_launch(int M, int N, int K, const void* a, const void* w_t, Epi epi,
                               hipStream_t s) {
-  switch (choose_tile(M, N)) {
+  constexpr bool wide = sizeof(T) == 2;
+  switch (choose_tile(M, N, wide)) {
+    case TILE_256x256:
+      if constexpr (wide) return gemm_launch_cfg<T, 256, 256, 4, 2>(M, N, K, a, w_t, epi, s);
+      break;
+    case TILE_256x192:
+      if constexpr (wide) return gemm_launch_cfg<T, 256, 192, 4, 2>(M, N, K, a, w_t, epi, s);
+      break;
+    case TILE_256x128: return gemm_launch_cfg<T, 256, 128, 4, 2>(M, N, K, a, w_t, epi, s);
     case TILE_128x128: return gemm_launch_cfg<T, 128, 128, 2, 2>(M, N, K, a, w_t, epi, s);
     case TILE_64x64: return gemm_launch_cfg<T, 64, 64, 2, 2>(M, N, K, a, w_t, epi, s);
     case TILE_32x32: return gemm_launch_cfg<T, 32, 32, 1, 1>(M, N, K, a, w_t, epi, s);
+    default: break;
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
 static hipError_t linear_t(int M, int N, int K, const void* a, const void* w_t, const void* bias,
-                           bool gelu, void* c, hipStream_t s) {
-  if (gelu) return gemm_launch<T>(M, N, K, a, w_t, EpiLinear<T, true>{(T*)c, (const T*)bias}, s);
-  return gemm_launch<T>(M, N, K, a, w_t, EpiLinear<T, false>{(T*)c, (const T*)bias}, s);
+                           bool gelu, bool out_f32, void* c, hipStream_t s) {
+  if (out_f32) {
+    if (gelu) return gemm_launch<T>(M, N, K, a, w_t, EpiLinear<T, true, float>{(float*)c, (const T*)bias, M, N}, s);
+    return gemm_launch<T>(M, N, K, a, w_t, EpiLinear<T, false, float>{(float*)c, (const T*)bias, M, N}, s);
+  }
+  if (gelu) return gemm_launch<T>(M, N, K, a, w_t, EpiLinear<T, true>{(T*)c, (const T*)bias, M, N}, s);
+  return gemm_launch<T>(M, N, K, a, w_t, EpiLinear<T, false>{(T*)c, (const T*)bias, M, N}, s);
 }
 
 hipError_t launch_linear(ftx_dtype dt, int M, int N, int K, const void* a, const void* w_t,
-                         const void* bias, bool gelu, void* c, hipStream_t s) {
+                         const void* bias, bool gelu, void* c, hipStream_t s, bool out_f32) {
   switch (dt) {
-    case FTX_FP32: return linear_t<float>(M, N, K, a, w_t, bias, gelu, c, s);
-    case FTX_FP16: return linear_t<f16>(M, N, K, a, w_t, bias, gelu, c, s);
-    case FTX_BF16: return linear_t<bf16>(M, N, K, a, w_t, bias, gelu, c, s);
+    case FTX_FP32: return linear_t<float>(M, N, K, a, w_t, bias, gelu, false, c, s);
+    case FTX_FP16: return linear_t<f16>(M, N, K, a, w_t, bias, gelu, out_f32, c, s);
+    case FTX_BF16: return linear_t<bf16>(M, N, K, a, w_t, bias, gelu, out_f32, c, s);
   }
   return hipErrorInvalidValue;
 }
@@ -296,7 +410,7 @@ template <typename T>
 static hipError_t qkv_t(int B, int S, int nh, int d, const void* x, const void* w, const void* b,
                         void* q, void* k, void* vt, hipStream_t s) {
   const int M = B * S, H = nh * d;
-  EpiQKV<T> epi{(T*)q, (T*)k, (T*)vt, (const T*)b, S, nh, d};
+  EpiQKV<T> epi{(T*)q, (T*)k, (T*)vt, (const T*)b, S, nh, d, M, 3 * H};
   return gemm_launch<T>(M, 3 * H, H, x, w, epi, s);
 }
 

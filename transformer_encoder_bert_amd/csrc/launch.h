@@ -8,8 +8,10 @@
 
 namespace ftx {
 
+// out_f32: c is written as fp32 (16-bit dtypes; ignored in fp32 mode).
 hipError_t launch_linear(ftx_dtype dt, int M, int N, int K, const void* a, const void* w_t,
-                         const void* bias, bool gelu, void* c, hipStream_t s);
+                         const void* bias, bool gelu, void* c, hipStream_t s,
+                         bool out_f32 = false);
 
 hipError_t launch_qkv_projection(ftx_dtype dt, int B, int S, int nh, int d, const void* x,
                                  const void* w_qkv_t, const void* b_qkv, void* q, void* k,
@@ -25,6 +27,15 @@ hipError_t launch_attention(ftx_dtype dt, int B, int S, int nh, int d, const voi
 hipError_t launch_bias_residual_layernorm(ftx_dtype dt, int rows, int cols, const void* x,
                                           const void* a, const void* bias, const void* gamma,
                                           const void* beta, void* y, hipStream_t s);
+
+// The same LayerNorm with an fp32 residual stream: the branch `a` is fp32, x is read as
+// fp32 when x_f32 (else in the storage type), and yf (non-null) receives y in fp32 as well
+// as y in the storage type.  16-bit dtypes only.
+hipError_t launch_bias_residual_layernorm_f32res(ftx_dtype dt, int rows, int cols,
+                                                 const void* x, bool x_f32, const float* a,
+                                                 const void* bias, const void* gamma,
+                                                 const void* beta, void* y, float* yf,
+                                                 hipStream_t s);
 
 hipError_t launch_bias_gelu(ftx_dtype dt, int rows, int cols, const void* u, const void* bias,
                             void* g, hipStream_t s);
