@@ -23,6 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "sequences/sec + TFLOPS (% MFMA peak), 12-layer BERT-base fp16, seq 32/128"
+WORKLOAD_DEFAULT = "bert_base_fp16_s32"
 PEAK_MFMA_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6, "fp32": 157.3}
 PEAK_HBM_GBS = 8000.0
 DTYPE_TAG = {"fp16": "f16", "bf16": "bf16", "fp32": "f32"}
@@ -33,7 +34,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="bert_base_fp16_s32")
+    p.add_argument("--workload", default=None, help=f"default {WORKLOAD_DEFAULT}")
     p.add_argument("--batch", type=int, default=None)
     p.add_argument("--unfused", action="store_true", help="standalone bias+split and bias+GELU kernels")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
@@ -42,6 +43,11 @@ def parse():
     p.add_argument("--copy-calib-mb", type=int, default=0,
                    help="before the forwards, run a plain device copy kernel (torch.neg, fp16) over "
                         "this many MiB three times, so a counter run also sees a kernel of known traffic")
+    p.add_argument("--summarize-rocprof", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                   help="write profiles/<--summary-name>.md and _traffic.json from rocprofv3 output "
+                        "of this benchmark, then exit (no GPU needed)")
+    p.add_argument("--summary-name", default=None)
+    p.add_argument("--summary-commands", nargs="*", default=[])
     return p.parse_args()
 
 
@@ -67,6 +73,147 @@ def step_work(shape, step: str):
     if step == "bias_qkv_split":
         return 0.0, 2 * 3 * T * H * e
     raise KeyError(step)
+
+
+# ----------------------------------------------------------------- rocprofv3 summaries
+# Kernel sources whose hash tags a traffic measurement: traffic figures are reported only
+# while these files are unchanged since the counters were taken.
+KERNEL_SOURCES = ("transformer_encoder_bert_amd/csrc/gemm.hip",
+                  "transformer_encoder_bert_amd/csrc/attention.hip",
+                  "transformer_encoder_bert_amd/csrc/elementwise.hip",
+                  "transformer_encoder_bert_amd/csrc/device_common.h")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def classify_dispatches(names):
+    """Step class of each kernel dispatch of a forward, from the fixed launch order of a
+    layer (the attention-output and FFN-output projections share one kernel symbol)."""
+    import re
+    steps, prev = [], None
+    for n in names:
+        st = None
+        if "gemm_kernel" in n and "EpiQKV" in n:
+            st = "qkv_gemm"
+        elif "attention" in n and "ftx" in n:
+            st = "attention"
+        elif "layernorm_kernel" in n:
+            st = "ln1" if prev in ("attn_out_gemm", "attention") else "ln2"
+        elif "gemm_kernel" in n and "EpiLinear" in n:
+            m = re.search(r"EpiLinearI\w+?Lb([01])E", n)
+            gelu = m is not None and m.group(1) == "1"
+            if gelu or prev == "ln1":
+                st = "ffn1_gemm"
+            elif prev == "attention":
+                st = "attn_out_gemm"
+            else:
+                st = "ffn2_gemm"
+        elif "bias_gelu_kernel" in n:
+            st = "bias_gelu"
+        elif "bias_qkv_split_kernel" in n:
+            st = "bias_qkv_split"
+        steps.append(st)
+        if st is not None:
+            prev = st
+    return steps
+
+
+def summarize_rocprof(args):
+    """Summarise a rocprofv3 kernel trace plus FETCH_SIZE / WRITE_SIZE counter runs of this
+    benchmark (made with --copy-calib-mb) into profiles/<name>.md and profiles/<name>_traffic.json."""
+    import csv
+    trace_dir, fetch_dir, write_dir = args.summarize_rocprof
+    def one(d, suffix):
+        fs = [os.path.join(d, f) for f in os.listdir(d) if f.endswith(suffix)]
+        if len(fs) != 1:
+            raise SystemExit(f"expected one *{suffix} in {d}")
+        return list(csv.DictReader(open(fs[0])))
+    trace = one(trace_dir, "_kernel_trace.csv")
+    trace.sort(key=lambda r: int(r["Dispatch_Id"]))
+    steps = classify_dispatches([r["Kernel_Name"] for r in trace])
+    dur = {}
+    sym = {}
+    for r, st in zip(trace, steps):
+        if st is None:
+            continue
+        dur.setdefault(st, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+        sym[st] = r["Kernel_Name"]
+    calib_bytes = args.copy_calib_mb * (1 << 20)
+    counters = {}
+    scale = {}
+    for name, d, suffix in (("FETCH_SIZE", fetch_dir, "_counter_collection.csv"),
+                            ("WRITE_SIZE", write_dir, "_counter_collection.csv")):
+        rows = one(d, suffix)
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        cal = [float(r["Counter_Value"]) for r in rows if "neg_kernel" in r["Kernel_Name"]]
+        if not cal:
+            raise SystemExit("no calibration copy kernel in the counter run")
+        scale[name] = calib_bytes / (sum(cal) / len(cal) * 1024.0)  # true bytes per counted byte
+        st_rows = classify_dispatches([r["Kernel_Name"] for r in rows])
+        for r, st in zip(rows, st_rows):
+            if st is None:
+                continue
+            counters.setdefault(st, {}).setdefault(name, []).append(float(r["Counter_Value"]) * 1024.0 * scale[name])
+    wl = WORKLOAD_DEFAULT if args.workload is None else args.workload
+    import synthetic_inputs as si
+    w = si.WORKLOADS[wl]
+    shape = w.shape(args.batch or max(w.batches))
+    out = {"workload": wl, "batch": shape.batch, "kernel_source_hash": kernel_source_hash(),
+           "scale": scale, "steps": {}}
+    lines = [f"# Kernel time and HBM traffic per step -- {wl}, batch {shape.batch}", "",
+             "Commands (from the repository root, on one MI355X):", "", "```",
+             *args.summary_commands, "```", "",
+             f"FETCH_SIZE and WRITE_SIZE are scaled by what they read for a plain copy kernel "
+             f"(torch.neg over {args.copy_calib_mb} MiB of fp16): true bytes per counted byte "
+             f"{scale['FETCH_SIZE']:.3f} (fetch) and {scale['WRITE_SIZE']:.3f} (write).", "",
+             "| step | launches | avg us | algorithmic MB | fetched MB | written MB | "
+             "algorithmic TFLOP/s | algorithmic GB/s |", "|---|---|---|---|---|---|---|---|"]
+    for st in ("qkv_gemm", "bias_qkv_split", "attention", "attn_out_gemm", "ln1", "ffn1_gemm",
+               "bias_gelu", "ffn2_gemm", "ln2"):
+        if st not in dur:
+            continue
+        avg = sum(dur[st]) / len(dur[st])
+        fl, by = step_work(shape, st)
+        c = counters.get(st, {})
+        fetch = sum(c.get("FETCH_SIZE", [0])) / max(1, len(c.get("FETCH_SIZE", [])))
+        write = sum(c.get("WRITE_SIZE", [0])) / max(1, len(c.get("WRITE_SIZE", [])))
+        out["steps"][st] = {"symbol": sym[st], "avg_us": avg, "launches": len(dur[st]),
+                            "fetch_bytes": fetch, "write_bytes": write,
+                            "algorithmic_bytes": by, "flops": fl}
+        lines.append(f"| {st} | {len(dur[st])} | {avg:.1f} | {by / 1e6:.1f} | {fetch / 1e6:.1f} | "
+                     f"{write / 1e6:.1f} | {fl / (avg * 1e-6) / 1e12 if fl else 0:.1f} | "
+                     f"{by / (avg * 1e-6) / 1e9:.0f} |")
+    lines += ["", "Kernel symbols:", ""]
+    lines += [f"- {st}: `{v['symbol']}`" for st, v in out["steps"].items()]
+    lines += ["", f"Kernel source hash: `{out['kernel_source_hash']}`"]
+    base = os.path.join(ROOT, "profiles", args.summary_name)
+    os.makedirs(os.path.dirname(base), exist_ok=True)
+    with open(base + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(base + "_traffic.json", "w") as f:
+        json.dump(out, f, indent=1)
+    print(base + ".md")
+
+
+def measured_traffic(workload: str, batch: int, step: str):
+    """HBM bytes per launch of `step` from the committed counter summary of this workload,
+    or None when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_b{batch}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash() or step not in t.get("steps", {}):
+        return None
+    s = t["steps"][step]
+    return s["fetch_bytes"] + s["write_bytes"]
 
 
 def blas_threads() -> int:
@@ -100,6 +247,13 @@ def cpu_baseline(case, target_s: float):
 
 def main():
     args = parse()
+    if args.summarize_rocprof:
+        if not args.summary_name:
+            raise SystemExit("--summary-name is required")
+        summarize_rocprof(args)
+        return
+    if args.workload is None:
+        args.workload = WORKLOAD_DEFAULT
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py runs on one GPU only: this encoder forward shards by data parallelism "
               f"with no collective, and no multi-GPU run is part of this build (asked: --gpus {args.gpus})",
@@ -213,8 +367,10 @@ def main():
             achieved, peak, unit, bound = fl / avg_s / 1e12, PEAK_MFMA_TFLOPS[dt], "TFLOP/s", "mfma"
         else:
             achieved, peak, unit, bound = by / avg_s / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+        traffic = measured_traffic(wl.name, shape.batch, dom)
         result["roofline"] = {"kernel": dom, "bound": bound, "achieved": achieved, "peak": peak,
-                              "unit": unit, "frac": achieved / peak, "traffic": None,
+                              "unit": unit, "frac": achieved / peak, "traffic": traffic,
+                              "traffic_gbs": None if traffic is None else traffic / avg_s / 1e9,
                               "work_per_launch": fl if bound == "mfma" else by,
                               "avg_launch_us": kernels[dom]["avg_us"]}
         result["kernels"] = kernels

@@ -4,7 +4,8 @@
 // section "Faster Transformer 优化原理": per layer, the batched Q K^T and P V matrix
 // multiplies with a SoftMax kernel between them (two SoftMax versions chosen by shape,
 // row sums by register shuffle, sums kept in float), plus the transposes around them.
-// Here the whole chain for one (sequence, head, 32-query block) runs in one wavefront:
+// Here the whole chain for one (sequence, head, 32-query block) runs in one wavefront,
+// with K and V^T of the head shared by the workgroup through LDS:
 //
 //   S^T = K Q^T       v_mfma 32x32 tiles, keys on rows, the wave's 32 queries on columns;
 //                     a lane then holds 16 of the 32 keys of one query per tile;
@@ -14,13 +15,12 @@
 //   C^T = V^T P^T     the probabilities stay in registers and are fed, converted to the
 //                     storage type, straight into the next MFMA as its B operand; V is
 //                     read from the per-head transposed layout V^T[d][S];
-//   merge heads       the result is stored at ctx[b*S + i][h*d + e] directly.
+//   merge heads       the result is staged in LDS and stored at ctx[b*S + i][h*d + e].
 //
 // Key tiles are processed in chunks of up to 4 (128 keys) with the running-max
 // rescaling of the streaming softmax, so S = 512 uses the same kernel; for S <= 128 the
-// loop runs once.  Key tiles entirely beyond len_b are skipped: their probabilities are
-// exactly 0, so skipping them changes nothing.  Every query row, padded or not, is
-// computed.
+// loop runs once.  Key tiles entirely beyond len_b are neither loaded nor multiplied:
+// their probabilities are exactly 0.  Every query row, padded or not, is computed.
 
 #include <math.h>
 
@@ -54,8 +54,11 @@ template <> struct AttnMfma<float> {
   }
 };
 
+// Fallback for shapes whose K and V^T do not fit in LDS (fp32 with d = 64 and S > 256):
+// the same chain with every wave reading its head's K and V^T straight from global
+// memory, and the output stored from registers.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ q,
+__global__ __launch_bounds__(256) void attention_global_kernel(const T* __restrict__ q,
                                                         const T* __restrict__ k,
                                                         const T* __restrict__ vt,
                                                         const int32_t* __restrict__ lens,
@@ -205,21 +208,236 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ q,
     }
 }
 
+
+// One workgroup per (sequence, head, group of up to 8 query blocks of 32).  The workgroup
+// first copies K [keys][d] and V^T [d][keys] of its head -- only the key tiles below the
+// sequence's valid length -- into row-padded LDS with 16-byte coalesced loads; every wave
+// then reads its MFMA fragments from LDS, so K and V leave HBM once per workgroup instead
+// of once per wave.  At the end the waves stage their context tiles in LDS (rows of d) and
+// store whole 2*D-byte rows of the merged-heads output with 16-byte vectors.
+template <typename T, int D, int SMAX> struct AttnCfg {
+  static constexpr int VE = 16 / sizeof(T);          // elements per 16-byte vector
+  static constexpr int NW = SMAX / 32 < 8 ? SMAX / 32 : 8;  // waves per workgroup
+  static constexpr int KST = D + VE;                 // LDS row stride of K (elements)
+  static constexpr int VST = SMAX + VE;              // LDS row stride of V^T
+  static constexpr int OST = D + VE;                 // LDS row stride of the output stage
+  static constexpr int LDS = SMAX * KST + D * VST;   // elements
+  static_assert(NW * 32 * OST <= LDS, "output stage must fit in the K/V area");
+};
+
+template <typename T, int D, int SMAX>
+__global__ __launch_bounds__((AttnCfg<T, D, SMAX>::NW * kWave)) void attention_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt,
+    const int32_t* __restrict__ lens, T* __restrict__ ctx, int B, int S, int nh,
+    float scale_log2e) {
+  typedef AttnCfg<T, D, SMAX> C;
+  typedef AttnMfma<T> MF;
+  typedef typename MF::frag frag;
+  typedef typename VecT<T, 4>::type v4;
+  typedef typename Vec16<T>::type vec;
+  constexpr int VEC = MF::VEC;
+  constexpr int KF = 2 * VEC;   // d consumed per fragment pair
+  constexpr int NQF = D / KF;   // fragments along d
+  constexpr int DT = D / 32;    // 32-row tiles of the transposed output along d
+  constexpr int CH = SMAX / 32 < 4 ? SMAX / 32 : 4;  // key tiles per softmax chunk
+  constexpr int NT = C::NW * kWave;
+  __shared__ __attribute__((aligned(16))) T smem[C::LDS];
+  T* Ks = smem;
+  T* Vs = smem + SMAX * C::KST;
+
+  const int qblocks = S / 32;
+  const int groups = (qblocks + C::NW - 1) / C::NW;
+  const int bh = blockIdx.x / groups, grp = blockIdx.x % groups;
+  const int b = bh / nh, h = bh % nh;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int lr = lane % 32, g = lane / 32;
+  const int qb = grp * C::NW + wave;
+  const bool active = qb < qblocks;
+  int len = lens ? lens[b] : S;
+  len = min(max(len, 1), S);
+  const int nkt = (len + 31) / 32;
+  const int nk = nkt * 32;  // keys held in LDS
+
+  frag qf[NQF];
+  if (active) {
+    const T* qp = q + ((size_t)bh * S + qb * 32 + lr) * D + g * VEC;
+#pragma unroll
+    for (int f = 0; f < NQF; ++f) qf[f] = *(const frag*)(qp + f * KF);
+  }
+  {
+    const T* kg = k + (size_t)bh * S * D;
+    for (int c = threadIdx.x; c < nk * (D / C::VE); c += NT) {
+      const int r = c / (D / C::VE), col = (c % (D / C::VE)) * C::VE;
+      *(vec*)(Ks + r * C::KST + col) = *(const vec*)(kg + (size_t)r * D + col);
+    }
+    const T* vg = vt + (size_t)bh * D * S;
+    const int cpr = nk / C::VE;
+    for (int c = threadIdx.x; c < D * cpr; c += NT) {
+      const int r = c / cpr, col = (c % cpr) * C::VE;
+      *(vec*)(Vs + r * C::VST + col) = *(const vec*)(vg + (size_t)r * S + col);
+    }
+  }
+  __syncthreads();
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  float l_run = 1.f;
+
+  if (active) {
+    float m_run = -INFINITY;
+    l_run = 0.f;
+    for (int c0 = 0; c0 < nkt; c0 += CH) {
+      f32x16 sc[CH];
+#pragma unroll
+      for (int t = 0; t < CH; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
+        const int kt = c0 + t;
+        if (kt < nkt) {
+          const T* kr = Ks + (kt * 32 + lr) * C::KST + g * VEC;
+#pragma unroll
+          for (int f = 0; f < NQF; ++f) MF::mma(*(const frag*)(kr + f * KF), qf[f], sc[t]);
+        }
+      }
+      // mask and chunk maximum (key of register r: tile*32 + 8*(r/4) + 4*g + r%4)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < CH; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = (c0 + t) * 32 + 8 * (r / 4) + 4 * g + (r % 4);
+          if (key >= len) sc[t][r] = -INFINITY;
+          mx = fmaxf(mx, sc[t][r]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);  // finite: every chunk holds a key below len
+      const float alpha = exp2f((m_run - m_new) * scale_log2e);
+      float psum = 0.f;
+#pragma unroll
+      for (int t = 0; t < CH; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2f((sc[t][r] - m_new) * scale_log2e);
+          sc[t][r] = p;
+          psum += p;
+        }
+      psum += __shfl_xor(psum, 32);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+
+      // context: o[dt] += V^T[dt tile][keys] * P^T[keys][queries]
+#pragma unroll
+      for (int t = 0; t < CH; ++t) {
+        const int kt = c0 + t;
+        if (kt >= nkt) continue;
+        if constexpr (VEC == 8) {
+          // MFMA u consumes P registers 8u..8u+7 = keys kt*32 + 16u + {0..3, 8..11} + 4g
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            frag pf;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) pf[s] = from_f32<T>(sc[t][8 * u + s]);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+              const T* vr = Vs + (dt * 32 + lr) * C::VST + kt * 32 + 16 * u + 4 * g;
+              const v4 lo = *(const v4*)(vr);
+              const v4 hi = *(const v4*)(vr + 8);
+              frag vf;
+#pragma unroll
+              for (int s = 0; s < 4; ++s) {
+                vf[s] = lo[s];
+                vf[s + 4] = hi[s];
+              }
+              MF::mma(vf, pf, o[dt]);
+            }
+          }
+        } else {
+          // fp32: call u consumes registers 4u..4u+3 = keys kt*32 + 8u + 4g + {0..3}
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            frag pf;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) pf[s] = sc[t][4 * u + s];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+              const T* vr = Vs + (dt * 32 + lr) * C::VST + kt * 32 + 8 * u + 4 * g;
+              MF::mma(*(const frag*)vr, pf, o[dt]);
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // normalise, stage [query][d] in LDS (the K/V area is free once every wave is past here),
+  // then store whole rows of this head's D columns
+  __syncthreads();
+  T* os = smem + wave * 32 * C::OST;
+  const float inv = 1.0f / l_run;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v4 vv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vv[e] = from_f32<T>(o[dt][4 * s + e] * inv);
+      *(v4*)(os + lr * C::OST + dt * 32 + 8 * s + 4 * g) = vv;
+    }
+  if (!active) return;  // no further barrier: the stage of a wave is read by that wave only
+  const int H = nh * D;
+  constexpr int CPR = D / C::VE;       // vectors per output row
+  constexpr int RPP = kWave / CPR;     // rows per pass
+  T* out = ctx + ((size_t)b * S + qb * 32) * H + h * D;
+#pragma unroll
+  for (int p = 0; p < 32 / RPP; ++p) {
+    const int row = p * RPP + lane / CPR, col = (lane % CPR) * C::VE;
+    *(vec*)(out + (size_t)row * H + col) = *(const vec*)(os + row * C::OST + col);
+  }
+}
+
+constexpr size_t kMaxLdsBytes = 160 * 1024;  // per workgroup on gfx950
+
+template <typename T, int D, int SMAX>
+static hipError_t attn_launch_cfg(int B, int S, int nh, const void* q, const void* k,
+                                  const void* vt, const int32_t* lens, void* ctx,
+                                  float scale_log2e, hipStream_t s) {
+  typedef AttnCfg<T, D, SMAX> C;
+  const int groups = (S / 32 + C::NW - 1) / C::NW;
+  attention_kernel<T, D, SMAX><<<B * nh * groups, C::NW * kWave, 0, s>>>(
+      (const T*)q, (const T*)k, (const T*)vt, lens, (T*)ctx, B, S, nh, scale_log2e);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t attn_launch_d(int B, int S, int nh, const void* q, const void* k,
+                                const void* vt, const int32_t* lens, void* ctx,
+                                float scale_log2e, hipStream_t s) {
+  if (S <= 32) return attn_launch_cfg<T, D, 32>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s);
+  if (S <= 64) return attn_launch_cfg<T, D, 64>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s);
+  if (S <= 128) return attn_launch_cfg<T, D, 128>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s);
+  if (S <= 256) return attn_launch_cfg<T, D, 256>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s);
+  if constexpr (AttnCfg<T, D, 512>::LDS * sizeof(T) <= kMaxLdsBytes)
+    return attn_launch_cfg<T, D, 512>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s);
+  const int blocks = (B * nh * (S / 32) + 3) / 4;
+  attention_global_kernel<T, D><<<blocks, 256, 0, s>>>((const T*)q, (const T*)k, (const T*)vt, lens,
+                                                       (T*)ctx, B, S, nh, scale_log2e);
+  return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t attn_launch(int B, int S, int nh, int d, const void* q, const void* k,
                               const void* vt, const int32_t* lens, void* ctx, hipStream_t s) {
-  const int ntasks = B * nh * (S / 32);
-  const int blocks = (ntasks + 3) / 4;
   const float scale_log2e = (float)(1.4426950408889634 / sqrt((double)d));
-  if (d == 64)
-    attention_kernel<T, 64><<<blocks, 256, 0, s>>>((const T*)q, (const T*)k, (const T*)vt, lens,
-                                                   (T*)ctx, B, S, nh, scale_log2e);
-  else if (d == 32)
-    attention_kernel<T, 32><<<blocks, 256, 0, s>>>((const T*)q, (const T*)k, (const T*)vt, lens,
-                                                   (T*)ctx, B, S, nh, scale_log2e);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (d == 64) return attn_launch_d<T, 64>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s);
+  if (d == 32) return attn_launch_d<T, 32>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attention(ftx_dtype dt, int B, int S, int nh, int d, const void* q,

@@ -23,6 +23,8 @@
 // so the four consecutive accumulator rows a lane holds are four consecutive columns n of
 // one output row m; the epilogue regroups them through LDS into 16-byte row vectors.
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -211,7 +213,7 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
   tn = in_group / gsz;
 }
 
-template <typename T, int BM, int BN, int WM, int WN, typename Epi>
+template <typename T, int BM, int BN, int WM, int WN, typename Epi, int PF = 1>  // PF: 1 or 2
 __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restrict__ A,
                                                                const T* __restrict__ Bt, int M,
                                                                int N, int K, Epi epi) {
@@ -244,47 +246,55 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
 #pragma unroll
     for (int q = 0; q < 4; ++q) bq[j][q] = epi.bias4(n0 + (wn * C::TN + j) * 32 + 8 * q + 4 * g);
 
-  frag ra[C::A_CH], rb[C::B_CH];
+  // PF register sets of the next K slabs: slab kt lives in set kt % PF between its global
+  // load (PF iterations ahead) and its store into LDS (at the end of iteration kt - 1)
+  frag ra[PF][C::A_CH], rb[PF][C::B_CH];
   const frag zero = {};
 
-  auto gload = [&](int k0) {
+  auto gload = [&](int set, int k0) {
 #pragma unroll
     for (int i = 0; i < C::A_CH; ++i) {
       const int c = tid + i * C::NT;
       const int r = c / C::CPR, kc = (c % C::CPR) * C::VEC;
       const int gr = m0 + r, gk = k0 + kc;
-      ra[i] = (gr < M && gk < K) ? *(const frag*)(A + (size_t)gr * K + gk) : zero;
+      ra[set][i] = (gr < M && gk < K) ? *(const frag*)(A + (size_t)gr * K + gk) : zero;
     }
 #pragma unroll
     for (int i = 0; i < C::B_CH; ++i) {
       const int c = tid + i * C::NT;
       const int r = c / C::CPR, kc = (c % C::CPR) * C::VEC;
       const int gr = n0 + r, gk = k0 + kc;
-      rb[i] = (gr < N && gk < K) ? *(const frag*)(Bt + (size_t)gr * K + gk) : zero;
+      rb[set][i] = (gr < N && gk < K) ? *(const frag*)(Bt + (size_t)gr * K + gk) : zero;
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int set, int buf) {
     T* As = smem + buf * C::STAGE;
     T* Bs = As + BM * C::LDS_STRIDE;
 #pragma unroll
     for (int i = 0; i < C::A_CH; ++i) {
       const int c = tid + i * C::NT;
-      *(frag*)(As + (c / C::CPR) * C::LDS_STRIDE + (c % C::CPR) * C::VEC) = ra[i];
+      *(frag*)(As + (c / C::CPR) * C::LDS_STRIDE + (c % C::CPR) * C::VEC) = ra[set][i];
     }
 #pragma unroll
     for (int i = 0; i < C::B_CH; ++i) {
       const int c = tid + i * C::NT;
-      *(frag*)(Bs + (c / C::CPR) * C::LDS_STRIDE + (c % C::CPR) * C::VEC) = rb[i];
+      *(frag*)(Bs + (c / C::CPR) * C::LDS_STRIDE + (c % C::CPR) * C::VEC) = rb[set][i];
     }
   };
 
   const int nk = (K + C::BK - 1) / C::BK;
-  gload(0);
-  sstore(0);
+  gload(0, 0);
+  sstore(0, 0);
+#pragma unroll
+  for (int p = 1; p < PF; ++p)
+    if (p < nk) gload(p % PF, p * C::BK);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
+  // iteration kt (= p mod PF) loads slab kt + PF into set p and stores slab kt + 1 from set
+  // (p + 1) % PF into the other LDS buffer; the unroll by PF keeps the set indices constant
+  auto iteration = [&](int kt, auto pc) {
+    constexpr int p = decltype(pc)::value;
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * C::BK);
+    if (kt + PF < nk) gload(p, (kt + PF) * C::BK);
     const T* As = smem + cur * C::STAGE + (wm * C::TM * 32 + lr) * C::LDS_STRIDE + g * C::VEC;
     const T* Bs = smem + cur * C::STAGE + (BM + wn * C::TN * 32 + lr) * C::LDS_STRIDE + g * C::VEC;
 #pragma unroll
@@ -299,8 +309,13 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) MF::mma(b[j], a[i], acc[j][i]);
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
+    if (kt + 1 < nk) sstore((p + 1) % PF, cur ^ 1);
     __syncthreads();
+  };
+  for (int kt0 = 0; kt0 < nk; kt0 += PF) {
+    iteration(kt0, std::integral_constant<int, 0>());
+    if constexpr (PF > 1)
+      if (kt0 + 1 < nk) iteration(kt0 + 1, std::integral_constant<int, 1>());
   }
 
   // the K loop ended with a barrier, so the LDS is free: each wave stages its tiles in its
