@@ -23,8 +23,6 @@
 // so the four consecutive accumulator rows a lane holds are four consecutive columns n of
 // one output row m; the epilogue regroups them through LDS into 16-byte row vectors.
 
-#include <type_traits>
-
 #include "device_common.h"
 #include "launch.h"
 
@@ -179,6 +177,17 @@ __device__ __forceinline__ void epilogue_tile(const Epi& epi, typename Epi::out_
 
 // ---------------------------------------------------------------------------------- kernel
 
+// Workgroup barrier for the LDS double buffer: this wave's LDS writes have completed
+// (lgkmcnt 0) and every wave has arrived.  Unlike __syncthreads() it does not wait for
+// outstanding global loads (vmcnt), so prefetches of later K slabs stay in flight across
+// it; the empty asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <typename T, int BM, int BN, int WM, int WN> struct GemmCfg {
   typedef Mfma<T> MF;
   static constexpr int VEC = MF::VEC;
@@ -213,7 +222,7 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
   tn = in_group / gsz;
 }
 
-template <typename T, int BM, int BN, int WM, int WN, typename Epi, int PF = 1>  // PF: 1 or 2
+template <typename T, int BM, int BN, int WM, int WN, typename Epi>
 __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restrict__ A,
                                                                const T* __restrict__ Bt, int M,
                                                                int N, int K, Epi epi) {
@@ -246,76 +255,89 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
 #pragma unroll
     for (int q = 0; q < 4; ++q) bq[j][q] = epi.bias4(n0 + (wn * C::TN + j) * 32 + 8 * q + 4 * g);
 
-  // PF register sets of the next K slabs: slab kt lives in set kt % PF between its global
-  // load (PF iterations ahead) and its store into LDS (at the end of iteration kt - 1)
-  frag ra[PF][C::A_CH], rb[PF][C::B_CH];
+  // the next K slab, fetched into registers while the current one is multiplied
+  frag ra[C::A_CH], rb[C::B_CH];
   const frag zero = {};
 
-  auto gload = [&](int set, int k0) {
+  // Loads past the last row or K column read a clamped in-range address, with no branch
+  // around the load, so the compiler can count the loads still in flight exactly instead of
+  // draining them at a control-flow merge.  Rows past M (of A) or N (of W^T) only feed
+  // outputs that are never stored; K columns past K are zeroed when the slab is written to
+  // LDS, where the loaded data is needed anyway.
+  auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < C::A_CH; ++i) {
       const int c = tid + i * C::NT;
       const int r = c / C::CPR, kc = (c % C::CPR) * C::VEC;
-      const int gr = m0 + r, gk = k0 + kc;
-      ra[set][i] = (gr < M && gk < K) ? *(const frag*)(A + (size_t)gr * K + gk) : zero;
+      ra[i] = *(const frag*)(A + (size_t)min(m0 + r, M - 1) * K + min(k0 + kc, K - C::VEC));
     }
 #pragma unroll
     for (int i = 0; i < C::B_CH; ++i) {
       const int c = tid + i * C::NT;
       const int r = c / C::CPR, kc = (c % C::CPR) * C::VEC;
-      const int gr = n0 + r, gk = k0 + kc;
-      rb[set][i] = (gr < N && gk < K) ? *(const frag*)(Bt + (size_t)gr * K + gk) : zero;
+      rb[i] = *(const frag*)(Bt + (size_t)min(n0 + r, N - 1) * K + min(k0 + kc, K - C::VEC));
     }
   };
-  auto sstore = [&](int set, int buf) {
+  auto sstore = [&](int buf, int k0) {
     T* As = smem + buf * C::STAGE;
     T* Bs = As + BM * C::LDS_STRIDE;
 #pragma unroll
     for (int i = 0; i < C::A_CH; ++i) {
       const int c = tid + i * C::NT;
-      *(frag*)(As + (c / C::CPR) * C::LDS_STRIDE + (c % C::CPR) * C::VEC) = ra[set][i];
+      const int kc = (c % C::CPR) * C::VEC;
+      *(frag*)(As + (c / C::CPR) * C::LDS_STRIDE + kc) = k0 + kc < K ? ra[i] : zero;
     }
 #pragma unroll
     for (int i = 0; i < C::B_CH; ++i) {
       const int c = tid + i * C::NT;
-      *(frag*)(Bs + (c / C::CPR) * C::LDS_STRIDE + (c % C::CPR) * C::VEC) = rb[set][i];
+      const int kc = (c % C::CPR) * C::VEC;
+      *(frag*)(Bs + (c / C::CPR) * C::LDS_STRIDE + kc) = k0 + kc < K ? rb[i] : zero;
     }
   };
 
   const int nk = (K + C::BK - 1) / C::BK;
-  gload(0, 0);
+  gload(0);
   sstore(0, 0);
-#pragma unroll
-  for (int p = 1; p < PF; ++p)
-    if (p < nk) gload(p % PF, p * C::BK);
   __syncthreads();
-  // iteration kt (= p mod PF) loads slab kt + PF into set p and stores slab kt + 1 from set
-  // (p + 1) % PF into the other LDS buffer; the unroll by PF keeps the set indices constant
-  auto iteration = [&](int kt, auto pc) {
-    constexpr int p = decltype(pc)::value;
+  // MFMA fragments are double-buffered in registers (FDB): while the MFMAs of sub-step s
+  // run, the fragments of sub-step s + 1 are read from LDS; the first sub-step of the next
+  // slab is read right after the barrier that publishes it.  The 256x256 tile has no room
+  // for the second set (it would spill), so it reads each sub-step's fragments just before
+  // their MFMAs.
+  constexpr int NS = C::BK / MF::KF;  // sub-steps per slab (even)
+  constexpr bool FDB = C::TM + C::TN <= 5;
+  static_assert(NS % 2 == 0, "fragment double buffer assumes an even sub-step count");
+  frag fa[FDB ? 2 : 1][C::TM], fb[FDB ? 2 : 1][C::TN];
+  auto read_frags = [&](int buf, int s, int fbuf) {
+    const T* As = smem + buf * C::STAGE + (wm * C::TM * 32 + lr) * C::LDS_STRIDE + g * C::VEC + s * MF::KF;
+    const T* Bs = smem + buf * C::STAGE + (BM + wn * C::TN * 32 + lr) * C::LDS_STRIDE + g * C::VEC + s * MF::KF;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) fa[fbuf][i] = *(const frag*)(As + i * 32 * C::LDS_STRIDE);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) fb[fbuf][j] = *(const frag*)(Bs + j * 32 * C::LDS_STRIDE);
+  };
+  if constexpr (FDB) read_frags(0, 0, 0);
+
+  for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + PF < nk) gload(p, (kt + PF) * C::BK);
-    const T* As = smem + cur * C::STAGE + (wm * C::TM * 32 + lr) * C::LDS_STRIDE + g * C::VEC;
-    const T* Bs = smem + cur * C::STAGE + (BM + wn * C::TN * 32 + lr) * C::LDS_STRIDE + g * C::VEC;
+    if (kt + 1 < nk) gload((kt + 1) * C::BK);
 #pragma unroll
-    for (int kk = 0; kk < C::BK; kk += MF::KF) {
-      frag a[C::TM], b[C::TN];
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i) a[i] = *(const frag*)(As + i * 32 * C::LDS_STRIDE + kk);
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) b[j] = *(const frag*)(Bs + j * 32 * C::LDS_STRIDE + kk);
+    for (int s = 0; s < NS; ++s) {
+      constexpr int X = FDB ? 1 : 0;  // 1: fragment sets alternate
+      if constexpr (FDB) {
+        if (s + 1 < NS) read_frags(cur, s + 1, (s + 1) & 1);
+      } else {
+        read_frags(cur, s, 0);
+      }
 #pragma unroll
       for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-        for (int i = 0; i < C::TM; ++i) MF::mma(b[j], a[i], acc[j][i]);
+        for (int i = 0; i < C::TM; ++i) MF::mma(fb[s & X][j], fa[s & X][i], acc[j][i]);
     }
-    if (kt + 1 < nk) sstore((p + 1) % PF, cur ^ 1);
-    __syncthreads();
-  };
-  for (int kt0 = 0; kt0 < nk; kt0 += PF) {
-    iteration(kt0, std::integral_constant<int, 0>());
-    if constexpr (PF > 1)
-      if (kt0 + 1 < nk) iteration(kt0 + 1, std::integral_constant<int, 1>());
+    if (kt + 1 < nk) sstore(cur ^ 1, (kt + 1) * C::BK);
+    lds_barrier();
+    if constexpr (FDB)
+      if (kt + 1 < nk) read_frags(cur ^ 1, 0, 0);
   }
 
   // the K loop ended with a barrier, so the LDS is free: each wave stages its tiles in its
