@@ -65,12 +65,19 @@ template <> struct Mfma<float> {
 //   bias4(n)             the bias of columns n .. n+3 (read before the K loop, so its
 //                        latency hides behind the matrix multiply; zeros if there is none);
 //   act(v)               the element-wise work after the bias (GELU or nothing);
-//   transposed(nt)       whether the tile of columns nt .. nt+31 is stored column-major;
-//   store(m, n, v)       a 16-byte vector of consecutive columns n.. of row m;
-//   store_t(n, m, v)     a 16-byte vector of consecutive rows m.. of column n;
-// and the kernel stages each tile through LDS (converted to the output type) so that both
-// kinds of store are 16 bytes per lane, 64 contiguous bytes per row.  N is a multiple of 8,
-// M of the QKV projection a multiple of 32, so no vector straddles the end of a row.
+//   tile(mt, nt)         where the 32x32 tile at rows mt.., columns nt.. goes: its base
+//                        pointer, the pointer step per staged row, and whether it is stored
+//                        column-major (staged transposed) -- computed once per tile, so the
+//                        divisions behind it are not repeated per element;
+//   valid(mt, nt, r, c)  whether staged row r, column c (16-byte vector) is inside C;
+// and the kernel stages each tile through LDS (converted to the output type) so that every
+// store is 16 bytes per lane, 64 contiguous bytes per row.  N is a multiple of 8, M of the
+// QKV projection a multiple of 32, so no vector straddles the end of a row.
+template <typename TO> struct TileDst {
+  TO* base;    // element (staged row 0, column 0)
+  long step;   // elements between consecutive staged rows
+  bool tr;     // staged transposed: staged rows run along n, columns along m
+};
 
 // tanh-form GELU as u * sigmoid(2 y), y = sqrt(2/pi) (u + 0.044715 u^3) (the cube written
 // u*u*u), with one exp and the hardware reciprocal instead of a divide; large negative u
@@ -93,17 +100,18 @@ template <typename T, bool GELU, typename TO = T> struct EpiLinear {
     return v;
   }
   __device__ __forceinline__ float act(float v) const { return GELU ? gelu_fast(v) : v; }
-  __device__ __forceinline__ bool transposed(int) const { return false; }
-  __device__ __forceinline__ void store(int m, int n, const vec& v) const {
-    if (m < M && n < N) *(vec*)(c + (size_t)m * N + n) = v;
+  __device__ __forceinline__ TileDst<TO> tile(int mt, int nt) const {
+    return {c + (size_t)mt * N + nt, N, false};
   }
-  __device__ __forceinline__ void store_t(int, int, const vec&) const {}
+  __device__ __forceinline__ bool valid(int mt, int nt, int r, int col) const {
+    return mt + r < M && nt + col < N;
+  }
 };
 
 // bias + head split: a 32-column tile lies inside one of Q, K, V and inside one head (d is
-// 32 or 64 and H a multiple of 32); row m is token s = m % S of sequence b = m / S.
-// Q and K are written [B][n][S][d]; V transposed per head, [B][n][d][S], from tiles staged
-// column-major (32 consecutive tokens of one feature; S is a multiple of 32).
+// 32 or 64 and H a multiple of 32), and its 32 rows are consecutive tokens of one sequence
+// (S is a multiple of 32).  Q and K are written [B][n][S][d]; V transposed per head,
+// [B][n][d][S], from tiles staged column-major.
 template <typename T> struct EpiQKV {
   typedef T out_t;
   typedef typename Vec16<T>::type vec;
@@ -119,27 +127,23 @@ template <typename T> struct EpiQKV {
     return v;
   }
   __device__ __forceinline__ float act(float v) const { return v; }
-  __device__ __forceinline__ bool transposed(int nt) const { return nt >= 2 * nh * d; }
-  __device__ __forceinline__ void store(int m, int n, const vec& v) const {
-    if (m >= M || n >= N) return;
+  __device__ __forceinline__ TileDst<T> tile(int mt, int nt) const {
     const int H = nh * d;
-    const int which = n / H, rem = n - which * H;
-    const int h = rem / d, dd = rem - h * d;
-    const int b = m / S, s = m - b * S;
-    *(vec*)((which == 0 ? q : k) + (((size_t)b * nh + h) * S + s) * d + dd) = v;
+    const int which = nt / H, rem = nt - which * H;
+    const int h = rem / d, dd0 = rem - h * d;
+    const int b = mt / S, s0 = mt - b * S;
+    const size_t head = (size_t)b * nh + h;
+    if (which < 2) return {(which == 0 ? q : k) + (head * S + s0) * d + dd0, d, false};
+    return {vt + (head * d + dd0) * S + s0, S, true};
   }
-  __device__ __forceinline__ void store_t(int n, int m, const vec& v) const {
-    if (m >= M || n >= N) return;
-    const int rem = n - 2 * nh * d;
-    const int h = rem / d, dd = rem - h * d;
-    const int b = m / S, s = m - b * S;
-    *(vec*)(vt + (((size_t)b * nh + h) * d + dd) * S + s) = v;
+  __device__ __forceinline__ bool valid(int mt, int nt, int, int) const {
+    return mt < M && nt < N;
   }
 };
 
 // Stage one C^T tile (columns nt.., rows mt..) through this wave's LDS scratch `ws`
-// (32 x (32 + pad) elements of the output type) and hand it to the epilogue as 16-byte
-// vectors.  Wave-private: LDS accesses of one wave complete in order.
+// (32 x (32 + pad) elements of the output type) and store it as 16-byte vectors.
+// Wave-private: LDS accesses of one wave complete in order.
 template <typename Epi>
 __device__ __forceinline__ void epilogue_tile(const Epi& epi, typename Epi::out_t* ws, int mt,
                                               int nt, int lane, const f32x16& acc,
@@ -151,7 +155,7 @@ __device__ __forceinline__ void epilogue_tile(const Epi& epi, typename Epi::out_
   constexpr int CPR = 32 / EV;              // vectors per 32-element row
   constexpr int RPP = kWave / CPR;          // rows per pass
   const int lr = lane % 32, g = lane / 32;
-  const bool tr = epi.transposed(nt);
+  const TileDst<TO> dst = epi.tile(mt, nt);
   typedef typename VecT<TO, 4>::type t4;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -159,9 +163,9 @@ __device__ __forceinline__ void epilogue_tile(const Epi& epi, typename Epi::out_
     t4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = from_f32<TO>(epi.act(acc[4 * q + e] + to_f32(bq[q][e])));
-    if (tr) {
+    if (dst.tr) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ws[(nl + e) * LDW + lr] = o[e];  // LDS rows run along m
+      for (int e = 0; e < 4; ++e) ws[(nl + e) * LDW + lr] = o[e];  // LDS rows run along n
     } else {
       *(t4*)(ws + lr * LDW + nl) = o;
     }
@@ -170,8 +174,8 @@ __device__ __forceinline__ void epilogue_tile(const Epi& epi, typename Epi::out_
   for (int p = 0; p < 32 / RPP; ++p) {
     const int row = p * RPP + lane / CPR, c = (lane % CPR) * EV;
     const vec v = *(const vec*)(ws + row * LDW + c);
-    if (tr) epi.store_t(nt + row, mt + c, v);
-    else epi.store(mt + row, nt + c, v);
+    const bool ok = dst.tr ? epi.valid(mt + c, nt + row, 0, 0) : epi.valid(mt, nt, row, c);
+    if (ok) *(vec*)(dst.base + (size_t)row * dst.step + c) = v;
   }
 }
 
@@ -278,15 +282,17 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
       rb[i] = *(const frag*)(Bt + (size_t)min(n0 + r, N - 1) * K + min(k0 + kc, K - C::VEC));
     }
   };
-  auto sstore = [&](int buf, int k0) {
+  auto sstore_a = [&](int buf, int k0) {
     T* As = smem + buf * C::STAGE;
-    T* Bs = As + BM * C::LDS_STRIDE;
 #pragma unroll
     for (int i = 0; i < C::A_CH; ++i) {
       const int c = tid + i * C::NT;
       const int kc = (c % C::CPR) * C::VEC;
       *(frag*)(As + (c / C::CPR) * C::LDS_STRIDE + kc) = k0 + kc < K ? ra[i] : zero;
     }
+  };
+  auto sstore_b = [&](int buf, int k0) {
+    T* Bs = smem + buf * C::STAGE + BM * C::LDS_STRIDE;
 #pragma unroll
     for (int i = 0; i < C::B_CH; ++i) {
       const int c = tid + i * C::NT;
@@ -297,16 +303,20 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
 
   const int nk = (K + C::BK - 1) / C::BK;
   gload(0);
-  sstore(0, 0);
+  sstore_a(0, 0);
+  sstore_b(0, 0);
   __syncthreads();
   // MFMA fragments are double-buffered in registers (FDB): while the MFMAs of sub-step s
   // run, the fragments of sub-step s + 1 are read from LDS; the first sub-step of the next
-  // slab is read right after the barrier that publishes it.  The 256x256 tile has no room
-  // for the second set (it would spill), so it reads each sub-step's fragments just before
-  // their MFMAs.
+  // slab is read right after the barrier that publishes it.  The next slab's LDS writes
+  // (into the buffer every wave finished reading before the last barrier) are spread over
+  // the sub-steps -- A after the first, W^T after the third -- so they overlap the MFMAs of
+  // other waves instead of forming a write phase before the barrier.  The 256x256 tile has
+  // no room for the second fragment set (it would spill), so it reads each sub-step's
+  // fragments just before their MFMAs and writes the next slab at the end.
   constexpr int NS = C::BK / MF::KF;  // sub-steps per slab (even)
   constexpr bool FDB = C::TM + C::TN <= 5;
-  static_assert(NS % 2 == 0, "fragment double buffer assumes an even sub-step count");
+  static_assert(NS == 4, "the write placement assumes four sub-steps per slab");
   frag fa[FDB ? 2 : 1][C::TM], fb[FDB ? 2 : 1][C::TN];
   auto read_frags = [&](int buf, int s, int fbuf) {
     const T* As = smem + buf * C::STAGE + (wm * C::TM * 32 + lr) * C::LDS_STRIDE + g * C::VEC + s * MF::KF;
@@ -333,8 +343,17 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
       for (int j = 0; j < C::TN; ++j)
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) MF::mma(fb[s & X][j], fa[s & X][i], acc[j][i]);
+      if constexpr (FDB) {
+        if (s == 0 && kt + 1 < nk) sstore_a(cur ^ 1, (kt + 1) * C::BK);
+        if (s == 2 && kt + 1 < nk) sstore_b(cur ^ 1, (kt + 1) * C::BK);
+      }
     }
-    if (kt + 1 < nk) sstore(cur ^ 1, (kt + 1) * C::BK);
+    if constexpr (!FDB) {
+      if (kt + 1 < nk) {
+        sstore_a(cur ^ 1, (kt + 1) * C::BK);
+        sstore_b(cur ^ 1, (kt + 1) * C::BK);
+      }
+    }
     lds_barrier();
     if constexpr (FDB)
       if (kt + 1 < nk) read_frags(cur ^ 1, 0, 0);
