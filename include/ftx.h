@@ -79,13 +79,17 @@ typedef struct {
 /* Create an encoder for a fixed shape: the four runtime parameters of the article's
  * section "什么是 Faster Transformer" (head count, size per head, batch size, maximum
  * sentence length) plus the layer count and the storage dtype.
- *   batch_size >= 1; seq_len in [32, FTX_MAX_SEQ_LEN] and a multiple of 32;
+ *   batch_size >= 1; seq_len in [1, FTX_MAX_SEQ_LEN], any value (the article fixes it at
+ *   32/64/128 and names arbitrary lengths as its next feature: lengths that are not a
+ *   multiple of 32 are padded to one inside the handle, with an input and an output copy
+ *   per forward, and padding keys never take part in attention);
  *   size_per_head in {32, 64}; head_num >= 1 with head_num*size_per_head <= FTX_MAX_HIDDEN;
  *   num_layers >= 1; out != NULL (host pointer; receives the handle).
  * Non-positive values, an unknown dtype or out == NULL -> FTX_ERR_INVALID_ARG (no HIP call
  * is made).  Positive values outside the supported set -> FTX_ERR_UNSUPPORTED.
  * Allocates the workspace and the weight storage on the current device (hipMalloc):
- * about (10 B S H + L (12 H^2 + 13 H)) elements (plus 2 B S H fp32 values for FTX_BF16). */
+ * about (10 B S H + L (12 H^2 + 13 H)) elements (plus 2 B S H fp32 values for FTX_BF16,
+ * and 2 B S H elements when seq_len is not a multiple of 32; S = seq_len rounded up to 32). */
 ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int size_per_head,
                               int num_layers, ftx_dtype dtype, ftx_encoder **out);
 
@@ -100,7 +104,7 @@ ftx_status ftx_set_weights(ftx_encoder *enc, int layer, const ftx_layer_weights 
 /* Run the L-layer forward on `stream` (asynchronous: returns once enqueued).
  *   input    [B][S][H] device, 16-byte aligned, left unmodified;
  *   seq_lens [B] int32 device valid lengths, or NULL for "no padding".  Values are
- *            clamped to [1, S] on the device (the host cannot read them);
+ *            clamped to [1, seq_len] on the device (the host cannot read them);
  *   output   [B][S][H] device, 16-byte aligned, must not overlap input.
  * The caller keeps input, seq_lens and output alive until the stream passes the call.
  * FTX_ERR_NOT_READY if some layer has no weights. */

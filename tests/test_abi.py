@@ -67,7 +67,7 @@ def _create(lib, *args):
     ((1, 32, 12, 64, 0, 1), ftx.FTX_ERR_INVALID_ARG),      # no layers
     ((1, 32, 12, 64, 12, 7), ftx.FTX_ERR_INVALID_ARG),     # unknown dtype
     ((1, 32, 12, 48, 12, 1), ftx.FTX_ERR_UNSUPPORTED),     # head size 48
-    ((1, 100, 12, 64, 12, 1), ftx.FTX_ERR_UNSUPPORTED),    # seq not a multiple of 32
+    ((1, 513, 12, 64, 12, 1), ftx.FTX_ERR_UNSUPPORTED),    # seq above 512
     ((1, 1024, 12, 64, 12, 1), ftx.FTX_ERR_UNSUPPORTED),   # seq above 512
     ((1, 32, 65, 64, 1, 1), ftx.FTX_ERR_UNSUPPORTED),      # hidden above 4096
     ((1 << 20, 512, 16, 64, 1, 1), ftx.FTX_ERR_UNSUPPORTED),  # index range

@@ -214,6 +214,27 @@ def test_max_hidden_and_odd_heads():
         check(out, ref, shape.dtype, tol, f"{shape}")
 
 
+@pytest.mark.parametrize("shape,with_lens", [
+    (si.Shape(3, 100, 4, 32, 2, "fp16"), True),
+    (si.Shape(2, 100, 4, 32, 2, "fp16"), False),   # no seq_lens: keys limited to 100
+    (si.Shape(2, 1, 12, 64, 1, "fp32"), False),    # a single token
+    (si.Shape(2, 33, 2, 64, 2, "bf16"), True),
+    (si.Shape(1, 511, 2, 64, 1, "fp16"), True),
+    (si.Shape(4, 70, 12, 64, 1, "fp32"), True),
+])
+def test_ragged_sequence_lengths(shape, with_lens):
+    """Sequence lengths that are not a multiple of 32 (padded inside the handle)."""
+    c = si.custom_case(shape, 31 + shape.seq_len, params="random_affine",
+                       lens_range=(1, shape.seq_len) if with_lens else None)
+    layers = list(c.layers())
+    ref = oracle.encoder(c.x, layers, c.lens, shape.head_num)
+    enc = _encoder(shape, layers)
+    out = to_f64(enc.forward(to_dev(c.x, shape.dtype), dev_lens(c.lens)))
+    enc.close()
+    tol = stack_tol(shape.dtype) if shape.num_layers > 1 else layer_tol(shape.dtype)
+    check(out, ref, shape.dtype, tol, f"{shape} lens={with_lens}")
+
+
 def test_errors_on_device():
     c, layers = _case("single_layer_fp32", 1, "bert")
     enc = ftx.Encoder(1, 32, 4, 32, 1, "fp32")

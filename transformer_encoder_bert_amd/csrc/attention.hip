@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void attention_global_kernel(const T* __restri
                                                         const T* __restrict__ vt,
                                                         const int32_t* __restrict__ lens,
                                                         T* __restrict__ ctx, int B, int S, int nh,
-                                                        float scale_log2e) {
+                                                        float scale_log2e, int s_valid) {
   typedef AttnMfma<T> MF;
   typedef typename MF::frag frag;
   typedef typename VecT<T, 4>::type v4;
@@ -87,8 +87,8 @@ __global__ __launch_bounds__(256) void attention_global_kernel(const T* __restri
   if (task >= ntasks) return;
   const int bh = task / qblocks, qb = task % qblocks;
   const int b = bh / nh, h = bh % nh;
-  int len = lens ? lens[b] : S;
-  len = min(max(len, 1), S);
+  int len = lens ? lens[b] : s_valid;
+  len = min(max(len, 1), s_valid);
   const int nkt = (len + 31) / 32;
 
   frag qf[NQF];
@@ -229,7 +229,7 @@ template <typename T, int D, int SMAX>
 __global__ __launch_bounds__((AttnCfg<T, D, SMAX>::NW * kWave)) void attention_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt,
     const int32_t* __restrict__ lens, T* __restrict__ ctx, int B, int S, int nh,
-    float scale_log2e) {
+    float scale_log2e, int s_valid) {
   typedef AttnCfg<T, D, SMAX> C;
   typedef AttnMfma<T> MF;
   typedef typename MF::frag frag;
@@ -253,8 +253,8 @@ __global__ __launch_bounds__((AttnCfg<T, D, SMAX>::NW * kWave)) void attention_k
   const int lr = lane % 32, g = lane / 32;
   const int qb = grp * C::NW + wave;
   const bool active = qb < qblocks;
-  int len = lens ? lens[b] : S;
-  len = min(max(len, 1), S);
+  int len = lens ? lens[b] : s_valid;
+  len = min(max(len, 1), s_valid);
   const int nkt = (len + 31) / 32;
   const int nk = nkt * 32;  // keys held in LDS
 
@@ -407,46 +407,48 @@ constexpr size_t kMaxLdsBytes = 160 * 1024;  // per workgroup on gfx950
 template <typename T, int D, int SMAX>
 static hipError_t attn_launch_cfg(int B, int S, int nh, const void* q, const void* k,
                                   const void* vt, const int32_t* lens, void* ctx,
-                                  float scale_log2e, hipStream_t s) {
+                                  float scale_log2e, int s_valid, hipStream_t s) {
   typedef AttnCfg<T, D, SMAX> C;
   const int groups = (S / 32 + C::NW - 1) / C::NW;
   attention_kernel<T, D, SMAX><<<B * nh * groups, C::NW * kWave, 0, s>>>(
-      (const T*)q, (const T*)k, (const T*)vt, lens, (T*)ctx, B, S, nh, scale_log2e);
+      (const T*)q, (const T*)k, (const T*)vt, lens, (T*)ctx, B, S, nh, scale_log2e, s_valid);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t attn_launch_d(int B, int S, int nh, const void* q, const void* k,
                                 const void* vt, const int32_t* lens, void* ctx,
-                                float scale_log2e, hipStream_t s) {
-  if (S <= 32) return attn_launch_cfg<T, D, 32>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s);
-  if (S <= 64) return attn_launch_cfg<T, D, 64>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s);
-  if (S <= 128) return attn_launch_cfg<T, D, 128>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s);
-  if (S <= 256) return attn_launch_cfg<T, D, 256>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s);
+                                float scale_log2e, int s_valid, hipStream_t s) {
+  if (S <= 32) return attn_launch_cfg<T, D, 32>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, s);
+  if (S <= 64) return attn_launch_cfg<T, D, 64>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, s);
+  if (S <= 128) return attn_launch_cfg<T, D, 128>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, s);
+  if (S <= 256) return attn_launch_cfg<T, D, 256>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, s);
   if constexpr (AttnCfg<T, D, 512>::LDS * sizeof(T) <= kMaxLdsBytes)
-    return attn_launch_cfg<T, D, 512>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s);
+    return attn_launch_cfg<T, D, 512>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, s);
   const int blocks = (B * nh * (S / 32) + 3) / 4;
   attention_global_kernel<T, D><<<blocks, 256, 0, s>>>((const T*)q, (const T*)k, (const T*)vt, lens,
-                                                       (T*)ctx, B, S, nh, scale_log2e);
+                                                       (T*)ctx, B, S, nh, scale_log2e, s_valid);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t attn_launch(int B, int S, int nh, int d, const void* q, const void* k,
-                              const void* vt, const int32_t* lens, void* ctx, hipStream_t s) {
+                              const void* vt, const int32_t* lens, void* ctx, hipStream_t s,
+                              int s_valid) {
   const float scale_log2e = (float)(1.4426950408889634 / sqrt((double)d));
-  if (d == 64) return attn_launch_d<T, 64>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s);
-  if (d == 32) return attn_launch_d<T, 32>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s);
+  if (d == 64) return attn_launch_d<T, 64>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, s);
+  if (d == 32) return attn_launch_d<T, 32>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_attention(ftx_dtype dt, int B, int S, int nh, int d, const void* q,
                             const void* k, const void* vt, const int32_t* lens, void* ctx,
-                            hipStream_t s) {
+                            hipStream_t s, int s_valid) {
+  if (s_valid <= 0 || s_valid > S) s_valid = S;
   switch (dt) {
-    case FTX_FP32: return attn_launch<float>(B, S, nh, d, q, k, vt, lens, ctx, s);
-    case FTX_FP16: return attn_launch<f16>(B, S, nh, d, q, k, vt, lens, ctx, s);
-    case FTX_BF16: return attn_launch<bf16>(B, S, nh, d, q, k, vt, lens, ctx, s);
+    case FTX_FP32: return attn_launch<float>(B, S, nh, d, q, k, vt, lens, ctx, s, s_valid);
+    case FTX_FP16: return attn_launch<f16>(B, S, nh, d, q, k, vt, lens, ctx, s, s_valid);
+    case FTX_BF16: return attn_launch<bf16>(B, S, nh, d, q, k, vt, lens, ctx, s, s_valid);
   }
   return hipErrorInvalidValue;
 }

@@ -69,12 +69,16 @@ bool all_device(std::initializer_list<const void*> ps) {
   return true;
 }
 
-// Shape checks shared by create and the step entry points.
-ftx_status check_shape(int B, int S, int nh, int d) {
+// Shape checks shared by create and the step entry points.  The encoder takes any sequence
+// length up to FTX_MAX_SEQ_LEN (it pads internally to a multiple of 32); the step entry
+// points work on the padded layout and need the multiple of 32.
+ftx_status check_shape(int B, int S, int nh, int d, bool any_len = false) {
   if (B < 1 || S < 1 || nh < 1 || d < 1) return fail(FTX_ERR_INVALID_ARG, "shape values must be >= 1");
   if (d != 32 && d != 64) return fail(FTX_ERR_UNSUPPORTED, "size_per_head must be 32 or 64");
-  if (S % 32 != 0 || S > FTX_MAX_SEQ_LEN)
-    return fail(FTX_ERR_UNSUPPORTED, "seq_len must be a multiple of 32 in [32, 512]");
+  if (S > FTX_MAX_SEQ_LEN) return fail(FTX_ERR_UNSUPPORTED, "seq_len above 512");
+  if (!any_len && S % 32 != 0)
+    return fail(FTX_ERR_UNSUPPORTED, "the step entry points need seq_len a multiple of 32");
+  S = (S + 31) / 32 * 32;
   if ((long)nh * d > FTX_MAX_HIDDEN) return fail(FTX_ERR_UNSUPPORTED, "hidden size above 4096");
   // 32-bit element indices inside kernels: the largest tensor is [B*S][4H]
   if ((long long)B * S * 4 * nh * d >= (1LL << 31))
@@ -100,7 +104,8 @@ struct LayerW {
 }  // namespace
 
 struct ftx_encoder {
-  int B, S, nh, d, L, H, F, T;
+  int B, S, nh, d, L, H, F, T;  // S: internal (padded) length, a multiple of 32; T = B S
+  int Sv;                       // the caller's sequence length (S rounded up to 32 = S)
   ftx_dtype dt;
   size_t es;
   int device;
@@ -110,6 +115,7 @@ struct ftx_encoder {
   std::vector<char> ready;
   // workspace views
   void *q, *k, *vt, *ctx, *abuf, *y1, *u;
+  void *xpad = nullptr, *spad = nullptr;  // [B][S][H] input copy and layer state when Sv < S
   float* y1f = nullptr;  // fp32 copy of Y1, the residual of the second LayerNorm (bf16 only)
   int fused = 1;
   int timing = 0;
@@ -177,7 +183,7 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
   *out = nullptr;
   if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
   if (num_layers < 1) return fail(FTX_ERR_INVALID_ARG, "num_layers must be >= 1");
-  ftx_status st = check_shape(batch_size, seq_len, head_num, size_per_head);
+  ftx_status st = check_shape(batch_size, seq_len, head_num, size_per_head, true);
   if (st != FTX_OK) return st;
 
   int dev = 0;
@@ -190,13 +196,14 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
   ftx_encoder* e = new (std::nothrow) ftx_encoder();
   if (!e) return fail(FTX_ERR_OUT_OF_MEMORY, "host allocation");
   e->B = batch_size;
-  e->S = seq_len;
+  e->Sv = seq_len;
+  e->S = (seq_len + 31) / 32 * 32;
   e->nh = head_num;
   e->d = size_per_head;
   e->L = num_layers;
   e->H = head_num * size_per_head;
   e->F = 4 * e->H;
-  e->T = batch_size * seq_len;
+  e->T = batch_size * e->S;
   e->dt = dtype;
   e->es = dtype_size(dtype);
   e->device = dev;
@@ -218,8 +225,10 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
   // [2, 4) is 7.8e-3, and the LayerNorms pass such errors to the output with gain ~gamma.
   const bool f32res = dtype == FTX_BF16;
   const size_t TA = f32res ? pad(T * H * 4) : TH;  // abuf
+  const bool padded = e->Sv != e->S;
   const size_t ws_bytes = 3 * TH /*q,k,vt*/ + TH /*ctx*/ + TA /*abuf*/ + TH /*y1*/ +
-                          pad(T * F * es) /*u*/ + (f32res ? pad(T * H * 4) : 0) /*y1f*/;
+                          pad(T * F * es) /*u*/ + (f32res ? pad(T * H * 4) : 0) /*y1f*/ +
+                          (padded ? 2 * TH : 0) /*xpad, spad*/;
   err = hipMalloc(&e->ws, ws_bytes);
   if (err != hipSuccess) {
     hipFree(e->weights);
@@ -253,7 +262,24 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
   e->abuf = p; p += TA;
   e->y1 = p; p += TH;
   e->u = p; p += pad(T * F * es);
-  if (f32res) e->y1f = (float*)p;
+  if (f32res) {
+    e->y1f = (float*)p;
+    p += pad(T * H * 4);
+  }
+  if (padded) {
+    // the rows past Sv of each sequence are zero in the input copy (they are never written
+    // again) and finite in the state; neither reaches a row below Sv
+    e->xpad = p; p += TH;
+    e->spad = p; p += TH;
+    err = hipMemset(e->xpad, 0, 2 * TH);
+    if (err == hipSuccess) err = hipDeviceSynchronize();
+    if (err != hipSuccess) {
+      hipFree(e->ws);
+      hipFree(e->weights);
+      delete e;
+      return hip_fail(err, "hipMemset(padding)");
+    }
+  }
   *out = e;
   return FTX_OK;
 }
@@ -304,7 +330,7 @@ ftx_status ftx_forward(ftx_encoder* e, const void* input, const int32_t* seq_len
   if (!input || !output) return fail(FTX_ERR_INVALID_ARG, "input or output is NULL");
   if (!aligned16(input) || !aligned16(output))
     return fail(FTX_ERR_INVALID_ARG, "input and output must be 16-byte aligned");
-  const size_t bytes = (size_t)e->T * e->H * e->es;
+  const size_t bytes = (size_t)e->B * e->Sv * e->H * e->es;  // caller's [B][Sv][H]
   if (overlap(input, bytes, output, bytes)) return fail(FTX_ERR_INVALID_ARG, "output overlaps input");
   for (int l = 0; l < e->L; ++l)
     if (!e->ready[l]) return fail(FTX_ERR_NOT_READY, "layer " + std::to_string(l) + " has no weights");
@@ -314,9 +340,21 @@ ftx_status ftx_forward(ftx_encoder* e, const void* input, const int32_t* seq_len
   FTX_HIP(hipSetDevice(e->device));
   const ftx_dtype dt = e->dt;
   const int B = e->B, S = e->S, nh = e->nh, d = e->d, H = e->H, F = e->F, T = e->T;
+  // The stack's state lives in `output`, or -- when the caller's length Sv is not a multiple
+  // of 32 -- in the padded buffers: the input is copied to rows 0..Sv-1 of each sequence's
+  // S rows, the layers run at S, and rows 0..Sv-1 are copied back at the end.
+  const void* x0 = input;
+  void* state = output;
+  if (e->xpad) {
+    const size_t row = (size_t)H * e->es;
+    FTX_HIP(hipMemcpy2DAsync(e->xpad, S * row, input, e->Sv * row, e->Sv * row, B,
+                             hipMemcpyDeviceToDevice, s));
+    x0 = e->xpad;
+    state = e->spad;
+  }
   for (int l = 0; l < e->L; ++l) {
     const LayerW& w = e->layers[l];
-    const void* x = (l == 0) ? input : output;  // the stack's state lives in `output`
+    const void* x = (l == 0) ? x0 : state;
     ftx_status st;
     if (e->fused) {
       st = run_step(e, FTX_STEP_QKV_GEMM, s, [&] {
@@ -333,7 +371,7 @@ ftx_status ftx_forward(ftx_encoder* e, const void* input, const int32_t* seq_len
     }
     if (st != FTX_OK) return st;
     st = run_step(e, FTX_STEP_ATTENTION, s, [&] {
-      return launch_attention(dt, B, S, nh, d, e->q, e->k, e->vt, seq_lens, e->ctx, s);
+      return launch_attention(dt, B, S, nh, d, e->q, e->k, e->vt, seq_lens, e->ctx, s, e->Sv);
     });
     if (st != FTX_OK) return st;
     st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
@@ -368,10 +406,15 @@ ftx_status ftx_forward(ftx_encoder* e, const void* input, const int32_t* seq_len
     st = run_step(e, FTX_STEP_LN2, s, [&] {
       if (e->y1f)
         return launch_bias_residual_layernorm_f32res(dt, T, H, e->y1f, true, (const float*)e->abuf, w.b2,
-                                                     w.ln2_g, w.ln2_b, output, nullptr, s);
-      return launch_bias_residual_layernorm(dt, T, H, e->y1, e->abuf, w.b2, w.ln2_g, w.ln2_b, output, s);
+                                                     w.ln2_g, w.ln2_b, state, nullptr, s);
+      return launch_bias_residual_layernorm(dt, T, H, e->y1, e->abuf, w.b2, w.ln2_g, w.ln2_b, state, s);
     });
     if (st != FTX_OK) return st;
+  }
+  if (e->xpad) {
+    const size_t row = (size_t)H * e->es;
+    FTX_HIP(hipMemcpy2DAsync(output, e->Sv * row, state, S * row, e->Sv * row, B,
+                             hipMemcpyDeviceToDevice, s));
   }
   return FTX_OK;
 }

@@ -20,9 +20,11 @@ hipError_t launch_qkv_projection(ftx_dtype dt, int B, int S, int nh, int d, cons
 hipError_t launch_bias_qkv_split(ftx_dtype dt, int B, int S, int nh, int d, const void* qkv,
                                  const void* b_qkv, void* q, void* k, void* vt, hipStream_t s);
 
+// S: the (padded) length of the Q/K/V^T layout, a multiple of 32; s_valid (1..S, default S):
+// the sequence length keys are limited to when lens is NULL, and the bound lens are clamped to.
 hipError_t launch_attention(ftx_dtype dt, int B, int S, int nh, int d, const void* q,
                             const void* k, const void* vt, const int32_t* lens, void* ctx,
-                            hipStream_t s);
+                            hipStream_t s, int s_valid = 0);
 
 hipError_t launch_bias_residual_layernorm(ftx_dtype dt, int rows, int cols, const void* x,
                                           const void* a, const void* bias, const void* gamma,
