@@ -37,6 +37,7 @@ def parse():
     p.add_argument("--workload", default=None, help=f"default {WORKLOAD_DEFAULT}")
     p.add_argument("--batch", type=int, default=None)
     p.add_argument("--unfused", action="store_true", help="standalone bias+split and bias+GELU kernels")
+    p.add_argument("--graph", action="store_true", help="replay the forward as one HIP graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-kernel-times", action="store_true")
@@ -287,6 +288,8 @@ def main():
         enc.set_weights(l, {k: up(w[k]) for k in si.WEIGHT_NAMES})
     if args.unfused:
         enc.set_option(ftx.FTX_OPT_FUSED_EPILOGUES, 0)
+    if args.graph:
+        enc.set_option(ftx.FTX_OPT_GRAPH, 1)
     x = up(case.x)
     lens = None if case.lens is None else torch.from_numpy(case.lens).to(dev)
     out = torch.empty_like(x)
@@ -330,7 +333,8 @@ def main():
                    "seq_len": shape.seq_len, "layers": shape.num_layers,
                    "heads": shape.head_num, "size_per_head": shape.size_per_head,
                    "parallelism": "none (1 GPU)",
-                   "epilogues": "standalone" if args.unfused else "fused"},
+                   "epilogues": "standalone" if args.unfused else "fused",
+                   "launch": "hip graph" if args.graph else "stream"},
         "tflops": tflops, "frac_mfma_peak": tflops / PEAK_MFMA_TFLOPS[dt],
         "gpu_event_ms_per_step": gpu_ms / args.steps,
         "roofline": None, "cpu_baseline": None,

@@ -129,8 +129,16 @@ const char *ftx_last_error(void);
  *   FTX_OPT_KERNEL_TIMING (default 0): 1 = every forward records a HIP event pair around
  *     each launch, on the forward's stream, and accumulates per-step durations that
  *     ftx_kernel_times() returns.
+ *   FTX_OPT_GRAPH (default 0): 1 = ftx_forward replays one HIP graph of the whole forward
+ *     (the small-batch latency path: the article's small-batch bottleneck is kernel launch
+ *     count, section "Faster Transformer 优化原理").  The graph is captured, on a stream
+ *     the handle owns, at the first forward for a given (input, seq_lens, output) triple and
+ *     replayed on the caller's stream (the default stream included) while those three
+ *     pointers stay the same; other pointers cause a new capture.  Weights may change
+ *     between forwards (they live in handle memory the graph reads).  Ignored while
+ *     FTX_OPT_KERNEL_TIMING is on.
  * Unknown option -> FTX_ERR_INVALID_ARG. */
-typedef enum { FTX_OPT_FUSED_EPILOGUES = 0, FTX_OPT_KERNEL_TIMING = 1 } ftx_option;
+typedef enum { FTX_OPT_FUSED_EPILOGUES = 0, FTX_OPT_KERNEL_TIMING = 1, FTX_OPT_GRAPH = 2 } ftx_option;
 ftx_status ftx_set_option(ftx_encoder *enc, ftx_option option, int value);
 
 /* Step classes of the per-step timing. */

@@ -235,6 +235,41 @@ def test_ragged_sequence_lengths(shape, with_lens):
     check(out, ref, shape.dtype, tol, f"{shape} lens={with_lens}")
 
 
+@pytest.mark.parametrize("workload,batch,seq", [("bert_base_fp16_s32", 8, None),
+                                                ("bert_base_fp16_s128_varlen", 2, None),
+                                                ("bert_base_fp16_s32", 3, 100)])
+def test_graph_mode_replays_match_eager(workload, batch, seq):
+    """FTX_OPT_GRAPH: every replay equals the eager forward bitwise, with eager work on the
+    same stream between replays; new buffers trigger a new capture."""
+    c, layers = _case(workload, batch, "random_affine")
+    shape = c.shape if seq is None else si.Shape(batch, seq, c.shape.head_num, c.shape.size_per_head,
+                                                  c.shape.num_layers, c.shape.dtype)
+    if seq is not None:
+        c = si.custom_case(shape, 77, params="random_affine", lens_range=(1, seq))
+        layers = list(c.layers())
+    enc = _encoder(shape, layers)
+    x = to_dev(c.x, shape.dtype)
+    lens = dev_lens(c.lens)
+    ref = enc.forward(x, lens).clone()
+    enc.set_option(ftx.FTX_OPT_GRAPH, 1)
+    out = torch.empty_like(ref)
+    for i in range(4):
+        out.fill_(float("nan"))
+        enc.forward(x, lens, out)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i}"
+        junk = (x.float() * 3).sum()  # eager work on the stream between replays
+        torch.cuda.synchronize()
+    out2 = torch.empty_like(ref)
+    enc.forward(x, lens, out2)           # new output buffer: captured again
+    torch.cuda.synchronize()
+    assert torch.equal(out2, ref)
+    enc.set_option(ftx.FTX_OPT_GRAPH, 0)
+    assert torch.equal(enc.forward(x, lens), ref)
+    enc.close()
+    del junk
+
+
 def test_errors_on_device():
     c, layers = _case("single_layer_fp32", 1, "bert")
     enc = ftx.Encoder(1, 32, 4, 32, 1, "fp32")

@@ -119,6 +119,14 @@ struct ftx_encoder {
   float* y1f = nullptr;  // fp32 copy of Y1, the residual of the second LayerNorm (bf16 only)
   int fused = 1;
   int timing = 0;
+  int graph_mode = 0;
+  // graph of one whole forward, captured for the (input, seq_lens, output) it was made with
+  hipStream_t cap_stream = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t graph_exec = nullptr;
+  const void* g_in = nullptr;
+  const int32_t* g_lens = nullptr;
+  void* g_out = nullptr;
   struct Mark {
     hipEvent_t start, stop;
     int step;
@@ -154,6 +162,103 @@ ftx_status run_step(ftx_encoder* e, int step, hipStream_t s, F&& launch) {
   if (e->timing) {
     FTX_HIP(hipEventRecord(m.stop, s));
     e->marks.push_back(m);
+  }
+  return FTX_OK;
+}
+
+}  // namespace
+
+namespace {
+
+void drop_graph(ftx_encoder* e) {
+  if (e->graph_exec) hipGraphExecDestroy(e->graph_exec);
+  if (e->graph) hipGraphDestroy(e->graph);
+  e->graph_exec = nullptr;
+  e->graph = nullptr;
+  e->g_in = e->g_out = nullptr;
+  e->g_lens = nullptr;
+}
+
+// Enqueue the L-layer forward on `s` (arguments already validated).
+ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq_lens,
+                           void* output, hipStream_t s) {
+  const ftx_dtype dt = e->dt;
+  const int B = e->B, S = e->S, nh = e->nh, d = e->d, H = e->H, F = e->F, T = e->T;
+  // The stack's state lives in `output`, or -- when the caller's length Sv is not a multiple
+  // of 32 -- in the padded buffers: the input is copied to rows 0..Sv-1 of each sequence's
+  // S rows, the layers run at S, and rows 0..Sv-1 are copied back at the end.
+  const void* x0 = input;
+  void* state = output;
+  if (e->xpad) {
+    const size_t row = (size_t)H * e->es;
+    FTX_HIP(hipMemcpy2DAsync(e->xpad, S * row, input, e->Sv * row, e->Sv * row, B,
+                             hipMemcpyDeviceToDevice, s));
+    x0 = e->xpad;
+    state = e->spad;
+  }
+  for (int l = 0; l < e->L; ++l) {
+    const LayerW& w = e->layers[l];
+    const void* x = (l == 0) ? x0 : state;
+    ftx_status st;
+    if (e->fused) {
+      st = run_step(e, FTX_STEP_QKV_GEMM, s, [&] {
+        return launch_qkv_projection(dt, B, S, nh, d, x, w.w_qkv_t, w.b_qkv, e->q, e->k, e->vt, s);
+      });
+    } else {
+      st = run_step(e, FTX_STEP_QKV_GEMM, s, [&] {
+        return launch_linear(dt, T, 3 * H, H, x, w.w_qkv_t, nullptr, false, e->u, s);
+      });
+      if (st != FTX_OK) return st;
+      st = run_step(e, FTX_STEP_BIAS_QKV_SPLIT, s, [&] {
+        return launch_bias_qkv_split(dt, B, S, nh, d, e->u, w.b_qkv, e->q, e->k, e->vt, s);
+      });
+    }
+    if (st != FTX_OK) return st;
+    st = run_step(e, FTX_STEP_ATTENTION, s, [&] {
+      return launch_attention(dt, B, S, nh, d, e->q, e->k, e->vt, seq_lens, e->ctx, s, e->Sv);
+    });
+    if (st != FTX_OK) return st;
+    st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
+      return launch_linear(dt, T, H, H, e->ctx, w.w_o_t, nullptr, false, e->abuf, s, e->y1f != nullptr);
+    });
+    if (st != FTX_OK) return st;
+    st = run_step(e, FTX_STEP_LN1, s, [&] {
+      if (e->y1f)
+        return launch_bias_residual_layernorm_f32res(dt, T, H, x, false, (const float*)e->abuf, w.b_o, w.ln1_g,
+                                                     w.ln1_b, e->y1, e->y1f, s);
+      return launch_bias_residual_layernorm(dt, T, H, x, e->abuf, w.b_o, w.ln1_g, w.ln1_b, e->y1, s);
+    });
+    if (st != FTX_OK) return st;
+    if (e->fused) {
+      st = run_step(e, FTX_STEP_FFN1_GEMM, s, [&] {
+        return launch_linear(dt, T, F, H, e->y1, w.w1_t, w.b1, true, e->u, s);
+      });
+    } else {
+      st = run_step(e, FTX_STEP_FFN1_GEMM, s, [&] {
+        return launch_linear(dt, T, F, H, e->y1, w.w1_t, nullptr, false, e->u, s);
+      });
+      if (st != FTX_OK) return st;
+      st = run_step(e, FTX_STEP_BIAS_GELU, s, [&] {
+        return launch_bias_gelu(dt, T, F, e->u, w.b1, e->u, s);
+      });
+    }
+    if (st != FTX_OK) return st;
+    st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
+      return launch_linear(dt, T, H, F, e->u, w.w2_t, nullptr, false, e->abuf, s, e->y1f != nullptr);
+    });
+    if (st != FTX_OK) return st;
+    st = run_step(e, FTX_STEP_LN2, s, [&] {
+      if (e->y1f)
+        return launch_bias_residual_layernorm_f32res(dt, T, H, e->y1f, true, (const float*)e->abuf, w.b2,
+                                                     w.ln2_g, w.ln2_b, state, nullptr, s);
+      return launch_bias_residual_layernorm(dt, T, H, e->y1, e->abuf, w.b2, w.ln2_g, w.ln2_b, state, s);
+    });
+    if (st != FTX_OK) return st;
+  }
+  if (e->xpad) {
+    const size_t row = (size_t)H * e->es;
+    FTX_HIP(hipMemcpy2DAsync(output, e->Sv * row, state, S * row, e->Sv * row, B,
+                             hipMemcpyDeviceToDevice, s));
   }
   return FTX_OK;
 }
@@ -338,84 +443,34 @@ ftx_status ftx_forward(ftx_encoder* e, const void* input, const int32_t* seq_len
     return fail(FTX_ERR_INVALID_ARG, "input, output and seq_lens must be device memory");
   hipStream_t s = (hipStream_t)stream;
   FTX_HIP(hipSetDevice(e->device));
-  const ftx_dtype dt = e->dt;
-  const int B = e->B, S = e->S, nh = e->nh, d = e->d, H = e->H, F = e->F, T = e->T;
-  // The stack's state lives in `output`, or -- when the caller's length Sv is not a multiple
-  // of 32 -- in the padded buffers: the input is copied to rows 0..Sv-1 of each sequence's
-  // S rows, the layers run at S, and rows 0..Sv-1 are copied back at the end.
-  const void* x0 = input;
-  void* state = output;
-  if (e->xpad) {
-    const size_t row = (size_t)H * e->es;
-    FTX_HIP(hipMemcpy2DAsync(e->xpad, S * row, input, e->Sv * row, e->Sv * row, B,
-                             hipMemcpyDeviceToDevice, s));
-    x0 = e->xpad;
-    state = e->spad;
-  }
-  for (int l = 0; l < e->L; ++l) {
-    const LayerW& w = e->layers[l];
-    const void* x = (l == 0) ? x0 : state;
-    ftx_status st;
-    if (e->fused) {
-      st = run_step(e, FTX_STEP_QKV_GEMM, s, [&] {
-        return launch_qkv_projection(dt, B, S, nh, d, x, w.w_qkv_t, w.b_qkv, e->q, e->k, e->vt, s);
-      });
-    } else {
-      st = run_step(e, FTX_STEP_QKV_GEMM, s, [&] {
-        return launch_linear(dt, T, 3 * H, H, x, w.w_qkv_t, nullptr, false, e->u, s);
-      });
-      if (st != FTX_OK) return st;
-      st = run_step(e, FTX_STEP_BIAS_QKV_SPLIT, s, [&] {
-        return launch_bias_qkv_split(dt, B, S, nh, d, e->u, w.b_qkv, e->q, e->k, e->vt, s);
-      });
+  if (!e->graph_mode || e->timing) return enqueue_forward(e, input, seq_lens, output, s);
+
+  // graph mode: replay the captured forward if it was made for these buffers, else capture
+  // one on the handle's own stream (the caller's may be the default stream, which cannot be
+  // captured) and replay it on the caller's stream
+  if (!(e->graph_exec && e->g_in == input && e->g_lens == seq_lens && e->g_out == output)) {
+    drop_graph(e);
+    if (!e->cap_stream) FTX_HIP(hipStreamCreateWithFlags(&e->cap_stream, hipStreamNonBlocking));
+    FTX_HIP(hipStreamBeginCapture(e->cap_stream, hipStreamCaptureModeThreadLocal));
+    ftx_status st = enqueue_forward(e, input, seq_lens, output, e->cap_stream);
+    hipGraph_t g = nullptr;
+    hipError_t err = hipStreamEndCapture(e->cap_stream, &g);
+    if (st != FTX_OK) {
+      if (g) hipGraphDestroy(g);
+      return st;
     }
-    if (st != FTX_OK) return st;
-    st = run_step(e, FTX_STEP_ATTENTION, s, [&] {
-      return launch_attention(dt, B, S, nh, d, e->q, e->k, e->vt, seq_lens, e->ctx, s, e->Sv);
-    });
-    if (st != FTX_OK) return st;
-    st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
-      return launch_linear(dt, T, H, H, e->ctx, w.w_o_t, nullptr, false, e->abuf, s, e->y1f != nullptr);
-    });
-    if (st != FTX_OK) return st;
-    st = run_step(e, FTX_STEP_LN1, s, [&] {
-      if (e->y1f)
-        return launch_bias_residual_layernorm_f32res(dt, T, H, x, false, (const float*)e->abuf, w.b_o, w.ln1_g,
-                                                     w.ln1_b, e->y1, e->y1f, s);
-      return launch_bias_residual_layernorm(dt, T, H, x, e->abuf, w.b_o, w.ln1_g, w.ln1_b, e->y1, s);
-    });
-    if (st != FTX_OK) return st;
-    if (e->fused) {
-      st = run_step(e, FTX_STEP_FFN1_GEMM, s, [&] {
-        return launch_linear(dt, T, F, H, e->y1, w.w1_t, w.b1, true, e->u, s);
-      });
-    } else {
-      st = run_step(e, FTX_STEP_FFN1_GEMM, s, [&] {
-        return launch_linear(dt, T, F, H, e->y1, w.w1_t, nullptr, false, e->u, s);
-      });
-      if (st != FTX_OK) return st;
-      st = run_step(e, FTX_STEP_BIAS_GELU, s, [&] {
-        return launch_bias_gelu(dt, T, F, e->u, w.b1, e->u, s);
-      });
+    if (err != hipSuccess) return hip_fail(err, "hipStreamEndCapture");
+    e->graph = g;
+    err = hipGraphInstantiate(&e->graph_exec, g, nullptr, nullptr, 0);
+    if (err != hipSuccess) {
+      drop_graph(e);
+      return hip_fail(err, "hipGraphInstantiate");
     }
-    if (st != FTX_OK) return st;
-    st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
-      return launch_linear(dt, T, H, F, e->u, w.w2_t, nullptr, false, e->abuf, s, e->y1f != nullptr);
-    });
-    if (st != FTX_OK) return st;
-    st = run_step(e, FTX_STEP_LN2, s, [&] {
-      if (e->y1f)
-        return launch_bias_residual_layernorm_f32res(dt, T, H, e->y1f, true, (const float*)e->abuf, w.b2,
-                                                     w.ln2_g, w.ln2_b, state, nullptr, s);
-      return launch_bias_residual_layernorm(dt, T, H, e->y1, e->abuf, w.b2, w.ln2_g, w.ln2_b, state, s);
-    });
-    if (st != FTX_OK) return st;
+    e->g_in = input;
+    e->g_lens = seq_lens;
+    e->g_out = output;
   }
-  if (e->xpad) {
-    const size_t row = (size_t)H * e->es;
-    FTX_HIP(hipMemcpy2DAsync(output, e->Sv * row, state, S * row, e->Sv * row, B,
-                             hipMemcpyDeviceToDevice, s));
-  }
+  FTX_HIP(hipGraphLaunch(e->graph_exec, s));
   return FTX_OK;
 }
 
@@ -429,6 +484,8 @@ ftx_status ftx_destroy(ftx_encoder* e) {
     hipEventDestroy(m.stop);
   }
   for (auto ev : e->pool) hipEventDestroy(ev);
+  drop_graph(e);
+  if (e->cap_stream) hipStreamDestroy(e->cap_stream);
   hipFree(e->weights);
   hipFree(e->ws);
   delete e;
@@ -439,8 +496,15 @@ ftx_status ftx_set_option(ftx_encoder* e, ftx_option option, int value) {
   g_last_error.clear();
   if (!e) return fail(FTX_ERR_INVALID_ARG, "encoder is NULL");
   switch (option) {
-    case FTX_OPT_FUSED_EPILOGUES: e->fused = value ? 1 : 0; return FTX_OK;
+    case FTX_OPT_FUSED_EPILOGUES:
+      if (e->fused != (value ? 1 : 0)) drop_graph(e);  // the captured launch sequence changes
+      e->fused = value ? 1 : 0;
+      return FTX_OK;
     case FTX_OPT_KERNEL_TIMING: e->timing = value ? 1 : 0; return FTX_OK;
+    case FTX_OPT_GRAPH:
+      e->graph_mode = value ? 1 : 0;
+      if (!e->graph_mode) drop_graph(e);
+      return FTX_OK;
   }
   return fail(FTX_ERR_INVALID_ARG, "unknown option");
 }
