@@ -10,6 +10,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <initializer_list>
 #include <new>
 #include <string>
@@ -116,6 +117,8 @@ struct ftx_encoder {
   // workspace views
   void *q, *k, *vt, *ctx, *abuf, *y1, *u;
   void *xpad = nullptr, *spad = nullptr;  // [B][S][H] input copy and layer state when Sv < S
+  float* splitk = nullptr;                 // fp32 partial products of split-K projections
+  size_t splitk_elems = 0;
   float* y1f = nullptr;  // fp32 copy of Y1, the residual of the second LayerNorm (bf16 only)
   int fused = 1;
   int timing = 0;
@@ -202,11 +205,13 @@ ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq
     ftx_status st;
     if (e->fused) {
       st = run_step(e, FTX_STEP_QKV_GEMM, s, [&] {
-        return launch_qkv_projection(dt, B, S, nh, d, x, w.w_qkv_t, w.b_qkv, e->q, e->k, e->vt, s);
+        return launch_qkv_projection(dt, B, S, nh, d, x, w.w_qkv_t, w.b_qkv, e->q, e->k, e->vt, s,
+                                     e->splitk, e->splitk_elems);
       });
     } else {
       st = run_step(e, FTX_STEP_QKV_GEMM, s, [&] {
-        return launch_linear(dt, T, 3 * H, H, x, w.w_qkv_t, nullptr, false, e->u, s);
+        return launch_linear(dt, T, 3 * H, H, x, w.w_qkv_t, nullptr, false, e->u, s, false,
+                             e->splitk, e->splitk_elems);
       });
       if (st != FTX_OK) return st;
       st = run_step(e, FTX_STEP_BIAS_QKV_SPLIT, s, [&] {
@@ -219,7 +224,8 @@ ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq
     });
     if (st != FTX_OK) return st;
     st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
-      return launch_linear(dt, T, H, H, e->ctx, w.w_o_t, nullptr, false, e->abuf, s, e->y1f != nullptr);
+      return launch_linear(dt, T, H, H, e->ctx, w.w_o_t, nullptr, false, e->abuf, s, e->y1f != nullptr,
+                           e->splitk, e->splitk_elems);
     });
     if (st != FTX_OK) return st;
     st = run_step(e, FTX_STEP_LN1, s, [&] {
@@ -231,11 +237,13 @@ ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq
     if (st != FTX_OK) return st;
     if (e->fused) {
       st = run_step(e, FTX_STEP_FFN1_GEMM, s, [&] {
-        return launch_linear(dt, T, F, H, e->y1, w.w1_t, w.b1, true, e->u, s);
+        return launch_linear(dt, T, F, H, e->y1, w.w1_t, w.b1, true, e->u, s, false, e->splitk,
+                             e->splitk_elems);
       });
     } else {
       st = run_step(e, FTX_STEP_FFN1_GEMM, s, [&] {
-        return launch_linear(dt, T, F, H, e->y1, w.w1_t, nullptr, false, e->u, s);
+        return launch_linear(dt, T, F, H, e->y1, w.w1_t, nullptr, false, e->u, s, false, e->splitk,
+                             e->splitk_elems);
       });
       if (st != FTX_OK) return st;
       st = run_step(e, FTX_STEP_BIAS_GELU, s, [&] {
@@ -244,7 +252,8 @@ ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq
     }
     if (st != FTX_OK) return st;
     st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
-      return launch_linear(dt, T, H, F, e->u, w.w2_t, nullptr, false, e->abuf, s, e->y1f != nullptr);
+      return launch_linear(dt, T, H, F, e->u, w.w2_t, nullptr, false, e->abuf, s, e->y1f != nullptr,
+                           e->splitk, e->splitk_elems);
     });
     if (st != FTX_OK) return st;
     st = run_step(e, FTX_STEP_LN2, s, [&] {
@@ -385,6 +394,24 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
       return hip_fail(err, "hipMemset(padding)");
     }
   }
+  // split-K workspace: the largest any of the four projections plans for
+  {
+    const int Ti = e->T, Hi = e->H, Fi = e->F;
+    const size_t need = std::max(std::max(gemm_splitk_workspace(dtype, Ti, 3 * Hi, Hi),
+                                          gemm_splitk_workspace(dtype, Ti, Hi, Hi)),
+                                 std::max(gemm_splitk_workspace(dtype, Ti, Fi, Hi),
+                                          gemm_splitk_workspace(dtype, Ti, Hi, Fi)));
+    if (need) {
+      err = hipMalloc(&e->splitk, need * sizeof(float));
+      if (err != hipSuccess) {
+        hipFree(e->ws);
+        hipFree(e->weights);
+        delete e;
+        return hip_fail(err, "hipMalloc(split-K workspace)");
+      }
+      e->splitk_elems = need;
+    }
+  }
   *out = e;
   return FTX_OK;
 }
@@ -486,6 +513,7 @@ ftx_status ftx_destroy(ftx_encoder* e) {
   for (auto ev : e->pool) hipEventDestroy(ev);
   drop_graph(e);
   if (e->cap_stream) hipStreamDestroy(e->cap_stream);
+  if (e->splitk) hipFree(e->splitk);
   hipFree(e->weights);
   hipFree(e->ws);
   delete e;

@@ -23,6 +23,8 @@
 // so the four consecutive accumulator rows a lane holds are four consecutive columns n of
 // one output row m; the epilogue regroups them through LDS into 16-byte row vectors.
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -106,6 +108,13 @@ template <typename T, bool GELU, typename TO = T> struct EpiLinear {
   __device__ __forceinline__ bool valid(int mt, int nt, int r, int col) const {
     return mt + r < M && nt + col < N;
   }
+  // four finished columns n..n+3 of row m (the split-K reduction's store)
+  __device__ __forceinline__ void store4(int m, int n, const float (&v)[4]) const {
+    typename VecT<TO, 4>::type o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = from_f32<TO>(v[e]);
+    *(typename VecT<TO, 4>::type*)(c + (size_t)m * N + n) = o;
+  }
 };
 
 // bias + head split: a 32-column tile lies inside one of Q, K, V and inside one head (d is
@@ -139,7 +148,63 @@ template <typename T> struct EpiQKV {
   __device__ __forceinline__ bool valid(int mt, int nt, int, int) const {
     return mt < M && nt < N;
   }
+  // four finished columns n..n+3 of row m (the split-K reduction's store): they lie in one
+  // head of one of Q, K, V (d is a multiple of 4)
+  __device__ __forceinline__ void store4(int m, int n, const float (&v)[4]) const {
+    const int H = nh * d;
+    const int which = n / H, rem = n - which * H;
+    const int h = rem / d, dd = rem - h * d;
+    const int b = m / S, s = m - b * S;
+    const size_t head = (size_t)b * nh + h;
+    if (which < 2) {
+      b4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(v[e]);
+      *(b4*)((which == 0 ? q : k) + (head * S + s) * d + dd) = o;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vt[(head * d + dd + e) * S + s] = from_f32<T>(v[e]);
+    }
+  }
 };
+
+// Split-K partial products: the tile of K range blockIdx.y is written, unscaled and in fp32,
+// to P[blockIdx.y][M][N]; splitk_reduce_kernel then sums the ranges in order and applies
+// the real epilogue.
+struct EpiPartial {
+  typedef float out_t;
+  typedef f32x4 vec;
+  typedef f32x4 b4;
+  float* p;
+  int M, N;
+  __device__ __forceinline__ b4 bias4(int) const { return b4{}; }
+  __device__ __forceinline__ float act(float v) const { return v; }
+  __device__ __forceinline__ TileDst<float> tile(int mt, int nt) const {
+    return {p + (size_t)blockIdx.y * M * N + (size_t)mt * N + nt, N, false};
+  }
+  __device__ __forceinline__ bool valid(int mt, int nt, int r, int col) const {
+    return mt + r < M && nt + col < N;
+  }
+};
+
+// Sum of the split-K partials in split order (deterministic), then bias, activation and the
+// store of the epilogue `epi`; one thread per four consecutive columns of a row.
+template <typename Epi>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P,
+                                                            int splits, int M, int N, Epi epi) {
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int q4 = N / 4;
+  if (idx >= (int64_t)M * q4) return;
+  const int m = (int)(idx / q4), n = (int)(idx % q4) * 4;
+  const size_t mn = (size_t)M * N;
+  f32x4 acc = *(const f32x4*)(P + (size_t)m * N + n);
+  for (int z = 1; z < splits; ++z) acc += *(const f32x4*)(P + z * mn + (size_t)m * N + n);
+  const auto bv = epi.bias4(n);
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = epi.act(acc[e] + to_f32(bv[e]));
+  epi.store4(m, n, v);
+}
 
 // Stage one C^T tile (columns nt.., rows mt..) through this wave's LDS scratch `ws`
 // (32 x (32 + pad) elements of the output type) and store it as 16-byte vectors.
@@ -226,10 +291,12 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
   tn = in_group / gsz;
 }
 
+// K range of this block: [blockIdx.y * kchunk, min(K, (blockIdx.y + 1) * kchunk)); kchunk is
+// K (one range) or, under split-K, a multiple of the slab depth.
 template <typename T, int BM, int BN, int WM, int WN, typename Epi>
 __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restrict__ A,
                                                                const T* __restrict__ Bt, int M,
-                                                               int N, int K, Epi epi) {
+                                                               int N, int K, int kchunk, Epi epi) {
   typedef GemmCfg<T, BM, BN, WM, WN> C;
   typedef typename C::MF MF;
   typedef typename MF::frag frag;
@@ -259,6 +326,10 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
 #pragma unroll
     for (int q = 0; q < 4; ++q) bq[j][q] = epi.bias4(n0 + (wn * C::TN + j) * 32 + 8 * q + 4 * g);
 
+  // this block's K range: kn elements from kb; slab offsets k0 below are relative to kb
+  const int kb = blockIdx.y * kchunk;
+  const int kn = min(K - kb, kchunk);
+
   // the next K slab, fetched into registers while the current one is multiplied
   frag ra[C::A_CH], rb[C::B_CH];
   const frag zero = {};
@@ -266,20 +337,20 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
   // Loads past the last row or K column read a clamped in-range address, with no branch
   // around the load, so the compiler can count the loads still in flight exactly instead of
   // draining them at a control-flow merge.  Rows past M (of A) or N (of W^T) only feed
-  // outputs that are never stored; K columns past K are zeroed when the slab is written to
-  // LDS, where the loaded data is needed anyway.
+  // outputs that are never stored; K columns past the block's range are zeroed when the
+  // slab is written to LDS, where the loaded data is needed anyway.
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < C::A_CH; ++i) {
       const int c = tid + i * C::NT;
       const int r = c / C::CPR, kc = (c % C::CPR) * C::VEC;
-      ra[i] = *(const frag*)(A + (size_t)min(m0 + r, M - 1) * K + min(k0 + kc, K - C::VEC));
+      ra[i] = *(const frag*)(A + (size_t)min(m0 + r, M - 1) * K + min(kb + k0 + kc, K - C::VEC));
     }
 #pragma unroll
     for (int i = 0; i < C::B_CH; ++i) {
       const int c = tid + i * C::NT;
       const int r = c / C::CPR, kc = (c % C::CPR) * C::VEC;
-      rb[i] = *(const frag*)(Bt + (size_t)min(n0 + r, N - 1) * K + min(k0 + kc, K - C::VEC));
+      rb[i] = *(const frag*)(Bt + (size_t)min(n0 + r, N - 1) * K + min(kb + k0 + kc, K - C::VEC));
     }
   };
   auto sstore_a = [&](int buf, int k0) {
@@ -288,7 +359,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
     for (int i = 0; i < C::A_CH; ++i) {
       const int c = tid + i * C::NT;
       const int kc = (c % C::CPR) * C::VEC;
-      *(frag*)(As + (c / C::CPR) * C::LDS_STRIDE + kc) = k0 + kc < K ? ra[i] : zero;
+      *(frag*)(As + (c / C::CPR) * C::LDS_STRIDE + kc) = k0 + kc < kn ? ra[i] : zero;
     }
   };
   auto sstore_b = [&](int buf, int k0) {
@@ -297,11 +368,11 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
     for (int i = 0; i < C::B_CH; ++i) {
       const int c = tid + i * C::NT;
       const int kc = (c % C::CPR) * C::VEC;
-      *(frag*)(Bs + (c / C::CPR) * C::LDS_STRIDE + kc) = k0 + kc < K ? rb[i] : zero;
+      *(frag*)(Bs + (c / C::CPR) * C::LDS_STRIDE + kc) = k0 + kc < kn ? rb[i] : zero;
     }
   };
 
-  const int nk = (K + C::BK - 1) / C::BK;
+  const int nk = (kn + C::BK - 1) / C::BK;
   gload(0);
   sstore_a(0, 0);
   sstore_b(0, 0);
@@ -385,8 +456,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
 //    64x64,  4 waves (2 x 2),  37 KB LDS: 0.12, 4 blocks per CU
 //    32x32,  1 wave,           18 KB LDS: 0.05, 8 blocks per CU
 // The modelled time of a launch is (rounds of blocks over the 256 CUs) x (one block's
-// time); the candidate with the least modelled time wins, so small batches get small
-// tiles that still spread over every CU.  fp32 (twice the register footprint per element)
+// time, longer when several blocks share a CU); the candidate with the least modelled time
+// wins, so small batches get small tiles that still spread over every CU.  fp32 (twice the register footprint per element)
 // uses the table without its two largest tiles.
 
 enum TileCfg { TILE_256x256, TILE_256x192, TILE_256x128, TILE_128x128, TILE_64x64, TILE_32x32, TILE_COUNT };
@@ -402,8 +473,11 @@ static TileCfg choose_tile(int M, int N, bool wide) {
     const Cand& x = cand[c];
     const long tiles = (long)((M + x.bm - 1) / x.bm) * ((N + x.bn - 1) / x.bn);
     const long rounds = (tiles + (long)kCUs * x.per_cu - 1) / ((long)kCUs * x.per_cu);
-    // a block's time: its tile's work at its efficiency, shared with the other blocks on the CU
-    const double t = (double)rounds * x.bm * x.bn * x.per_cu / x.eff;
+    // blocks that share a CU in a round: up to per_cu, but no more than the grid puts there
+    const long share = std::min<long>(x.per_cu, (tiles + kCUs - 1) / kCUs);
+    // a block's time: its tile's work (MFMAs run on the whole tile, also on rows past M) at
+    // its efficiency, shared with the other blocks on its CU
+    const double t = (double)rounds * x.bm * x.bn * share / x.eff;
     if (t < best_t * 0.999) {
       best_t = t;
       best = c;
@@ -412,30 +486,80 @@ static TileCfg choose_tile(int M, int N, bool wide) {
   return (TileCfg)best;
 }
 
+// Split-K (the small-batch path): when the chosen configuration has fewer tiles than there
+// are CUs, K is cut into up to 16 ranges of at least two slabs each, so that
+// about 512 blocks run; the partial products go to an fp32 workspace [splits][M][N] and a
+// reduction kernel finishes them.  The partials are capped at 16 MiB (fewer splits, or
+// none): their round trip through memory must stay small against what the split saves --
+// at 4096 rows a 6-way split of the 768-wide projections would move 75 MB and lose.
+// Without a workspace of the planned size the GEMM is not split.
+struct GemmPlan {
+  TileCfg cfg;
+  int splits;  // 1 = no split
+  int kchunk;  // K elements per split (K when splits == 1)
+};
+
+static GemmPlan plan_gemm(int M, int N, int K, int elem_bytes) {
+  static const int bm[TILE_COUNT] = {256, 256, 256, 128, 64, 32};
+  static const int bn[TILE_COUNT] = {256, 192, 128, 128, 64, 32};
+  GemmPlan p{choose_tile(M, N, elem_bytes == 2), 1, K};
+  const int bk = 128 / elem_bytes;
+  const long tiles = (long)((M + bm[p.cfg] - 1) / bm[p.cfg]) * ((N + bn[p.cfg] - 1) / bn[p.cfg]);
+  const int nk = (K + bk - 1) / bk;
+  if (tiles < 256 && nk >= 4) {
+    constexpr size_t kMaxPartialBytes = 16u << 20;
+    const long by_bytes = (long)(kMaxPartialBytes / ((size_t)M * N * sizeof(float)));
+    int sp = (int)std::min<long>(std::min<long>((512 + tiles - 1) / tiles, nk / 2),
+                                 std::min<long>(16, by_bytes));
+    if (sp > 1) {
+      p.kchunk = (nk + sp - 1) / sp * bk;
+      p.splits = (K + p.kchunk - 1) / p.kchunk;
+    }
+  }
+  return p;
+}
+
+size_t gemm_splitk_workspace(ftx_dtype dt, int M, int N, int K) {
+  const GemmPlan p = plan_gemm(M, N, K, dt == FTX_FP32 ? 4 : 2);
+  return p.splits > 1 ? (size_t)p.splits * M * N : 0;
+}
+
 template <typename T, int BM, int BN, int WM, int WN, typename Epi>
 static hipError_t gemm_launch_cfg(int M, int N, int K, const void* a, const void* w_t, Epi epi,
-                                  hipStream_t s) {
+                                  const GemmPlan& plan, float* ws, hipStream_t s) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  gemm_kernel<T, BM, BN, WM, WN, Epi><<<tiles, WM * WN * kWave, 0, s>>>(
-      (const T*)a, (const T*)w_t, M, N, K, epi);
+  if (plan.splits > 1) {
+    gemm_kernel<T, BM, BN, WM, WN, EpiPartial><<<dim3(tiles, plan.splits), WM * WN * kWave, 0, s>>>(
+        (const T*)a, (const T*)w_t, M, N, K, plan.kchunk, EpiPartial{ws, M, N});
+    const int64_t threads = (int64_t)M * (N / 4);
+    splitk_reduce_kernel<Epi><<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(ws, plan.splits, M, N, epi);
+  } else {
+    gemm_kernel<T, BM, BN, WM, WN, Epi><<<tiles, WM * WN * kWave, 0, s>>>(
+        (const T*)a, (const T*)w_t, M, N, K, K, epi);
+  }
   return hipGetLastError();
 }
 
 template <typename T, typename Epi>
 static hipError_t gemm_launch(int M, int N, int K, const void* a, const void* w_t, Epi epi,
-                              hipStream_t s) {
+                              hipStream_t s, float* ws = nullptr, size_t ws_elems = 0) {
   constexpr bool wide = sizeof(T) == 2;
-  switch (choose_tile(M, N, wide)) {
+  GemmPlan plan = plan_gemm(M, N, K, (int)sizeof(T));
+  if (plan.splits > 1 && (!ws || ws_elems < (size_t)plan.splits * M * N)) {
+    plan.splits = 1;
+    plan.kchunk = K;
+  }
+  switch (plan.cfg) {
     case TILE_256x256:
-      if constexpr (wide) return gemm_launch_cfg<T, 256, 256, 4, 2>(M, N, K, a, w_t, epi, s);
+      if constexpr (wide) return gemm_launch_cfg<T, 256, 256, 4, 2>(M, N, K, a, w_t, epi, plan, ws, s);
       break;
     case TILE_256x192:
-      if constexpr (wide) return gemm_launch_cfg<T, 256, 192, 4, 2>(M, N, K, a, w_t, epi, s);
+      if constexpr (wide) return gemm_launch_cfg<T, 256, 192, 4, 2>(M, N, K, a, w_t, epi, plan, ws, s);
       break;
-    case TILE_256x128: return gemm_launch_cfg<T, 256, 128, 4, 2>(M, N, K, a, w_t, epi, s);
-    case TILE_128x128: return gemm_launch_cfg<T, 128, 128, 2, 2>(M, N, K, a, w_t, epi, s);
-    case TILE_64x64: return gemm_launch_cfg<T, 64, 64, 2, 2>(M, N, K, a, w_t, epi, s);
-    case TILE_32x32: return gemm_launch_cfg<T, 32, 32, 1, 1>(M, N, K, a, w_t, epi, s);
+    case TILE_256x128: return gemm_launch_cfg<T, 256, 128, 4, 2>(M, N, K, a, w_t, epi, plan, ws, s);
+    case TILE_128x128: return gemm_launch_cfg<T, 128, 128, 2, 2>(M, N, K, a, w_t, epi, plan, ws, s);
+    case TILE_64x64: return gemm_launch_cfg<T, 64, 64, 2, 2>(M, N, K, a, w_t, epi, plan, ws, s);
+    case TILE_32x32: return gemm_launch_cfg<T, 32, 32, 1, 1>(M, N, K, a, w_t, epi, plan, ws, s);
     default: break;
   }
   return hipErrorInvalidValue;
@@ -443,40 +567,42 @@ static hipError_t gemm_launch(int M, int N, int K, const void* a, const void* w_
 
 template <typename T>
 static hipError_t linear_t(int M, int N, int K, const void* a, const void* w_t, const void* bias,
-                           bool gelu, bool out_f32, void* c, hipStream_t s) {
+                           bool gelu, bool out_f32, void* c, hipStream_t s, float* ws,
+                           size_t wn) {
   if (out_f32) {
-    if (gelu) return gemm_launch<T>(M, N, K, a, w_t, EpiLinear<T, true, float>{(float*)c, (const T*)bias, M, N}, s);
-    return gemm_launch<T>(M, N, K, a, w_t, EpiLinear<T, false, float>{(float*)c, (const T*)bias, M, N}, s);
+    if (gelu) return gemm_launch<T>(M, N, K, a, w_t, EpiLinear<T, true, float>{(float*)c, (const T*)bias, M, N}, s, ws, wn);
+    return gemm_launch<T>(M, N, K, a, w_t, EpiLinear<T, false, float>{(float*)c, (const T*)bias, M, N}, s, ws, wn);
   }
-  if (gelu) return gemm_launch<T>(M, N, K, a, w_t, EpiLinear<T, true>{(T*)c, (const T*)bias, M, N}, s);
-  return gemm_launch<T>(M, N, K, a, w_t, EpiLinear<T, false>{(T*)c, (const T*)bias, M, N}, s);
+  if (gelu) return gemm_launch<T>(M, N, K, a, w_t, EpiLinear<T, true>{(T*)c, (const T*)bias, M, N}, s, ws, wn);
+  return gemm_launch<T>(M, N, K, a, w_t, EpiLinear<T, false>{(T*)c, (const T*)bias, M, N}, s, ws, wn);
 }
 
 hipError_t launch_linear(ftx_dtype dt, int M, int N, int K, const void* a, const void* w_t,
-                         const void* bias, bool gelu, void* c, hipStream_t s, bool out_f32) {
+                         const void* bias, bool gelu, void* c, hipStream_t s, bool out_f32,
+                         float* ws, size_t ws_elems) {
   switch (dt) {
-    case FTX_FP32: return linear_t<float>(M, N, K, a, w_t, bias, gelu, false, c, s);
-    case FTX_FP16: return linear_t<f16>(M, N, K, a, w_t, bias, gelu, out_f32, c, s);
-    case FTX_BF16: return linear_t<bf16>(M, N, K, a, w_t, bias, gelu, out_f32, c, s);
+    case FTX_FP32: return linear_t<float>(M, N, K, a, w_t, bias, gelu, false, c, s, ws, ws_elems);
+    case FTX_FP16: return linear_t<f16>(M, N, K, a, w_t, bias, gelu, out_f32, c, s, ws, ws_elems);
+    case FTX_BF16: return linear_t<bf16>(M, N, K, a, w_t, bias, gelu, out_f32, c, s, ws, ws_elems);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
 static hipError_t qkv_t(int B, int S, int nh, int d, const void* x, const void* w, const void* b,
-                        void* q, void* k, void* vt, hipStream_t s) {
+                        void* q, void* k, void* vt, hipStream_t s, float* ws, size_t wn) {
   const int M = B * S, H = nh * d;
   EpiQKV<T> epi{(T*)q, (T*)k, (T*)vt, (const T*)b, S, nh, d, M, 3 * H};
-  return gemm_launch<T>(M, 3 * H, H, x, w, epi, s);
+  return gemm_launch<T>(M, 3 * H, H, x, w, epi, s, ws, wn);
 }
 
 hipError_t launch_qkv_projection(ftx_dtype dt, int B, int S, int nh, int d, const void* x,
                                  const void* w_qkv_t, const void* b_qkv, void* q, void* k,
-                                 void* vt, hipStream_t s) {
+                                 void* vt, hipStream_t s, float* ws, size_t ws_elems) {
   switch (dt) {
-    case FTX_FP32: return qkv_t<float>(B, S, nh, d, x, w_qkv_t, b_qkv, q, k, vt, s);
-    case FTX_FP16: return qkv_t<f16>(B, S, nh, d, x, w_qkv_t, b_qkv, q, k, vt, s);
-    case FTX_BF16: return qkv_t<bf16>(B, S, nh, d, x, w_qkv_t, b_qkv, q, k, vt, s);
+    case FTX_FP32: return qkv_t<float>(B, S, nh, d, x, w_qkv_t, b_qkv, q, k, vt, s, ws, ws_elems);
+    case FTX_FP16: return qkv_t<f16>(B, S, nh, d, x, w_qkv_t, b_qkv, q, k, vt, s, ws, ws_elems);
+    case FTX_BF16: return qkv_t<bf16>(B, S, nh, d, x, w_qkv_t, b_qkv, q, k, vt, s, ws, ws_elems);
   }
   return hipErrorInvalidValue;
 }

@@ -9,13 +9,19 @@
 namespace ftx {
 
 // out_f32: c is written as fp32 (16-bit dtypes; ignored in fp32 mode).
+// ws / ws_elems: fp32 workspace for split-K; a GEMM whose plan splits K runs unsplit when
+// the workspace is missing or smaller than gemm_splitk_workspace() says.
 hipError_t launch_linear(ftx_dtype dt, int M, int N, int K, const void* a, const void* w_t,
                          const void* bias, bool gelu, void* c, hipStream_t s,
-                         bool out_f32 = false);
+                         bool out_f32 = false, float* ws = nullptr, size_t ws_elems = 0);
 
 hipError_t launch_qkv_projection(ftx_dtype dt, int B, int S, int nh, int d, const void* x,
                                  const void* w_qkv_t, const void* b_qkv, void* q, void* k,
-                                 void* vt, hipStream_t s);
+                                 void* vt, hipStream_t s, float* ws = nullptr,
+                                 size_t ws_elems = 0);
+
+// fp32 elements of split-K workspace the GEMM of this shape uses (0: it does not split).
+size_t gemm_splitk_workspace(ftx_dtype dt, int M, int N, int K);
 
 hipError_t launch_bias_qkv_split(ftx_dtype dt, int B, int S, int nh, int d, const void* qkv,
                                  const void* b_qkv, void* q, void* k, void* vt, hipStream_t s);
