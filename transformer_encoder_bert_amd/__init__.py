@@ -3,6 +3,7 @@
 The compute path is libftx.so (hand-written HIP kernels behind a C ABI, see
 include/ftx.h); ``transformer_encoder_bert_amd.ftx`` is its ctypes binding.  Importing
 this package does not load the library; the binding loads it on first use and raises
-if it has not been built.
+if it has not been built.  ``transformer_encoder_bert_amd.torch_op`` registers the forward
+as the PyTorch operator ``torch.ops.ftx.encoder_forward``.
 """
-__all__ = ["ftx"]
+__all__ = ["ftx", "torch_op"]
