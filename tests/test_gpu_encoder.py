@@ -149,7 +149,12 @@ def test_deterministic_and_input_untouched():
 
 
 def test_batch_slices_match_the_batch():
-    """Sequence b run alone equals sequence b run inside the batch (batch independence)."""
+    """Sequence b run alone equals sequence b run inside the batch (batch independence).
+
+    The two runs take different GEMM tilings (one sequence is 128 rows, which the planner
+    splits along K), so they agree to rounding, not bit for bit: after 12 fp16 layers a few
+    outputs near 6 differ by 4 ulp (0.016).  A leak across sequences moves outputs by O(1),
+    so the bar is the stack tolerance each run meets against the oracle."""
     c, layers = _case("bert_base_fp16_s128_varlen", 4, "random_affine")
     enc = _encoder(c.shape, layers)
     full = to_f64(enc.forward(to_dev(c.x, "fp16"), dev_lens(c.lens)))
@@ -158,7 +163,7 @@ def test_batch_slices_match_the_batch():
     enc1 = _encoder(one, layers)
     for b in (0, 3):
         o = to_f64(enc1.forward(to_dev(c.x[b:b + 1], "fp16"), dev_lens(c.lens[b:b + 1])))
-        assert_within(o[0], full[b], 1e-2, 0.0, f"sequence {b}")
+        assert_within(o[0], full[b], 5e-2, 0.0, f"sequence {b}")
     enc1.close()
 
 
@@ -268,6 +273,20 @@ def test_graph_mode_replays_match_eager(workload, batch, seq):
     assert torch.equal(enc.forward(x, lens), ref)
     enc.close()
     del junk
+
+
+def test_torch_operator_matches_the_c_abi():
+    """torch.ops.ftx.encoder_forward (and the nn.Module around it) is ftx_forward."""
+    from transformer_encoder_bert_amd import torch_op
+    c, layers = _case("bert_base_fp16_s128_varlen", 4, "random_affine")
+    enc = _encoder(c.shape, layers)
+    x = to_dev(c.x, "fp16")
+    lens = dev_lens(c.lens)
+    ref = enc.forward(x, lens).clone()
+    mod = torch_op.EncoderModule(enc)
+    assert torch.equal(mod(x, lens), ref)
+    assert torch.equal(torch.ops.ftx.encoder_forward(x, lens, mod.op_id), ref)
+    mod.close()
 
 
 def test_errors_on_device():

@@ -181,7 +181,8 @@ def test_attention_lens_are_clamped(dtype):
 # ------------------------------------------------------------------------------ LayerNorm, GELU
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("rows,cols", [(1, 128), (33, 768), (64, 1024), (5, 96), (7, 2048), (3, 4096), (4, 200)])
+@pytest.mark.parametrize("rows,cols", [(1, 128), (33, 768), (64, 1024), (5, 96), (7, 2048), (3, 4096),
+                                       (4, 200), (2, 36), (3, 260), (2, 1000), (9, 384), (5, 512)])
 def test_bias_residual_layernorm(dtype, rows, cols):
     rng = np.random.default_rng(rows * 3 + cols)
     x = _rand(rng, (rows, cols), dtype)

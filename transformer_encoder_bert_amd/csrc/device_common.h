@@ -15,6 +15,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
@@ -24,6 +25,7 @@ template <typename T, int N> struct VecT;
 template <> struct VecT<float, 1> { typedef float type; };
 template <> struct VecT<float, 2> { typedef f32x2 type; };
 template <> struct VecT<float, 4> { typedef f32x4 type; };
+template <> struct VecT<float, 8> { typedef f32x8 type; };
 template <> struct VecT<f16, 4> { typedef f16x4 type; };
 template <> struct VecT<f16, 8> { typedef f16x8 type; };
 template <> struct VecT<bf16, 4> { typedef bf16x4 type; };

@@ -16,40 +16,42 @@ namespace ftx {
 
 // ------------------------------------------------------------------------------------
 // bias + residual + LayerNorm: y = gamma * (z - mean) * rsqrt(var + eps) + beta,
-// z = x + a + bias.  LPR lanes own one row; each lane holds MAXV 4-element vectors,
-// vector v of a lane sits at column 4 * (v * LPR + sub) so that a wave's loads of one v
-// are contiguous.  EXACT: every lane owns exactly MAXV vectors (cols == 4 * LPR * MAXV).
+// z = x + a + bias.  LPR lanes own one row; each lane holds MAXV vectors of EV elements,
+// vector v of a lane sits at column EV * (v * LPR + sub) so that a wave's loads of one v
+// are contiguous.  EXACT: every lane owns exactly MAXV vectors (cols == EV * LPR * MAXV).
+// EV = 8 for 16-bit data (16-byte vectors) when rows allow it, else 4.
 // TX and TA are the types of the residual x and the branch a (T, or float when the
 // residual stream is kept in fp32); yf, when non-null, receives an fp32 copy of y.
-template <typename T, typename TX, typename TA, int LPR, int MAXV, bool EXACT>
+template <typename T, typename TX, typename TA, int EV, int LPR, int MAXV, bool EXACT>
 __global__ __launch_bounds__(256) void layernorm_kernel(const TX* __restrict__ x,
                                                         const TA* __restrict__ a,
                                                         const T* __restrict__ bias,
                                                         const T* __restrict__ gamma,
                                                         const T* __restrict__ beta,
                                                         T* y, float* yf, int rows, int cols) {
-  typedef typename VecT<T, 4>::type v4;
-  typedef typename VecT<TX, 4>::type x4;
-  typedef typename VecT<TA, 4>::type a4;
+  typedef typename VecT<T, EV>::type tv;
+  typedef typename VecT<TX, EV>::type xv_t;
+  typedef typename VecT<TA, EV>::type av_t;
+  typedef typename VecT<float, EV>::type fv;
   constexpr int RPW = kWave / LPR;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int row = (blockIdx.x * (blockDim.x / kWave) + wave) * RPW + lane / LPR;
   const int sub = lane % LPR;
   if (row >= rows) return;  // whole LPR-lane groups leave together
-  const int nvec = cols / 4;
+  const int nvec = cols / EV;
   const size_t base = (size_t)row * cols;
 
-  float z[MAXV][4];
+  float z[MAXV][EV];
   float sum = 0.f;
 #pragma unroll
   for (int v = 0; v < MAXV; ++v) {
     const int vi = v * LPR + sub;
     if (EXACT || vi < nvec) {
-      const x4 xv = *(const x4*)(x + base + 4 * vi);
-      const a4 av = *(const a4*)(a + base + 4 * vi);
-      const v4 bv = *(const v4*)(bias + 4 * vi);
+      const xv_t xv = *(const xv_t*)(x + base + EV * vi);
+      const av_t av = *(const av_t*)(a + base + EV * vi);
+      const tv bv = *(const tv*)(bias + EV * vi);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < EV; ++e) {
         z[v][e] = to_f32(xv[e]) + to_f32(av[e]) + to_f32(bv[e]);
         sum += z[v][e];
       }
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const TX* __restrict__ x
     const int vi = v * LPR + sub;
     if (EXACT || vi < nvec) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < EV; ++e) {
         const float c = z[v][e] - mean;
         sq += c * c;
       }
@@ -75,28 +77,28 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const TX* __restrict__ x
   for (int v = 0; v < MAXV; ++v) {
     const int vi = v * LPR + sub;
     if (EXACT || vi < nvec) {
-      const v4 gv = *(const v4*)(gamma + 4 * vi);
-      const v4 btv = *(const v4*)(beta + 4 * vi);
-      f32x4 of;
-      v4 o;
+      const tv gv = *(const tv*)(gamma + EV * vi);
+      const tv btv = *(const tv*)(beta + EV * vi);
+      fv of;
+      tv o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < EV; ++e) {
         of[e] = to_f32(gv[e]) * ((z[v][e] - mean) * rs) + to_f32(btv[e]);
         o[e] = from_f32<T>(of[e]);
       }
-      *(v4*)(y + base + 4 * vi) = o;
-      if (yf) *(f32x4*)(yf + base + 4 * vi) = of;
+      *(tv*)(y + base + EV * vi) = o;
+      if (yf) *(fv*)(yf + base + EV * vi) = of;
     }
   }
 }
 
-template <typename T, typename TX, typename TA, int LPR, int MAXV, bool EXACT>
+template <typename T, typename TX, typename TA, int EV, int LPR, int MAXV, bool EXACT>
 static hipError_t ln_launch(int rows, int cols, const void* x, const void* a, const void* bias,
                             const void* gamma, const void* beta, void* y, float* yf,
                             hipStream_t s) {
   constexpr int rows_per_block = (256 / kWave) * (kWave / LPR);
   const int grid = (rows + rows_per_block - 1) / rows_per_block;
-  layernorm_kernel<T, TX, TA, LPR, MAXV, EXACT><<<grid, 256, 0, s>>>(
+  layernorm_kernel<T, TX, TA, EV, LPR, MAXV, EXACT><<<grid, 256, 0, s>>>(
       (const TX*)x, (const TA*)a, (const T*)bias, (const T*)gamma, (const T*)beta, (T*)y, yf,
       rows, cols);
   return hipGetLastError();
@@ -106,18 +108,39 @@ template <typename T, typename TX, typename TA>
 static hipError_t ln_dispatch(int rows, int cols, const void* x, const void* a, const void* bias,
                               const void* gamma, const void* beta, void* y, float* yf,
                               hipStream_t s) {
-  switch (cols) {  // exact register tilings for the common hidden sizes
-    case 128: return ln_launch<T, TX, TA, 32, 1, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
-    case 256: return ln_launch<T, TX, TA, 64, 1, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
-    case 384: return ln_launch<T, TX, TA, 32, 3, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
-    case 512: return ln_launch<T, TX, TA, 64, 2, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
-    case 768: return ln_launch<T, TX, TA, 64, 3, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
-    case 1024: return ln_launch<T, TX, TA, 64, 4, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+  // 16-byte vectors of 16-bit data when every row start and parameter vector is 16-byte
+  // aligned (rows a multiple of 8 elements)
+  bool wide = sizeof(T) == 2 && cols % 8 == 0;
+  for (const void* p : {x, a, bias, gamma, beta, (const void*)y, (const void*)yf})
+    if (p && ((uintptr_t)p & 15)) wide = false;
+  if constexpr (sizeof(T) == 2) {
+    if (wide) {
+      switch (cols) {  // exact register tilings for the common hidden sizes
+        case 128: return ln_launch<T, TX, TA, 8, 16, 1, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+        case 256: return ln_launch<T, TX, TA, 8, 32, 1, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+        case 384: return ln_launch<T, TX, TA, 8, 16, 3, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+        case 512: return ln_launch<T, TX, TA, 8, 32, 2, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+        case 768: return ln_launch<T, TX, TA, 8, 32, 3, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+        case 1024: return ln_launch<T, TX, TA, 8, 32, 4, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+        default: break;
+      }
+      if (cols <= 8 * 16 * 4)  // small rows: a quarter wave per row
+        return ln_launch<T, TX, TA, 8, 16, 4, false>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+      return ln_launch<T, TX, TA, 8, 64, 8, false>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+    }
+  }
+  switch (cols) {
+    case 128: return ln_launch<T, TX, TA, 4, 32, 1, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+    case 256: return ln_launch<T, TX, TA, 4, 64, 1, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+    case 384: return ln_launch<T, TX, TA, 4, 32, 3, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+    case 512: return ln_launch<T, TX, TA, 4, 64, 2, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+    case 768: return ln_launch<T, TX, TA, 4, 64, 3, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+    case 1024: return ln_launch<T, TX, TA, 4, 64, 4, true>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
     default: break;
   }
   if (cols <= 4 * 16 * 4)  // small rows: a quarter wave per row
-    return ln_launch<T, TX, TA, 16, 4, false>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
-  return ln_launch<T, TX, TA, 64, 16, false>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+    return ln_launch<T, TX, TA, 4, 16, 4, false>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
+  return ln_launch<T, TX, TA, 4, 64, 16, false>(rows, cols, x, a, bias, gamma, beta, y, yf, s);
 }
 
 hipError_t launch_bias_residual_layernorm(ftx_dtype dt, int rows, int cols, const void* x,
