@@ -28,12 +28,13 @@ extern "C" {
  * TRANSPOSED, w_t[N][K] (row n holds column n of W).  bias [N] or NULL (no bias).
  * gelu != 0 applies the tanh GELU to every output element after the bias.
  * M >= 1; N, K >= 8 and multiples of 8.  fp32 accumulation in every dtype.
- * (Steps a7, a9 with the a10 epilogue, a11.) */
+ * (The attention-output projection, the first FFN projection with its GELU epilogue,
+ * and the second FFN projection.)  K <= 2^20, else FTX_ERR_UNSUPPORTED. */
 ftx_status ftx_step_linear(ftx_dtype dtype, int M, int N, int K, const void *a,
                            const void *w_t, const void *bias, int gelu, void *c,
                            void *stream);
 
-/* Fused Q/K/V projection with the bias + head-split epilogue (steps a1 + a2):
+/* Fused Q/K/V projection with the bias + head-split epilogue:
  *   x [T][H], w_qkv_t [3H][H] (rows 0..H-1 = Wq^T, H..2H-1 = Wk^T, 2H..3H-1 = Wv^T),
  *   b_qkv [3H] (bq | bk | bv) ->
  *   q [B][n][S][d], k [B][n][S][d], v_t [B][n][d][S] (V stored transposed per head). */
@@ -41,13 +42,13 @@ ftx_status ftx_step_qkv_projection(ftx_dtype dtype, int B, int S, int n, int d,
                                    const void *x, const void *w_qkv_t, const void *b_qkv,
                                    void *q, void *k, void *v_t, void *stream);
 
-/* Standalone bias + head split/transpose (step a2 as its own kernel):
+/* Standalone bias + head split/transpose (the projection's epilogue as its own kernel):
  *   qkv [T][3H] (projection output without bias), b_qkv [3H] -> q, k, v_t as above. */
 ftx_status ftx_step_bias_qkv_split(ftx_dtype dtype, int B, int S, int n, int d,
                                    const void *qkv, const void *b_qkv, void *q, void *k,
                                    void *v_t, void *stream);
 
-/* Fused attention (steps a3-a6): per (b, h), scores Q K^T / sqrt(d), softmax over keys
+/* Fused attention: per (b, h), scores Q K^T / sqrt(d), softmax over keys
  * j < len_b (keys beyond get probability 0; row max and sum in fp32), context P V,
  * written with heads merged: ctx[T][H] with ctx[b*S+i][h*d+e].
  *   q, k [B][n][S][d], v_t [B][n][d][S]; seq_lens [B] int32 (clamped to [1, S]) or NULL. */
@@ -55,7 +56,8 @@ ftx_status ftx_step_attention(ftx_dtype dtype, int B, int S, int n, int d, const
                               const void *k, const void *v_t, const int32_t *seq_lens,
                               void *ctx, void *stream);
 
-/* Bias + residual + LayerNorm (steps a8, a12), one row of `cols` per token:
+/* Bias + residual + LayerNorm (after the attention block and after the FFN), one row of
+ * `cols` per token:
  *   y = LN(x + a + bias; gamma, beta) with epsilon FTX_LN_EPSILON, biased variance,
  *   statistics in fp32.  x, a, y [rows][cols]; bias, gamma, beta [cols].
  *   y may alias x or a (each row is read completely before it is written).
@@ -65,8 +67,8 @@ ftx_status ftx_step_bias_residual_layernorm(ftx_dtype dtype, int rows, int cols,
                                             const void *gamma, const void *beta, void *y,
                                             void *stream);
 
-/* Standalone bias + GELU (step a10 as its own kernel): g = gelu(u + bias) element-wise,
- * u, g [rows][cols] (g may alias u), bias [cols]; cols a multiple of 8. */
+/* Standalone bias + GELU (the first FFN projection's epilogue as its own kernel):
+ * g = gelu(u + bias) element-wise, u, g [rows][cols] (g may alias u), bias [cols]; cols a multiple of 8. */
 ftx_status ftx_step_bias_gelu(ftx_dtype dtype, int rows, int cols, const void *u,
                               const void *bias, void *g, void *stream);
 

@@ -569,6 +569,7 @@ ftx_status ftx_step_linear(ftx_dtype dtype, int M, int N, int K, const void* a, 
     return fail(FTX_ERR_INVALID_ARG, "need M >= 1 and N, K positive multiples of 8");
   if ((long long)M * N >= (1LL << 31) || (long long)M * K >= (1LL << 31) || (long long)N * K >= (1LL << 31))
     return fail(FTX_ERR_UNSUPPORTED, "operand above 2^31 elements");
+  if (K > kMaxInnerDim) return fail(FTX_ERR_UNSUPPORTED, "K above 2^20");
   if (!a || !w_t || !c) return fail(FTX_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned16(a) || !aligned16(w_t) || !aligned16(c)) return fail(FTX_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
   const size_t es = dtype_size(dtype);

@@ -7,9 +7,11 @@
 //   C[M][N] = A[M][K] * W[K][N], W held transposed (Wt[N][K], K contiguous) so both
 //   operands are read along K with 16-byte loads;
 //   v_mfma_f32_32x32x16_{f16,bf16} (fp32 accumulate) or v_mfma_f32_32x32x2f32 for fp32;
-//   a block tile BM x BN staged through double-buffered, row-padded LDS (the next K slab
-//   is fetched into registers while the current one is multiplied), waves WM x WN each
-//   owning a (BM/WM) x (BN/WN) sub-tile of 32x32 accumulators;
+//   a block tile BM x BN staged through two LDS buffers that the buffer loads fill
+//   directly (global memory to LDS, no register hop), 128 bytes of K per row and slab,
+//   XOR-swizzled so the fragment reads are free of bank conflicts; the next slab loads
+//   while the current one is multiplied; waves WM x WN each own a (BM/WM) x (BN/WN)
+//   sub-tile of 32x32 accumulators;
 //   the bias, the tanh GELU and the Q/K/V head split are applied in the epilogue on the
 //   fp32 accumulators, so U never makes a round trip through memory before its GELU.
 //
@@ -246,31 +248,53 @@ __device__ __forceinline__ void epilogue_tile(const Epi& epi, typename Epi::out_
 
 // ---------------------------------------------------------------------------------- kernel
 
-// Workgroup barrier for the LDS double buffer: this wave's LDS writes have completed
-// (lgkmcnt 0) and every wave has arrived.  Unlike __syncthreads() it does not wait for
-// outstanding global loads (vmcnt), so prefetches of later K slabs stay in flight across
-// it; the empty asm statements keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
+// 16 bytes per lane from byte offset voff of buffer resource r into LDS at lds + 16 * lane
+// (buffer_load_dwordx4 ... lds: the LDS address is wave-uniform, the lane offset implicit).
+// An offset at or past the resource's byte count reads as zero and touches no memory.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, int voff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding; LDS and
+// scalar counters unconstrained.  The loads into LDS are only tracked by this counter.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads() (which would also wait for
+// every outstanding load); the empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void workgroup_barrier() {
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
+// LDS row of a slab: 128 bytes of K (8 chunks of 16 bytes).  Chunk c of tile row R sits at
+// position c ^ swz(R).  A wave's fragment read takes one 16-byte chunk from each of 32
+// consecutive rows; with this swizzle any 8 consecutive rows hit 8 different positions and
+// any 16 consecutive rows cover each (row parity, position) pair once, so the reads are free
+// of bank conflicts whether the LDS serves 8 or 16 lanes per pass.  swz depends on R mod 32
+// only, so the 32-row tiles of a wave differ by a constant offset.
+__device__ __forceinline__ int swz(int R) { return (R & 7) ^ ((R >> 3) & 3); }
+
 template <typename T, int BM, int BN, int WM, int WN> struct GemmCfg {
   typedef Mfma<T> MF;
-  static constexpr int VEC = MF::VEC;
-  static constexpr int BK = 128 / sizeof(T);        // 128 bytes of K per tile row
-  static constexpr int LDS_STRIDE = BK + VEC;       // +16 bytes: conflict-free 16-byte reads
-  static constexpr int NT = WM * WN * kWave;
+  static constexpr int VEC = MF::VEC;               // elements per 16-byte chunk
+  static constexpr int ROWB = 128;                  // bytes of K per tile row and slab
+  static constexpr int BK = ROWB / sizeof(T);       // K per slab
+  static constexpr int NS = BK / MF::KF;            // MFMA sub-steps per slab
+  static constexpr int NW = WM * WN;
   static constexpr int TM = BM / WM / 32;
   static constexpr int TN = BN / WN / 32;
-  static constexpr int CPR = BK / VEC;              // 16-byte chunks per tile row
-  static constexpr int A_CH = BM * CPR / NT;
-  static constexpr int B_CH = BN * CPR / NT;
-  static constexpr int STAGE = (BM + BN) * LDS_STRIDE;  // elements per LDS buffer
+  static constexpr int AQ = BM / 8 / NW;            // 1 KB (8-row) loads per wave and slab
+  static constexpr int BQ = BN / 8 / NW;
+  static constexpr int STAGE = (BM + BN) * ROWB;    // bytes per LDS buffer
+  static_assert(NS == 4, "a slab holds four fragment sub-steps");
   static_assert(TM >= 1 && TN >= 1 && TM * WM * 32 == BM && TN * WN * 32 == BN, "wave tiling");
-  static_assert(A_CH * NT == BM * CPR && B_CH * NT == BN * CPR, "tile not divisible");
+  static_assert(AQ * 8 * NW == BM && BQ * 8 * NW == BN, "slab loads not divisible");
 };
 
 // Map the linear block id to a (tile_m, tile_n): blocks are handed to the 8 XCDs round
@@ -292,7 +316,8 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 }
 
 // K range of this block: [blockIdx.y * kchunk, min(K, (blockIdx.y + 1) * kchunk)); kchunk is
-// K (one range) or, under split-K, a multiple of the slab depth.
+// K (one range) or, under split-K, a multiple of the slab depth.  K * BM * sizeof(T) and
+// K * BN * sizeof(T) stay below 2^31 (callers bound K).
 template <typename T, int BM, int BN, int WM, int WN, typename Epi>
 __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restrict__ A,
                                                                const T* __restrict__ Bt, int M,
@@ -300,147 +325,136 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
   typedef GemmCfg<T, BM, BN, WM, WN> C;
   typedef typename C::MF MF;
   typedef typename MF::frag frag;
-  __shared__ __attribute__((aligned(16))) T smem[2 * C::STAGE];
+  constexpr int TM = C::TM, TN = C::TN, AQ = C::AQ, BQ = C::BQ, ROWB = C::ROWB;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane % 32, g = lane / 32;
 
-  f32x16 acc[C::TN][C::TM];
+  f32x16 acc[TN][TM];
 #pragma unroll
-  for (int j = 0; j < C::TN; ++j)
+  for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
 
   // this lane's bias vectors for its columns nt + 8 q + 4 g of each of its column tiles
-  typename Epi::b4 bq[C::TN][4];
+  typename Epi::b4 bq[TN][4];
 #pragma unroll
-  for (int j = 0; j < C::TN; ++j)
+  for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) bq[j][q] = epi.bias4(n0 + (wn * C::TN + j) * 32 + 8 * q + 4 * g);
+    for (int q = 0; q < 4; ++q) bq[j][q] = epi.bias4(n0 + (wn * TN + j) * 32 + 8 * q + 4 * g);
 
-  // this block's K range: kn elements from kb; slab offsets k0 below are relative to kb
   const int kb = blockIdx.y * kchunk;
   const int kn = min(K - kb, kchunk);
-
-  // the next K slab, fetched into registers while the current one is multiplied
-  frag ra[C::A_CH], rb[C::B_CH];
-  const frag zero = {};
-
-  // Loads past the last row or K column read a clamped in-range address, with no branch
-  // around the load, so the compiler can count the loads still in flight exactly instead of
-  // draining them at a control-flow merge.  Rows past M (of A) or N (of W^T) only feed
-  // outputs that are never stored; K columns past the block's range are zeroed when the
-  // slab is written to LDS, where the loaded data is needed anyway.
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < C::A_CH; ++i) {
-      const int c = tid + i * C::NT;
-      const int r = c / C::CPR, kc = (c % C::CPR) * C::VEC;
-      ra[i] = *(const frag*)(A + (size_t)min(m0 + r, M - 1) * K + min(kb + k0 + kc, K - C::VEC));
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_CH; ++i) {
-      const int c = tid + i * C::NT;
-      const int r = c / C::CPR, kc = (c % C::CPR) * C::VEC;
-      rb[i] = *(const frag*)(Bt + (size_t)min(n0 + r, N - 1) * K + min(kb + k0 + kc, K - C::VEC));
-    }
-  };
-  auto sstore_a = [&](int buf, int k0) {
-    T* As = smem + buf * C::STAGE;
-#pragma unroll
-    for (int i = 0; i < C::A_CH; ++i) {
-      const int c = tid + i * C::NT;
-      const int kc = (c % C::CPR) * C::VEC;
-      *(frag*)(As + (c / C::CPR) * C::LDS_STRIDE + kc) = k0 + kc < kn ? ra[i] : zero;
-    }
-  };
-  auto sstore_b = [&](int buf, int k0) {
-    T* Bs = smem + buf * C::STAGE + BM * C::LDS_STRIDE;
-#pragma unroll
-    for (int i = 0; i < C::B_CH; ++i) {
-      const int c = tid + i * C::NT;
-      const int kc = (c % C::CPR) * C::VEC;
-      *(frag*)(Bs + (c / C::CPR) * C::LDS_STRIDE + kc) = k0 + kc < kn ? rb[i] : zero;
-    }
-  };
-
   const int nk = (kn + C::BK - 1) / C::BK;
-  gload(0);
-  sstore_a(0, 0);
-  sstore_b(0, 0);
-  __syncthreads();
-  // MFMA fragments are double-buffered in registers (FDB): while the MFMAs of sub-step s
-  // run, the fragments of sub-step s + 1 are read from LDS; the first sub-step of the next
-  // slab is read right after the barrier that publishes it.  The next slab's LDS writes
-  // (into the buffer every wave finished reading before the last barrier) are spread over
-  // the sub-steps -- A after the first, W^T after the third -- so they overlap the MFMAs of
-  // other waves instead of forming a write phase before the barrier.  The 256x256 tile has
-  // no room for the second fragment set (it would spill), so it reads each sub-step's
-  // fragments just before their MFMAs and writes the next slab at the end.
-  constexpr int NS = C::BK / MF::KF;  // sub-steps per slab (even)
-  constexpr bool FDB = C::TM + C::TN <= 5;
-  static_assert(NS == 4, "the write placement assumes four sub-steps per slab");
-  frag fa[FDB ? 2 : 1][C::TM], fb[FDB ? 2 : 1][C::TN];
-  auto read_frags = [&](int buf, int s, int fbuf) {
-    const T* As = smem + buf * C::STAGE + (wm * C::TM * 32 + lr) * C::LDS_STRIDE + g * C::VEC + s * MF::KF;
-    const T* Bs = smem + buf * C::STAGE + (BM + wn * C::TN * 32 + lr) * C::LDS_STRIDE + g * C::VEC + s * MF::KF;
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) fa[fbuf][i] = *(const frag*)(As + i * 32 * C::LDS_STRIDE);
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) fb[fbuf][j] = *(const frag*)(Bs + j * 32 * C::LDS_STRIDE);
-  };
-  if constexpr (FDB) read_frags(0, 0, 0);
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * C::BK);
+  // Slabs go from global memory straight into LDS (no register staging).  The buffer
+  // resources cover this block's row panels of A and W^T, so rows past M (N) read as zero.
+  // Load q of this wave fills tile rows 8 grp .. 8 grp + 7 (grp = wave * AQ + q): lane l
+  // lands at position l % 8 of row 8 grp + l / 8 and so fetches chunk (l % 8) ^ swz(row).
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A + (size_t)m0 * K), (short)0, min(BM, M - m0) * K * (int)sizeof(T), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Bt + (size_t)n0 * K), (short)0, min(BN, N - n0) * K * (int)sizeof(T), 0x00020000);
+  int avo[AQ], bvo[BQ];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      constexpr int X = FDB ? 1 : 0;  // 1: fragment sets alternate
-      if constexpr (FDB) {
-        if (s + 1 < NS) read_frags(cur, s + 1, (s + 1) & 1);
-      } else {
-        read_frags(cur, s, 0);
-      }
+  for (int q = 0; q < AQ; ++q) {
+    const int R = (wave * AQ + q) * 8 + lane / 8;
+    avo[q] = (R * K + kb + ((lane & 7) ^ swz(R)) * C::VEC) * (int)sizeof(T);
+  }
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j)
+  for (int q = 0; q < BQ; ++q) {
+    const int R = (wave * BQ + q) * 8 + lane / 8;
+    bvo[q] = (R * K + kb + ((lane & 7) ^ swz(R)) * C::VEC) * (int)sizeof(T);
+  }
+  auto load_slab = [&](int kt, int buf) {
+    char* base = smem + buf * C::STAGE;
+    const int kbytes = kt * ROWB;
 #pragma unroll
-        for (int i = 0; i < C::TM; ++i) MF::mma(fb[s & X][j], fa[s & X][i], acc[j][i]);
-      if constexpr (FDB) {
-        if (s == 0 && kt + 1 < nk) sstore_a(cur ^ 1, (kt + 1) * C::BK);
-        if (s == 2 && kt + 1 < nk) sstore_b(cur ^ 1, (kt + 1) * C::BK);
+    for (int q = 0; q < AQ; ++q) lds_dma16(ra, avo[q] + kbytes, base + (wave * AQ + q) * 1024);
+#pragma unroll
+    for (int q = 0; q < BQ; ++q)
+      lds_dma16(rb, bvo[q] + kbytes, base + BM * ROWB + (wave * BQ + q) * 1024);
+  };
+  // A slab that runs past the block's K range (the last one, when kn is not a multiple of
+  // BK) holds the next columns of each row there: zero them in both operands.
+  auto zero_k_tail = [&](int buf, int kv) {
+    char* base = smem + buf * C::STAGE;
+    for (int it = threadIdx.x; it < (BM + BN) * 8; it += C::NW * kWave) {
+      const int R = it / 8, p = it % 8;
+      if ((p ^ swz(R)) * C::VEC >= kv) *(frag*)(base + R * ROWB + p * 16) = frag{};
+    }
+  };
+
+  // fragment reads: row (32-row tile base + lr), chunk 2 s + g of sub-step s
+  const int hl = swz(lr);
+  const int a_row = (wm * TM * 32 + lr) * ROWB, b_row = BM * ROWB + (wn * TN * 32 + lr) * ROWB;
+  frag fa[2][TM], fb[2][TN];
+  auto read_frags = [&](int buf, int s, int set) {
+    const int pos = ((2 * s + g) ^ hl) * 16;
+    const char* As = smem + buf * C::STAGE + a_row + pos;
+    const char* Bs = smem + buf * C::STAGE + b_row + pos;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[set][i] = *(const frag*)(As + i * 32 * ROWB);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[set][j] = *(const frag*)(Bs + j * 32 * ROWB);
+  };
+
+  // Double-buffered slabs: at the top of step kt every wave waits for its own loads of slab
+  // kt, and the barrier makes all of them visible and tells that every wave is done with
+  // the other buffer, which then receives slab kt + 1 while slab kt is multiplied.  Inside
+  // a slab the fragments of sub-step s + 1 are read before the MFMAs of sub-step s; the
+  // scheduling barriers keep the compiler from regrouping them, so LDS latency hides
+  // behind the MFMAs.
+  if (nk > 0) load_slab(0, 0);
+  for (int k0 = 0; k0 < nk; k0 += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int kt = k0 + u;
+      if (kt < nk) {
+        wait_vmcnt<0>();
+        workgroup_barrier();
+        if (kt == nk - 1 && kn - kt * C::BK < C::BK) {
+          zero_k_tail(u, kn - kt * C::BK);
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's zero stores done
+          workgroup_barrier();
+        }
+        if (kt + 1 < nk) load_slab(kt + 1, u ^ 1);
+        read_frags(u, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s) {
+          if (s + 1 < C::NS) read_frags(u, s + 1, (s + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int i = 0; i < TM; ++i) MF::mma(fb[s & 1][j], fa[s & 1][i], acc[j][i]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
-    if constexpr (!FDB) {
-      if (kt + 1 < nk) {
-        sstore_a(cur ^ 1, (kt + 1) * C::BK);
-        sstore_b(cur ^ 1, (kt + 1) * C::BK);
-      }
-    }
-    lds_barrier();
-    if constexpr (FDB)
-      if (kt + 1 < nk) read_frags(cur ^ 1, 0, 0);
   }
 
-  // the K loop ended with a barrier, so the LDS is free: each wave stages its tiles in its
-  // own slice of it
+  // every wave is done with both buffers before the LDS is reused as epilogue scratch
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  workgroup_barrier();
   typedef typename Epi::out_t TO;
   constexpr int SCRATCH = 32 * (32 + 16 / sizeof(TO));  // elements of TO per wave
-  static_assert(SCRATCH * sizeof(TO) * (C::NT / kWave) <= sizeof(smem), "epilogue scratch");
+  static_assert(SCRATCH * sizeof(TO) * C::NW <= sizeof(smem), "epilogue scratch");
   TO* ws = (TO*)smem + wave * SCRATCH;
 #pragma unroll
-  for (int j = 0; j < C::TN; ++j)
+  for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-      epilogue_tile(epi, ws, m0 + (wm * C::TM + i) * 32, n0 + (wn * C::TN + j) * 32, lane, acc[j][i],
+    for (int i = 0; i < TM; ++i)
+      epilogue_tile(epi, ws, m0 + (wm * TM + i) * 32, n0 + (wn * TN + j) * 32, lane, acc[j][i],
                     bq[j]);
 }
 
@@ -448,24 +462,25 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
 // The launch configuration is chosen per shape (the article tunes grid and block sizes to
 // the number of input rows, which ranges from tens at batch 1 to thousands at batch in the
 // hundreds).  Candidates, with the fraction of MFMA peak a full CU reaches in each
-// (measured on the BERT-base projections at 16384 rows), and how many blocks share a CU:
-//   256x256, 8 waves (4 x 2), 147 KB LDS: 0.34, 1 block per CU
-//   256x192, 8 waves (4 x 2), 129 KB LDS: 0.33, 1 block per CU
-//   256x128, 8 waves (4 x 2), 111 KB LDS: 0.30, 1 block per CU
-//   128x128, 4 waves (2 x 2),  74 KB LDS: 0.25, 2 blocks per CU
-//    64x64,  4 waves (2 x 2),  37 KB LDS: 0.12, 4 blocks per CU
-//    32x32,  1 wave,           18 KB LDS: 0.05, 8 blocks per CU
+// (measured on the BERT-base and BERT-large projections at 16384 rows; 64x64 and 32x32 at
+// 2048 to 4096 rows), and how many blocks share a CU:
+//   256x256, 8 waves (4 x 2), 128 KB LDS: 0.37, 1 block per CU
+//   256x192, 8 waves (4 x 2), 112 KB LDS: 0.36, 1 block per CU
+//   256x128, 8 waves (4 x 2),  96 KB LDS: 0.34, 1 block per CU
+//   128x128, 4 waves (2 x 2),  64 KB LDS: 0.36, 2 blocks per CU
+//    64x64,  4 waves (2 x 2),  32 KB LDS: 0.25, 4 blocks per CU
+//    32x32,  1 wave,           16 KB LDS: 0.18, 8 blocks per CU
 // The modelled time of a launch is (rounds of blocks over the 256 CUs) x (one block's
 // time, longer when several blocks share a CU); the candidate with the least modelled time
-// wins, so small batches get small tiles that still spread over every CU.  fp32 (twice the register footprint per element)
-// uses the table without its two largest tiles.
+// wins, so small batches get small tiles that still spread over every CU.  fp32 (twice the
+// register footprint per element) uses the table without its two largest tiles.
 
 enum TileCfg { TILE_256x256, TILE_256x192, TILE_256x128, TILE_128x128, TILE_64x64, TILE_32x32, TILE_COUNT };
 
 static TileCfg choose_tile(int M, int N, bool wide) {
   struct Cand { int bm, bn, per_cu; double eff; };
-  static const Cand cand[TILE_COUNT] = {{256, 256, 1, 0.34}, {256, 192, 1, 0.33}, {256, 128, 1, 0.30},
-                                        {128, 128, 2, 0.25}, {64, 64, 4, 0.12},   {32, 32, 8, 0.05}};
+  static const Cand cand[TILE_COUNT] = {{256, 256, 1, 0.37}, {256, 192, 1, 0.36}, {256, 128, 1, 0.34},
+                                        {128, 128, 2, 0.36}, {64, 64, 4, 0.25},   {32, 32, 8, 0.18}};
   constexpr int kCUs = 256;
   int best = TILE_32x32;
   double best_t = 1e300;
