@@ -39,14 +39,17 @@ template <typename T> struct Vec16 {
 template <typename T> __device__ __forceinline__ float to_f32(T v) { return static_cast<float>(v); }
 template <typename T> __device__ __forceinline__ T from_f32(float v) { return static_cast<T>(v); }
 
-// tanh-form GELU, 0.5 u (1 + tanh(sqrt(2/pi)(u + 0.044715 u^3))), evaluated through the
-// identity 0.5 (1 + tanh(y)) = 1 / (1 + exp(-2 y)) so that one exp and one divide suffice;
-// the cube is written as u*u*u.  Large negative u gives exp -> inf and a result of -0.
+// tanh-form GELU, 0.5 u (1 + tanh(y)) with y = sqrt(2/pi) (u + 0.044715 u^3), through the
+// identity 0.5 (1 + tanh(y)) = 1 / (1 + e^(-2y)) = 1 / (1 + 2^z), z = -2 log2(e) y.  With
+// log2(e) folded into the constants, z = u (c1 + c3 u^2) (the cube as plain products, no
+// pow): one multiply-add, two multiplies, one add, and the hardware base-2 exponential and
+// reciprocal per element.  Large negative u gives 2^z -> inf, a reciprocal of 0 and a result
+// of -0; large positive u gives 2^z -> 0 and the result u.
 __device__ __forceinline__ float gelu_tanh(float u) {
-  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-  const float k1 = 0.044715f;
-  float y = k0 * (u + k1 * u * u * u);
-  return u / (1.0f + __expf(-2.0f * y));
+  constexpr float c1 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  constexpr float c3 = c1 * 0.044715f;
+  const float z = u * __builtin_fmaf(c3, u * u, c1);
+  return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
 }
 
 // Sum / max over groups of `width` consecutive lanes (width a power of two <= 64).

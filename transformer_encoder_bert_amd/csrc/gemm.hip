@@ -83,14 +83,6 @@ template <typename TO> struct TileDst {
   bool tr;     // staged transposed: staged rows run along n, columns along m
 };
 
-// tanh-form GELU as u * sigmoid(2 y), y = sqrt(2/pi) (u + 0.044715 u^3) (the cube written
-// u*u*u), with one exp and the hardware reciprocal instead of a divide; large negative u
-// gives exp -> inf, rcp -> 0 and a result of -0.
-__device__ __forceinline__ float gelu_fast(float u) {
-  const float y = 0.7978845608028654f * (u + 0.044715f * u * u * u);
-  return u * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * y));
-}
-
 template <typename T, bool GELU, typename TO = T> struct EpiLinear {
   typedef TO out_t;
   typedef typename Vec16<TO>::type vec;
@@ -103,7 +95,7 @@ template <typename T, bool GELU, typename TO = T> struct EpiLinear {
     if (bias && n < N) v = *(const b4*)(bias + n);
     return v;
   }
-  __device__ __forceinline__ float act(float v) const { return GELU ? gelu_fast(v) : v; }
+  __device__ __forceinline__ float act(float v) const { return GELU ? gelu_tanh(v) : v; }
   __device__ __forceinline__ TileDst<TO> tile(int mt, int nt) const {
     return {c + (size_t)mt * N + nt, N, false};
   }
@@ -585,7 +577,7 @@ static hipError_t linear_t(int M, int N, int K, const void* a, const void* w_t, 
                            bool gelu, bool out_f32, void* c, hipStream_t s, float* ws,
                            size_t wn) {
   if (out_f32) {
-    if (gelu) return gemm_launch<T>(M, N, K, a, w_t, EpiLinear<T, true, float>{(float*)c, (const T*)bias, M, N}, s, ws, wn);
+    if (gelu) return hipErrorInvalidValue;  // the GELU output is stored in the data type
     return gemm_launch<T>(M, N, K, a, w_t, EpiLinear<T, false, float>{(float*)c, (const T*)bias, M, N}, s, ws, wn);
   }
   if (gelu) return gemm_launch<T>(M, N, K, a, w_t, EpiLinear<T, true>{(T*)c, (const T*)bias, M, N}, s, ws, wn);

@@ -8,7 +8,7 @@
 
 namespace ftx {
 
-// out_f32: c is written as fp32 (16-bit dtypes; ignored in fp32 mode).
+// out_f32: c is written as fp32 (16-bit dtypes, without GELU; ignored in fp32 mode).
 // ws / ws_elems: fp32 workspace for split-K; a GEMM whose plan splits K runs unsplit when
 // the workspace is missing or smaller than gemm_splitk_workspace() says.
 hipError_t launch_linear(ftx_dtype dt, int M, int N, int K, const void* a, const void* w_t,
