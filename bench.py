@@ -340,6 +340,18 @@ def main():
         "roofline": None, "cpu_baseline": None,
     }
 
+    # latency distribution: the same K forwards again, each between its own event pair on the
+    # forward's stream (after the timed region, so the headline figure carries no extra events)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        enc.forward(x, lens, out)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    lat = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    result["latency_ms"] = {"p10": float(np.percentile(lat, 10)), "p50": float(np.percentile(lat, 50)),
+                            "p90": float(np.percentile(lat, 90))}
+
     if not args.no_kernel_times:
         # the same K forwards again, with a HIP event pair around every launch on `stream`
         enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)
