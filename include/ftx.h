@@ -143,15 +143,15 @@ ftx_status ftx_set_option(ftx_encoder *enc, ftx_option option, int value);
 
 /* Step classes of the per-step timing. */
 typedef enum {
-  FTX_STEP_QKV_GEMM = 0,        /* a1 (+a2 when fused) */
-  FTX_STEP_BIAS_QKV_SPLIT = 1,  /* a2 standalone */
-  FTX_STEP_ATTENTION = 2,       /* a3-a6 fused */
-  FTX_STEP_ATTN_OUT_GEMM = 3,   /* a7 */
-  FTX_STEP_LN1 = 4,             /* a8 */
-  FTX_STEP_FFN1_GEMM = 5,       /* a9 (+a10 when fused) */
-  FTX_STEP_BIAS_GELU = 6,       /* a10 standalone */
-  FTX_STEP_FFN2_GEMM = 7,       /* a11 */
-  FTX_STEP_LN2 = 8,             /* a12 */
+  FTX_STEP_QKV_GEMM = 0,        /* Q/K/V projection (with bias + head split when fused) */
+  FTX_STEP_BIAS_QKV_SPLIT = 1,  /* bias + head split as its own kernel */
+  FTX_STEP_ATTENTION = 2,       /* scores, masked softmax, context: one fused kernel */
+  FTX_STEP_ATTN_OUT_GEMM = 3,   /* attention-output projection */
+  FTX_STEP_LN1 = 4,             /* bias + residual + LayerNorm after attention */
+  FTX_STEP_FFN1_GEMM = 5,       /* first FFN projection (with bias + GELU when fused) */
+  FTX_STEP_BIAS_GELU = 6,       /* bias + GELU as its own kernel */
+  FTX_STEP_FFN2_GEMM = 7,       /* second FFN projection */
+  FTX_STEP_LN2 = 8,             /* bias + residual + LayerNorm after the FFN */
   FTX_NUM_STEPS = 9
 } ftx_step;
 
