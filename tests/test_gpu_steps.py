@@ -141,6 +141,8 @@ ATTN_CASES = [
     (2, 512, 2, 64, [512, 200]),     # several softmax chunks
     (1, 512, 1, 64, [64]),
     (2, 96, 2, 64, [96, 40]),        # S not a power of two
+    (2, 32, 3, 64, [32, 9]),         # S = 32, few heads: the kernel without LDS
+    (172, 32, 12, 64, None),         # S = 32, over 2048 heads: the LDS kernel
 ]
 
 
