@@ -267,16 +267,35 @@ __global__ __launch_bounds__((AttnCfg<T, D, SMAX>::NW * kWave)) void attention_k
     for (int f = 0; f < NQF; ++f) qf[f] = *(const frag*)(qp + f * KF);
   }
   {
+    // K rows and V^T columns below nk, as 16-byte vectors; the loops run to the
+    // compile-time maximum with a per-vector predicate, so every load of a thread is issued
+    // before its first LDS store
+    constexpr int KCH = D / C::VE;                   // vectors per K row
+    constexpr int KPT = (SMAX * KCH + NT - 1) / NT;  // K vectors per thread
+    constexpr int VCH = SMAX / C::VE;                // vectors per V^T row
+    constexpr int VPT = (D * VCH + NT - 1) / NT;
     const T* kg = k + (size_t)bh * S * D;
-    for (int c = threadIdx.x; c < nk * (D / C::VE); c += NT) {
-      const int r = c / (D / C::VE), col = (c % (D / C::VE)) * C::VE;
-      *(vec*)(Ks + r * C::KST + col) = *(const vec*)(kg + (size_t)r * D + col);
-    }
     const T* vg = vt + (size_t)bh * D * S;
-    const int cpr = nk / C::VE;
-    for (int c = threadIdx.x; c < D * cpr; c += NT) {
-      const int r = c / cpr, col = (c % cpr) * C::VE;
-      *(vec*)(Vs + r * C::VST + col) = *(const vec*)(vg + (size_t)r * S + col);
+    vec kb[KPT], vb[VPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = threadIdx.x + i * NT, r = c / KCH;
+      if (c < SMAX * KCH && r < nk) kb[i] = *(const vec*)(kg + (size_t)r * D + (c % KCH) * C::VE);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = threadIdx.x + i * NT, col = (c % VCH) * C::VE;
+      if (c < D * VCH && col < nk) vb[i] = *(const vec*)(vg + (size_t)(c / VCH) * S + col);
+    }
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = threadIdx.x + i * NT, r = c / KCH;
+      if (c < SMAX * KCH && r < nk) *(vec*)(Ks + r * C::KST + (c % KCH) * C::VE) = kb[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = threadIdx.x + i * NT, col = (c % VCH) * C::VE;
+      if (c < D * VCH && col < nk) *(vec*)(Vs + (c / VCH) * C::VST + col) = vb[i];
     }
   }
   __syncthreads();
