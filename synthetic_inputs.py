@@ -265,6 +265,118 @@ def custom_case(shape: Shape, seed: int, *, lens: Optional[np.ndarray] = None,
     return c
 
 
+# ----------------------------------------------------------------------------- decoder
+# Draws for the decoder forward (the article's roadmap item): the same conventions as the
+# encoder's -- float64 PCG64 draws rounded once to the storage format, one stream per tensor.
+
+# Field names of one decoder layer's weights, in the order of the C struct: causal
+# self-attention, cross-attention over the memory, feed-forward, each with its LayerNorm.
+DECODER_WEIGHT_NAMES = ("w_q", "b_q", "w_k", "b_k", "w_v", "b_v", "w_o", "b_o",
+                        "ln1_gamma", "ln1_beta",
+                        "w_q2", "b_q2", "w_k2", "b_k2", "w_v2", "b_v2", "w_o2", "b_o2",
+                        "ln2_gamma", "ln2_beta",
+                        "w_ffn1", "b_ffn1", "w_ffn2", "b_ffn2", "ln3_gamma", "ln3_beta")
+
+
+@dataclass(frozen=True)
+class DecoderShape:
+    batch: int
+    tgt_len: int      # decoder positions per sequence
+    mem_len: int      # memory (encoder output) positions per sequence
+    head_num: int
+    size_per_head: int
+    num_layers: int
+    dtype: str
+
+    @property
+    def hidden(self) -> int:
+        return self.head_num * self.size_per_head
+
+    @property
+    def ffn(self) -> int:
+        return 4 * self.hidden
+
+    def flops(self) -> float:
+        """Algorithmic dense-contraction flops of one forward at the padded lengths.
+
+        Per layer, T = B*tgt_len decoder rows and Tm = B*mem_len memory rows: self-attention
+        projections 8*T*H^2 (Q, K, V, O), cross-attention Q and O 4*T*H^2, its K and V on the
+        memory 4*Tm*H^2, feed-forward 16*T*H^2, and scores plus context 4*T*tgt_len*H
+        (self) and 4*T*mem_len*H (cross), all at the full padded extent.
+        """
+        T, Tm, H = self.batch * self.tgt_len, self.batch * self.mem_len, self.hidden
+        per = 28.0 * T * H * H + 4.0 * Tm * H * H + 4.0 * T * (self.tgt_len + self.mem_len) * H
+        return float(self.num_layers) * per
+
+
+@dataclass
+class DecoderCase:
+    shape: DecoderShape
+    x: np.ndarray                  # [B, tgt_len, H]
+    mem: np.ndarray                # [B, mem_len, H]
+    mem_lens: Optional[np.ndarray]  # [B] int32 in [1, mem_len], or None
+    params: str
+    weight_std: float
+    _layer_seqs: list = field(default_factory=list, repr=False)
+
+    def layer(self, l: int) -> Dict[str, np.ndarray]:
+        sh, dt = self.shape, self.shape.dtype
+        H, F = sh.hidden, sh.ffn
+        seqs = {name: _child(self._layer_seqs[l], i) for i, name in enumerate(DECODER_WEIGHT_NAMES)}
+        out: Dict[str, np.ndarray] = {}
+        for name in DECODER_WEIGHT_NAMES:
+            rng = np.random.Generator(np.random.PCG64(seqs[name]))
+            if name.startswith("w_"):
+                dims = (H, F) if name == "w_ffn1" else (F, H) if name == "w_ffn2" else (H, H)
+                out[name] = round_to(rng.normal(0.0, self.weight_std, size=dims), dt)
+                continue
+            n = F if name == "b_ffn1" else H
+            if self.params == "bert":
+                val = np.ones(n) if name.endswith("gamma") else np.zeros(n)
+            elif self.params == "random_affine":
+                val = (1.0 if name.endswith("gamma") else 0.0) + rng.normal(0.0, 0.2, size=n)
+            else:
+                raise ValueError(self.params)
+            out[name] = round_to(val, dt)
+        return out
+
+    def layers(self) -> Iterator[Dict[str, np.ndarray]]:
+        for l in range(self.shape.num_layers):
+            yield self.layer(l)
+
+
+def make_decoder_case(shape: DecoderShape, seed: int, *, params: str = "bert",
+                      weight_std: float = 0.02,
+                      mem_lens_range: Optional[Tuple[int, int]] = None,
+                      mem_lens: Optional[np.ndarray] = None) -> DecoderCase:
+    """Decoder input x ~ N(0, 1), memory ~ N(0, 1) (standing in for an encoder output),
+    memory lengths uniform in ``mem_lens_range`` (or given, or None = no padding).
+    Streams: SeedSequence(seed) -> weights (one per layer, one per tensor), x, memory,
+    lengths."""
+    ss = np.random.SeedSequence(seed)
+    wseq, xseq, mseq, lseq = (_child(ss, i) for i in range(4))
+    B, H, dt = shape.batch, shape.hidden, shape.dtype
+    x = round_to(np.random.Generator(np.random.PCG64(xseq)).standard_normal((B, shape.tgt_len, H)), dt)
+    mem = round_to(np.random.Generator(np.random.PCG64(mseq)).standard_normal((B, shape.mem_len, H)), dt)
+    lens = None
+    if mem_lens is not None:
+        lens = np.asarray(mem_lens, dtype=np.int32).copy()
+    elif mem_lens_range is not None:
+        lo, hi = mem_lens_range
+        lens = np.random.Generator(np.random.PCG64(lseq)).integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+    return DecoderCase(shape, np.ascontiguousarray(x), np.ascontiguousarray(mem), lens, params,
+                       weight_std, [_child(wseq, l) for l in range(shape.num_layers)])
+
+
+# The decoder benchmark shape: BERT-base sized (12 layers, 12x64 heads), 32 decoder
+# positions attending to a 32-position memory with lengths uniform in [16, 32].
+DECODER_WORKLOAD = dict(name="decoder_base_fp16_s32",
+                        description="decoder 12 layers 12x64 fp16, 32 positions, memory 32 "
+                                    "(lengths uniform in [16,32])",
+                        tgt_len=32, mem_len=32, head_num=12, size_per_head=64, num_layers=12,
+                        dtype="fp16", batches=(1, 64, 512), seed=106, mem_lens_range=(16, 32))
+
+
 def host_array(a: np.ndarray, dtype: str) -> np.ndarray:
     """Storage-format numpy array of an exactly representable float64 array.
 
