@@ -246,6 +246,145 @@ def cpu_baseline(case, target_s: float):
             "cpu": platform.processor() or platform.machine()}
 
 
+DECODER_METRIC = "sequences/sec + TFLOPS (% MFMA peak), 12-layer decoder fp16, 32 positions over a 32-position memory"
+
+
+def dec_step_work(shape, step: str):
+    """Algorithmic work of ONE launch of a decoder step class: (flops, bytes)."""
+    B, Sd, Se, H, F = shape.batch, shape.tgt_len, shape.mem_len, shape.hidden, shape.ffn
+    T, Tm = B * Sd, B * Se
+    e = 4 if shape.dtype == "fp32" else 2
+    if step == "self_qkv_gemm":
+        return 2.0 * T * 3 * H * H, (T * H + 3 * H * H + 3 * T * H) * e
+    if step in ("self_out_gemm", "cross_out_gemm", "cross_q_gemm"):
+        return 2.0 * T * H * H, (2 * T * H + H * H) * e
+    if step == "cross_kv_gemm":
+        return 2.0 * Tm * 2 * H * H, (Tm * H + 2 * H * H + 2 * Tm * H) * e
+    if step == "ffn1_gemm":
+        return 2.0 * T * F * H, (T * H + F * H + T * F) * e
+    if step == "ffn2_gemm":
+        return 2.0 * T * H * F, (T * F + H * F + T * H) * e
+    if step == "self_attention":
+        return 4.0 * B * Sd * Sd * H, 4 * T * H * e
+    if step == "cross_attention":
+        return 4.0 * B * Sd * Se * H, (2 * T * H + 2 * Tm * H) * e
+    if step in ("ln1", "ln2", "ln3"):
+        return 0.0, 3 * T * H * e
+    raise KeyError(step)
+
+
+def bench_decoder(args):
+    """The decoder forward (the article's roadmap item): same timing and JSON fields as the
+    encoder's bench line, on the decoder workload of synthetic_inputs."""
+    import torch
+    import synthetic_inputs as si
+    from transformer_encoder_bert_amd import ftx
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wd = si.DECODER_WORKLOAD
+    batch = args.batch or max(wd["batches"])
+    shape = si.DecoderShape(batch, wd["tgt_len"], wd["mem_len"], wd["head_num"], wd["size_per_head"],
+                            wd["num_layers"], wd["dtype"])
+    case = si.make_decoder_case(shape, wd["seed"], mem_lens_range=wd["mem_lens_range"])
+    dt, dev = shape.dtype, "cuda:0"
+    torch.cuda.set_device(0)
+
+    def up(a):
+        return torch.from_numpy(si.host_array(a, dt)).to(dev)
+
+    dec = ftx.Decoder(batch, shape.tgt_len, shape.mem_len, shape.head_num, shape.size_per_head,
+                      shape.num_layers, dt)
+    for l, w in enumerate(case.layers()):
+        dec.set_weights(l, {k: up(w[k]) for k in si.DECODER_WEIGHT_NAMES})
+    x, mem = up(case.x), up(case.mem)
+    lens = None if case.mem_lens is None else torch.from_numpy(case.mem_lens).to(dev)
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        dec.forward(x, mem, lens, out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dec.forward(x, mem, lens, out)
+    torch.cuda.synchronize()
+    ms_per_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    tflops = shape.flops() / (ms_per_step * 1e-3) / 1e12
+    result = {
+        "metric": DECODER_METRIC, "value": batch / (ms_per_step * 1e-3), "unit": "sequences/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_TAG[dt],
+        "data": "synthetic",
+        "config": {"workload": f"{wd['name']}: {wd['description']}", "global_batch": batch,
+                   "tgt_len": shape.tgt_len, "mem_len": shape.mem_len, "layers": shape.num_layers,
+                   "heads": shape.head_num, "size_per_head": shape.size_per_head,
+                   "parallelism": "none (1 GPU)"},
+        "tflops": tflops, "frac_mfma_peak": tflops / PEAK_MFMA_TFLOPS[dt],
+        "roofline": None, "cpu_baseline": None,
+    }
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        dec.forward(x, mem, lens, out)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    lat = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    result["latency_ms"] = {q: float(np.percentile(lat, v)) for q, v in (("p10", 10), ("p50", 50), ("p90", 90))}
+    if not args.no_kernel_times:
+        dec.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)
+        dec.kernel_times()
+        for _ in range(args.steps):
+            dec.forward(x, mem, lens, out)
+        torch.cuda.synchronize()
+        times = dec.kernel_times()
+        dec.set_option(ftx.FTX_OPT_KERNEL_TIMING, 0)
+        kernels = {}
+        for name, (ms, cnt) in times.items():
+            if cnt:
+                fl, by = dec_step_work(shape, name)
+                avg = ms / cnt
+                kernels[name] = {"avg_us": 1e3 * avg, "launches": cnt, "share": 0.0,
+                                 "tflops": fl / (avg * 1e-3) / 1e12 if fl else None,
+                                 "gbs_algorithmic": by / (avg * 1e-3) / 1e9}
+        total = sum(v["avg_us"] * v["launches"] for v in kernels.values())
+        for v in kernels.values():
+            v["share"] = v["avg_us"] * v["launches"] / total
+        dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
+        fl, by = dec_step_work(shape, dom)
+        avg_s = kernels[dom]["avg_us"] * 1e-6
+        if fl > 0 and "attention" not in dom:
+            achieved, peak, unit, bound = fl / avg_s / 1e12, PEAK_MFMA_TFLOPS[dt], "TFLOP/s", "mfma"
+        else:
+            achieved, peak, unit, bound = by / avg_s / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+        result["roofline"] = {"kernel": dom, "bound": bound, "achieved": achieved, "peak": peak,
+                              "unit": unit, "frac": achieved / peak, "traffic": None,
+                              "traffic_gbs": None, "work_per_launch": fl if bound == "mfma" else by,
+                              "avg_launch_us": kernels[dom]["avg_us"]}
+        result["kernels"] = kernels
+    dec.close()
+    if not args.no_cpu_baseline:
+        import oracle
+        layers = list(case.layers())
+
+        def run(n):
+            ml = None if case.mem_lens is None else case.mem_lens[:n]
+            oracle.decoder(case.x[:n], case.mem[:n], layers, ml, shape.head_num)
+        t0 = time.perf_counter()
+        run(1)
+        one = time.perf_counter() - t0
+        n = int(max(1, min(batch, args.cpu_seconds / max(one, 1e-3))))
+        t0 = time.perf_counter()
+        run(n)
+        el = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": n / el, "unit": "sequences/s", "cores": blas_threads(),
+                                  "kind": "oracle",
+                                  "sample": f"first {n} of {batch} sequences, all {shape.num_layers} "
+                                            f"layers, numpy float64 ({el:.1f} s)",
+                                  "cpu": platform.processor() or platform.machine()}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_rocprof:
@@ -261,8 +400,10 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import torch
     import synthetic_inputs as si
+    if args.workload == si.DECODER_WORKLOAD["name"]:
+        return bench_decoder(args)
+    import torch
     from transformer_encoder_bert_amd import ftx
 
     if not torch.cuda.is_available():

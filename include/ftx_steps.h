@@ -56,6 +56,17 @@ ftx_status ftx_step_attention(ftx_dtype dtype, int B, int S, int n, int d, const
                               const void *k, const void *v_t, const int32_t *seq_lens,
                               void *ctx, void *stream);
 
+/* The same attention with separate query and key lengths (cross-attention: queries of one
+ * sequence over the keys of another) and an optional causal mask (a decoder's
+ * self-attention: query i ignores keys j > i; needs Sq == Sk):
+ *   q [B][n][Sq][d], k [B][n][Sk][d], v_t [B][n][d][Sk]; key_lens [B] int32 (keys
+ *   j >= key_lens[b] get probability 0; clamped to [1, Sk]) or NULL; ctx [B][Sq][n*d].
+ * Sq, Sk multiples of 32 in [32, 512]. */
+ftx_status ftx_step_masked_attention(ftx_dtype dtype, int B, int Sq, int Sk, int n, int d,
+                                     const void *q, const void *k, const void *v_t,
+                                     const int32_t *key_lens, int causal, void *ctx,
+                                     void *stream);
+
 /* Bias + residual + LayerNorm (after the attention block and after the FFN), one row of
  * `cols` per token:
  *   y = LN(x + a + bias; gamma, beta) with epsilon FTX_LN_EPSILON, biased variance,

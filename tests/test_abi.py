@@ -113,3 +113,35 @@ def test_step_argument_checks(lib):
     assert lib.ftx_step_bias_gelu(1, 4, 12, 256, 512, 768, None) == E
     assert lib.ftx_step_transpose(1, 4, 4, 256, 256 + 8, None) == E
     assert lib.ftx_step_transpose(3, 4, 4, 256, 4096, None) == E
+
+
+@pytest.mark.parametrize("args,expected", [
+    ((0, 32, 32, 12, 64, 2, 1), ftx.FTX_ERR_INVALID_ARG),     # batch 0
+    ((1, 32, 32, 12, 64, 0, 1), ftx.FTX_ERR_INVALID_ARG),     # no layers
+    ((1, 32, 32, 12, 64, 2, 9), ftx.FTX_ERR_INVALID_ARG),     # unknown dtype
+    ((1, 40, 32, 12, 64, 2, 1), ftx.FTX_ERR_UNSUPPORTED),     # decoder length not a multiple of 32
+    ((1, 32, 48, 12, 64, 2, 1), ftx.FTX_ERR_UNSUPPORTED),     # memory length not a multiple of 32
+    ((1, 32, 544, 12, 64, 2, 1), ftx.FTX_ERR_UNSUPPORTED),    # memory above 512
+    ((1, 32, 32, 12, 48, 2, 1), ftx.FTX_ERR_UNSUPPORTED),     # head size 48
+])
+def test_decoder_create_rejects_before_device(lib, args, expected):
+    h = ctypes.c_void_p()
+    assert lib.ftx_decoder_create(*args, ctypes.byref(h)) == expected
+    assert not h.value
+    assert lib.ftx_last_error()
+
+
+def test_decoder_null_paths(lib):
+    assert lib.ftx_decoder_create(1, 32, 32, 12, 64, 1, 1, None) == ftx.FTX_ERR_INVALID_ARG
+    assert lib.ftx_decoder_destroy(None) == ftx.FTX_OK
+    w = ftx.ftx_decoder_layer_weights()
+    assert lib.ftx_decoder_set_weights(None, 0, ctypes.byref(w), None) == ftx.FTX_ERR_INVALID_ARG
+    assert lib.ftx_decoder_forward(None, 256, 512, None, 1024, None) == ftx.FTX_ERR_INVALID_ARG
+
+
+def test_masked_attention_argument_checks(lib):
+    E = ftx.FTX_ERR_INVALID_ARG
+    # causal needs equal lengths; unsupported lengths; NULL pointers
+    assert lib.ftx_step_masked_attention(1, 1, 32, 64, 2, 64, 256, 512, 768, None, 1, 1024, None) == E
+    assert lib.ftx_step_masked_attention(1, 1, 32, 48, 2, 64, 256, 512, 768, None, 0, 1024, None) == ftx.FTX_ERR_UNSUPPORTED
+    assert lib.ftx_step_masked_attention(1, 1, 32, 64, 2, 64, None, 512, 768, None, 0, 1024, None) == E

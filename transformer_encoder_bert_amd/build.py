@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libftx.so")
-SOURCES = ("elementwise.hip", "gemm.hip", "attention.hip", "encoder.hip")
+SOURCES = ("elementwise.hip", "gemm.hip", "attention.hip", "encoder.hip", "decoder.hip")
 ARCH = "gfx950"
 
 

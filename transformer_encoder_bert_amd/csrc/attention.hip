@@ -64,8 +64,9 @@ __global__ __launch_bounds__(256) void attention_global_kernel(const T* __restri
                                                         const T* __restrict__ k,
                                                         const T* __restrict__ vt,
                                                         const int32_t* __restrict__ lens,
-                                                        T* __restrict__ ctx, int B, int S, int nh,
-                                                        float scale_log2e, int s_valid) {
+                                                        T* __restrict__ ctx, int B, int Sq, int Sk,
+                                                        int nh, float scale_log2e, int s_valid,
+                                                        int causal) {
   typedef AttnMfma<T> MF;
   typedef typename MF::frag frag;
   typedef typename VecT<T, 4>::type v4;
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(256) void attention_global_kernel(const T* __restri
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int lr = lane % 32, g = lane / 32;
-  const int qblocks = S / 32;
+  const int qblocks = Sq / 32;
   const int ntasks = B * nh * qblocks;
   // hand each XCD a contiguous range of tasks so the waves reading one head's K and V
   // share that XCD's L2
@@ -91,16 +92,18 @@ __global__ __launch_bounds__(256) void attention_global_kernel(const T* __restri
   const int b = bh / nh, h = bh % nh;
   int len = lens ? lens[b] : s_valid;
   len = min(max(len, 1), s_valid);
-  const int nkt = (len + 31) / 32;
+  int nkt = (len + 31) / 32;
+  if (causal) nkt = min(nkt, qb + 1);  // later key tiles are entirely in the future
+  const int query = qb * 32 + lr;
 
   frag qf[NQF];
   {
-    const T* qp = q + ((size_t)bh * S + qb * 32 + lr) * D + g * VEC;
+    const T* qp = q + ((size_t)bh * Sq + qb * 32 + lr) * D + g * VEC;
 #pragma unroll
     for (int f = 0; f < NQF; ++f) qf[f] = *(const frag*)(qp + f * KF);
   }
-  const T* kbase = k + (size_t)bh * S * D + g * VEC;
-  const T* vbase = vt + (size_t)bh * D * S;
+  const T* kbase = k + (size_t)bh * Sk * D + g * VEC;
+  const T* vbase = vt + (size_t)bh * D * Sk;
 
   f32x16 o[DT];
 #pragma unroll
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(256) void attention_global_kernel(const T* __restri
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = (c0 + t) * 32 + 8 * (r / 4) + 4 * g + (r % 4);
-        if (key >= len) sc[t][r] = -INFINITY;
+        if (key >= len || (causal && key > query)) sc[t][r] = -INFINITY;
         mx = fmaxf(mx, sc[t][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(256) void attention_global_kernel(const T* __restri
           for (int s = 0; s < 8; ++s) pf[s] = from_f32<T>(sc[t][8 * u + s]);
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const T* vr = vbase + (size_t)(dt * 32 + lr) * S + kt * 32 + 16 * u + 4 * g;
+            const T* vr = vbase + (size_t)(dt * 32 + lr) * Sk + kt * 32 + 16 * u + 4 * g;
             const v4 lo = *(const v4*)(vr);
             const v4 hi = *(const v4*)(vr + 8);
             frag vf;
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(256) void attention_global_kernel(const T* __restri
           for (int s = 0; s < 4; ++s) pf[s] = sc[t][4 * u + s];
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const T* vr = vbase + (size_t)(dt * 32 + lr) * S + kt * 32 + 8 * u + 4 * g;
+            const T* vr = vbase + (size_t)(dt * 32 + lr) * Sk + kt * 32 + 8 * u + 4 * g;
             MF::mma(*(const frag*)vr, pf, o[dt]);
           }
         }
@@ -195,10 +198,10 @@ __global__ __launch_bounds__(256) void attention_global_kernel(const T* __restri
     }
   }
 
-  // normalise and store with heads merged: ctx[b*S + query][h*D + dd]
+  // normalise and store with heads merged: ctx[b*Sq + query][h*D + dd]
   const float inv = 1.0f / l_run;
   const int H = nh * D;
-  T* out = ctx + ((size_t)b * S + qb * 32 + lr) * H + h * D + 4 * g;
+  T* out = ctx + ((size_t)b * Sq + qb * 32 + lr) * H + h * D + 4 * g;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -230,8 +233,8 @@ template <typename T, int D, int SMAX> struct AttnCfg {
 template <typename T, int D, int SMAX>
 __global__ __launch_bounds__((AttnCfg<T, D, SMAX>::NW * kWave)) void attention_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt,
-    const int32_t* __restrict__ lens, T* __restrict__ ctx, int B, int S, int nh,
-    float scale_log2e, int s_valid) {
+    const int32_t* __restrict__ lens, T* __restrict__ ctx, int B, int Sq, int Sk, int nh,
+    float scale_log2e, int s_valid, int causal) {
   typedef AttnCfg<T, D, SMAX> C;
   typedef AttnMfma<T> MF;
   typedef typename MF::frag frag;
@@ -247,7 +250,7 @@ __global__ __launch_bounds__((AttnCfg<T, D, SMAX>::NW * kWave)) void attention_k
   T* Ks = smem;
   T* Vs = smem + SMAX * C::KST;
 
-  const int qblocks = S / 32;
+  const int qblocks = Sq / 32;
   const int groups = (qblocks + C::NW - 1) / C::NW;
   const int bh = blockIdx.x / groups, grp = blockIdx.x % groups;
   const int b = bh / nh, h = bh % nh;
@@ -257,12 +260,18 @@ __global__ __launch_bounds__((AttnCfg<T, D, SMAX>::NW * kWave)) void attention_k
   const bool active = qb < qblocks;
   int len = lens ? lens[b] : s_valid;
   len = min(max(len, 1), s_valid);
-  const int nkt = (len + 31) / 32;
-  const int nk = nkt * 32;  // keys held in LDS
+  int nkt = (len + 31) / 32;       // key tiles of this wave
+  int nk = nkt * 32;               // keys held in LDS (for every wave of the group)
+  if (causal) {
+    // key tiles after a query block are entirely in its future
+    nk = min(nkt, min(grp * C::NW + C::NW, qblocks)) * 32;
+    nkt = min(nkt, qb + 1);
+  }
+  const int query = qb * 32 + lr;
 
   frag qf[NQF];
   if (active) {
-    const T* qp = q + ((size_t)bh * S + qb * 32 + lr) * D + g * VEC;
+    const T* qp = q + ((size_t)bh * Sq + qb * 32 + lr) * D + g * VEC;
 #pragma unroll
     for (int f = 0; f < NQF; ++f) qf[f] = *(const frag*)(qp + f * KF);
   }
@@ -274,8 +283,8 @@ __global__ __launch_bounds__((AttnCfg<T, D, SMAX>::NW * kWave)) void attention_k
     constexpr int KPT = (SMAX * KCH + NT - 1) / NT;  // K vectors per thread
     constexpr int VCH = SMAX / C::VE;                // vectors per V^T row
     constexpr int VPT = (D * VCH + NT - 1) / NT;
-    const T* kg = k + (size_t)bh * S * D;
-    const T* vg = vt + (size_t)bh * D * S;
+    const T* kg = k + (size_t)bh * Sk * D;
+    const T* vg = vt + (size_t)bh * D * Sk;
     vec kb[KPT], vb[VPT];
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
@@ -285,7 +294,7 @@ __global__ __launch_bounds__((AttnCfg<T, D, SMAX>::NW * kWave)) void attention_k
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int c = threadIdx.x + i * NT, col = (c % VCH) * C::VE;
-      if (c < D * VCH && col < nk) vb[i] = *(const vec*)(vg + (size_t)(c / VCH) * S + col);
+      if (c < D * VCH && col < nk) vb[i] = *(const vec*)(vg + (size_t)(c / VCH) * Sk + col);
     }
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
@@ -330,11 +339,12 @@ __global__ __launch_bounds__((AttnCfg<T, D, SMAX>::NW * kWave)) void attention_k
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = (c0 + t) * 32 + 8 * (r / 4) + 4 * g + (r % 4);
-          if (key >= len) sc[t][r] = -INFINITY;
+          if (key >= len || (causal && key > query)) sc[t][r] = -INFINITY;
           mx = fmaxf(mx, sc[t][r]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);  // finite: every chunk holds a key below len
+      // finite: every chunk's first key is below len and (causal) not after the query
+      const float m_new = fmaxf(m_run, mx);
       const float alpha = exp2f((m_run - m_new) * scale_log2e);
       float psum = 0.f;
 #pragma unroll
@@ -415,7 +425,7 @@ __global__ __launch_bounds__((AttnCfg<T, D, SMAX>::NW * kWave)) void attention_k
   const int H = nh * D;
   constexpr int CPR = D / C::VE;       // vectors per output row
   constexpr int RPP = kWave / CPR;     // rows per pass
-  T* out = ctx + ((size_t)b * S + qb * 32) * H + h * D;
+  T* out = ctx + ((size_t)b * Sq + qb * 32) * H + h * D;
 #pragma unroll
   for (int p = 0; p < 32 / RPP; ++p) {
     const int row = p * RPP + lane / CPR, col = (lane % CPR) * C::VE;
@@ -435,7 +445,7 @@ __global__ __launch_bounds__(256) void attention_s32_kernel(const T* __restrict_
                                                            const int32_t* __restrict__ lens,
                                                            T* __restrict__ ctx, int B, int S,
                                                            int nh, float scale_log2e,
-                                                           int s_valid) {
+                                                           int s_valid, int causal) {
   typedef AttnMfma<T> MF;
   typedef typename MF::frag frag;
   typedef typename VecT<T, 4>::type v4;
@@ -486,7 +496,8 @@ __global__ __launch_bounds__(256) void attention_s32_kernel(const T* __restrict_
   float mx = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    if (8 * (r / 4) + 4 * g + (r % 4) >= len) sc[r] = -INFINITY;
+    const int key = 8 * (r / 4) + 4 * g + (r % 4);
+    if (key >= len || (causal && key > lr)) sc[r] = -INFINITY;
     mx = fmaxf(mx, sc[r]);
   }
   mx = fmaxf(mx, __shfl_xor(mx, 32));  // finite: key 0 is always valid
@@ -530,61 +541,65 @@ __global__ __launch_bounds__(256) void attention_s32_kernel(const T* __restrict_
 constexpr size_t kMaxLdsBytes = 160 * 1024;  // per workgroup on gfx950
 
 template <typename T, int D, int SMAX>
-static hipError_t attn_launch_cfg(int B, int S, int nh, const void* q, const void* k,
+static hipError_t attn_launch_cfg(int B, int Sq, int Sk, int nh, const void* q, const void* k,
                                   const void* vt, const int32_t* lens, void* ctx,
-                                  float scale_log2e, int s_valid, hipStream_t s) {
+                                  float scale_log2e, int s_valid, int causal, hipStream_t s) {
   typedef AttnCfg<T, D, SMAX> C;
-  const int groups = (S / 32 + C::NW - 1) / C::NW;
+  const int groups = (Sq / 32 + C::NW - 1) / C::NW;
   attention_kernel<T, D, SMAX><<<B * nh * groups, C::NW * kWave, 0, s>>>(
-      (const T*)q, (const T*)k, (const T*)vt, lens, (T*)ctx, B, S, nh, scale_log2e, s_valid);
+      (const T*)q, (const T*)k, (const T*)vt, lens, (T*)ctx, B, Sq, Sk, nh, scale_log2e, s_valid,
+      causal);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t attn_launch_d(int B, int S, int nh, const void* q, const void* k,
+static hipError_t attn_launch_d(int B, int Sq, int Sk, int nh, const void* q, const void* k,
                                 const void* vt, const int32_t* lens, void* ctx,
-                                float scale_log2e, int s_valid, hipStream_t s) {
-  if (S <= 32) {
+                                float scale_log2e, int s_valid, int causal, hipStream_t s) {
+  if (Sk <= 32) {
     // the register-only kernel has the shorter chain (no LDS round trip, no barrier) and wins
     // while few heads are in flight; with thousands its 32-row fragment loads cost more in
     // address processing than the LDS kernel's contiguous 1 KB staging loads (measured at
     // BERT-base: 6.9 vs 8.8 us at 768 heads, 25.9 vs 23.5 us at 6144)
-    if constexpr (sizeof(T) == 2) if (B * nh <= 2048) {
+    if constexpr (sizeof(T) == 2) if (Sq == 32 && B * nh <= 2048) {
       attention_s32_kernel<T, D><<<(B * nh + 3) / 4, 256, 0, s>>>(
-          (const T*)q, (const T*)k, (const T*)vt, lens, (T*)ctx, B, S, nh, scale_log2e, s_valid);
+          (const T*)q, (const T*)k, (const T*)vt, lens, (T*)ctx, B, 32, nh, scale_log2e, s_valid,
+          causal);
       return hipGetLastError();
     }
-    return attn_launch_cfg<T, D, 32>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, s);
+    return attn_launch_cfg<T, D, 32>(B, Sq, Sk, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, causal, s);
   }
-  if (S <= 64) return attn_launch_cfg<T, D, 64>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, s);
-  if (S <= 128) return attn_launch_cfg<T, D, 128>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, s);
-  if (S <= 256) return attn_launch_cfg<T, D, 256>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, s);
+  if (Sk <= 64) return attn_launch_cfg<T, D, 64>(B, Sq, Sk, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, causal, s);
+  if (Sk <= 128) return attn_launch_cfg<T, D, 128>(B, Sq, Sk, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, causal, s);
+  if (Sk <= 256) return attn_launch_cfg<T, D, 256>(B, Sq, Sk, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, causal, s);
   if constexpr (AttnCfg<T, D, 512>::LDS * sizeof(T) <= kMaxLdsBytes)
-    return attn_launch_cfg<T, D, 512>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, s);
-  const int blocks = (B * nh * (S / 32) + 3) / 4;
+    return attn_launch_cfg<T, D, 512>(B, Sq, Sk, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, causal, s);
+  const int blocks = (B * nh * (Sq / 32) + 3) / 4;
   attention_global_kernel<T, D><<<blocks, 256, 0, s>>>((const T*)q, (const T*)k, (const T*)vt, lens,
-                                                       (T*)ctx, B, S, nh, scale_log2e, s_valid);
+                                                       (T*)ctx, B, Sq, Sk, nh, scale_log2e, s_valid,
+                                                       causal);
   return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t attn_launch(int B, int S, int nh, int d, const void* q, const void* k,
+static hipError_t attn_launch(int B, int Sq, int Sk, int nh, int d, const void* q, const void* k,
                               const void* vt, const int32_t* lens, void* ctx, hipStream_t s,
-                              int s_valid) {
+                              int s_valid, int causal) {
   const float scale_log2e = (float)(1.4426950408889634 / sqrt((double)d));
-  if (d == 64) return attn_launch_d<T, 64>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, s);
-  if (d == 32) return attn_launch_d<T, 32>(B, S, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, s);
+  if (d == 64) return attn_launch_d<T, 64>(B, Sq, Sk, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, causal, s);
+  if (d == 32) return attn_launch_d<T, 32>(B, Sq, Sk, nh, q, k, vt, lens, ctx, scale_log2e, s_valid, causal, s);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attention(ftx_dtype dt, int B, int S, int nh, int d, const void* q,
+hipError_t launch_attention(ftx_dtype dt, int B, int Sq, int Sk, int nh, int d, const void* q,
                             const void* k, const void* vt, const int32_t* lens, void* ctx,
-                            hipStream_t s, int s_valid) {
-  if (s_valid <= 0 || s_valid > S) s_valid = S;
+                            hipStream_t s, int s_valid, bool causal) {
+  if (s_valid <= 0 || s_valid > Sk) s_valid = Sk;
+  const int c = causal ? 1 : 0;
   switch (dt) {
-    case FTX_FP32: return attn_launch<float>(B, S, nh, d, q, k, vt, lens, ctx, s, s_valid);
-    case FTX_FP16: return attn_launch<f16>(B, S, nh, d, q, k, vt, lens, ctx, s, s_valid);
-    case FTX_BF16: return attn_launch<bf16>(B, S, nh, d, q, k, vt, lens, ctx, s, s_valid);
+    case FTX_FP32: return attn_launch<float>(B, Sq, Sk, nh, d, q, k, vt, lens, ctx, s, s_valid, c);
+    case FTX_FP16: return attn_launch<f16>(B, Sq, Sk, nh, d, q, k, vt, lens, ctx, s, s_valid, c);
+    case FTX_BF16: return attn_launch<bf16>(B, Sq, Sk, nh, d, q, k, vt, lens, ctx, s, s_valid, c);
   }
   return hipErrorInvalidValue;
 }

@@ -18,62 +18,20 @@
 
 #include "ftx.h"
 #include "ftx_steps.h"
+#include "abi_common.h"
 #include "launch.h"
 
 using namespace ftx;
 
-namespace {
-
-thread_local std::string g_last_error;
-
-ftx_status fail(ftx_status s, const std::string& msg) {
-  g_last_error = msg;
-  return s;
-}
-
-ftx_status hip_fail(hipError_t e, const char* what) {
-  if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
-    return fail(FTX_ERR_OUT_OF_MEMORY, std::string(what) + ": " + hipGetErrorString(e));
-  return fail(FTX_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
-}
-
-#define FTX_HIP(call)                                   \
-  do {                                                  \
-    hipError_t e_ = (call);                             \
-    if (e_ != hipSuccess) return hip_fail(e_, #call);   \
-  } while (0)
-
-size_t dtype_size(ftx_dtype dt) { return dt == FTX_FP32 ? 4 : 2; }
-bool dtype_ok(int dt) { return dt == FTX_FP32 || dt == FTX_FP16 || dt == FTX_BF16; }
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-
-bool overlap(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return x < y + nb && y < x + na;
-}
-
-// True if `p` points into device memory (or managed memory) of the HIP runtime.  Kernels
-// given a host pointer would fault, so every entry point checks its tensor pointers.
-bool is_device_ptr(const void* p) {
-  if (!p) return false;
-  hipPointerAttribute_t a;
-  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
-    (void)hipGetLastError();
-    return false;
-  }
-  return a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged;
-}
-
-bool all_device(std::initializer_list<const void*> ps) {
-  for (const void* p : ps)
-    if (p && !is_device_ptr(p)) return false;
-  return true;
+std::string& ftx::last_error_slot() {
+  thread_local std::string msg;
+  return msg;
 }
 
 // Shape checks shared by create and the step entry points.  The encoder takes any sequence
 // length up to FTX_MAX_SEQ_LEN (it pads internally to a multiple of 32); the step entry
 // points work on the padded layout and need the multiple of 32.
-ftx_status check_shape(int B, int S, int nh, int d, bool any_len = false) {
+ftx_status ftx::check_shape(int B, int S, int nh, int d, bool any_len) {
   if (B < 1 || S < 1 || nh < 1 || d < 1) return fail(FTX_ERR_INVALID_ARG, "shape values must be >= 1");
   if (d != 32 && d != 64) return fail(FTX_ERR_UNSUPPORTED, "size_per_head must be 32 or 64");
   if (S > FTX_MAX_SEQ_LEN) return fail(FTX_ERR_UNSUPPORTED, "seq_len above 512");
@@ -86,6 +44,8 @@ ftx_status check_shape(int B, int S, int nh, int d, bool any_len = false) {
     return fail(FTX_ERR_UNSUPPORTED, "batch * seq_len * 4 * hidden must stay below 2^31");
   return FTX_OK;
 }
+
+namespace {
 
 struct LayerW {
   void* w_qkv_t;  // [3H][H]
@@ -220,7 +180,7 @@ ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq
     }
     if (st != FTX_OK) return st;
     st = run_step(e, FTX_STEP_ATTENTION, s, [&] {
-      return launch_attention(dt, B, S, nh, d, e->q, e->k, e->vt, seq_lens, e->ctx, s, e->Sv);
+      return launch_attention(dt, B, S, S, nh, d, e->q, e->k, e->vt, seq_lens, e->ctx, s, e->Sv);
     });
     if (st != FTX_OK) return st;
     st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
@@ -288,11 +248,11 @@ const char* ftx_status_string(ftx_status s) {
   return "unknown status";
 }
 
-const char* ftx_last_error(void) { return g_last_error.c_str(); }
+const char* ftx_last_error(void) { return last_error_slot().c_str(); }
 
 ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int size_per_head,
                               int num_layers, ftx_dtype dtype, ftx_encoder** out) {
-  g_last_error.clear();
+  last_error_slot().clear();
   if (!out) return fail(FTX_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
@@ -417,7 +377,7 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
 }
 
 ftx_status ftx_set_weights(ftx_encoder* e, int layer, const ftx_layer_weights* w, void* stream) {
-  g_last_error.clear();
+  last_error_slot().clear();
   if (!e) return fail(FTX_ERR_INVALID_ARG, "encoder is NULL");
   if (!w) return fail(FTX_ERR_INVALID_ARG, "weights struct is NULL");
   if (layer < 0 || layer >= e->L) return fail(FTX_ERR_INVALID_ARG, "layer out of range");
@@ -457,7 +417,7 @@ ftx_status ftx_set_weights(ftx_encoder* e, int layer, const ftx_layer_weights* w
 
 ftx_status ftx_forward(ftx_encoder* e, const void* input, const int32_t* seq_lens, void* output,
                        void* stream) {
-  g_last_error.clear();
+  last_error_slot().clear();
   if (!e) return fail(FTX_ERR_INVALID_ARG, "encoder is NULL");
   if (!input || !output) return fail(FTX_ERR_INVALID_ARG, "input or output is NULL");
   if (!aligned16(input) || !aligned16(output))
@@ -502,7 +462,7 @@ ftx_status ftx_forward(ftx_encoder* e, const void* input, const int32_t* seq_len
 }
 
 ftx_status ftx_destroy(ftx_encoder* e) {
-  g_last_error.clear();
+  last_error_slot().clear();
   if (!e) return FTX_OK;
   hipSetDevice(e->device);
   hipDeviceSynchronize();
@@ -521,7 +481,7 @@ ftx_status ftx_destroy(ftx_encoder* e) {
 }
 
 ftx_status ftx_set_option(ftx_encoder* e, ftx_option option, int value) {
-  g_last_error.clear();
+  last_error_slot().clear();
   if (!e) return fail(FTX_ERR_INVALID_ARG, "encoder is NULL");
   switch (option) {
     case FTX_OPT_FUSED_EPILOGUES:
@@ -538,7 +498,7 @@ ftx_status ftx_set_option(ftx_encoder* e, ftx_option option, int value) {
 }
 
 ftx_status ftx_kernel_times(ftx_encoder* e, double* ms, int64_t* counts) {
-  g_last_error.clear();
+  last_error_slot().clear();
   if (!e) return fail(FTX_ERR_INVALID_ARG, "encoder is NULL");
   double acc[FTX_NUM_STEPS] = {0};
   int64_t cnt[FTX_NUM_STEPS] = {0};
@@ -563,7 +523,7 @@ ftx_status ftx_kernel_times(ftx_encoder* e, double* ms, int64_t* counts) {
 
 ftx_status ftx_step_linear(ftx_dtype dtype, int M, int N, int K, const void* a, const void* w_t,
                            const void* bias, int gelu, void* c, void* stream) {
-  g_last_error.clear();
+  last_error_slot().clear();
   if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
   if (M < 1 || N < 8 || K < 8 || N % 8 || K % 8)
     return fail(FTX_ERR_INVALID_ARG, "need M >= 1 and N, K positive multiples of 8");
@@ -583,7 +543,7 @@ ftx_status ftx_step_linear(ftx_dtype dtype, int M, int N, int K, const void* a, 
 ftx_status ftx_step_qkv_projection(ftx_dtype dtype, int B, int S, int n, int d, const void* x,
                                    const void* w_qkv_t, const void* b_qkv, void* q, void* k,
                                    void* v_t, void* stream) {
-  g_last_error.clear();
+  last_error_slot().clear();
   if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
   ftx_status st = check_shape(B, S, n, d);
   if (st != FTX_OK) return st;
@@ -597,7 +557,7 @@ ftx_status ftx_step_qkv_projection(ftx_dtype dtype, int B, int S, int n, int d, 
 
 ftx_status ftx_step_bias_qkv_split(ftx_dtype dtype, int B, int S, int n, int d, const void* qkv,
                                    const void* b_qkv, void* q, void* k, void* v_t, void* stream) {
-  g_last_error.clear();
+  last_error_slot().clear();
   if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
   ftx_status st = check_shape(B, S, n, d);
   if (st != FTX_OK) return st;
@@ -612,7 +572,7 @@ ftx_status ftx_step_bias_qkv_split(ftx_dtype dtype, int B, int S, int n, int d, 
 ftx_status ftx_step_attention(ftx_dtype dtype, int B, int S, int n, int d, const void* q,
                               const void* k, const void* v_t, const int32_t* seq_lens, void* ctx,
                               void* stream) {
-  g_last_error.clear();
+  last_error_slot().clear();
   if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
   ftx_status st = check_shape(B, S, n, d);
   if (st != FTX_OK) return st;
@@ -620,14 +580,33 @@ ftx_status ftx_step_attention(ftx_dtype dtype, int B, int S, int n, int d, const
   if (!aligned16(q) || !aligned16(k) || !aligned16(v_t) || !aligned16(ctx))
     return fail(FTX_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
   if (!all_device({q, k, v_t, seq_lens, ctx})) return fail(FTX_ERR_INVALID_ARG, "pointers must be device memory");
-  hipError_t err = launch_attention(dtype, B, S, n, d, q, k, v_t, seq_lens, ctx, (hipStream_t)stream);
+  hipError_t err = launch_attention(dtype, B, S, S, n, d, q, k, v_t, seq_lens, ctx, (hipStream_t)stream);
+  return err == hipSuccess ? FTX_OK : hip_fail(err, "attention launch");
+}
+
+ftx_status ftx_step_masked_attention(ftx_dtype dtype, int B, int Sq, int Sk, int n, int d,
+                                     const void* q, const void* k, const void* v_t,
+                                     const int32_t* key_lens, int causal, void* ctx,
+                                     void* stream) {
+  last_error_slot().clear();
+  if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
+  ftx_status st = check_shape(B, Sq, n, d);
+  if (st == FTX_OK) st = check_shape(B, Sk, n, d);
+  if (st != FTX_OK) return st;
+  if (causal && Sq != Sk) return fail(FTX_ERR_INVALID_ARG, "causal attention needs Sq == Sk");
+  if (!q || !k || !v_t || !ctx) return fail(FTX_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v_t) || !aligned16(ctx))
+    return fail(FTX_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (!all_device({q, k, v_t, key_lens, ctx})) return fail(FTX_ERR_INVALID_ARG, "pointers must be device memory");
+  hipError_t err = launch_attention(dtype, B, Sq, Sk, n, d, q, k, v_t, key_lens, ctx,
+                                    (hipStream_t)stream, 0, causal != 0);
   return err == hipSuccess ? FTX_OK : hip_fail(err, "attention launch");
 }
 
 ftx_status ftx_step_bias_residual_layernorm(ftx_dtype dtype, int rows, int cols, const void* x,
                                             const void* a, const void* bias, const void* gamma,
                                             const void* beta, void* y, void* stream) {
-  g_last_error.clear();
+  last_error_slot().clear();
   if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
   if (rows < 1 || cols < 4 || cols % 4) return fail(FTX_ERR_INVALID_ARG, "need rows >= 1, cols a positive multiple of 4");
   if (cols > kMaxLayerNormCols) return fail(FTX_ERR_UNSUPPORTED, "cols above 4096");
@@ -643,7 +622,7 @@ ftx_status ftx_step_bias_residual_layernorm(ftx_dtype dtype, int rows, int cols,
 
 ftx_status ftx_step_bias_gelu(ftx_dtype dtype, int rows, int cols, const void* u, const void* bias,
                               void* g, void* stream) {
-  g_last_error.clear();
+  last_error_slot().clear();
   if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
   if (rows < 1 || cols < 8 || cols % 8) return fail(FTX_ERR_INVALID_ARG, "need rows >= 1, cols a positive multiple of 8");
   if ((long long)rows * cols >= (1LL << 31)) return fail(FTX_ERR_UNSUPPORTED, "tensor above 2^31 elements");
@@ -656,7 +635,7 @@ ftx_status ftx_step_bias_gelu(ftx_dtype dtype, int rows, int cols, const void* u
 
 ftx_status ftx_step_transpose(ftx_dtype dtype, int rows, int cols, const void* in, void* out,
                               void* stream) {
-  g_last_error.clear();
+  last_error_slot().clear();
   if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
   if (rows < 1 || cols < 1) return fail(FTX_ERR_INVALID_ARG, "need rows, cols >= 1");
   if ((long long)rows * cols >= (1LL << 31)) return fail(FTX_ERR_UNSUPPORTED, "tensor above 2^31 elements");

@@ -114,7 +114,10 @@ template <typename T, bool GELU, typename TO = T> struct EpiLinear {
 // bias + head split: a 32-column tile lies inside one of Q, K, V and inside one head (d is
 // 32 or 64 and H a multiple of 32), and its 32 rows are consecutive tokens of one sequence
 // (S is a multiple of 32).  Q and K are written [B][n][S][d]; V transposed per head,
-// [B][n][d][S], from tiles staged column-major.
+// [B][n][d][S], from tiles staged column-major.  Column block c of the projection (H
+// columns each) goes to slot first + c of (Q, K, V): the fused Q/K/V projection has
+// first = 0 and three blocks; a cross-attention's query projection first = 0 and one, its
+// key/value projection over the memory first = 1 and two.
 template <typename T> struct EpiQKV {
   typedef T out_t;
   typedef typename Vec16<T>::type vec;
@@ -123,7 +126,7 @@ template <typename T> struct EpiQKV {
   T* k;
   T* vt;
   const T* bias;
-  int S, nh, d, M, N;
+  int S, nh, d, M, N, first;
   __device__ __forceinline__ b4 bias4(int n) const {
     b4 v = {};
     if (n < N) v = *(const b4*)(bias + n);
@@ -132,7 +135,7 @@ template <typename T> struct EpiQKV {
   __device__ __forceinline__ float act(float v) const { return v; }
   __device__ __forceinline__ TileDst<T> tile(int mt, int nt) const {
     const int H = nh * d;
-    const int which = nt / H, rem = nt - which * H;
+    const int blk = nt / H, rem = nt - blk * H, which = first + blk;
     const int h = rem / d, dd0 = rem - h * d;
     const int b = mt / S, s0 = mt - b * S;
     const size_t head = (size_t)b * nh + h;
@@ -146,7 +149,7 @@ template <typename T> struct EpiQKV {
   // head of one of Q, K, V (d is a multiple of 4)
   __device__ __forceinline__ void store4(int m, int n, const float (&v)[4]) const {
     const int H = nh * d;
-    const int which = n / H, rem = n - which * H;
+    const int blk = n / H, rem = n - blk * H, which = first + blk;
     const int h = rem / d, dd = rem - h * d;
     const int b = m / S, s = m - b * S;
     const size_t head = (size_t)b * nh + h;
@@ -596,22 +599,32 @@ hipError_t launch_linear(ftx_dtype dt, int M, int N, int K, const void* a, const
 }
 
 template <typename T>
-static hipError_t qkv_t(int B, int S, int nh, int d, const void* x, const void* w, const void* b,
-                        void* q, void* k, void* vt, hipStream_t s, float* ws, size_t wn) {
+static hipError_t heads_t(int B, int S, int nh, int d, const void* x, const void* w, const void* b,
+                          int first, int count, void* q, void* k, void* vt, hipStream_t s,
+                          float* ws, size_t wn) {
   const int M = B * S, H = nh * d;
-  EpiQKV<T> epi{(T*)q, (T*)k, (T*)vt, (const T*)b, S, nh, d, M, 3 * H};
-  return gemm_launch<T>(M, 3 * H, H, x, w, epi, s, ws, wn);
+  EpiQKV<T> epi{(T*)q, (T*)k, (T*)vt, (const T*)b, S, nh, d, M, count * H, first};
+  return gemm_launch<T>(M, count * H, H, x, w, epi, s, ws, wn);
+}
+
+hipError_t launch_head_projection(ftx_dtype dt, int B, int S, int nh, int d, const void* x,
+                                  const void* w_t, const void* bias, int first, int count,
+                                  void* q, void* k, void* vt, hipStream_t s, float* ws,
+                                  size_t ws_elems) {
+  if (first < 0 || count < 1 || first + count > 3) return hipErrorInvalidValue;
+  switch (dt) {
+    case FTX_FP32: return heads_t<float>(B, S, nh, d, x, w_t, bias, first, count, q, k, vt, s, ws, ws_elems);
+    case FTX_FP16: return heads_t<f16>(B, S, nh, d, x, w_t, bias, first, count, q, k, vt, s, ws, ws_elems);
+    case FTX_BF16: return heads_t<bf16>(B, S, nh, d, x, w_t, bias, first, count, q, k, vt, s, ws, ws_elems);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_qkv_projection(ftx_dtype dt, int B, int S, int nh, int d, const void* x,
                                  const void* w_qkv_t, const void* b_qkv, void* q, void* k,
                                  void* vt, hipStream_t s, float* ws, size_t ws_elems) {
-  switch (dt) {
-    case FTX_FP32: return qkv_t<float>(B, S, nh, d, x, w_qkv_t, b_qkv, q, k, vt, s, ws, ws_elems);
-    case FTX_FP16: return qkv_t<f16>(B, S, nh, d, x, w_qkv_t, b_qkv, q, k, vt, s, ws, ws_elems);
-    case FTX_BF16: return qkv_t<bf16>(B, S, nh, d, x, w_qkv_t, b_qkv, q, k, vt, s, ws, ws_elems);
-  }
-  return hipErrorInvalidValue;
+  return launch_head_projection(dt, B, S, nh, d, x, w_qkv_t, b_qkv, 0, 3, q, k, vt, s, ws,
+                                ws_elems);
 }
 
 }  // namespace ftx

@@ -20,17 +20,27 @@ hipError_t launch_qkv_projection(ftx_dtype dt, int B, int S, int nh, int d, cons
                                  void* vt, hipStream_t s, float* ws = nullptr,
                                  size_t ws_elems = 0);
 
+// Projection of x [B*S][H] onto `count` blocks of H columns (w_t [count*H][H], bias
+// [count*H]) written head-split: block c goes to slot first + c of (q [B][n][S][d],
+// k [B][n][S][d], vt [B][n][d][S]); first + count <= 3.  Slots not written may be NULL.
+hipError_t launch_head_projection(ftx_dtype dt, int B, int S, int nh, int d, const void* x,
+                                  const void* w_t, const void* bias, int first, int count,
+                                  void* q, void* k, void* vt, hipStream_t s,
+                                  float* ws = nullptr, size_t ws_elems = 0);
+
 // fp32 elements of split-K workspace the GEMM of this shape uses (0: it does not split).
 size_t gemm_splitk_workspace(ftx_dtype dt, int M, int N, int K);
 
 hipError_t launch_bias_qkv_split(ftx_dtype dt, int B, int S, int nh, int d, const void* qkv,
                                  const void* b_qkv, void* q, void* k, void* vt, hipStream_t s);
 
-// S: the (padded) length of the Q/K/V^T layout, a multiple of 32; s_valid (1..S, default S):
-// the sequence length keys are limited to when lens is NULL, and the bound lens are clamped to.
-hipError_t launch_attention(ftx_dtype dt, int B, int S, int nh, int d, const void* q,
+// Sq, Sk: the (padded) query and key lengths of the Q [B][n][Sq][d] and K [B][n][Sk][d],
+// V^T [B][n][d][Sk] layouts, multiples of 32; ctx [B*Sq][n*d].  s_valid (1..Sk, default
+// Sk): the length keys are limited to when lens is NULL, and the bound lens are clamped to.
+// causal (Sq == Sk): query i also ignores keys j > i.
+hipError_t launch_attention(ftx_dtype dt, int B, int Sq, int Sk, int nh, int d, const void* q,
                             const void* k, const void* vt, const int32_t* lens, void* ctx,
-                            hipStream_t s, int s_valid = 0);
+                            hipStream_t s, int s_valid = 0, bool causal = false);
 
 hipError_t launch_bias_residual_layernorm(ftx_dtype dt, int rows, int cols, const void* x,
                                           const void* a, const void* bias, const void* gamma,

@@ -1,9 +1,10 @@
-"""ctypes binding of libftx.so, the C ABI declared in include/ftx.h and include/ftx_steps.h.
+"""ctypes binding of libftx.so, the C ABI declared in include/ftx.h, include/ftx_steps.h and
+include/ftx_decoder.h.
 
 Argument marshalling only: every function here checks what a C caller would have to
 get right (dtype, device, contiguity, shape), turns tensors into device pointers and
 the current torch stream into a hipStream_t, and calls the C function of the same
-name.  No step of the encoder is computed in Python.  If libftx.so is missing the
+name.  No step of the encoder or decoder is computed in Python.  If libftx.so is missing the
 functions raise: there is no fallback.
 """
 from __future__ import annotations
@@ -28,11 +29,22 @@ FTX_NUM_STEPS = len(STEP_NAMES)
 WEIGHT_FIELDS = ("w_q", "b_q", "w_k", "b_k", "w_v", "b_v", "w_o", "b_o", "ln1_gamma", "ln1_beta",
                  "w_ffn1", "b_ffn1", "w_ffn2", "b_ffn2", "ln2_gamma", "ln2_beta")
 
+DECODER_WEIGHT_FIELDS = ("w_q", "b_q", "w_k", "b_k", "w_v", "b_v", "w_o", "b_o", "ln1_gamma",
+                         "ln1_beta", "w_q2", "b_q2", "w_k2", "b_k2", "w_v2", "b_v2", "w_o2", "b_o2",
+                         "ln2_gamma", "ln2_beta", "w_ffn1", "b_ffn1", "w_ffn2", "b_ffn2",
+                         "ln3_gamma", "ln3_beta")
+
+
 EXPORTED = ("ftx_encoder_create", "ftx_set_weights", "ftx_forward", "ftx_destroy",
             "ftx_status_string", "ftx_last_error", "ftx_set_option", "ftx_kernel_times",
             "ftx_step_linear", "ftx_step_qkv_projection", "ftx_step_bias_qkv_split",
-            "ftx_step_attention", "ftx_step_bias_residual_layernorm", "ftx_step_bias_gelu",
-            "ftx_step_transpose")
+            "ftx_step_attention", "ftx_step_masked_attention", "ftx_step_bias_residual_layernorm",
+            "ftx_step_bias_gelu", "ftx_step_transpose",
+            "ftx_decoder_create", "ftx_decoder_set_weights", "ftx_decoder_forward",
+            "ftx_decoder_set_option", "ftx_decoder_kernel_times", "ftx_decoder_destroy")
+DEC_STEP_NAMES = ("self_qkv_gemm", "self_attention", "self_out_gemm", "ln1", "cross_q_gemm",
+                  "cross_kv_gemm", "cross_attention", "cross_out_gemm", "ln2", "ffn1_gemm",
+                  "ffn2_gemm", "ln3")
 
 _DTYPES = {torch.float32: FTX_FP32, torch.float16: FTX_FP16, torch.bfloat16: FTX_BF16}
 _NAMES = {"fp32": FTX_FP32, "fp16": FTX_FP16, "bf16": FTX_BF16}
@@ -47,6 +59,10 @@ class FtxError(RuntimeError):
 
 class ftx_layer_weights(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in WEIGHT_FIELDS]
+
+
+class ftx_decoder_layer_weights(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in DECODER_WEIGHT_FIELDS]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -74,6 +90,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ftx_step_qkv_projection": (i, [i, i, i, i, i, p, p, p, p, p, p, v]),
         "ftx_step_bias_qkv_split": (i, [i, i, i, i, i, p, p, p, p, p, v]),
         "ftx_step_attention": (i, [i, i, i, i, i, p, p, p, p, p, v]),
+        "ftx_step_masked_attention": (i, [i, i, i, i, i, i, p, p, p, p, i, p, v]),
+        "ftx_decoder_create": (i, [i, i, i, i, i, i, i, ctypes.POINTER(p)]),
+        "ftx_decoder_set_weights": (i, [p, i, ctypes.POINTER(ftx_decoder_layer_weights), v]),
+        "ftx_decoder_forward": (i, [p, p, p, p, p, v]),
+        "ftx_decoder_destroy": (i, [p]),
+        "ftx_decoder_set_option": (i, [p, i, i]),
+        "ftx_decoder_kernel_times": (i, [p, p, p]),
         "ftx_step_bias_residual_layernorm": (i, [i, i, i, p, p, p, p, p, p, v]),
         "ftx_step_bias_gelu": (i, [i, i, i, p, p, p, v]),
         "ftx_step_transpose": (i, [i, i, i, p, p, v]),
@@ -218,6 +241,102 @@ class Encoder:
             pass
 
 
+# ------------------------------------------------------------------------ decoder
+
+def ftx_decoder_create(batch_size: int, tgt_len: int, mem_len: int, head_num: int,
+                       size_per_head: int, num_layers: int, dtype) -> ctypes.c_void_p:
+    lib = load_library()
+    h = ctypes.c_void_p()
+    _check(lib.ftx_decoder_create(batch_size, tgt_len, mem_len, head_num, size_per_head,
+                                  num_layers, _dt(dtype), ctypes.byref(h)), "ftx_decoder_create")
+    return h
+
+
+def ftx_decoder_set_weights(dec, layer: int, weights: Dict[str, torch.Tensor], stream=None) -> None:
+    w = ftx_decoder_layer_weights(**{k: _ptr(weights[k]) for k in DECODER_WEIGHT_FIELDS})
+    _check(load_library().ftx_decoder_set_weights(dec, layer, ctypes.byref(w), _stream(stream)),
+           "ftx_decoder_set_weights")
+
+
+def ftx_decoder_forward(dec, x: torch.Tensor, memory: torch.Tensor,
+                        mem_lens: Optional[torch.Tensor], out: torch.Tensor, stream=None) -> None:
+    if mem_lens is not None:
+        _need(mem_lens, "mem_lens", torch.int32)
+    _check(load_library().ftx_decoder_forward(dec, _ptr(x), _ptr(memory), _ptr(mem_lens), _ptr(out),
+                                              _stream(stream)), "ftx_decoder_forward")
+
+
+def ftx_decoder_destroy(dec) -> None:
+    _check(load_library().ftx_decoder_destroy(dec), "ftx_decoder_destroy")
+
+
+def ftx_decoder_set_option(dec, option: int, value: int) -> None:
+    _check(load_library().ftx_decoder_set_option(dec, option, value), "ftx_decoder_set_option")
+
+
+def ftx_decoder_kernel_times(dec):
+    n = len(DEC_STEP_NAMES)
+    ms = (ctypes.c_double * n)()
+    counts = (ctypes.c_int64 * n)()
+    _check(load_library().ftx_decoder_kernel_times(dec, ms, counts), "ftx_decoder_kernel_times")
+    return {DEC_STEP_NAMES[i]: (ms[i], counts[i]) for i in range(n)}
+
+
+class Decoder:
+    """Owns one decoder handle.  ``forward(x, memory, mem_lens)`` allocates the output and
+    calls ftx_decoder_forward."""
+
+    def __init__(self, batch_size: int, tgt_len: int, mem_len: int, head_num: int,
+                 size_per_head: int, num_layers: int, dtype: str):
+        H = head_num * size_per_head
+        self.shape = (batch_size, tgt_len, H)
+        self.mem_shape = (batch_size, mem_len, H)
+        self.num_layers = num_layers
+        self.dtype = TORCH_DTYPE[dtype]
+        self.handle = ftx_decoder_create(batch_size, tgt_len, mem_len, head_num, size_per_head,
+                                         num_layers, dtype)
+
+    def set_weights(self, layer: int, weights: Dict[str, torch.Tensor], stream=None) -> None:
+        for k in DECODER_WEIGHT_FIELDS:
+            _need(weights[k], k, self.dtype)
+        ftx_decoder_set_weights(self.handle, layer, weights, stream)
+
+    def forward(self, x: torch.Tensor, memory: torch.Tensor, mem_lens: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        _need(x, "input", self.dtype, self.shape[0] * self.shape[1] * self.shape[2])
+        _need(memory, "memory", self.dtype, self.mem_shape[0] * self.mem_shape[1] * self.mem_shape[2])
+        if mem_lens is not None:
+            _need(mem_lens, "mem_lens", torch.int32, self.shape[0])
+        if out is None:
+            out = torch.empty(self.shape, dtype=self.dtype, device=x.device)
+        _need(out, "output", self.dtype, x.numel())
+        ftx_decoder_forward(self.handle, x, memory, mem_lens, out, stream)
+        return out
+
+    def set_option(self, option: int, value: int) -> None:
+        ftx_decoder_set_option(self.handle, option, value)
+
+    def kernel_times(self):
+        return ftx_decoder_kernel_times(self.handle)
+
+    def close(self) -> None:
+        if self.handle is not None:
+            ftx_decoder_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 # ------------------------------------------------------------------------ step entry points
 
 def ftx_step_linear(a: torch.Tensor, w_t: torch.Tensor, bias: Optional[torch.Tensor], gelu: bool,
@@ -266,6 +385,20 @@ def ftx_step_attention(B, S, n, d, q, k, v_t, seq_lens, ctx, stream=None) -> Non
     _check(load_library().ftx_step_attention(_dt(q.dtype), B, S, n, d, _ptr(q), _ptr(k), _ptr(v_t),
                                              _ptr(seq_lens), _ptr(ctx), _stream(stream)),
            "ftx_step_attention")
+
+
+def ftx_step_masked_attention(B, Sq, Sk, n, d, q, k, v_t, key_lens, causal, ctx, stream=None) -> None:
+    H = n * d
+    _need(q, "q", q.dtype, B * Sq * H)
+    _need(k, "k", q.dtype, B * Sk * H)
+    _need(v_t, "v_t", q.dtype, B * Sk * H)
+    _need(ctx, "ctx", q.dtype, B * Sq * H)
+    if key_lens is not None:
+        _need(key_lens, "key_lens", torch.int32, B)
+    _check(load_library().ftx_step_masked_attention(_dt(q.dtype), B, Sq, Sk, n, d, _ptr(q), _ptr(k),
+                                                    _ptr(v_t), _ptr(key_lens), int(bool(causal)),
+                                                    _ptr(ctx), _stream(stream)),
+           "ftx_step_masked_attention")
 
 
 def ftx_step_bias_residual_layernorm(x, a, bias, gamma, beta, y, stream=None) -> None:
