@@ -46,8 +46,10 @@ typedef struct {
 
 /* Create a decoder for batch_size sequences of tgt_len decoder positions attending to a
  * memory of mem_len positions; head_num x size_per_head (32 or 64) heads, num_layers
- * layers.  tgt_len and mem_len: multiples of 32 in [32, FTX_MAX_SEQ_LEN].  Allocates the
- * weights and workspace on the current device.
+ * layers.  tgt_len and mem_len: any length in [1, FTX_MAX_SEQ_LEN]; a length that is not a
+ * multiple of 32 is padded internally (one 2-D copy in per forward for the input and for
+ * the memory, one out for the output; cross-attention keys are limited to mem_len).
+ * Allocates the weights and workspace on the current device.
  * Errors: FTX_ERR_INVALID_ARG (out == NULL, values < 1, unknown dtype),
  * FTX_ERR_UNSUPPORTED (sizes outside the ranges above, not a gfx950 device),
  * FTX_ERR_OUT_OF_MEMORY, FTX_ERR_DEVICE. */

@@ -119,8 +119,9 @@ def test_step_argument_checks(lib):
     ((0, 32, 32, 12, 64, 2, 1), ftx.FTX_ERR_INVALID_ARG),     # batch 0
     ((1, 32, 32, 12, 64, 0, 1), ftx.FTX_ERR_INVALID_ARG),     # no layers
     ((1, 32, 32, 12, 64, 2, 9), ftx.FTX_ERR_INVALID_ARG),     # unknown dtype
-    ((1, 40, 32, 12, 64, 2, 1), ftx.FTX_ERR_UNSUPPORTED),     # decoder length not a multiple of 32
-    ((1, 32, 48, 12, 64, 2, 1), ftx.FTX_ERR_UNSUPPORTED),     # memory length not a multiple of 32
+    ((1, 0, 32, 12, 64, 2, 1), ftx.FTX_ERR_INVALID_ARG),      # decoder length 0
+    ((1, 32, 0, 12, 64, 2, 1), ftx.FTX_ERR_INVALID_ARG),      # memory length 0
+    ((1, 513, 32, 12, 64, 2, 1), ftx.FTX_ERR_UNSUPPORTED),    # decoder above 512
     ((1, 32, 544, 12, 64, 2, 1), ftx.FTX_ERR_UNSUPPORTED),    # memory above 512
     ((1, 32, 32, 12, 48, 2, 1), ftx.FTX_ERR_UNSUPPORTED),     # head size 48
 ])

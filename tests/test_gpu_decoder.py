@@ -136,6 +136,23 @@ def test_stack(case):
     check(got, ref, sh.dtype, STACK_TOL[sh.dtype], "stack")
 
 
+@pytest.mark.parametrize("Sd,Se,dtype,with_lens", [
+    (1, 1, "fp16", False), (17, 40, "fp16", True), (33, 100, "bf16", True),
+    (70, 33, "fp32", False), (5, 511, "fp16", True), (100, 7, "bf16", False)])
+def test_ragged_lengths(Sd, Se, dtype, with_lens):
+    """Lengths that are not multiples of 32: padded inside the handle, compared with the
+    oracle at the caller's lengths."""
+    sh = si.DecoderShape(2, Sd, Se, 4, 32, 2, dtype)
+    c = si.make_decoder_case(sh, 31 + Sd + Se, params="random_affine",
+                             mem_lens_range=(1, Se) if with_lens else None)
+    layers = list(c.layers())
+    dec = _decoder(sh, layers)
+    got = to_f64(dec.forward(to_dev(c.x, dtype), to_dev(c.mem, dtype), dev_lens(c.mem_lens)))
+    dec.close()
+    ref = oracle.decoder(c.x, c.mem, layers, c.mem_lens, sh.head_num)
+    check(got, ref, dtype, STACK_TOL[dtype], f"Sd={Sd} Se={Se}")
+
+
 def test_later_positions_do_not_reach_earlier_rows():
     """Causality on the GPU: rows i+1.. of the input perturbed, rows 0..i of the output
     unchanged bit for bit."""

@@ -34,7 +34,9 @@ struct DecLayerW {
 }  // namespace
 
 struct ftx_decoder {
-  int B, Sd, Se, nh, d, L, H, F, Td, Tm;  // Td = B Sd decoder rows, Tm = B Se memory rows
+  int B, Sd, Se, nh, d, L, H, F, Td, Tm;  // Sd, Se: internal lengths, multiples of 32;
+                                          // Td = B Sd decoder rows, Tm = B Se memory rows
+  int Sdv, Sev;                           // the caller's lengths (Sd, Se rounded up to 32)
   ftx_dtype dt;
   size_t es;
   int device;
@@ -50,6 +52,9 @@ struct ftx_decoder {
   float* y2f = nullptr;  // (bf16 only)
   float* splitk = nullptr;
   size_t splitk_elems = 0;
+  // when a caller length is not a multiple of 32: [B][Sd][H] input copy and layer state,
+  // [B][Se][H] memory copy, their padding rows zero
+  void *xpad = nullptr, *spad = nullptr, *mpad = nullptr;
   int timing = 0;
   struct Mark {
     hipEvent_t start, stop;
@@ -99,9 +104,26 @@ ftx_status enqueue_decoder(ftx_decoder* e, const void* input, const void* memory
   float* ws = e->splitk;
   const size_t wn = e->splitk_elems;
   ftx_status st;
+  // Caller lengths below the internal ones: rows 0..Sdv-1 (0..Sev-1) of each sequence go to
+  // the padded copies, the layers run at Sd and Se, and rows 0..Sdv-1 come back at the end.
+  // Padded decoder rows follow the valid ones, so the causal mask keeps them out of every
+  // valid row; padded memory rows are beyond the key range the cross-attention is limited to.
+  const size_t row = (size_t)H * e->es;
+  void* state = output;
+  if (e->xpad) {
+    FTX_HIP(hipMemcpy2DAsync(e->xpad, Sd * row, input, e->Sdv * row, e->Sdv * row, B,
+                             hipMemcpyDeviceToDevice, s));
+    input = e->xpad;
+    state = e->spad;
+  }
+  if (e->mpad) {
+    FTX_HIP(hipMemcpy2DAsync(e->mpad, Se * row, memory, e->Sev * row, e->Sev * row, B,
+                             hipMemcpyDeviceToDevice, s));
+    memory = e->mpad;
+  }
   for (int l = 0; l < e->L; ++l) {
     const DecLayerW& w = e->layers[l];
-    const void* x = l == 0 ? input : output;
+    const void* x = l == 0 ? input : state;
     // causal self-attention, add & LayerNorm 1
     if ((st = step(e, FTX_DEC_STEP_SELF_QKV_GEMM, s, [&] {
            return launch_qkv_projection(dt, B, Sd, nh, d, x, w.w_qkv_t, w.b_qkv, e->q, e->k, e->vt,
@@ -132,7 +154,7 @@ ftx_status enqueue_decoder(ftx_decoder* e, const void* input, const void* memory
          })) != FTX_OK) return st;
     if ((st = step(e, FTX_DEC_STEP_CROSS_ATTENTION, s, [&] {
            return launch_attention(dt, B, Sd, Se, nh, d, e->q2, e->k2, e->vt2, mem_lens, e->ctx, s,
-                                   Se, false);
+                                   e->Sev, false);
          })) != FTX_OK) return st;
     if ((st = step(e, FTX_DEC_STEP_CROSS_OUT_GEMM, s, [&] {
            return launch_linear(dt, Td, H, H, e->ctx, w.w_o2_t, nullptr, false, e->abuf, s, f32res,
@@ -154,11 +176,14 @@ ftx_status enqueue_decoder(ftx_decoder* e, const void* input, const void* memory
          })) != FTX_OK) return st;
     if ((st = step(e, FTX_DEC_STEP_LN3, s, [&] {
            return f32res ? launch_bias_residual_layernorm_f32res(dt, Td, H, e->y2f, true, (const float*)e->abuf,
-                                                                 w.b2, w.ln3_g, w.ln3_b, output, nullptr, s)
+                                                                 w.b2, w.ln3_g, w.ln3_b, state, nullptr, s)
                          : launch_bias_residual_layernorm(dt, Td, H, e->y2, e->abuf, w.b2, w.ln3_g,
-                                                          w.ln3_b, output, s);
+                                                          w.ln3_b, state, s);
          })) != FTX_OK) return st;
   }
+  if (e->xpad)
+    FTX_HIP(hipMemcpy2DAsync(output, e->Sdv * row, state, Sd * row, e->Sdv * row, B,
+                             hipMemcpyDeviceToDevice, s));
   return FTX_OK;
 }
 
@@ -174,8 +199,8 @@ ftx_status ftx_decoder_create(int batch_size, int tgt_len, int mem_len, int head
   *out = nullptr;
   if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
   if (num_layers < 1) return fail(FTX_ERR_INVALID_ARG, "num_layers must be >= 1");
-  ftx_status st = check_shape(batch_size, tgt_len, head_num, size_per_head);
-  if (st == FTX_OK) st = check_shape(batch_size, mem_len, head_num, size_per_head);
+  ftx_status st = check_shape(batch_size, tgt_len, head_num, size_per_head, true);
+  if (st == FTX_OK) st = check_shape(batch_size, mem_len, head_num, size_per_head, true);
   if (st != FTX_OK) return st;
 
   int dev = 0;
@@ -188,15 +213,17 @@ ftx_status ftx_decoder_create(int batch_size, int tgt_len, int mem_len, int head
   ftx_decoder* e = new (std::nothrow) ftx_decoder();
   if (!e) return fail(FTX_ERR_OUT_OF_MEMORY, "host allocation");
   e->B = batch_size;
-  e->Sd = tgt_len;
-  e->Se = mem_len;
+  e->Sdv = tgt_len;
+  e->Sev = mem_len;
+  e->Sd = (tgt_len + 31) / 32 * 32;
+  e->Se = (mem_len + 31) / 32 * 32;
   e->nh = head_num;
   e->d = size_per_head;
   e->L = num_layers;
   e->H = head_num * size_per_head;
   e->F = 4 * e->H;
-  e->Td = batch_size * tgt_len;
-  e->Tm = batch_size * mem_len;
+  e->Td = batch_size * e->Sd;
+  e->Tm = batch_size * e->Se;
   e->dt = dtype;
   e->es = dtype_size(dtype);
   e->device = dev;
@@ -215,9 +242,11 @@ ftx_status ftx_decoder_create(int batch_size, int tgt_len, int mem_len, int head
   }
   const bool f32res = dtype == FTX_BF16;
   const size_t TdH = pad(Td * H * es), TmH = pad(Tm * H * es), F32 = pad(Td * H * 4);
+  const bool xpadded = e->Sdv != e->Sd, mpadded = e->Sev != e->Se;
   const size_t ws_bytes = 4 * TdH /*q,k,vt,q2*/ + 2 * TmH /*k2,vt2*/ + TdH /*ctx*/ +
                           (f32res ? F32 : TdH) /*abuf*/ + 2 * TdH /*y1,y2*/ +
-                          pad(Td * F * es) /*u*/ + (f32res ? 2 * F32 : 0) /*y1f,y2f*/;
+                          pad(Td * F * es) /*u*/ + (f32res ? 2 * F32 : 0) /*y1f,y2f*/ +
+                          (xpadded ? 2 * TdH : 0) /*xpad,spad*/ + (mpadded ? TmH : 0) /*mpad*/;
   err = hipMalloc(&e->ws, ws_bytes);
   if (err != hipSuccess) {
     hipFree(e->weights);
@@ -266,6 +295,27 @@ ftx_status ftx_decoder_create(int batch_size, int tgt_len, int mem_len, int head
   if (f32res) {
     e->y1f = (float*)p; p += F32;
     e->y2f = (float*)p; p += F32;
+  }
+  if (xpadded) {
+    e->xpad = p; p += TdH;
+    e->spad = p; p += TdH;
+  }
+  if (mpadded) {
+    e->mpad = p; p += TmH;
+  }
+  if (xpadded || mpadded) {
+    // padding rows of the copies stay zero (only rows below the caller's lengths are ever
+    // written); the state's padding rows are computed and never reach a valid row
+    hipError_t zerr = hipSuccess;
+    if (xpadded) zerr = hipMemset(e->xpad, 0, 2 * TdH);
+    if (zerr == hipSuccess && mpadded) zerr = hipMemset(e->mpad, 0, TmH);
+    if (zerr == hipSuccess) zerr = hipDeviceSynchronize();
+    if (zerr != hipSuccess) {
+      hipFree(e->ws);
+      hipFree(e->weights);
+      delete e;
+      return hip_fail(zerr, "hipMemset(padding)");
+    }
   }
   // split-K workspace: the largest any of the six projections plans for
   const int Tdi = e->Td, Tmi = e->Tm, Hi = e->H, Fi = e->F;
@@ -354,7 +404,7 @@ ftx_status ftx_decoder_forward(ftx_decoder* e, const void* input, const void* me
   if (!input || !memory || !output) return fail(FTX_ERR_INVALID_ARG, "input, memory or output is NULL");
   if (!aligned16(input) || !aligned16(memory) || !aligned16(output))
     return fail(FTX_ERR_INVALID_ARG, "input, memory and output must be 16-byte aligned");
-  const size_t xb = (size_t)e->Td * e->H * e->es, mb = (size_t)e->Tm * e->H * e->es;
+  const size_t xb = (size_t)e->B * e->Sdv * e->H * e->es, mb = (size_t)e->B * e->Sev * e->H * e->es;
   if (overlap(input, xb, output, xb) || overlap(memory, mb, output, xb))
     return fail(FTX_ERR_INVALID_ARG, "output overlaps input or memory");
   for (int l = 0; l < e->L; ++l)
