@@ -126,6 +126,19 @@ def classify_dispatches(names):
     return steps
 
 
+def profile_commands(wl, calib_mb, name):
+    """The three rocprofv3 runs a traffic summary is made from, and the summarizing call."""
+    w = "" if wl == WORKLOAD_DEFAULT else f" --workload {wl}"
+    run = f"python3 bench.py{w} --no-cpu-baseline --copy-calib-mb {calib_mb}"
+    return [
+        f"rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o trace -- {run} --steps 5 --warmup 2",
+        f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_fetch -o fetch -- {run} --steps 2 --warmup 1 --no-kernel-times",
+        f"rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_write -o write -- {run} --steps 2 --warmup 1 --no-kernel-times",
+        f"python3 bench.py{w} --copy-calib-mb {calib_mb} --summarize-rocprof gpurun_out/prof_trace "
+        f"gpurun_out/prof_fetch gpurun_out/prof_write --summary-name {name}",
+    ]
+
+
 def summarize_rocprof(args):
     """Summarise a rocprofv3 kernel trace plus FETCH_SIZE / WRITE_SIZE counter runs of this
     benchmark (made with --copy-calib-mb) into profiles/<name>.md and profiles/<name>_traffic.json."""
@@ -168,9 +181,10 @@ def summarize_rocprof(args):
     shape = w.shape(args.batch or max(w.batches))
     out = {"workload": wl, "batch": shape.batch, "kernel_source_hash": kernel_source_hash(),
            "scale": scale, "steps": {}}
+    commands = args.summary_commands or profile_commands(wl, args.copy_calib_mb, args.summary_name)
     lines = [f"# Kernel time and HBM traffic per step -- {wl}, batch {shape.batch}", "",
-             "Commands (from the repository root, on one MI355X):", "", "```",
-             *args.summary_commands, "```", "",
+             "Commands (from the repository root, on one MI355X, with TMPDIR=/tmp):", "", "```",
+             *commands, "```", "",
              f"FETCH_SIZE and WRITE_SIZE are scaled by what they read for a plain copy kernel "
              f"(torch.neg over {args.copy_calib_mb} MiB of fp16): true bytes per counted byte "
              f"{scale['FETCH_SIZE']:.3f} (fetch) and {scale['WRITE_SIZE']:.3f} (write).", "",
