@@ -38,6 +38,9 @@ def parse():
     p.add_argument("--batch", type=int, default=None)
     p.add_argument("--unfused", action="store_true", help="standalone bias+split and bias+GELU kernels")
     p.add_argument("--graph", action="store_true", help="replay the forward as one HIP graph")
+    p.add_argument("--fused-attention", type=int, default=1, choices=(0, 1, 2),
+                   help="projection + attention in one kernel: 0 never, 1 when the grid fills "
+                        "the chip (default), 2 whenever the shape fits")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-kernel-times", action="store_true")
@@ -67,6 +70,8 @@ def step_work(shape, step: str):
         return 2.0 * T * H * F, (T * F + H * F + T * H) * e
     if step == "attention":
         return 4.0 * B * S * S * H, 4 * T * H * e
+    if step == "qkv_attention":  # Q, K and V stay on chip
+        return 2.0 * T * 3 * H * H + 4.0 * B * S * S * H, (T * H + 3 * H * H + T * H) * e
     if step in ("ln1", "ln2"):
         return 0.0, 3 * T * H * e
     if step == "bias_gelu":
@@ -101,7 +106,9 @@ def classify_dispatches(names):
     steps, prev = [], None
     for n in names:
         st = None
-        if "gemm_kernel" in n and "EpiQKV" in n:
+        if "gemm_kernel" in n and "EpiQKVAttn" in n:
+            st = "qkv_attention"
+        elif "gemm_kernel" in n and "EpiQKV" in n:
             st = "qkv_gemm"
         elif "attention" in n and "ftx" in n:
             st = "attention"
@@ -112,7 +119,7 @@ def classify_dispatches(names):
             gelu = m is not None and m.group(1) == "1"
             if gelu or prev == "ln1":
                 st = "ffn1_gemm"
-            elif prev == "attention":
+            elif prev in ("attention", "qkv_attention"):
                 st = "attn_out_gemm"
             else:
                 st = "ffn2_gemm"
@@ -190,7 +197,7 @@ def summarize_rocprof(args):
              f"{scale['FETCH_SIZE']:.3f} (fetch) and {scale['WRITE_SIZE']:.3f} (write).", "",
              "| step | launches | avg us | algorithmic MB | fetched MB | written MB | "
              "algorithmic TFLOP/s | algorithmic GB/s |", "|---|---|---|---|---|---|---|---|"]
-    for st in ("qkv_gemm", "bias_qkv_split", "attention", "attn_out_gemm", "ln1", "ffn1_gemm",
+    for st in ("qkv_attention", "qkv_gemm", "bias_qkv_split", "attention", "attn_out_gemm", "ln1", "ffn1_gemm",
                "bias_gelu", "ffn2_gemm", "ln2"):
         if st not in dur:
             continue
@@ -443,6 +450,7 @@ def main():
         enc.set_weights(l, {k: up(w[k]) for k in si.WEIGHT_NAMES})
     if args.unfused:
         enc.set_option(ftx.FTX_OPT_FUSED_EPILOGUES, 0)
+    enc.set_option(ftx.FTX_OPT_FUSED_ATTENTION, args.fused_attention)
     if args.graph:
         enc.set_option(ftx.FTX_OPT_GRAPH, 1)
     x = up(case.x)
@@ -462,6 +470,12 @@ def main():
 
     for _ in range(args.warmup):
         enc.forward(x, lens, out)
+    torch.cuda.synchronize()
+    # which attention path the handle takes (one forward with launch counts, untimed)
+    enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)
+    enc.forward(x, lens, out)
+    attn_fused = enc.kernel_times()["qkv_attention"][1] > 0
+    enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 0)
     torch.cuda.synchronize()
 
     # timed region: K forwards between a synchronize on each side
@@ -489,6 +503,7 @@ def main():
                    "heads": shape.head_num, "size_per_head": shape.size_per_head,
                    "parallelism": "none (1 GPU)",
                    "epilogues": "standalone" if args.unfused else "fused",
+                   "attention": "in the Q/K/V projection's epilogue" if attn_fused else "own kernel",
                    "launch": "hip graph" if args.graph else "stream"},
         "tflops": tflops, "frac_mfma_peak": tflops / PEAK_MFMA_TFLOPS[dt],
         "gpu_event_ms_per_step": gpu_ms / args.steps,

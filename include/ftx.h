@@ -137,8 +137,20 @@ const char *ftx_last_error(void);
  *     pointers stay the same; other pointers cause a new capture.  Weights may change
  *     between forwards (they live in handle memory the graph reads).  Ignored while
  *     FTX_OPT_KERNEL_TIMING is on.
+ *   FTX_OPT_FUSED_ATTENTION (default 1): for seq_len <= 32 (padded to 32), size_per_head 64
+ *     and a 16-bit dtype, the Q/K/V projection and the attention run as one kernel that
+ *     attends each 256 x 192 projection tile (eight sequences, one head) in its epilogue, so
+ *     Q, K and V never reach memory (ftx_step_qkv_attention).  0 = never; 1 = when its grid
+ *     (ceil(batch/8) x head_num tiles) covers the 256 CUs at least once, else the separate
+ *     kernels; 2 = whenever the shape fits.  Needs FTX_OPT_FUSED_EPILOGUES = 1.  Values
+ *     outside 0..2 -> FTX_ERR_INVALID_ARG.
  * Unknown option -> FTX_ERR_INVALID_ARG. */
-typedef enum { FTX_OPT_FUSED_EPILOGUES = 0, FTX_OPT_KERNEL_TIMING = 1, FTX_OPT_GRAPH = 2 } ftx_option;
+typedef enum {
+  FTX_OPT_FUSED_EPILOGUES = 0,
+  FTX_OPT_KERNEL_TIMING = 1,
+  FTX_OPT_GRAPH = 2,
+  FTX_OPT_FUSED_ATTENTION = 3
+} ftx_option;
 ftx_status ftx_set_option(ftx_encoder *enc, ftx_option option, int value);
 
 /* Step classes of the per-step timing. */
@@ -152,7 +164,8 @@ typedef enum {
   FTX_STEP_BIAS_GELU = 6,       /* bias + GELU as its own kernel */
   FTX_STEP_FFN2_GEMM = 7,       /* second FFN projection */
   FTX_STEP_LN2 = 8,             /* bias + residual + LayerNorm after the FFN */
-  FTX_NUM_STEPS = 9
+  FTX_STEP_QKV_ATTENTION = 9,   /* Q/K/V projection with the attention in its epilogue */
+  FTX_NUM_STEPS = 10
 } ftx_step;
 
 /* Synchronize the events recorded since the last call and return, per step class, the

@@ -1,0 +1,210 @@
+"""The Q/K/V projection with the attention in its epilogue (ftx_step_qkv_attention, and the
+encoder path FTX_OPT_FUSED_ATTENTION), against the fp64 oracle through the C ABI.
+
+Step parity: inputs built so that every projection value is exact in fp32 and in the
+16-bit storage formats (small integers times sparse +-1/2 weights, half-integer biases), so
+the kernel's Q, K and V equal the oracle's bit for bit and the bar is that of the attention
+step: |gpu - oracle| <= 2u max|v| + 2u |oracle| (u = unit roundoff of the format): the
+probabilities are rounded to the storage format before the P V product, the output once.
+Encoder parity: the stack bars of tests/test_gpu_encoder.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+from gpu_util import DEV, TORCH, UNIT, announce, assert_within, dev_layer, dev_lens, need_gpu, to_dev, to_f64
+from transformer_encoder_bert_amd import ftx
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu(request):
+    need_gpu()
+    announce(request.node.nodeid)
+    yield
+    torch.cuda.synchronize()
+
+
+def exact_case(B, n, seed):
+    """x in {-2..2}, each weight column with 8 nonzeros of +-1/2, biases in {-1, -1/2, 0, 1/2,
+    1}: |q|, |k|, |v| <= 9, half-integers, exact in fp16 and bf16 and summed exactly in fp32."""
+    H = 64 * n
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-2, 3, size=(B, 32, H)).astype(np.float64)
+    ws = []
+    for _ in range(3):
+        w = np.zeros((H, H))
+        for c in range(H):
+            rows = rng.choice(H, size=8, replace=False)
+            w[rows, c] = rng.choice([-0.5, 0.5], size=8)
+        ws.append(w)
+    bs = [rng.integers(-2, 3, size=H) * 0.5 for _ in range(3)]
+    return x, ws, bs
+
+
+def per_head_rows(mats, n):
+    """[Q|K|V] blocks of H rows -> rows ordered per head: Q_h, K_h, V_h (64 rows each)."""
+    return np.concatenate([m[h * 64:(h + 1) * 64] for h in range(n) for m in mats], axis=0)
+
+
+def reference(x, ws, bs, n, lens):
+    q, k, v = (oracle.split_heads(oracle.linear(x, w, b), n) for w, b in zip(ws, bs))
+    p = oracle.masked_softmax(oracle.scaled_scores(q, k), lens)
+    return oracle.merge_heads(oracle.context(p, v)), np.abs(v).max()
+
+
+CASES = [
+    # B, n, lens
+    (1, 1, None),
+    (8, 2, "random"),       # one full tile row of eight sequences
+    (9, 2, "random"),       # a second tile row with one sequence
+    (20, 3, [1] * 10 + [32] * 10),
+    (40, 12, "random"),     # BERT-base heads
+]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("B,n,lens", CASES)
+def test_step_matches_oracle(dtype, B, n, lens):
+    x, ws, bs = exact_case(B, n, 1000 + 31 * B + n)
+    if lens == "random":
+        lens = np.random.default_rng(B + n).integers(1, 33, size=B)
+    lens_np = None if lens is None else np.asarray(lens, dtype=np.int32)
+    ref, vmax = reference(x, ws, bs, n, lens_np)
+    w_t = per_head_rows([w.T for w in ws], n)
+    b = per_head_rows([bb[:, None] for bb in bs], n)[:, 0]
+    ctx = torch.empty((B, 32, 64 * n), dtype=TORCH[dtype], device=DEV)
+    ftx.ftx_step_qkv_attention(B, 32, n, 64, to_dev(x, dtype), to_dev(w_t, dtype), to_dev(b, dtype),
+                               dev_lens(lens_np), ctx)
+    u = UNIT[dtype]
+    assert_within(to_f64(ctx), ref, 2 * u * vmax + 1e-6, 2 * u, "qkv attention")
+
+
+def test_step_equals_separate_steps_at_full_size():
+    """BERT-base heads at 512 sequences (the benchmark's grid), random weights: the fused
+    kernel against the projection + attention steps run separately on the same inputs.
+    Q, K and V go through the same K loop in the same order, so they agree up to the
+    split-free projections' identical rounding; the bar is the attention step's."""
+    B, n, H = 512, 12, 768
+    rng = np.random.default_rng(77)
+    x = si.round_to(rng.normal(size=(B, 32, H)), "fp16")
+    ws = [si.round_to(rng.normal(size=(H, H)) * 0.04, "fp16") for _ in range(3)]
+    bs = [si.round_to(rng.normal(size=H) * 0.1, "fp16") for _ in range(3)]
+    lens = rng.integers(1, 33, size=B).astype(np.int32)
+    xd, ld = to_dev(x, "fp16"), dev_lens(lens)
+    ctx = torch.empty((B, 32, H), dtype=torch.float16, device=DEV)
+    ftx.ftx_step_qkv_attention(B, 32, n, 64, xd, to_dev(per_head_rows([w.T for w in ws], n), "fp16"),
+                               to_dev(per_head_rows([b[:, None] for b in bs], n)[:, 0], "fp16"), ld, ctx)
+    q = torch.empty((B, n, 32, 64), dtype=torch.float16, device=DEV)
+    k = torch.empty_like(q)
+    vt = torch.empty((B, n, 64, 32), dtype=torch.float16, device=DEV)
+    ftx.ftx_step_qkv_projection(B, 32, n, 64, xd, to_dev(np.concatenate([w.T for w in ws]), "fp16"),
+                                to_dev(np.concatenate(bs), "fp16"), q, k, vt)
+    ctx2 = torch.empty_like(ctx)
+    ftx.ftx_step_attention(B, 32, n, 64, q, k, vt, ld, ctx2)
+    v = to_f64(vt)
+    u = UNIT["fp16"]
+    assert_within(to_f64(ctx), to_f64(ctx2), 2 * u * np.abs(v).max() + 1e-6, 2 * u, "fused vs separate")
+
+
+def test_step_rejects_other_shapes():
+    x = torch.zeros((2, 32, 128), dtype=torch.float16, device=DEV)
+    w = torch.zeros((384, 128), dtype=torch.float16, device=DEV)
+    b = torch.zeros(384, dtype=torch.float16, device=DEV)
+    ctx = torch.empty_like(x)
+    with pytest.raises(ftx.FtxError) as e:
+        ftx.ftx_step_qkv_attention(2, 32, 4, 32, x, w, b, None, ctx)   # d = 32
+    assert e.value.status == ftx.FTX_ERR_UNSUPPORTED
+    xf, wf, bf, cf = (t.float() for t in (x, w, b, ctx))
+    with pytest.raises(ftx.FtxError) as e:
+        ftx.ftx_step_qkv_attention(2, 32, 2, 64, xf, wf, bf, None, cf)  # fp32
+    assert e.value.status == ftx.FTX_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------------ the encoder path
+
+def _encoder(shape, layers, mode):
+    enc = ftx.Encoder(shape.batch, shape.seq_len, shape.head_num, shape.size_per_head,
+                      len(layers), shape.dtype)
+    enc.set_option(ftx.FTX_OPT_FUSED_ATTENTION, mode)
+    for l, w in enumerate(layers):
+        enc.set_weights(l, dev_layer(w, shape.dtype))
+    torch.cuda.synchronize()
+    return enc
+
+
+STACK = [
+    # B, S, n, dtype, lens range
+    (9, 32, 4, "fp16", (1, 32)),
+    (3, 17, 2, "fp16", None),         # S padded to 32 inside the handle
+    (10, 32, 12, "bf16", (5, 32)),
+    (2, 32, 2, "fp16", None),
+]
+
+
+@pytest.mark.parametrize("B,S,n,dtype,lens", STACK)
+def test_encoder_forced_fused_matches_oracle(B, S, n, dtype, lens):
+    sh = si.Shape(B, S, n, 64, 2, dtype)
+    c = si.custom_case(sh, 500 + B + S + n, params="random_affine", lens_range=lens)
+    layers = list(c.layers())
+    enc = _encoder(sh, layers, 2)
+    enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)
+    got = to_f64(enc.forward(to_dev(c.x, dtype), dev_lens(c.lens)))
+    t = enc.kernel_times()
+    enc.close()
+    assert t["qkv_attention"][1] == 2 and t["attention"][1] == 0 and t["qkv_gemm"][1] == 0
+    ref = oracle.encoder(c.x, layers, c.lens, n)
+    tol = {"fp16": (5e-2, 0.0), "bf16": (5e-2, 2.0 ** -8)}[dtype]
+    assert_within(got, ref, tol[0], tol[1], f"fused encoder B={B} S={S} n={n}")
+
+
+def test_encoder_fused_and_separate_agree():
+    c = si.make_case("bert_base_fp16_s32", 24, params="bert", num_layers=2)
+    layers = list(c.layers())
+    x, lens = to_dev(c.x, "fp16"), dev_lens(c.lens)
+    outs = []
+    for mode in (2, 0):
+        enc = _encoder(c.shape, layers, mode)
+        outs.append(to_f64(enc.forward(x, lens)))
+        enc.close()
+    assert_within(outs[0], outs[1], 2e-2, 0.0, "fused vs separate attention")
+
+
+def test_encoder_auto_mode_follows_the_grid():
+    """Default mode: fused once ceil(B/8) x heads covers 256 CUs, separate below."""
+    for B, fused in ((168, False), (176, True)):
+        c = si.make_case("bert_base_fp16_s32", B, params="bert", num_layers=1)
+        enc = _encoder(c.shape, list(c.layers()), 1)
+        enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)
+        enc.forward(to_dev(c.x, "fp16"))
+        t = enc.kernel_times()
+        enc.close()
+        assert (t["qkv_attention"][1] == 1) == fused and (t["attention"][1] == 1) == (not fused)
+
+
+def test_option_values():
+    c = si.make_case("bert_base_fp16_s32", 1, params="bert", num_layers=1)
+    enc = _encoder(c.shape, list(c.layers()), 0)
+    with pytest.raises(ftx.FtxError) as e:
+        enc.set_option(ftx.FTX_OPT_FUSED_ATTENTION, 3)
+    assert e.value.status == ftx.FTX_ERR_INVALID_ARG
+    enc.close()
+
+
+def test_graph_replays_of_the_fused_path():
+    c = si.make_case("bert_base_fp16_s32", 16, params="bert", num_layers=2)
+    layers = list(c.layers())
+    enc = _encoder(c.shape, layers, 2)
+    x, lens = to_dev(c.x, "fp16"), dev_lens(c.lens)
+    out = torch.empty_like(x)
+    eager = enc.forward(x, lens, out).clone()
+    enc.set_option(ftx.FTX_OPT_GRAPH, 1)
+    for _ in range(3):
+        out.zero_()
+        enc.forward(x, lens, out)
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+    enc.close()

@@ -50,6 +50,8 @@ namespace {
 struct LayerW {
   void* w_qkv_t;  // [3H][H]
   void* b_qkv;    // [3H]
+  void* w_qkvh_t; // [3H][H] rows ordered per head (Q_h, K_h, V_h), or null (fused attention)
+  void* b_qkvh;   // [3H] in the same order
   void* w_o_t;    // [H][H]
   void* b_o;
   void* ln1_g;
@@ -81,6 +83,8 @@ struct ftx_encoder {
   size_t splitk_elems = 0;
   float* y1f = nullptr;  // fp32 copy of Y1, the residual of the second LayerNorm (bf16 only)
   int fused = 1;
+  int fused_attention = 1;  // 0 off, 1 when the grid fills the chip, 2 whenever the shape fits
+  bool attn_fits = false;   // the per-head weight copy exists (16-bit, S = 32, d = 64)
   int timing = 0;
   int graph_mode = 0;
   // graph of one whole forward, captured for the (input, seq_lens, output) it was made with
@@ -142,6 +146,15 @@ void drop_graph(ftx_encoder* e) {
   e->g_lens = nullptr;
 }
 
+// The projection with the attention in its epilogue replaces the projection + attention
+// pair when the shape fits and, in the default mode, when its grid of 256 x 192 tiles (eight
+// sequences by one head each) covers the 256 CUs at least once: on a smaller grid the
+// separate kernels spread the same work over more CUs.
+bool use_fused_attention(const ftx_encoder* e) {
+  if (!e->fused || !e->attn_fits || e->fused_attention == 0) return false;
+  return e->fused_attention == 2 || (long)((e->B + 7) / 8) * e->nh >= 256;
+}
+
 // Enqueue the L-layer forward on `s` (arguments already validated).
 ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq_lens,
                            void* output, hipStream_t s) {
@@ -163,7 +176,12 @@ ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq
     const LayerW& w = e->layers[l];
     const void* x = (l == 0) ? x0 : state;
     ftx_status st;
-    if (e->fused) {
+    if (use_fused_attention(e)) {
+      st = run_step(e, FTX_STEP_QKV_ATTENTION, s, [&] {
+        return launch_qkv_attention(dt, B, S, nh, d, x, w.w_qkvh_t, w.b_qkvh, seq_lens, e->Sv,
+                                    e->ctx, s);
+      });
+    } else if (e->fused) {
       st = run_step(e, FTX_STEP_QKV_GEMM, s, [&] {
         return launch_qkv_projection(dt, B, S, nh, d, x, w.w_qkv_t, w.b_qkv, e->q, e->k, e->vt, s,
                                      e->splitk, e->splitk_elems);
@@ -179,10 +197,12 @@ ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq
       });
     }
     if (st != FTX_OK) return st;
-    st = run_step(e, FTX_STEP_ATTENTION, s, [&] {
-      return launch_attention(dt, B, S, S, nh, d, e->q, e->k, e->vt, seq_lens, e->ctx, s, e->Sv);
-    });
-    if (st != FTX_OK) return st;
+    if (!use_fused_attention(e)) {
+      st = run_step(e, FTX_STEP_ATTENTION, s, [&] {
+        return launch_attention(dt, B, S, S, nh, d, e->q, e->k, e->vt, seq_lens, e->ctx, s, e->Sv);
+      });
+      if (st != FTX_OK) return st;
+    }
     st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
       return launch_linear(dt, T, H, H, e->ctx, w.w_o_t, nullptr, false, e->abuf, s, e->y1f != nullptr,
                            e->splitk, e->splitk_elems);
@@ -282,12 +302,16 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
   e->es = dtype_size(dtype);
   e->device = dev;
 
+  e->attn_fits = qkv_attention_fits(dtype, e->S, size_per_head);
+
   const size_t H = e->H, F = e->F, T = e->T, es = e->es;
-  // weights: per layer 3H*H + 3H + H*H + H + 2H + F*H + F + H*F + H + 2H elements, each
-  // tensor padded to 256 bytes
+  // weights: per layer 3H*H + 3H + H*H + H + 2H + F*H + F + H*F + H + 2H elements (plus a
+  // second 3H*H + 3H in per-head order for the fused attention), each tensor padded to 256
+  // bytes
   auto pad = [](size_t bytes) { return (bytes + 255) / 256 * 256; };
   const size_t per_layer = pad(3 * H * H * es) + pad(3 * H * es) + pad(H * H * es) + 5 * pad(H * es) +
-                           pad(F * H * es) + pad(F * es) + pad(H * F * es) + pad(H * es);
+                           pad(F * H * es) + pad(F * es) + pad(H * F * es) + pad(H * es) +
+                           (e->attn_fits ? pad(3 * H * H * es) + pad(3 * H * es) : 0);
   hipError_t err = hipMalloc(&e->weights, per_layer * e->L);
   if (err != hipSuccess) {
     delete e;
@@ -326,6 +350,8 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
     lw.b2 = take(H * es);
     lw.ln2_g = take(H * es);
     lw.ln2_b = take(H * es);
+    lw.w_qkvh_t = e->attn_fits ? take(3 * H * H * es) : nullptr;
+    lw.b_qkvh = e->attn_fits ? take(3 * H * es) : nullptr;
   }
   e->ready.assign(e->L, 0);
   char* p = (char*)e->ws;
@@ -410,6 +436,17 @@ ftx_status ftx_set_weights(ftx_encoder* e, int layer, const ftx_layer_weights* w
   FTX_HIP(hipMemcpyAsync(lw.b2, w->b_ffn2, H * es, hipMemcpyDeviceToDevice, s));
   FTX_HIP(hipMemcpyAsync(lw.ln2_g, w->ln2_gamma, H * es, hipMemcpyDeviceToDevice, s));
   FTX_HIP(hipMemcpyAsync(lw.ln2_b, w->ln2_beta, H * es, hipMemcpyDeviceToDevice, s));
+  if (lw.w_qkvh_t) {
+    // rows of head h of Q (K, V) go to rows 192 h .. (+64, +128): d = 64 here
+    const size_t d = e->d;
+    for (int part = 0; part < 3; ++part) {
+      FTX_HIP(hipMemcpy2DAsync((char*)lw.w_qkvh_t + part * d * H * es, 3 * d * H * es,
+                               qkv + part * H * H * es, d * H * es, d * H * es, e->nh,
+                               hipMemcpyDeviceToDevice, s));
+      FTX_HIP(hipMemcpy2DAsync((char*)lw.b_qkvh + part * d * es, 3 * d * es, bqkv + part * H * es,
+                               d * es, d * es, e->nh, hipMemcpyDeviceToDevice, s));
+    }
+  }
   FTX_HIP(hipStreamSynchronize(s));
   e->ready[layer] = 1;
   return FTX_OK;
@@ -489,6 +526,11 @@ ftx_status ftx_set_option(ftx_encoder* e, ftx_option option, int value) {
       e->fused = value ? 1 : 0;
       return FTX_OK;
     case FTX_OPT_KERNEL_TIMING: e->timing = value ? 1 : 0; return FTX_OK;
+    case FTX_OPT_FUSED_ATTENTION:
+      if (value < 0 || value > 2) return fail(FTX_ERR_INVALID_ARG, "fused attention mode is 0, 1 or 2");
+      if (e->fused_attention != value) drop_graph(e);
+      e->fused_attention = value;
+      return FTX_OK;
     case FTX_OPT_GRAPH:
       e->graph_mode = value ? 1 : 0;
       if (!e->graph_mode) drop_graph(e);
@@ -582,6 +624,25 @@ ftx_status ftx_step_attention(ftx_dtype dtype, int B, int S, int n, int d, const
   if (!all_device({q, k, v_t, seq_lens, ctx})) return fail(FTX_ERR_INVALID_ARG, "pointers must be device memory");
   hipError_t err = launch_attention(dtype, B, S, S, n, d, q, k, v_t, seq_lens, ctx, (hipStream_t)stream);
   return err == hipSuccess ? FTX_OK : hip_fail(err, "attention launch");
+}
+
+ftx_status ftx_step_qkv_attention(ftx_dtype dtype, int B, int S, int n, int d, const void* x,
+                                  const void* w_qkv_t, const void* b_qkv, const int32_t* seq_lens,
+                                  void* ctx, void* stream) {
+  last_error_slot().clear();
+  if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
+  ftx_status st = check_shape(B, S, n, d);
+  if (st != FTX_OK) return st;
+  if (!qkv_attention_fits(dtype, S, d))
+    return fail(FTX_ERR_UNSUPPORTED, "fused projection + attention needs fp16/bf16, S = 32, d = 64");
+  if (!x || !w_qkv_t || !b_qkv || !ctx) return fail(FTX_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(x) || !aligned16(w_qkv_t) || !aligned16(b_qkv) || !aligned16(ctx))
+    return fail(FTX_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (!all_device({x, w_qkv_t, b_qkv, seq_lens, ctx}))
+    return fail(FTX_ERR_INVALID_ARG, "pointers must be device memory");
+  hipError_t err = launch_qkv_attention(dtype, B, S, n, d, x, w_qkv_t, b_qkv, seq_lens, S, ctx,
+                                        (hipStream_t)stream);
+  return err == hipSuccess ? FTX_OK : hip_fail(err, "qkv attention launch");
 }
 
 ftx_status ftx_step_masked_attention(ftx_dtype dtype, int B, int Sq, int Sk, int n, int d,

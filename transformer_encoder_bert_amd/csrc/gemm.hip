@@ -25,6 +25,8 @@
 // so the four consecutive accumulator rows a lane holds are four consecutive columns n of
 // one output row m; the epilogue regroups them through LDS into 16-byte row vectors.
 
+#include <math.h>
+
 #include <algorithm>
 
 #include "device_common.h"
@@ -84,6 +86,7 @@ template <typename TO> struct TileDst {
 };
 
 template <typename T, bool GELU, typename TO = T> struct EpiLinear {
+  static constexpr bool kBlock = false;  // per-32x32-tile epilogue
   typedef TO out_t;
   typedef typename Vec16<TO>::type vec;
   typedef typename VecT<T, 4>::type b4;
@@ -119,6 +122,7 @@ template <typename T, bool GELU, typename TO = T> struct EpiLinear {
 // first = 0 and three blocks; a cross-attention's query projection first = 0 and one, its
 // key/value projection over the memory first = 1 and two.
 template <typename T> struct EpiQKV {
+  static constexpr bool kBlock = false;
   typedef T out_t;
   typedef typename Vec16<T>::type vec;
   typedef typename VecT<T, 4>::type b4;
@@ -169,6 +173,7 @@ template <typename T> struct EpiQKV {
 // to P[blockIdx.y][M][N]; splitk_reduce_kernel then sums the ranges in order and applies
 // the real epilogue.
 struct EpiPartial {
+  static constexpr bool kBlock = false;
   typedef float out_t;
   typedef f32x4 vec;
   typedef f32x4 b4;
@@ -274,6 +279,160 @@ __device__ __forceinline__ void workgroup_barrier() {
 // of bank conflicts whether the LDS serves 8 or 16 lanes per pass.  swz depends on R mod 32
 // only, so the 32-row tiles of a wave differ by a constant offset.
 __device__ __forceinline__ int swz(int R) { return (R & 7) ^ ((R >> 3) & 3); }
+
+// Q/K/V projection of 32-token sequences with head size 64, and the attention of each
+// (sequence, head) in the epilogue (the layer's first two steps, section "Faster Transformer
+// 优化原理" of the Faster Transformer article; S = 32 is its headline length).  The weight
+// rows (output columns) are ordered per head, [Q_h | K_h | V_h] for h = 0 .. nh-1, so the
+// 192 columns of tile column h are exactly Q, K and V of head h, and the 256 rows of a tile
+// are eight whole sequences.  After the K loop the tile is biased, rounded to the storage
+// type (as Q, K and V are when they go through memory) and split in LDS into Q and K (rows
+// of 64 d) and V^T (rows of 256 tokens); then wave w takes sequence w of the tile and runs
+// the chain of the attention kernel: S^T = K Q^T (four MFMAs), the key mask at the
+// sequence's valid length and the exp2 softmax on the fp32 scores, C^T = V^T P^T with the
+// probabilities rounded to the storage type, and the division by the row sum.  The context
+// is staged in the wave's own Q rows and stored as 128-byte rows of ctx[b*32 + i][h*64 + e].
+// Q, K and V never reach global memory.
+template <typename T> struct EpiQKVAttn {
+  static constexpr bool kBlock = true;
+  typedef T out_t;
+  typedef typename VecT<T, 4>::type b4;
+  typedef typename Vec16<T>::type vec;
+  T* ctx;               // [M][N / 3]
+  const T* bias;        // [N], ordered like the weight rows
+  const int32_t* lens;  // [M / 32] valid lengths, or null
+  int M, N;             // M = 32 * sequences, N = 3 * 64 * heads
+  int s_valid;          // keys at or past it are masked in every sequence
+  float scale_log2e;    // log2(e) / sqrt(64)
+  // LDS: Q and K rows padded to 72 elements, V^T rows (one per d) to 260 tokens, so the
+  // fragment reads of 32 consecutive rows fall in distinct banks
+  static constexpr int QLD = 72, VLD = 260;
+  static constexpr int KOFF = 256 * QLD, VOFF = 2 * 256 * QLD;
+  static constexpr size_t kLdsBytes = (size_t)(VOFF + 64 * VLD) * sizeof(T);
+  __device__ __forceinline__ b4 bias4(int n) const {
+    b4 v = {};
+    if (n < N) v = *(const b4*)(bias + n);
+    return v;
+  }
+  template <int TM, int TN, int WN>
+  __device__ __forceinline__ void block(char* smem, int m0, int n0, int wave, int lane,
+                                        const f32x16 (&acc)[TN][TM],
+                                        const b4 (&bq)[TN][4]) const {
+    static_assert(TM == 2 && TN == 3 && WN == 2, "256 x 192 tile of 4 x 2 waves");
+    typedef typename Mfma<T>::frag frag;
+    T* lds = (T*)smem;
+    const int wm = wave / WN, wn = wave % WN, lr = lane % 32, g = lane / 32;
+    // 1. register r of accumulator (j, i): tile column c0 + 8 (r / 4) + 4 g + r % 4 of row
+    //    (wm TM + i) 32 + lr; a 32-column tile lies inside one of Q, K, V
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int c0 = (wn * TN + j) * 32;
+      const int part = c0 / 64, dd0 = c0 % 64;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = (wm * TM + i) * 32 + lr;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int dd = dd0 + 8 * q + 4 * g;
+          b4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(acc[j][i][4 * q + e] + to_f32(bq[j][q][e]));
+          if (part < 2) {
+            *(b4*)(lds + part * KOFF + row * QLD + dd) = o;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) lds[VOFF + (dd + e) * VLD + row] = o[e];
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+    workgroup_barrier();
+
+    // 2. wave w: sequence m0 / 32 + w (rows r0 .. r0 + 31 of the tile); no barrier follows
+    const int r0 = wave * 32;
+    if (m0 + r0 >= M) return;
+    const int b = (m0 + r0) / 32;
+    int len = lens ? lens[b] : s_valid;
+    len = min(max(len, 1), s_valid);
+    // query lr of Q, key lr of K: d = 16 f + 8 g .. + 7 of fragment f
+    frag qf[4], kf[4];
+    const T* qrow = lds + (r0 + lr) * QLD + 8 * g;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      qf[f] = *(const frag*)(qrow + 16 * f);
+      kf[f] = *(const frag*)(qrow + KOFF + 16 * f);
+    }
+    // V^T rows d = 32 dt + lr, keys 16 u + 4 g + {0..3} and {8..11}
+    frag vf[2][2];
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const T* vp = lds + VOFF + (32 * dt + lr) * VLD + r0 + 16 * u + 4 * g;
+        const b4 lo = *(const b4*)vp, hi = *(const b4*)(vp + 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vf[dt][u][e] = lo[e];
+          vf[dt][u][e + 4] = hi[e];
+        }
+      }
+    // S^T = K Q^T: register r holds key 8 (r / 4) + 4 g + r % 4 of query lr
+    f32x16 sc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) Mfma<T>::mma(kf[f], qf[f], sc);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (8 * (r / 4) + 4 * g + (r % 4) >= len) sc[r] = -INFINITY;
+      mx = fmaxf(mx, sc[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));  // finite: key 0 is always valid
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sc[r] = exp2f((sc[r] - mx) * scale_log2e);
+      sum += sc[r];
+    }
+    sum += __shfl_xor(sum, 32);
+    // C^T = V^T P^T; MFMA u takes P registers 8u .. 8u+7 = keys 16u + {0..3, 8..11} + 4g
+    f32x16 o[2];
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      frag pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = from_f32<T>(sc[8 * u + e]);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) Mfma<T>::mma(vf[dt][u], pf, o[dt]);
+    }
+    // register r of o[dt]: d = 32 dt + 8 (r / 4) + 4 g + r % 4 of query lr; staged in this
+    // wave's own Q rows (no other wave reads them; a wave's LDS accesses complete in order)
+    const float inv = 1.0f / sum;
+    T* st = lds + r0 * QLD;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        b4 vv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vv[e] = from_f32<T>(o[dt][4 * s4 + e] * inv);
+        *(b4*)(st + lr * QLD + 32 * dt + 8 * s4 + 4 * g) = vv;
+      }
+    const int H = N / 3;
+    T* out = ctx + (size_t)(m0 + r0) * H + (n0 / 192) * 64;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int row = 8 * p + lane / 8, c = (lane % 8) * 8;
+      *(vec*)(out + (size_t)row * H + c) = *(const vec*)(st + row * QLD + c);
+    }
+  }
+};
 
 template <typename T, int BM, int BN, int WM, int WN> struct GemmCfg {
   typedef Mfma<T> MF;
@@ -441,16 +600,21 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
   // every wave is done with both buffers before the LDS is reused as epilogue scratch
   __builtin_amdgcn_s_waitcnt(0xC07F);
   workgroup_barrier();
-  typedef typename Epi::out_t TO;
-  constexpr int SCRATCH = 32 * (32 + 16 / sizeof(TO));  // elements of TO per wave
-  static_assert(SCRATCH * sizeof(TO) * C::NW <= sizeof(smem), "epilogue scratch");
-  TO* ws = (TO*)smem + wave * SCRATCH;
+  if constexpr (Epi::kBlock) {
+    static_assert(Epi::kLdsBytes <= sizeof(smem), "block epilogue LDS");
+    epi.template block<TM, TN, WN>(smem, m0, n0, wave, lane, acc, bq);
+  } else {
+    typedef typename Epi::out_t TO;
+    constexpr int SCRATCH = 32 * (32 + 16 / sizeof(TO));  // elements of TO per wave
+    static_assert(SCRATCH * sizeof(TO) * C::NW <= sizeof(smem), "epilogue scratch");
+    TO* ws = (TO*)smem + wave * SCRATCH;
 #pragma unroll
-  for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-      epilogue_tile(epi, ws, m0 + (wm * TM + i) * 32, n0 + (wn * TN + j) * 32, lane, acc[j][i],
-                    bq[j]);
+      for (int i = 0; i < TM; ++i)
+        epilogue_tile(epi, ws, m0 + (wm * TM + i) * 32, n0 + (wn * TN + j) * 32, lane, acc[j][i],
+                      bq[j]);
+  }
 }
 
 // --------------------------------------------------------------------------- tile choice
@@ -618,6 +782,32 @@ hipError_t launch_head_projection(ftx_dtype dt, int B, int S, int nh, int d, con
     case FTX_BF16: return heads_t<bf16>(B, S, nh, d, x, w_t, bias, first, count, q, k, vt, s, ws, ws_elems);
   }
   return hipErrorInvalidValue;
+}
+
+bool qkv_attention_fits(ftx_dtype dt, int S, int d) {
+  return dt != FTX_FP32 && S == 32 && d == 64;
+}
+
+template <typename T>
+static hipError_t qkv_attention_t(int B, int nh, const void* x, const void* w_t, const void* bias,
+                                  const int32_t* lens, int s_valid, void* ctx, hipStream_t s) {
+  const int M = 32 * B, N = 3 * 64 * nh, K = 64 * nh;
+  // log2(e) / sqrt(d), rounded once from double as the attention kernel does
+  const float scale_log2e = (float)(1.4426950408889634 / 8.0);
+  EpiQKVAttn<T> epi{(T*)ctx, (const T*)bias, lens, M, N, s_valid, scale_log2e};
+  const int tiles = ((M + 255) / 256) * (N / 192);
+  gemm_kernel<T, 256, 192, 4, 2, EpiQKVAttn<T>><<<tiles, 8 * kWave, 0, s>>>(
+      (const T*)x, (const T*)w_t, M, N, K, K, epi);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_attention(ftx_dtype dt, int B, int S, int nh, int d, const void* x,
+                                const void* w_qkv_t, const void* b_qkv, const int32_t* lens,
+                                int s_valid, void* ctx, hipStream_t s) {
+  if (!qkv_attention_fits(dt, S, d) || B < 1 || nh < 1) return hipErrorInvalidValue;
+  if (s_valid <= 0 || s_valid > S) s_valid = S;
+  if (dt == FTX_FP16) return qkv_attention_t<f16>(B, nh, x, w_qkv_t, b_qkv, lens, s_valid, ctx, s);
+  return qkv_attention_t<bf16>(B, nh, x, w_qkv_t, b_qkv, lens, s_valid, ctx, s);
 }
 
 hipError_t launch_qkv_projection(ftx_dtype dt, int B, int S, int nh, int d, const void* x,

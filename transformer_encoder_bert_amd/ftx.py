@@ -21,9 +21,9 @@ LIB_PATH = os.path.join(PKG, "libftx.so")
 FTX_FP32, FTX_FP16, FTX_BF16 = 0, 1, 2
 FTX_OK, FTX_ERR_INVALID_ARG, FTX_ERR_UNSUPPORTED, FTX_ERR_OUT_OF_MEMORY, FTX_ERR_DEVICE, \
     FTX_ERR_NOT_READY = range(6)
-FTX_OPT_FUSED_EPILOGUES, FTX_OPT_KERNEL_TIMING, FTX_OPT_GRAPH = 0, 1, 2
+FTX_OPT_FUSED_EPILOGUES, FTX_OPT_KERNEL_TIMING, FTX_OPT_GRAPH, FTX_OPT_FUSED_ATTENTION = 0, 1, 2, 3
 STEP_NAMES = ("qkv_gemm", "bias_qkv_split", "attention", "attn_out_gemm", "ln1", "ffn1_gemm",
-              "bias_gelu", "ffn2_gemm", "ln2")
+              "bias_gelu", "ffn2_gemm", "ln2", "qkv_attention")
 FTX_NUM_STEPS = len(STEP_NAMES)
 
 WEIGHT_FIELDS = ("w_q", "b_q", "w_k", "b_k", "w_v", "b_v", "w_o", "b_o", "ln1_gamma", "ln1_beta",
@@ -37,7 +37,8 @@ DECODER_WEIGHT_FIELDS = ("w_q", "b_q", "w_k", "b_k", "w_v", "b_v", "w_o", "b_o",
 
 EXPORTED = ("ftx_encoder_create", "ftx_set_weights", "ftx_forward", "ftx_destroy",
             "ftx_status_string", "ftx_last_error", "ftx_set_option", "ftx_kernel_times",
-            "ftx_step_linear", "ftx_step_qkv_projection", "ftx_step_bias_qkv_split",
+            "ftx_step_linear", "ftx_step_qkv_projection", "ftx_step_qkv_attention",
+            "ftx_step_bias_qkv_split",
             "ftx_step_attention", "ftx_step_masked_attention", "ftx_step_bias_residual_layernorm",
             "ftx_step_bias_gelu", "ftx_step_transpose",
             "ftx_decoder_create", "ftx_decoder_set_weights", "ftx_decoder_forward",
@@ -88,6 +89,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ftx_kernel_times": (i, [p, p, p]),
         "ftx_step_linear": (i, [i, i, i, i, p, p, p, i, p, v]),
         "ftx_step_qkv_projection": (i, [i, i, i, i, i, p, p, p, p, p, p, v]),
+        "ftx_step_qkv_attention": (i, [i, i, i, i, i, p, p, p, p, p, v]),
         "ftx_step_bias_qkv_split": (i, [i, i, i, i, i, p, p, p, p, p, v]),
         "ftx_step_attention": (i, [i, i, i, i, i, p, p, p, p, p, v]),
         "ftx_step_masked_attention": (i, [i, i, i, i, i, i, p, p, p, p, i, p, v]),
@@ -363,6 +365,20 @@ def ftx_step_qkv_projection(B, S, n, d, x, w_qkv_t, b_qkv, q, k, v_t, stream=Non
     _check(load_library().ftx_step_qkv_projection(_dt(x.dtype), B, S, n, d, _ptr(x), _ptr(w_qkv_t),
                                                   _ptr(b_qkv), _ptr(q), _ptr(k), _ptr(v_t),
                                                   _stream(stream)), "ftx_step_qkv_projection")
+
+
+def ftx_step_qkv_attention(B, S, n, d, x, w_qkv_t, b_qkv, seq_lens, ctx, stream=None) -> None:
+    """w_qkv_t / b_qkv rows ordered per head: [Q_h | K_h | V_h] for h = 0 .. n-1."""
+    H = n * d
+    _need(x, "x", x.dtype, B * S * H)
+    _need(w_qkv_t, "w_qkv_t", x.dtype, 3 * H * H)
+    _need(b_qkv, "b_qkv", x.dtype, 3 * H)
+    _need(ctx, "ctx", x.dtype, B * S * H)
+    if seq_lens is not None:
+        _need(seq_lens, "seq_lens", torch.int32, B)
+    _check(load_library().ftx_step_qkv_attention(_dt(x.dtype), B, S, n, d, _ptr(x), _ptr(w_qkv_t),
+                                                 _ptr(b_qkv), _ptr(seq_lens), _ptr(ctx),
+                                                 _stream(stream)), "ftx_step_qkv_attention")
 
 
 def ftx_step_bias_qkv_split(B, S, n, d, qkv, b_qkv, q, k, v_t, stream=None) -> None:
