@@ -105,11 +105,12 @@ def test_step_argument_checks(lib):
     assert lib.ftx_step_attention(1, 1, 32, 2, 64, None, 512, 768, None, 1024, None) == E
     assert lib.ftx_step_bias_qkv_split(1, 0, 32, 2, 64, 256, 512, 768, 1024, 2048, None) == E
     assert lib.ftx_step_qkv_projection(1, 1, 32, 2, 40, 256, 512, 768, 1024, 2048, 4096, None) == ftx.FTX_ERR_UNSUPPORTED
-    # projection + attention: fp16/bf16, S = 32 and d = 64 only (refused before any pointer is
-    # looked at), then the pointer checks
+    # projection + attention: fp16/bf16, S in {32, 64, 128, 256} and d = 64 only (refused
+    # before any pointer is looked at), then the pointer checks
     U = ftx.FTX_ERR_UNSUPPORTED
     assert lib.ftx_step_qkv_attention(0, 1, 32, 2, 64, 256, 512, 768, None, 1024, None) == U
-    assert lib.ftx_step_qkv_attention(1, 1, 64, 2, 64, 256, 512, 768, None, 1024, None) == U
+    assert lib.ftx_step_qkv_attention(1, 1, 96, 2, 64, 256, 512, 768, None, 1024, None) == U
+    assert lib.ftx_step_qkv_attention(1, 1, 512, 2, 64, 256, 512, 768, None, 1024, None) == U
     assert lib.ftx_step_qkv_attention(2, 1, 32, 2, 32, 256, 512, 768, None, 1024, None) == U
     assert lib.ftx_step_qkv_attention(1, 1, 32, 2, 64, None, 512, 768, None, 1024, None) == E
     assert lib.ftx_step_qkv_attention(1, 1, 32, 2, 64, 256, 512, 776, None, 1024, None) == E

@@ -28,12 +28,12 @@ def _gpu(request):
     torch.cuda.synchronize()
 
 
-def exact_case(B, n, seed):
+def exact_case(B, S, n, seed):
     """x in {-2..2}, each weight column with 8 nonzeros of +-1/2, biases in {-1, -1/2, 0, 1/2,
     1}: |q|, |k|, |v| <= 9, half-integers, exact in fp16 and bf16 and summed exactly in fp32."""
     H = 64 * n
     rng = np.random.default_rng(seed)
-    x = rng.integers(-2, 3, size=(B, 32, H)).astype(np.float64)
+    x = rng.integers(-2, 3, size=(B, S, H)).astype(np.float64)
     ws = []
     for _ in range(3):
         w = np.zeros((H, H))
@@ -57,27 +57,31 @@ def reference(x, ws, bs, n, lens):
 
 
 CASES = [
-    # B, n, lens
-    (1, 1, None),
-    (8, 2, "random"),       # one full tile row of eight sequences
-    (9, 2, "random"),       # a second tile row with one sequence
-    (20, 3, [1] * 10 + [32] * 10),
-    (40, 12, "random"),     # BERT-base heads
+    # B, S, n, lens
+    (1, 32, 1, None),
+    (8, 32, 2, "random"),       # one full tile row of eight sequences
+    (9, 32, 2, "random"),       # a second tile row with one sequence
+    (20, 32, 3, [1] * 10 + [32] * 10),
+    (40, 32, 12, "random"),     # BERT-base heads
+    (5, 64, 2, "random"),       # four sequences per tile, two waves each; a partial tile row
+    (3, 128, 2, [128, 97, 1]),  # two sequences per tile, key tiles skipped past the length
+    (2, 256, 2, [256, 37]),     # one sequence per tile, eight query blocks
+    (1, 256, 1, None),
 ]
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
-@pytest.mark.parametrize("B,n,lens", CASES)
-def test_step_matches_oracle(dtype, B, n, lens):
-    x, ws, bs = exact_case(B, n, 1000 + 31 * B + n)
+@pytest.mark.parametrize("B,S,n,lens", CASES)
+def test_step_matches_oracle(dtype, B, S, n, lens):
+    x, ws, bs = exact_case(B, S, n, 1000 + 31 * B + S + n)
     if lens == "random":
-        lens = np.random.default_rng(B + n).integers(1, 33, size=B)
+        lens = np.random.default_rng(B + n).integers(1, S + 1, size=B)
     lens_np = None if lens is None else np.asarray(lens, dtype=np.int32)
     ref, vmax = reference(x, ws, bs, n, lens_np)
     w_t = per_head_rows([w.T for w in ws], n)
     b = per_head_rows([bb[:, None] for bb in bs], n)[:, 0]
-    ctx = torch.empty((B, 32, 64 * n), dtype=TORCH[dtype], device=DEV)
-    ftx.ftx_step_qkv_attention(B, 32, n, 64, to_dev(x, dtype), to_dev(w_t, dtype), to_dev(b, dtype),
+    ctx = torch.empty((B, S, 64 * n), dtype=TORCH[dtype], device=DEV)
+    ftx.ftx_step_qkv_attention(B, S, n, 64, to_dev(x, dtype), to_dev(w_t, dtype), to_dev(b, dtype),
                                dev_lens(lens_np), ctx)
     u = UNIT[dtype]
     assert_within(to_f64(ctx), ref, 2 * u * vmax + 1e-6, 2 * u, "qkv attention")
@@ -111,6 +115,7 @@ def test_step_equals_separate_steps_at_full_size():
 
 
 def test_step_rejects_other_shapes():
+    """d = 32 and fp32 are refused (S outside {32, 64, 128, 256}: tests/test_abi.py)."""
     x = torch.zeros((2, 32, 128), dtype=torch.float16, device=DEV)
     w = torch.zeros((384, 128), dtype=torch.float16, device=DEV)
     b = torch.zeros(384, dtype=torch.float16, device=DEV)
@@ -142,6 +147,9 @@ STACK = [
     (3, 17, 2, "fp16", None),         # S padded to 32 inside the handle
     (10, 32, 12, "bf16", (5, 32)),
     (2, 32, 2, "fp16", None),
+    (3, 50, 2, "fp16", (1, 50)),      # padded to 64
+    (3, 100, 2, "bf16", (1, 100)),    # padded to 128
+    (2, 230, 2, "fp16", None),        # padded to 256
 ]
 
 

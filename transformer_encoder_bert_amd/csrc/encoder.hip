@@ -147,12 +147,12 @@ void drop_graph(ftx_encoder* e) {
 }
 
 // The projection with the attention in its epilogue replaces the projection + attention
-// pair when the shape fits and, in the default mode, when its grid of 256 x 192 tiles (eight
-// sequences by one head each) covers the 256 CUs at least once: on a smaller grid the
-// separate kernels spread the same work over more CUs.
+// pair when the shape fits and, in the default mode, when its grid of 256 x 192 tiles (256
+// tokens of whole sequences by one head each) covers the 256 CUs at least once: on a smaller
+// grid the separate kernels spread the same work over more CUs.
 bool use_fused_attention(const ftx_encoder* e) {
   if (!e->fused || !e->attn_fits || e->fused_attention == 0) return false;
-  return e->fused_attention == 2 || (long)((e->B + 7) / 8) * e->nh >= 256;
+  return e->fused_attention == 2 || ((long)e->T + 255) / 256 * e->nh >= 256;
 }
 
 // Enqueue the L-layer forward on `s` (arguments already validated).
@@ -634,7 +634,7 @@ ftx_status ftx_step_qkv_attention(ftx_dtype dtype, int B, int S, int n, int d, c
   ftx_status st = check_shape(B, S, n, d);
   if (st != FTX_OK) return st;
   if (!qkv_attention_fits(dtype, S, d))
-    return fail(FTX_ERR_UNSUPPORTED, "fused projection + attention needs fp16/bf16, S = 32, d = 64");
+    return fail(FTX_ERR_UNSUPPORTED, "fused projection + attention needs fp16/bf16, S in {32, 64, 128, 256}, d = 64");
   if (!x || !w_qkv_t || !b_qkv || !ctx) return fail(FTX_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned16(x) || !aligned16(w_qkv_t) || !aligned16(b_qkv) || !aligned16(ctx))
     return fail(FTX_ERR_INVALID_ARG, "pointers must be 16-byte aligned");

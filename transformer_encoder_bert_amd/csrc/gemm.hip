@@ -280,28 +280,32 @@ __device__ __forceinline__ void workgroup_barrier() {
 // only, so the 32-row tiles of a wave differ by a constant offset.
 __device__ __forceinline__ int swz(int R) { return (R & 7) ^ ((R >> 3) & 3); }
 
-// Q/K/V projection of 32-token sequences with head size 64, and the attention of each
-// (sequence, head) in the epilogue (the layer's first two steps, section "Faster Transformer
-// 优化原理" of the Faster Transformer article; S = 32 is its headline length).  The weight
-// rows (output columns) are ordered per head, [Q_h | K_h | V_h] for h = 0 .. nh-1, so the
-// 192 columns of tile column h are exactly Q, K and V of head h, and the 256 rows of a tile
-// are eight whole sequences.  After the K loop the tile is biased, rounded to the storage
-// type (as Q, K and V are when they go through memory) and split in LDS into Q and K (rows
-// of 64 d) and V^T (rows of 256 tokens); then wave w takes sequence w of the tile and runs
-// the chain of the attention kernel: S^T = K Q^T (four MFMAs), the key mask at the
-// sequence's valid length and the exp2 softmax on the fp32 scores, C^T = V^T P^T with the
-// probabilities rounded to the storage type, and the division by the row sum.  The context
-// is staged in the wave's own Q rows and stored as 128-byte rows of ctx[b*32 + i][h*64 + e].
-// Q, K and V never reach global memory.
-template <typename T> struct EpiQKVAttn {
+// Q/K/V projection of SEQ-token sequences (SEQ = 32, 64, 128 or 256) with head size 64, and
+// the attention of each (sequence, head) in the epilogue (the layer's first steps, section
+// "Faster Transformer 优化原理" of the Faster Transformer article).  The weight rows (output
+// columns) are ordered per head, [Q_h | K_h | V_h] for h = 0 .. nh-1, so the 192 columns of
+// tile column h are exactly Q, K and V of head h, and the 256 rows of a tile are 256 / SEQ
+// whole sequences.  After the K loop the tile is biased, rounded to the storage type (as Q,
+// K and V are when they go through memory) and split in LDS into Q and K (rows of 64 d) and
+// V^T (rows of 256 tokens); then each wave takes one block of 32 queries (wave w: sequence
+// w / (SEQ/32), query block w % (SEQ/32)) and runs the chain of the attention kernel over
+// all keys of its sequence: S^T = K Q^T per 32-key tile (four MFMAs), the key mask at the
+// sequence's valid length and the exp2 softmax on the fp32 scores (key tiles wholly past it
+// are skipped: their probabilities are 0), C^T = V^T P^T with the probabilities rounded to
+// the storage type, and the division by the row sum.  The context is staged in the wave's
+// own Q rows and stored as 128-byte rows of ctx[b*SEQ + i][h*64 + e].  Q, K and V never
+// reach global memory.
+template <typename T, int SEQ> struct EpiQKVAttn {
+  static_assert(SEQ == 32 || SEQ == 64 || SEQ == 128 || SEQ == 256, "whole sequences per tile");
   static constexpr bool kBlock = true;
+  static constexpr int NKT = SEQ / 32;  // key tiles (and query blocks) per sequence
   typedef T out_t;
   typedef typename VecT<T, 4>::type b4;
   typedef typename Vec16<T>::type vec;
   T* ctx;               // [M][N / 3]
   const T* bias;        // [N], ordered like the weight rows
-  const int32_t* lens;  // [M / 32] valid lengths, or null
-  int M, N;             // M = 32 * sequences, N = 3 * 64 * heads
+  const int32_t* lens;  // [M / SEQ] valid lengths, or null
+  int M, N;             // M = SEQ * sequences, N = 3 * 64 * heads
   int s_valid;          // keys at or past it are masked in every sequence
   float scale_log2e;    // log2(e) / sqrt(64)
   // LDS: Q and K rows padded to 72 elements, V^T rows (one per d) to 260 tokens, so the
@@ -349,68 +353,80 @@ template <typename T> struct EpiQKVAttn {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
     workgroup_barrier();
 
-    // 2. wave w: sequence m0 / 32 + w (rows r0 .. r0 + 31 of the tile); no barrier follows
-    const int r0 = wave * 32;
-    if (m0 + r0 >= M) return;
-    const int b = (m0 + r0) / 32;
+    // 2. this wave's queries: tile rows r0 .. r0 + 31 of the sequence at tile row k0; no
+    //    barrier follows
+    const int k0 = (wave / NKT) * SEQ, r0 = k0 + (wave % NKT) * 32;
+    if (m0 + k0 >= M) return;
+    const int b = (m0 + k0) / SEQ;
     int len = lens ? lens[b] : s_valid;
     len = min(max(len, 1), s_valid);
-    // query lr of Q, key lr of K: d = 16 f + 8 g .. + 7 of fragment f
-    frag qf[4], kf[4];
-    const T* qrow = lds + (r0 + lr) * QLD + 8 * g;
+    const int nkt = (len + 31) / 32;
+    // query lr of Q: d = 16 f + 8 g .. + 7 of fragment f
+    frag qf[4];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      qf[f] = *(const frag*)(qrow + 16 * f);
-      kf[f] = *(const frag*)(qrow + KOFF + 16 * f);
-    }
-    // V^T rows d = 32 dt + lr, keys 16 u + 4 g + {0..3} and {8..11}
-    frag vf[2][2];
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const T* vp = lds + VOFF + (32 * dt + lr) * VLD + r0 + 16 * u + 4 * g;
-        const b4 lo = *(const b4*)vp, hi = *(const b4*)(vp + 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vf[dt][u][e] = lo[e];
-          vf[dt][u][e + 4] = hi[e];
-        }
-      }
-    // S^T = K Q^T: register r holds key 8 (r / 4) + 4 g + r % 4 of query lr
-    f32x16 sc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
-#pragma unroll
-    for (int f = 0; f < 4; ++f) Mfma<T>::mma(kf[f], qf[f], sc);
+    for (int f = 0; f < 4; ++f) qf[f] = *(const frag*)(lds + (r0 + lr) * QLD + 8 * g + 16 * f);
+    // S^T = K Q^T per key tile: register r of sc[t] holds key 32 t + 8 (r / 4) + 4 g + r % 4
+    // of query lr
+    f32x16 sc[NKT];
     float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (8 * (r / 4) + 4 * g + (r % 4) >= len) sc[r] = -INFINITY;
-      mx = fmaxf(mx, sc[r]);
+    for (int t = 0; t < NKT; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[t][r] = -INFINITY;
+      if (t < nkt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
+        const T* krow = lds + KOFF + (k0 + 32 * t + lr) * QLD + 8 * g;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) Mfma<T>::mma(*(const frag*)(krow + 16 * f), qf[f], sc[t]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (32 * t + 8 * (r / 4) + 4 * g + (r % 4) >= len) sc[t][r] = -INFINITY;
+          mx = fmaxf(mx, sc[t][r]);
+        }
+      }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));  // finite: key 0 is always valid
     float sum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sc[r] = exp2f((sc[r] - mx) * scale_log2e);
-      sum += sc[r];
-    }
+    for (int t = 0; t < NKT; ++t)
+      if (t < nkt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sc[t][r] = exp2f((sc[t][r] - mx) * scale_log2e);
+          sum += sc[t][r];
+        }
+      }
     sum += __shfl_xor(sum, 32);
-    // C^T = V^T P^T; MFMA u takes P registers 8u .. 8u+7 = keys 16u + {0..3, 8..11} + 4g
+    // C^T = V^T P^T; MFMA (t, u) takes P registers 8u .. 8u+7 of key tile t = keys
+    // 32 t + 16 u + {0..3, 8..11} + 4 g, against V^T rows d = 32 dt + lr at those keys
     f32x16 o[2];
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      frag pf;
+    for (int t = 0; t < NKT; ++t)
+      if (t < nkt) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = from_f32<T>(sc[8 * u + e]);
+        for (int u = 0; u < 2; ++u) {
+          frag pf;
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) Mfma<T>::mma(vf[dt][u], pf, o[dt]);
-    }
+          for (int e = 0; e < 8; ++e) pf[e] = from_f32<T>(sc[t][8 * u + e]);
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) {
+            const T* vp = lds + VOFF + (32 * dt + lr) * VLD + k0 + 32 * t + 16 * u + 4 * g;
+            const b4 lo = *(const b4*)vp, hi = *(const b4*)(vp + 8);
+            frag vf;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              vf[e] = lo[e];
+              vf[e + 4] = hi[e];
+            }
+            Mfma<T>::mma(vf, pf, o[dt]);
+          }
+        }
+      }
     // register r of o[dt]: d = 32 dt + 8 (r / 4) + 4 g + r % 4 of query lr; staged in this
     // wave's own Q rows (no other wave reads them; a wave's LDS accesses complete in order)
     const float inv = 1.0f / sum;
@@ -785,20 +801,33 @@ hipError_t launch_head_projection(ftx_dtype dt, int B, int S, int nh, int d, con
 }
 
 bool qkv_attention_fits(ftx_dtype dt, int S, int d) {
-  return dt != FTX_FP32 && S == 32 && d == 64;
+  return dt != FTX_FP32 && (S == 32 || S == 64 || S == 128 || S == 256) && d == 64;
+}
+
+template <typename T, int SEQ>
+static hipError_t qkv_attention_t(int B, int nh, const void* x, const void* w_t, const void* bias,
+                                  const int32_t* lens, int s_valid, void* ctx, hipStream_t s) {
+  const int M = SEQ * B, N = 3 * 64 * nh, K = 64 * nh;
+  // log2(e) / sqrt(d), rounded once from double as the attention kernel does
+  const float scale_log2e = (float)(1.4426950408889634 / 8.0);
+  EpiQKVAttn<T, SEQ> epi{(T*)ctx, (const T*)bias, lens, M, N, s_valid, scale_log2e};
+  const int tiles = ((M + 255) / 256) * (N / 192);
+  gemm_kernel<T, 256, 192, 4, 2, EpiQKVAttn<T, SEQ>><<<tiles, 8 * kWave, 0, s>>>(
+      (const T*)x, (const T*)w_t, M, N, K, K, epi);
+  return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t qkv_attention_t(int B, int nh, const void* x, const void* w_t, const void* bias,
-                                  const int32_t* lens, int s_valid, void* ctx, hipStream_t s) {
-  const int M = 32 * B, N = 3 * 64 * nh, K = 64 * nh;
-  // log2(e) / sqrt(d), rounded once from double as the attention kernel does
-  const float scale_log2e = (float)(1.4426950408889634 / 8.0);
-  EpiQKVAttn<T> epi{(T*)ctx, (const T*)bias, lens, M, N, s_valid, scale_log2e};
-  const int tiles = ((M + 255) / 256) * (N / 192);
-  gemm_kernel<T, 256, 192, 4, 2, EpiQKVAttn<T>><<<tiles, 8 * kWave, 0, s>>>(
-      (const T*)x, (const T*)w_t, M, N, K, K, epi);
-  return hipGetLastError();
+static hipError_t qkv_attention_s(int B, int S, int nh, const void* x, const void* w_t,
+                                  const void* bias, const int32_t* lens, int s_valid, void* ctx,
+                                  hipStream_t s) {
+  switch (S) {
+    case 32: return qkv_attention_t<T, 32>(B, nh, x, w_t, bias, lens, s_valid, ctx, s);
+    case 64: return qkv_attention_t<T, 64>(B, nh, x, w_t, bias, lens, s_valid, ctx, s);
+    case 128: return qkv_attention_t<T, 128>(B, nh, x, w_t, bias, lens, s_valid, ctx, s);
+    case 256: return qkv_attention_t<T, 256>(B, nh, x, w_t, bias, lens, s_valid, ctx, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_qkv_attention(ftx_dtype dt, int B, int S, int nh, int d, const void* x,
@@ -806,8 +835,8 @@ hipError_t launch_qkv_attention(ftx_dtype dt, int B, int S, int nh, int d, const
                                 int s_valid, void* ctx, hipStream_t s) {
   if (!qkv_attention_fits(dt, S, d) || B < 1 || nh < 1) return hipErrorInvalidValue;
   if (s_valid <= 0 || s_valid > S) s_valid = S;
-  if (dt == FTX_FP16) return qkv_attention_t<f16>(B, nh, x, w_qkv_t, b_qkv, lens, s_valid, ctx, s);
-  return qkv_attention_t<bf16>(B, nh, x, w_qkv_t, b_qkv, lens, s_valid, ctx, s);
+  if (dt == FTX_FP16) return qkv_attention_s<f16>(B, S, nh, x, w_qkv_t, b_qkv, lens, s_valid, ctx, s);
+  return qkv_attention_s<bf16>(B, S, nh, x, w_qkv_t, b_qkv, lens, s_valid, ctx, s);
 }
 
 hipError_t launch_qkv_projection(ftx_dtype dt, int B, int S, int nh, int d, const void* x,

@@ -28,14 +28,14 @@ hipError_t launch_head_projection(ftx_dtype dt, int B, int S, int nh, int d, con
                                   void* q, void* k, void* vt, hipStream_t s,
                                   float* ws = nullptr, size_t ws_elems = 0);
 
-// Whether the fused projection + attention below takes this shape: a 16-bit dtype, S = 32
-// (the padded length), d = 64.
+// Whether the fused projection + attention below takes this shape: a 16-bit dtype, S (the
+// padded length) 32, 64, 128 or 256, d = 64.
 bool qkv_attention_fits(ftx_dtype dt, int S, int d);
 
-// Q/K/V projection of x [B*32][H] with the attention of every (sequence, head) in the same
+// Q/K/V projection of x [B*S][H] with the attention of every (sequence, head) in the same
 // kernel: w_qkv_t [3H][H] and b_qkv [3H] ordered per head ([Q_h | K_h | V_h], 192 rows each),
-// ctx [B*32][H] as launch_attention writes it.  Keys at or past min(lens[b], s_valid) are
-// masked (s_valid 1..32, default 32; lens NULL: s_valid).  hipErrorInvalidValue when the
+// ctx [B*S][H] as launch_attention writes it.  Keys at or past min(lens[b], s_valid) are
+// masked (s_valid 1..S, default S; lens NULL: s_valid).  hipErrorInvalidValue when the
 // shape does not fit.
 hipError_t launch_qkv_attention(ftx_dtype dt, int B, int S, int nh, int d, const void* x,
                                 const void* w_qkv_t, const void* b_qkv, const int32_t* lens,
