@@ -141,9 +141,9 @@ const char *ftx_last_error(void);
  *     up to 256, rounded up to a multiple of 32 that is one of those), size_per_head 64 and a
  *     16-bit dtype, the Q/K/V projection and the attention run as one kernel that attends
  *     each 256 x 192 projection tile (256/S whole sequences, one head) in its epilogue, so
- *     Q, K and V never reach memory (ftx_step_qkv_attention).  0 = never; 1 = when its grid
- *     (ceil(batch*S/256) x head_num tiles) covers the 256 CUs at least once, else the
- *     separate kernels; 2 = whenever the shape fits.  Needs FTX_OPT_FUSED_EPILOGUES = 1.
+ *     Q, K and V never reach memory (ftx_step_qkv_attention).  0 = never; 1 = when
+ *     batch*S >= 256 (at least one whole tile of rows), else the separate kernels; 2 =
+ *     whenever the shape fits.  Needs FTX_OPT_FUSED_EPILOGUES = 1.
  *     Values outside 0..2 -> FTX_ERR_INVALID_ARG.
  * Unknown option -> FTX_ERR_INVALID_ARG. */
 typedef enum {

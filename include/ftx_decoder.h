@@ -72,9 +72,15 @@ ftx_status ftx_decoder_set_weights(ftx_decoder *dec, int layer,
 ftx_status ftx_decoder_forward(ftx_decoder *dec, const void *input, const void *memory,
                                const int32_t *mem_lens, void *output, void *stream);
 
-/* Options: FTX_OPT_KERNEL_TIMING (value != 0: an event pair around every launch of the
- * following forwards, read back by ftx_decoder_kernel_times) is the only one a decoder
- * takes; others -> FTX_ERR_INVALID_ARG. */
+/* Options a decoder takes (others -> FTX_ERR_INVALID_ARG):
+ *   FTX_OPT_KERNEL_TIMING (value != 0: an event pair around every launch of the following
+ *     forwards, read back by ftx_decoder_kernel_times);
+ *   FTX_OPT_FUSED_ATTENTION (default 1): as for the encoder (ftx.h), for the causal
+ *     self-attention: with a 16-bit dtype, size_per_head 64 and an internal decoder length of
+ *     32, 64, 128 or 256, the self Q/K/V projection attends each of its 256 x 192 tiles in its
+ *     epilogue (step class FTX_DEC_STEP_SELF_QKV_ATTENTION); 0 never, 1 when batch*len >=
+ *     256 (len: the internal decoder length), 2 whenever the shape fits; other values ->
+ *     FTX_ERR_INVALID_ARG. */
 ftx_status ftx_decoder_set_option(ftx_decoder *dec, ftx_option option, int value);
 
 /* Step classes of the decoder's per-step timing. */
@@ -91,7 +97,8 @@ typedef enum {
   FTX_DEC_STEP_FFN1_GEMM = 9,      /* with bias + GELU */
   FTX_DEC_STEP_FFN2_GEMM = 10,
   FTX_DEC_STEP_LN3 = 11,
-  FTX_DEC_NUM_STEPS = 12
+  FTX_DEC_STEP_SELF_QKV_ATTENTION = 12, /* Q/K/V projection with the causal attention inside */
+  FTX_DEC_NUM_STEPS = 13
 } ftx_decoder_step;
 
 /* Synchronize the events recorded since the last call and return, per step class, the

@@ -62,12 +62,13 @@ ftx_status ftx_step_attention(ftx_dtype dtype, int B, int S, int n, int d, const
  * by ftx_step_attention, except that the weight rows are ordered per head:
  *   w_qkv_t [3H][H], rows 192h .. 192h+63 = rows h*64 .. h*64+63 of Wq^T, the next 64 of
  *   Wk^T, the next 64 of Wv^T (h = 0 .. n-1); b_qkv [3H] in the same order;
- *   seq_lens [B] int32 (clamped to [1, S]) or NULL.
+ *   seq_lens [B] int32 (clamped to [1, S]) or NULL; causal != 0: query i also ignores keys
+ *   j > i (a decoder's self-attention).
  * Q, K and V stay on chip: each 256 x 192 output tile (256/S whole sequences, one head) is
  * attended in the projection's epilogue. */
 ftx_status ftx_step_qkv_attention(ftx_dtype dtype, int B, int S, int n, int d, const void *x,
                                   const void *w_qkv_t, const void *b_qkv,
-                                  const int32_t *seq_lens, void *ctx, void *stream);
+                                  const int32_t *seq_lens, int causal, void *ctx, void *stream);
 
 /* The same attention with separate query and key lengths (cross-attention: queries of one
  * sequence over the keys of another) and an optional causal mask (a decoder's

@@ -108,12 +108,12 @@ def test_step_argument_checks(lib):
     # projection + attention: fp16/bf16, S in {32, 64, 128, 256} and d = 64 only (refused
     # before any pointer is looked at), then the pointer checks
     U = ftx.FTX_ERR_UNSUPPORTED
-    assert lib.ftx_step_qkv_attention(0, 1, 32, 2, 64, 256, 512, 768, None, 1024, None) == U
-    assert lib.ftx_step_qkv_attention(1, 1, 96, 2, 64, 256, 512, 768, None, 1024, None) == U
-    assert lib.ftx_step_qkv_attention(1, 1, 512, 2, 64, 256, 512, 768, None, 1024, None) == U
-    assert lib.ftx_step_qkv_attention(2, 1, 32, 2, 32, 256, 512, 768, None, 1024, None) == U
-    assert lib.ftx_step_qkv_attention(1, 1, 32, 2, 64, None, 512, 768, None, 1024, None) == E
-    assert lib.ftx_step_qkv_attention(1, 1, 32, 2, 64, 256, 512, 776, None, 1024, None) == E
+    assert lib.ftx_step_qkv_attention(0, 1, 32, 2, 64, 256, 512, 768, None, 0, 1024, None) == U
+    assert lib.ftx_step_qkv_attention(1, 1, 96, 2, 64, 256, 512, 768, None, 0, 1024, None) == U
+    assert lib.ftx_step_qkv_attention(1, 1, 512, 2, 64, 256, 512, 768, None, 0, 1024, None) == U
+    assert lib.ftx_step_qkv_attention(2, 1, 32, 2, 32, 256, 512, 768, None, 0, 1024, None) == U
+    assert lib.ftx_step_qkv_attention(1, 1, 32, 2, 64, None, 512, 768, None, 0, 1024, None) == E
+    assert lib.ftx_step_qkv_attention(1, 1, 32, 2, 64, 256, 512, 776, None, 1, 1024, None) == E
     # layernorm: cols not a multiple of 4, above the limit, misaligned
     assert lib.ftx_step_bias_residual_layernorm(1, 4, 6, 256, 512, 768, 1024, 2048, 4096, None) == E
     assert lib.ftx_step_bias_residual_layernorm(1, 4, 8192, 256, 512, 768, 1024, 2048, 4096, None) == ftx.FTX_ERR_UNSUPPORTED

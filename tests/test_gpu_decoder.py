@@ -198,6 +198,47 @@ def test_deterministic_and_inputs_untouched():
     assert torch.equal(a, b) and torch.equal(x, x0) and torch.equal(mem, m0)
 
 
+@pytest.mark.parametrize("Sd,Se,dtype", [(32, 64, "fp16"), (64, 32, "bf16"), (100, 40, "fp16")])
+def test_fused_self_attention_matches_oracle(Sd, Se, dtype):
+    """FTX_OPT_FUSED_ATTENTION = 2: the causal self-attention inside the self Q/K/V
+    projection (d = 64; Sd = 100 is padded to 128)."""
+    sh = si.DecoderShape(3, Sd, Se, 2, 64, 2, dtype)
+    c = si.make_decoder_case(sh, 41 + Sd + Se, params="random_affine", mem_lens_range=(1, Se))
+    layers = list(c.layers())
+    dec = ftx.Decoder(sh.batch, sh.tgt_len, sh.mem_len, sh.head_num, sh.size_per_head, 2, dtype)
+    dec.set_option(ftx.FTX_OPT_FUSED_ATTENTION, 2)
+    dec.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)
+    for l, w in enumerate(layers):
+        dec.set_weights(l, {k: to_dev(w[k], dtype) for k in si.DECODER_WEIGHT_NAMES})
+    got = to_f64(dec.forward(to_dev(c.x, dtype), to_dev(c.mem, dtype), dev_lens(c.mem_lens)))
+    t = dec.kernel_times()
+    dec.close()
+    assert t["self_qkv_attention"][1] == 2 and t["self_attention"][1] == 0
+    ref = oracle.decoder(c.x, c.mem, layers, c.mem_lens, sh.head_num)
+    check(got, ref, dtype, STACK_TOL[dtype], f"fused self-attention Sd={Sd}")
+
+
+def test_fused_self_attention_is_causal():
+    """Rows after i perturbed: rows 0..i of the output unchanged bit for bit, fused path."""
+    sh = si.DecoderShape(2, 64, 32, 2, 64, 2, "fp16")
+    c = si.make_decoder_case(sh, 5, params="random_affine", mem_lens_range=(5, 32))
+    layers = list(c.layers())
+    dec = ftx.Decoder(2, 64, 32, 2, 64, 2, "fp16")
+    dec.set_option(ftx.FTX_OPT_FUSED_ATTENTION, 2)
+    for l, w in enumerate(layers):
+        dec.set_weights(l, {k: to_dev(w[k], "fp16") for k in si.DECODER_WEIGHT_NAMES})
+    mem, lens = to_dev(c.mem, "fp16"), dev_lens(c.mem_lens)
+    base = to_f64(dec.forward(to_dev(c.x, "fp16"), mem, lens))
+    rng = np.random.default_rng(3)
+    for i in (0, 31, 40):
+        x1 = c.x.copy()
+        x1[:, i + 1:] = si.round_to(rng.normal(size=x1[:, i + 1:].shape) * 3, "fp16")
+        out = to_f64(dec.forward(to_dev(x1, "fp16"), mem, lens))
+        np.testing.assert_array_equal(out[:, : i + 1], base[:, : i + 1])
+        assert not np.array_equal(out[:, i + 1:], base[:, i + 1:])
+    dec.close()
+
+
 def test_decoder_errors_on_device():
     c, layers = _case(*CASES[1])
     sh = c.shape

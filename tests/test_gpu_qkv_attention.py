@@ -87,6 +87,21 @@ def test_step_matches_oracle(dtype, B, S, n, lens):
     assert_within(to_f64(ctx), ref, 2 * u * vmax + 1e-6, 2 * u, "qkv attention")
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("B,S,n", [(2, 32, 2), (3, 64, 2), (2, 128, 1), (1, 256, 2)])
+def test_step_causal_matches_oracle(dtype, B, S, n):
+    """The decoder's self-attention: query i sees keys j <= i (no length vector)."""
+    x, ws, bs = exact_case(B, S, n, 3000 + B + S + n)
+    q, k, v = (oracle.split_heads(oracle.linear(x, w, b), n) for w, b in zip(ws, bs))
+    ref = oracle.merge_heads(oracle.context(oracle.causal_softmax(oracle.scaled_scores(q, k)), v))
+    ctx = torch.empty((B, S, 64 * n), dtype=TORCH[dtype], device=DEV)
+    ftx.ftx_step_qkv_attention(B, S, n, 64, to_dev(x, dtype), to_dev(per_head_rows([w.T for w in ws], n), dtype),
+                               to_dev(per_head_rows([bb[:, None] for bb in bs], n)[:, 0], dtype), None, ctx,
+                               causal=True)
+    u = UNIT[dtype]
+    assert_within(to_f64(ctx), ref, 2 * u * np.abs(v).max() + 1e-6, 2 * u, "causal qkv attention")
+
+
 def test_step_equals_separate_steps_at_full_size():
     """BERT-base heads at 512 sequences (the benchmark's grid), random weights: the fused
     kernel against the projection + attention steps run separately on the same inputs.
@@ -181,9 +196,9 @@ def test_encoder_fused_and_separate_agree():
     assert_within(outs[0], outs[1], 2e-2, 0.0, "fused vs separate attention")
 
 
-def test_encoder_auto_mode_follows_the_grid():
-    """Default mode: fused once ceil(B/8) x heads covers 256 CUs, separate below."""
-    for B, fused in ((168, False), (176, True)):
+def test_encoder_auto_mode_needs_a_whole_tile():
+    """Default mode: fused from 256 tokens (B = 8 at S = 32), separate below."""
+    for B, fused in ((7, False), (8, True)):
         c = si.make_case("bert_base_fp16_s32", B, params="bert", num_layers=1)
         enc = _encoder(c.shape, list(c.layers()), 1)
         enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)

@@ -29,6 +29,8 @@ struct DecLayerW {
   void *w_kv2_t, *b_kv2;    // [2H][H], [2H]: cross-attention K | V over the memory
   void *w_o2_t, *b_o2, *ln2_g, *ln2_b;
   void *w1_t, *b1, *w2_t, *b2, *ln3_g, *ln3_b;
+  void *w_qkvh_t, *b_qkvh;  // the self-attention Q | K | V rows ordered per head (Q_h, K_h,
+                            // V_h), for the projection with the attention in its epilogue
 };
 
 }  // namespace
@@ -56,6 +58,8 @@ struct ftx_decoder {
   // [B][Se][H] memory copy, their padding rows zero
   void *xpad = nullptr, *spad = nullptr, *mpad = nullptr;
   int timing = 0;
+  int fused_attention = 1;  // 0 off, 1 from 256 rows (one whole tile), 2 whenever the shape fits
+  bool attn_fits = false;   // the per-head weight copy exists (16-bit, Sd in {32..256}, d = 64)
   struct Mark {
     hipEvent_t start, stop;
     int step;
@@ -95,6 +99,14 @@ ftx_status step(ftx_decoder* e, int cls, hipStream_t s, F&& launch) {
   return FTX_OK;
 }
 
+// The causal self-attention runs inside the self Q/K/V projection when the shape fits and,
+// in the default mode, when there are at least 256 decoder rows (one whole tile), as in the
+// encoder.
+bool use_fused_self_attention(const ftx_decoder* e) {
+  if (!e->attn_fits || e->fused_attention == 0) return false;
+  return e->fused_attention == 2 || e->Td >= 256;
+}
+
 ftx_status enqueue_decoder(ftx_decoder* e, const void* input, const void* memory,
                            const int32_t* mem_lens, void* output, hipStream_t s) {
   const ftx_dtype dt = e->dt;
@@ -125,14 +137,21 @@ ftx_status enqueue_decoder(ftx_decoder* e, const void* input, const void* memory
     const DecLayerW& w = e->layers[l];
     const void* x = l == 0 ? input : state;
     // causal self-attention, add & LayerNorm 1
-    if ((st = step(e, FTX_DEC_STEP_SELF_QKV_GEMM, s, [&] {
-           return launch_qkv_projection(dt, B, Sd, nh, d, x, w.w_qkv_t, w.b_qkv, e->q, e->k, e->vt,
-                                        s, ws, wn);
-         })) != FTX_OK) return st;
-    if ((st = step(e, FTX_DEC_STEP_SELF_ATTENTION, s, [&] {
-           return launch_attention(dt, B, Sd, Sd, nh, d, e->q, e->k, e->vt, nullptr, e->ctx, s, Sd,
-                                   true);
-         })) != FTX_OK) return st;
+    if (use_fused_self_attention(e)) {
+      if ((st = step(e, FTX_DEC_STEP_SELF_QKV_ATTENTION, s, [&] {
+             return launch_qkv_attention(dt, B, Sd, nh, d, x, w.w_qkvh_t, w.b_qkvh, nullptr, Sd,
+                                         e->ctx, s, true);
+           })) != FTX_OK) return st;
+    } else {
+      if ((st = step(e, FTX_DEC_STEP_SELF_QKV_GEMM, s, [&] {
+             return launch_qkv_projection(dt, B, Sd, nh, d, x, w.w_qkv_t, w.b_qkv, e->q, e->k,
+                                          e->vt, s, ws, wn);
+           })) != FTX_OK) return st;
+      if ((st = step(e, FTX_DEC_STEP_SELF_ATTENTION, s, [&] {
+             return launch_attention(dt, B, Sd, Sd, nh, d, e->q, e->k, e->vt, nullptr, e->ctx, s,
+                                     Sd, true);
+           })) != FTX_OK) return st;
+    }
     if ((st = step(e, FTX_DEC_STEP_SELF_OUT_GEMM, s, [&] {
            return launch_linear(dt, Td, H, H, e->ctx, w.w_o_t, nullptr, false, e->abuf, s, f32res,
                                 ws, wn);
@@ -232,9 +251,12 @@ ftx_status ftx_decoder_create(int batch_size, int tgt_len, int mem_len, int head
   auto pad = [](size_t bytes) { return (bytes + 255) / 256 * 256; };
   // per layer: Wqkv 3HH + 3H, Wo HH + H, LN1 2H, Wq2 HH + H, Wkv2 2HH + 2H, Wo2 HH + H,
   // LN2 2H, W1 FH + F, W2 HF + H, LN3 2H
+  // (+ 3HH + 3H in per-head order when the fused self-attention fits)
+  e->attn_fits = qkv_attention_fits(dtype, e->Sd, size_per_head);
   const size_t per_layer = pad(3 * H * H * es) + pad(3 * H * es) + 3 * pad(H * H * es) +
                            pad(2 * H * H * es) + pad(2 * H * es) + pad(F * H * es) + pad(F * es) +
-                           pad(H * F * es) + 10 * pad(H * es);
+                           pad(H * F * es) + 10 * pad(H * es) +
+                           (e->attn_fits ? pad(3 * H * H * es) + pad(3 * H * es) : 0);
   hipError_t err = hipMalloc(&e->weights, per_layer * e->L);
   if (err != hipSuccess) {
     delete e;
@@ -278,6 +300,8 @@ ftx_status ftx_decoder_create(int batch_size, int tgt_len, int mem_len, int head
     lw.b2 = take(H * es);
     lw.ln3_g = take(H * es);
     lw.ln3_b = take(H * es);
+    lw.w_qkvh_t = e->attn_fits ? take(3 * H * H * es) : nullptr;
+    lw.b_qkvh = e->attn_fits ? take(3 * H * es) : nullptr;
   }
   e->ready.assign(e->L, 0);
   char* p = (char*)e->ws;
@@ -392,6 +416,17 @@ ftx_status ftx_decoder_set_weights(ftx_decoder* e, int layer, const ftx_decoder_
   FTX_HIP(copy(lw.b2, w->b_ffn2, H));
   FTX_HIP(copy(lw.ln3_g, w->ln3_gamma, H));
   FTX_HIP(copy(lw.ln3_b, w->ln3_beta, H));
+  if (lw.w_qkvh_t) {
+    // rows of head h of Q (K, V) go to rows 192 h .. (+64, +128): d = 64 here
+    const size_t d = e->d;
+    for (int part = 0; part < 3; ++part) {
+      FTX_HIP(hipMemcpy2DAsync((char*)lw.w_qkvh_t + part * d * H * es, 3 * d * H * es,
+                               qkv + part * HH, d * H * es, d * H * es, e->nh,
+                               hipMemcpyDeviceToDevice, s));
+      FTX_HIP(hipMemcpy2DAsync((char*)lw.b_qkvh + part * d * es, 3 * d * es, bqkv + part * H * es,
+                               d * es, d * es, e->nh, hipMemcpyDeviceToDevice, s));
+    }
+  }
   FTX_HIP(hipStreamSynchronize(s));
   e->ready[layer] = 1;
   return FTX_OK;
@@ -418,9 +453,16 @@ ftx_status ftx_decoder_forward(ftx_decoder* e, const void* input, const void* me
 ftx_status ftx_decoder_set_option(ftx_decoder* e, ftx_option option, int value) {
   last_error_slot().clear();
   if (!e) return fail(FTX_ERR_INVALID_ARG, "decoder is NULL");
-  if (option != FTX_OPT_KERNEL_TIMING) return fail(FTX_ERR_INVALID_ARG, "option not available for the decoder");
-  e->timing = value ? 1 : 0;
-  return FTX_OK;
+  if (option == FTX_OPT_KERNEL_TIMING) {
+    e->timing = value ? 1 : 0;
+    return FTX_OK;
+  }
+  if (option == FTX_OPT_FUSED_ATTENTION) {
+    if (value < 0 || value > 2) return fail(FTX_ERR_INVALID_ARG, "fused attention mode is 0, 1 or 2");
+    e->fused_attention = value;
+    return FTX_OK;
+  }
+  return fail(FTX_ERR_INVALID_ARG, "option not available for the decoder");
 }
 
 ftx_status ftx_decoder_kernel_times(ftx_decoder* e, double* ms, int64_t* counts) {

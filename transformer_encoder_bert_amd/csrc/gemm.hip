@@ -292,8 +292,10 @@ __device__ __forceinline__ int swz(int R) { return (R & 7) ^ ((R >> 3) & 3); }
 // all keys of its sequence: S^T = K Q^T per 32-key tile (four MFMAs), the key mask at the
 // sequence's valid length and the exp2 softmax on the fp32 scores (key tiles wholly past it
 // are skipped: their probabilities are 0), C^T = V^T P^T with the probabilities rounded to
-// the storage type, and the division by the row sum.  The context is staged in the wave's
-// own Q rows and stored as 128-byte rows of ctx[b*SEQ + i][h*64 + e].  Q, K and V never
+// the storage type, and the division by the row sum; with the causal flag (a decoder's
+// self-attention) query i also ignores keys j > i and key tiles past its own block are
+// skipped.  The context is staged in the wave's own Q rows and stored as 128-byte rows of
+// ctx[b*SEQ + i][h*64 + e].  Q, K and V never
 // reach global memory.
 template <typename T, int SEQ> struct EpiQKVAttn {
   static_assert(SEQ == 32 || SEQ == 64 || SEQ == 128 || SEQ == 256, "whole sequences per tile");
@@ -308,6 +310,7 @@ template <typename T, int SEQ> struct EpiQKVAttn {
   int M, N;             // M = SEQ * sequences, N = 3 * 64 * heads
   int s_valid;          // keys at or past it are masked in every sequence
   float scale_log2e;    // log2(e) / sqrt(64)
+  int causal;           // non-zero: query i also ignores keys j > i
   // LDS: Q and K rows padded to 72 elements, V^T rows (one per d) to 260 tokens, so the
   // fragment reads of 32 consecutive rows fall in distinct banks
   static constexpr int QLD = 72, VLD = 260;
@@ -355,12 +358,14 @@ template <typename T, int SEQ> struct EpiQKVAttn {
 
     // 2. this wave's queries: tile rows r0 .. r0 + 31 of the sequence at tile row k0; no
     //    barrier follows
-    const int k0 = (wave / NKT) * SEQ, r0 = k0 + (wave % NKT) * 32;
+    const int qb = wave % NKT, k0 = (wave / NKT) * SEQ, r0 = k0 + qb * 32;
     if (m0 + k0 >= M) return;
     const int b = (m0 + k0) / SEQ;
     int len = lens ? lens[b] : s_valid;
     len = min(max(len, 1), s_valid);
-    const int nkt = (len + 31) / 32;
+    int nkt = (len + 31) / 32;
+    if (causal) nkt = min(nkt, qb + 1);  // later key tiles are entirely in the future
+    const int query = qb * 32 + lr;
     // query lr of Q: d = 16 f + 8 g .. + 7 of fragment f
     frag qf[4];
 #pragma unroll
@@ -381,7 +386,8 @@ template <typename T, int SEQ> struct EpiQKVAttn {
         for (int f = 0; f < 4; ++f) Mfma<T>::mma(*(const frag*)(krow + 16 * f), qf[f], sc[t]);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          if (32 * t + 8 * (r / 4) + 4 * g + (r % 4) >= len) sc[t][r] = -INFINITY;
+          const int key = 32 * t + 8 * (r / 4) + 4 * g + (r % 4);
+          if (key >= len || (causal && key > query)) sc[t][r] = -INFINITY;
           mx = fmaxf(mx, sc[t][r]);
         }
       }
@@ -806,11 +812,12 @@ bool qkv_attention_fits(ftx_dtype dt, int S, int d) {
 
 template <typename T, int SEQ>
 static hipError_t qkv_attention_t(int B, int nh, const void* x, const void* w_t, const void* bias,
-                                  const int32_t* lens, int s_valid, void* ctx, hipStream_t s) {
+                                  const int32_t* lens, int s_valid, int causal, void* ctx,
+                                  hipStream_t s) {
   const int M = SEQ * B, N = 3 * 64 * nh, K = 64 * nh;
   // log2(e) / sqrt(d), rounded once from double as the attention kernel does
   const float scale_log2e = (float)(1.4426950408889634 / 8.0);
-  EpiQKVAttn<T, SEQ> epi{(T*)ctx, (const T*)bias, lens, M, N, s_valid, scale_log2e};
+  EpiQKVAttn<T, SEQ> epi{(T*)ctx, (const T*)bias, lens, M, N, s_valid, scale_log2e, causal};
   const int tiles = ((M + 255) / 256) * (N / 192);
   gemm_kernel<T, 256, 192, 4, 2, EpiQKVAttn<T, SEQ>><<<tiles, 8 * kWave, 0, s>>>(
       (const T*)x, (const T*)w_t, M, N, K, K, epi);
@@ -819,24 +826,25 @@ static hipError_t qkv_attention_t(int B, int nh, const void* x, const void* w_t,
 
 template <typename T>
 static hipError_t qkv_attention_s(int B, int S, int nh, const void* x, const void* w_t,
-                                  const void* bias, const int32_t* lens, int s_valid, void* ctx,
-                                  hipStream_t s) {
+                                  const void* bias, const int32_t* lens, int s_valid, int causal,
+                                  void* ctx, hipStream_t s) {
   switch (S) {
-    case 32: return qkv_attention_t<T, 32>(B, nh, x, w_t, bias, lens, s_valid, ctx, s);
-    case 64: return qkv_attention_t<T, 64>(B, nh, x, w_t, bias, lens, s_valid, ctx, s);
-    case 128: return qkv_attention_t<T, 128>(B, nh, x, w_t, bias, lens, s_valid, ctx, s);
-    case 256: return qkv_attention_t<T, 256>(B, nh, x, w_t, bias, lens, s_valid, ctx, s);
+    case 32: return qkv_attention_t<T, 32>(B, nh, x, w_t, bias, lens, s_valid, causal, ctx, s);
+    case 64: return qkv_attention_t<T, 64>(B, nh, x, w_t, bias, lens, s_valid, causal, ctx, s);
+    case 128: return qkv_attention_t<T, 128>(B, nh, x, w_t, bias, lens, s_valid, causal, ctx, s);
+    case 256: return qkv_attention_t<T, 256>(B, nh, x, w_t, bias, lens, s_valid, causal, ctx, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_qkv_attention(ftx_dtype dt, int B, int S, int nh, int d, const void* x,
                                 const void* w_qkv_t, const void* b_qkv, const int32_t* lens,
-                                int s_valid, void* ctx, hipStream_t s) {
+                                int s_valid, void* ctx, hipStream_t s, bool causal) {
   if (!qkv_attention_fits(dt, S, d) || B < 1 || nh < 1) return hipErrorInvalidValue;
   if (s_valid <= 0 || s_valid > S) s_valid = S;
-  if (dt == FTX_FP16) return qkv_attention_s<f16>(B, S, nh, x, w_qkv_t, b_qkv, lens, s_valid, ctx, s);
-  return qkv_attention_s<bf16>(B, S, nh, x, w_qkv_t, b_qkv, lens, s_valid, ctx, s);
+  const int c = causal ? 1 : 0;
+  if (dt == FTX_FP16) return qkv_attention_s<f16>(B, S, nh, x, w_qkv_t, b_qkv, lens, s_valid, c, ctx, s);
+  return qkv_attention_s<bf16>(B, S, nh, x, w_qkv_t, b_qkv, lens, s_valid, c, ctx, s);
 }
 
 hipError_t launch_qkv_projection(ftx_dtype dt, int B, int S, int nh, int d, const void* x,

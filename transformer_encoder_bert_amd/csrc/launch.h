@@ -35,11 +35,11 @@ bool qkv_attention_fits(ftx_dtype dt, int S, int d);
 // Q/K/V projection of x [B*S][H] with the attention of every (sequence, head) in the same
 // kernel: w_qkv_t [3H][H] and b_qkv [3H] ordered per head ([Q_h | K_h | V_h], 192 rows each),
 // ctx [B*S][H] as launch_attention writes it.  Keys at or past min(lens[b], s_valid) are
-// masked (s_valid 1..S, default S; lens NULL: s_valid).  hipErrorInvalidValue when the
-// shape does not fit.
+// masked (s_valid 1..S, default S; lens NULL: s_valid); causal: query i also ignores keys
+// j > i.  hipErrorInvalidValue when the shape does not fit.
 hipError_t launch_qkv_attention(ftx_dtype dt, int B, int S, int nh, int d, const void* x,
                                 const void* w_qkv_t, const void* b_qkv, const int32_t* lens,
-                                int s_valid, void* ctx, hipStream_t s);
+                                int s_valid, void* ctx, hipStream_t s, bool causal = false);
 
 // fp32 elements of split-K workspace the GEMM of this shape uses (0: it does not split).
 size_t gemm_splitk_workspace(ftx_dtype dt, int M, int N, int K);

@@ -45,7 +45,7 @@ EXPORTED = ("ftx_encoder_create", "ftx_set_weights", "ftx_forward", "ftx_destroy
             "ftx_decoder_set_option", "ftx_decoder_kernel_times", "ftx_decoder_destroy")
 DEC_STEP_NAMES = ("self_qkv_gemm", "self_attention", "self_out_gemm", "ln1", "cross_q_gemm",
                   "cross_kv_gemm", "cross_attention", "cross_out_gemm", "ln2", "ffn1_gemm",
-                  "ffn2_gemm", "ln3")
+                  "ffn2_gemm", "ln3", "self_qkv_attention")
 
 _DTYPES = {torch.float32: FTX_FP32, torch.float16: FTX_FP16, torch.bfloat16: FTX_BF16}
 _NAMES = {"fp32": FTX_FP32, "fp16": FTX_FP16, "bf16": FTX_BF16}
@@ -89,7 +89,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ftx_kernel_times": (i, [p, p, p]),
         "ftx_step_linear": (i, [i, i, i, i, p, p, p, i, p, v]),
         "ftx_step_qkv_projection": (i, [i, i, i, i, i, p, p, p, p, p, p, v]),
-        "ftx_step_qkv_attention": (i, [i, i, i, i, i, p, p, p, p, p, v]),
+        "ftx_step_qkv_attention": (i, [i, i, i, i, i, p, p, p, p, i, p, v]),
         "ftx_step_bias_qkv_split": (i, [i, i, i, i, i, p, p, p, p, p, v]),
         "ftx_step_attention": (i, [i, i, i, i, i, p, p, p, p, p, v]),
         "ftx_step_masked_attention": (i, [i, i, i, i, i, i, p, p, p, p, i, p, v]),
@@ -367,7 +367,8 @@ def ftx_step_qkv_projection(B, S, n, d, x, w_qkv_t, b_qkv, q, k, v_t, stream=Non
                                                   _stream(stream)), "ftx_step_qkv_projection")
 
 
-def ftx_step_qkv_attention(B, S, n, d, x, w_qkv_t, b_qkv, seq_lens, ctx, stream=None) -> None:
+def ftx_step_qkv_attention(B, S, n, d, x, w_qkv_t, b_qkv, seq_lens, ctx, causal=False,
+                           stream=None) -> None:
     """w_qkv_t / b_qkv rows ordered per head: [Q_h | K_h | V_h] for h = 0 .. n-1."""
     H = n * d
     _need(x, "x", x.dtype, B * S * H)
@@ -377,8 +378,8 @@ def ftx_step_qkv_attention(B, S, n, d, x, w_qkv_t, b_qkv, seq_lens, ctx, stream=
     if seq_lens is not None:
         _need(seq_lens, "seq_lens", torch.int32, B)
     _check(load_library().ftx_step_qkv_attention(_dt(x.dtype), B, S, n, d, _ptr(x), _ptr(w_qkv_t),
-                                                 _ptr(b_qkv), _ptr(seq_lens), _ptr(ctx),
-                                                 _stream(stream)), "ftx_step_qkv_attention")
+                                                 _ptr(b_qkv), _ptr(seq_lens), int(bool(causal)),
+                                                 _ptr(ctx), _stream(stream)), "ftx_step_qkv_attention")
 
 
 def ftx_step_bias_qkv_split(B, S, n, d, qkv, b_qkv, q, k, v_t, stream=None) -> None:
