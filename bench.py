@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--summarize-rocprof", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                    help="write profiles/<--summary-name>.md and _traffic.json from rocprofv3 output "
                         "of this benchmark, then exit (no GPU needed)")
+    p.add_argument("--summarize-trace", metavar="TRACE_DIR", default=None,
+                   help="write profiles/<--summary-name>.md from a rocprofv3 kernel-trace run of "
+                        "this benchmark (kernel stats only), then exit (no GPU needed)")
     p.add_argument("--summary-name", default=None)
     p.add_argument("--summary-commands", nargs="*", default=[])
     return p.parse_args()
@@ -144,6 +147,58 @@ def profile_commands(wl, calib_mb, name):
         f"python3 bench.py{w} --copy-calib-mb {calib_mb} --summarize-rocprof gpurun_out/prof_trace "
         f"gpurun_out/prof_fetch gpurun_out/prof_write --summary-name {name}",
     ]
+
+
+# what each ftx kernel symbol is, for the kernel-trace summaries (demangling by hand: the
+# host's c++filt predates the _Float16 mangling)
+KERNEL_ROLES = (
+    ("EpiQKVAttn", "Q/K/V projection with the attention in its epilogue"),
+    ("EpiQKV", "Q/K/V (or Q-only, K/V-only) projection with bias + head split"),
+    ("EpiLinearIDF16_Lb1", "projection with bias + GELU (FFN-in)"),
+    ("EpiLinearIDF16bLb1", "projection with bias + GELU (FFN-in)"),
+    ("EpiLinear", "projection (attention output, FFN-out)"),
+    ("EpiPartial", "split-K partial products"),
+    ("splitk_reduce", "split-K reduction + epilogue"),
+    ("attention", "attention (scores, masked softmax, context)"),
+    ("layernorm", "bias + residual + LayerNorm"),
+    ("transpose", "weight repacking (set_weights, not in the forward)"),
+)
+
+
+def summarize_trace(args):
+    """Summarise the kernel statistics of a rocprofv3 --kernel-trace --stats run of this
+    benchmark into profiles/<name>.md (ftx kernels only)."""
+    import csv
+    fs = [os.path.join(args.summarize_trace, f) for f in os.listdir(args.summarize_trace)
+          if f.endswith("_kernel_stats.csv")]
+    if len(fs) != 1:
+        raise SystemExit(f"expected one *_kernel_stats.csv in {args.summarize_trace}")
+    rows = [r for r in csv.DictReader(open(fs[0])) if "ftx" in r["Name"]]
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    wl = args.workload or WORKLOAD_DEFAULT
+    import synthetic_inputs as si
+    batches = si.DECODER_WORKLOAD["batches"] if wl == si.DECODER_WORKLOAD["name"] else si.WORKLOADS[wl].batches
+    batch = args.batch or max(batches)
+    flags = (f" --workload {wl}" if wl != WORKLOAD_DEFAULT else "") + (f" --batch {args.batch}" if args.batch else "")
+    d = os.path.relpath(os.path.abspath(args.summarize_trace), ROOT)
+    lines = [f"# Kernel time per forward -- {wl}, batch {batch}", "",
+             "Commands (from the repository root, on one MI355X, with TMPDIR=/tmp):", "", "```",
+             f"rocprofv3 --kernel-trace --stats -f csv -d {d} -o trace -- python3 bench.py"
+             f"{flags} --steps 5 --warmup 2 --no-cpu-baseline",
+             f"python3 bench.py{flags} --summarize-trace {d} --summary-name {args.summary_name}",
+             "```", "",
+             "The run makes 2 warm-up forwards, one forward that reads the launch counts, 5 timed",
+             "forwards, 5 latency-timed forwards and 5 with per-launch events.", "",
+             "| kernel | role | calls | avg us | share of ftx kernel time % |", "|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        role = next((v for k, v in KERNEL_ROLES if k in r["Name"]), "")
+        lines.append(f"| `{r['Name']}` | {role} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{100 * float(r['TotalDurationNs']) / total:.1f} |")
+    lines += ["", f"Kernel source hash: `{kernel_source_hash()}`"]
+    path = os.path.join(ROOT, "profiles", args.summary_name + ".md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
 
 
 def summarize_rocprof(args):
@@ -419,10 +474,13 @@ def bench_decoder(args):
 
 def main():
     args = parse()
-    if args.summarize_rocprof:
+    if args.summarize_rocprof or args.summarize_trace:
         if not args.summary_name:
             raise SystemExit("--summary-name is required")
-        summarize_rocprof(args)
+        if args.summarize_rocprof:
+            summarize_rocprof(args)
+        else:
+            summarize_trace(args)
         return
     if args.workload is None:
         args.workload = WORKLOAD_DEFAULT

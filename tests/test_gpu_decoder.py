@@ -252,3 +252,24 @@ def test_decoder_errors_on_device():
         ftx.ftx_decoder_forward(dec.handle, x, mem, None, x)   # output aliases the input
     assert e.value.status == ftx.FTX_ERR_INVALID_ARG
     dec.close()
+
+
+def test_full_size_sampled_rows():
+    """The decoder workload at batch 512 in the launch configuration the benchmark times (the
+    causal self-attention inside the projection); the oracle checks sampled sequences
+    (sequences are independent)."""
+    wd = si.DECODER_WORKLOAD
+    sh = si.DecoderShape(512, wd["tgt_len"], wd["mem_len"], wd["head_num"], wd["size_per_head"],
+                         wd["num_layers"], wd["dtype"])
+    c = si.make_decoder_case(sh, wd["seed"], mem_lens_range=wd["mem_lens_range"])
+    layers = list(c.layers())
+    dec = _decoder(sh, layers)
+    dec.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)
+    out = dec.forward(to_dev(c.x, sh.dtype), to_dev(c.mem, sh.dtype), dev_lens(c.mem_lens))
+    t = dec.kernel_times()
+    rows = [0, 255, 511]
+    got = to_f64(out[rows])
+    dec.close()
+    assert t["self_qkv_attention"][1] == sh.num_layers
+    ref = oracle.decoder(c.x[rows], c.mem[rows], layers, c.mem_lens[rows], sh.head_num)
+    check(got, ref, sh.dtype, STACK_TOL[sh.dtype], f"decoder B512 rows {rows}")
