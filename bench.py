@@ -39,8 +39,8 @@ def parse():
     p.add_argument("--unfused", action="store_true", help="standalone bias+split and bias+GELU kernels")
     p.add_argument("--graph", action="store_true", help="replay the forward as one HIP graph")
     p.add_argument("--fused-attention", type=int, default=1, choices=(0, 1, 2),
-                   help="projection + attention in one kernel: 0 never, 1 from 256 tokens "
-                        "(default), 2 whenever the shape fits")
+                   help="projection + attention in one kernel: 0 never, 1 from 256 tokens and "
+                        "64 tiles (default), 2 whenever the shape fits")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-kernel-times", action="store_true")

@@ -138,12 +138,14 @@ const char *ftx_last_error(void);
  *     between forwards (they live in handle memory the graph reads).  Ignored while
  *     FTX_OPT_KERNEL_TIMING is on.
  *   FTX_OPT_FUSED_ATTENTION (default 1): for a padded length S of 32, 64, 128 or 256 (seq_len
- *     up to 256, rounded up to a multiple of 32 that is one of those), size_per_head 64 and a
- *     16-bit dtype, the Q/K/V projection and the attention run as one kernel that attends
- *     each 256 x 192 projection tile (256/S whole sequences, one head) in its epilogue, so
+ *     up to 256, rounded up to a multiple of 32 that is one of those), size_per_head 64 (or
+ *     32 with an even head_num) and a 16-bit dtype, the Q/K/V projection and the attention
+ *     run as one kernel that attends each 256 x 192 projection tile (256/S whole sequences,
+ *     64/size_per_head heads) in its epilogue, so
  *     Q, K and V never reach memory (ftx_step_qkv_attention).  0 = never; 1 = when
- *     batch*S >= 256 (at least one whole tile of rows), else the separate kernels; 2 =
- *     whenever the shape fits.  Needs FTX_OPT_FUSED_EPILOGUES = 1.
+ *     batch*S >= 256 (at least one whole tile of rows) and the grid has at least 64 tiles
+ *     (ceil(batch*S/256) * 3*hidden/192), else the separate kernels; 2 = whenever the shape
+ *     fits.  Needs FTX_OPT_FUSED_EPILOGUES = 1.
  *     Values outside 0..2 -> FTX_ERR_INVALID_ARG.
  * Unknown option -> FTX_ERR_INVALID_ARG. */
 typedef enum {

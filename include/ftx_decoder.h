@@ -76,11 +76,12 @@ ftx_status ftx_decoder_forward(ftx_decoder *dec, const void *input, const void *
  *   FTX_OPT_KERNEL_TIMING (value != 0: an event pair around every launch of the following
  *     forwards, read back by ftx_decoder_kernel_times);
  *   FTX_OPT_FUSED_ATTENTION (default 1): as for the encoder (ftx.h), for the causal
- *     self-attention: with a 16-bit dtype, size_per_head 64 and an internal decoder length of
- *     32, 64, 128 or 256, the self Q/K/V projection attends each of its 256 x 192 tiles in its
- *     epilogue (step class FTX_DEC_STEP_SELF_QKV_ATTENTION); 0 never, 1 when batch*len >=
- *     256 (len: the internal decoder length), 2 whenever the shape fits; other values ->
- *     FTX_ERR_INVALID_ARG. */
+ *     self-attention: with a 16-bit dtype, size_per_head 64 (or 32 with an even head_num)
+ *     and an internal decoder length of 32, 64, 128 or 256, the self Q/K/V projection
+ *     attends each of its 256 x 192 tiles in its epilogue (step class
+ *     FTX_DEC_STEP_SELF_QKV_ATTENTION); 0 never; 1 when batch*len >= 256 (len: the internal
+ *     decoder length) and the grid has at least 64 tiles; 2 whenever the shape fits; other
+ *     values -> FTX_ERR_INVALID_ARG. */
 ftx_status ftx_decoder_set_option(ftx_decoder *dec, ftx_option option, int value);
 
 /* Step classes of the decoder's per-step timing. */

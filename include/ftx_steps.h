@@ -56,16 +56,17 @@ ftx_status ftx_step_attention(ftx_dtype dtype, int B, int S, int n, int d, const
                               const void *k, const void *v_t, const int32_t *seq_lens,
                               void *ctx, void *stream);
 
-/* Q/K/V projection and attention in one kernel, for S = 32, 64, 128 or 256, d = 64 and a
- * 16-bit dtype (FTX_FP16 or FTX_BF16; other shapes -> FTX_ERR_UNSUPPORTED): x [B*S][H] ->
+/* Q/K/V projection and attention in one kernel, for S = 32, 64, 128 or 256, d = 64 (or 32
+ * with an even n) and a 16-bit dtype (FTX_FP16 or FTX_BF16; other shapes ->
+ * FTX_ERR_UNSUPPORTED): x [B*S][H] ->
  * ctx [B*S][H] with ctx[b*S+i][h*64+e], the result of ftx_step_qkv_projection followed
  * by ftx_step_attention, except that the weight rows are ordered per head:
- *   w_qkv_t [3H][H], rows 192h .. 192h+63 = rows h*64 .. h*64+63 of Wq^T, the next 64 of
- *   Wk^T, the next 64 of Wv^T (h = 0 .. n-1); b_qkv [3H] in the same order;
+ *   w_qkv_t [3H][H], rows 3dh .. 3dh+d-1 = rows h*d .. h*d+d-1 of Wq^T, the next d of Wk^T,
+ *   the next d of Wv^T (h = 0 .. n-1); b_qkv [3H] in the same order;
  *   seq_lens [B] int32 (clamped to [1, S]) or NULL; causal != 0: query i also ignores keys
  *   j > i (a decoder's self-attention).
- * Q, K and V stay on chip: each 256 x 192 output tile (256/S whole sequences, one head) is
- * attended in the projection's epilogue. */
+ * Q, K and V stay on chip: each 256 x 192 output tile (256/S whole sequences, 64/d heads)
+ * is attended in the projection's epilogue. */
 ftx_status ftx_step_qkv_attention(ftx_dtype dtype, int B, int S, int n, int d, const void *x,
                                   const void *w_qkv_t, const void *b_qkv,
                                   const int32_t *seq_lens, int causal, void *ctx, void *stream);

@@ -111,7 +111,7 @@ def test_step_argument_checks(lib):
     assert lib.ftx_step_qkv_attention(0, 1, 32, 2, 64, 256, 512, 768, None, 0, 1024, None) == U
     assert lib.ftx_step_qkv_attention(1, 1, 96, 2, 64, 256, 512, 768, None, 0, 1024, None) == U
     assert lib.ftx_step_qkv_attention(1, 1, 512, 2, 64, 256, 512, 768, None, 0, 1024, None) == U
-    assert lib.ftx_step_qkv_attention(2, 1, 32, 2, 32, 256, 512, 768, None, 0, 1024, None) == U
+    assert lib.ftx_step_qkv_attention(2, 1, 32, 3, 32, 256, 512, 768, None, 0, 1024, None) == U  # odd n, d 32
     assert lib.ftx_step_qkv_attention(1, 1, 32, 2, 64, None, 512, 768, None, 0, 1024, None) == E
     assert lib.ftx_step_qkv_attention(1, 1, 32, 2, 64, 256, 512, 776, None, 1, 1024, None) == E
     # layernorm: cols not a multiple of 4, above the limit, misaligned

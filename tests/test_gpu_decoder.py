@@ -198,11 +198,12 @@ def test_deterministic_and_inputs_untouched():
     assert torch.equal(a, b) and torch.equal(x, x0) and torch.equal(mem, m0)
 
 
-@pytest.mark.parametrize("Sd,Se,dtype", [(32, 64, "fp16"), (64, 32, "bf16"), (100, 40, "fp16")])
-def test_fused_self_attention_matches_oracle(Sd, Se, dtype):
+@pytest.mark.parametrize("Sd,Se,d,dtype", [(32, 64, 64, "fp16"), (64, 32, 64, "bf16"), (100, 40, 64, "fp16"),
+                                          (32, 32, 32, "fp16")])
+def test_fused_self_attention_matches_oracle(Sd, Se, d, dtype):
     """FTX_OPT_FUSED_ATTENTION = 2: the causal self-attention inside the self Q/K/V
-    projection (d = 64; Sd = 100 is padded to 128)."""
-    sh = si.DecoderShape(3, Sd, Se, 2, 64, 2, dtype)
+    projection (Sd = 100 is padded to 128; d = 32 puts two heads in a tile)."""
+    sh = si.DecoderShape(3, Sd, Se, 2, d, 2, dtype)
     c = si.make_decoder_case(sh, 41 + Sd + Se, params="random_affine", mem_lens_range=(1, Se))
     layers = list(c.layers())
     dec = ftx.Decoder(sh.batch, sh.tgt_len, sh.mem_len, sh.head_num, sh.size_per_head, 2, dtype)

@@ -28,10 +28,10 @@ def _gpu(request):
     torch.cuda.synchronize()
 
 
-def exact_case(B, S, n, seed):
+def exact_case(B, S, n, seed, d=64):
     """x in {-2..2}, each weight column with 8 nonzeros of +-1/2, biases in {-1, -1/2, 0, 1/2,
     1}: |q|, |k|, |v| <= 9, half-integers, exact in fp16 and bf16 and summed exactly in fp32."""
-    H = 64 * n
+    H = d * n
     rng = np.random.default_rng(seed)
     x = rng.integers(-2, 3, size=(B, S, H)).astype(np.float64)
     ws = []
@@ -45,9 +45,9 @@ def exact_case(B, S, n, seed):
     return x, ws, bs
 
 
-def per_head_rows(mats, n):
-    """[Q|K|V] blocks of H rows -> rows ordered per head: Q_h, K_h, V_h (64 rows each)."""
-    return np.concatenate([m[h * 64:(h + 1) * 64] for h in range(n) for m in mats], axis=0)
+def per_head_rows(mats, n, d=64):
+    """[Q|K|V] blocks of H rows -> rows ordered per head: Q_h, K_h, V_h (d rows each)."""
+    return np.concatenate([m[h * d:(h + 1) * d] for h in range(n) for m in mats], axis=0)
 
 
 def reference(x, ws, bs, n, lens):
@@ -57,46 +57,50 @@ def reference(x, ws, bs, n, lens):
 
 
 CASES = [
-    # B, S, n, lens
-    (1, 32, 1, None),
-    (8, 32, 2, "random"),       # one full tile row of eight sequences
-    (9, 32, 2, "random"),       # a second tile row with one sequence
-    (20, 32, 3, [1] * 10 + [32] * 10),
-    (40, 32, 12, "random"),     # BERT-base heads
-    (5, 64, 2, "random"),       # four sequences per tile, two waves each; a partial tile row
-    (3, 128, 2, [128, 97, 1]),  # two sequences per tile, key tiles skipped past the length
-    (2, 256, 2, [256, 37]),     # one sequence per tile, eight query blocks
-    (1, 256, 1, None),
+    # B, S, n, d, lens
+    (1, 32, 1, 64, None),
+    (8, 32, 2, 64, "random"),       # one full tile row of eight sequences
+    (9, 32, 2, 64, "random"),       # a second tile row with one sequence
+    (20, 32, 3, 64, [1] * 10 + [32] * 10),
+    (40, 32, 12, 64, "random"),     # BERT-base heads
+    (5, 64, 2, 64, "random"),       # four sequences per tile, two waves each; a partial tile row
+    (3, 128, 2, 64, [128, 97, 1]),  # two sequences per tile, key tiles skipped past the length
+    (2, 256, 2, 64, [256, 37]),     # one sequence per tile, eight query blocks
+    (1, 256, 1, 64, None),
+    (9, 32, 4, 32, "random"),       # d = 32: two heads per tile (the pruned model's 4 x 32)
+    (3, 32, 2, 32, None),
+    (3, 128, 6, 32, [128, 50, 1]),
 ]
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
-@pytest.mark.parametrize("B,S,n,lens", CASES)
-def test_step_matches_oracle(dtype, B, S, n, lens):
-    x, ws, bs = exact_case(B, S, n, 1000 + 31 * B + S + n)
+@pytest.mark.parametrize("B,S,n,d,lens", CASES)
+def test_step_matches_oracle(dtype, B, S, n, d, lens):
+    x, ws, bs = exact_case(B, S, n, 1000 + 31 * B + S + n + d, d)
     if lens == "random":
         lens = np.random.default_rng(B + n).integers(1, S + 1, size=B)
     lens_np = None if lens is None else np.asarray(lens, dtype=np.int32)
     ref, vmax = reference(x, ws, bs, n, lens_np)
-    w_t = per_head_rows([w.T for w in ws], n)
-    b = per_head_rows([bb[:, None] for bb in bs], n)[:, 0]
-    ctx = torch.empty((B, S, 64 * n), dtype=TORCH[dtype], device=DEV)
-    ftx.ftx_step_qkv_attention(B, S, n, 64, to_dev(x, dtype), to_dev(w_t, dtype), to_dev(b, dtype),
+    w_t = per_head_rows([w.T for w in ws], n, d)
+    b = per_head_rows([bb[:, None] for bb in bs], n, d)[:, 0]
+    ctx = torch.empty((B, S, d * n), dtype=TORCH[dtype], device=DEV)
+    ftx.ftx_step_qkv_attention(B, S, n, d, to_dev(x, dtype), to_dev(w_t, dtype), to_dev(b, dtype),
                                dev_lens(lens_np), ctx)
     u = UNIT[dtype]
     assert_within(to_f64(ctx), ref, 2 * u * vmax + 1e-6, 2 * u, "qkv attention")
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
-@pytest.mark.parametrize("B,S,n", [(2, 32, 2), (3, 64, 2), (2, 128, 1), (1, 256, 2)])
-def test_step_causal_matches_oracle(dtype, B, S, n):
+@pytest.mark.parametrize("B,S,n,d", [(2, 32, 2, 64), (3, 64, 2, 64), (2, 128, 1, 64), (1, 256, 2, 64),
+                                     (2, 64, 2, 32)])
+def test_step_causal_matches_oracle(dtype, B, S, n, d):
     """The decoder's self-attention: query i sees keys j <= i (no length vector)."""
-    x, ws, bs = exact_case(B, S, n, 3000 + B + S + n)
+    x, ws, bs = exact_case(B, S, n, 3000 + B + S + n + d, d)
     q, k, v = (oracle.split_heads(oracle.linear(x, w, b), n) for w, b in zip(ws, bs))
     ref = oracle.merge_heads(oracle.context(oracle.causal_softmax(oracle.scaled_scores(q, k)), v))
-    ctx = torch.empty((B, S, 64 * n), dtype=TORCH[dtype], device=DEV)
-    ftx.ftx_step_qkv_attention(B, S, n, 64, to_dev(x, dtype), to_dev(per_head_rows([w.T for w in ws], n), dtype),
-                               to_dev(per_head_rows([bb[:, None] for bb in bs], n)[:, 0], dtype), None, ctx,
+    ctx = torch.empty((B, S, d * n), dtype=TORCH[dtype], device=DEV)
+    ftx.ftx_step_qkv_attention(B, S, n, d, to_dev(x, dtype), to_dev(per_head_rows([w.T for w in ws], n, d), dtype),
+                               to_dev(per_head_rows([bb[:, None] for bb in bs], n, d)[:, 0], dtype), None, ctx,
                                causal=True)
     u = UNIT[dtype]
     assert_within(to_f64(ctx), ref, 2 * u * np.abs(v).max() + 1e-6, 2 * u, "causal qkv attention")
@@ -130,17 +134,18 @@ def test_step_equals_separate_steps_at_full_size():
 
 
 def test_step_rejects_other_shapes():
-    """d = 32 and fp32 are refused (S outside {32, 64, 128, 256}: tests/test_abi.py)."""
-    x = torch.zeros((2, 32, 128), dtype=torch.float16, device=DEV)
-    w = torch.zeros((384, 128), dtype=torch.float16, device=DEV)
-    b = torch.zeros(384, dtype=torch.float16, device=DEV)
+    """d = 32 with an odd head count and fp32 are refused (S outside {32, 64, 128, 256}:
+    tests/test_abi.py)."""
+    x = torch.zeros((2, 32, 96), dtype=torch.float16, device=DEV)
+    w = torch.zeros((288, 96), dtype=torch.float16, device=DEV)
+    b = torch.zeros(288, dtype=torch.float16, device=DEV)
     ctx = torch.empty_like(x)
     with pytest.raises(ftx.FtxError) as e:
-        ftx.ftx_step_qkv_attention(2, 32, 4, 32, x, w, b, None, ctx)   # d = 32
+        ftx.ftx_step_qkv_attention(2, 32, 3, 32, x, w, b, None, ctx)   # d = 32, three heads
     assert e.value.status == ftx.FTX_ERR_UNSUPPORTED
     xf, wf, bf, cf = (t.float() for t in (x, w, b, ctx))
     with pytest.raises(ftx.FtxError) as e:
-        ftx.ftx_step_qkv_attention(2, 32, 2, 64, xf, wf, bf, None, cf)  # fp32
+        ftx.ftx_step_qkv_attention(2, 32, 3, 32, xf, wf, bf, None, cf)  # fp32
     assert e.value.status == ftx.FTX_ERR_UNSUPPORTED
 
 
@@ -157,21 +162,23 @@ def _encoder(shape, layers, mode):
 
 
 STACK = [
-    # B, S, n, dtype, lens range
-    (9, 32, 4, "fp16", (1, 32)),
-    (3, 17, 2, "fp16", None),         # S padded to 32 inside the handle
-    (10, 32, 12, "bf16", (5, 32)),
-    (2, 32, 2, "fp16", None),
-    (3, 50, 2, "fp16", (1, 50)),      # padded to 64
-    (3, 100, 2, "bf16", (1, 100)),    # padded to 128
-    (2, 230, 2, "fp16", None),        # padded to 256
+    # B, S, n, d, dtype, lens range
+    (9, 32, 4, 64, "fp16", (1, 32)),
+    (3, 17, 2, 64, "fp16", None),         # S padded to 32 inside the handle
+    (10, 32, 12, 64, "bf16", (5, 32)),
+    (2, 32, 2, 64, "fp16", None),
+    (3, 50, 2, 64, "fp16", (1, 50)),      # padded to 64
+    (3, 100, 2, 64, "bf16", (1, 100)),    # padded to 128
+    (2, 230, 2, 64, "fp16", None),        # padded to 256
+    (9, 32, 4, 32, "fp16", (1, 32)),      # the pruned model's 4 x 32
+    (3, 64, 4, 32, "bf16", None),
 ]
 
 
-@pytest.mark.parametrize("B,S,n,dtype,lens", STACK)
-def test_encoder_forced_fused_matches_oracle(B, S, n, dtype, lens):
-    sh = si.Shape(B, S, n, 64, 2, dtype)
-    c = si.custom_case(sh, 500 + B + S + n, params="random_affine", lens_range=lens)
+@pytest.mark.parametrize("B,S,n,d,dtype,lens", STACK)
+def test_encoder_forced_fused_matches_oracle(B, S, n, d, dtype, lens):
+    sh = si.Shape(B, S, n, d, 2, dtype)
+    c = si.custom_case(sh, 500 + B + S + n + d, params="random_affine", lens_range=lens)
     layers = list(c.layers())
     enc = _encoder(sh, layers, 2)
     enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)
@@ -196,9 +203,10 @@ def test_encoder_fused_and_separate_agree():
     assert_within(outs[0], outs[1], 2e-2, 0.0, "fused vs separate attention")
 
 
-def test_encoder_auto_mode_needs_a_whole_tile():
-    """Default mode: fused from 256 tokens (B = 8 at S = 32), separate below."""
-    for B, fused in ((7, False), (8, True)):
+def test_encoder_auto_mode_needs_64_tiles():
+    """Default mode: fused from 64 tiles of 256 x 192 (BERT-base S32: B = 48 gives 6 x 12),
+    separate below (B = 40 gives 5 x 12)."""
+    for B, fused in ((40, False), (48, True)):
         c = si.make_case("bert_base_fp16_s32", B, params="bert", num_layers=1)
         enc = _encoder(c.shape, list(c.layers()), 1)
         enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)

@@ -58,8 +58,8 @@ struct ftx_decoder {
   // [B][Se][H] memory copy, their padding rows zero
   void *xpad = nullptr, *spad = nullptr, *mpad = nullptr;
   int timing = 0;
-  int fused_attention = 1;  // 0 off, 1 from 256 rows (one whole tile), 2 whenever the shape fits
-  bool attn_fits = false;   // the per-head weight copy exists (16-bit, Sd in {32..256}, d = 64)
+  int fused_attention = 1;  // 0 off, 1 from 256 rows and 64 tiles, 2 whenever the shape fits
+  bool attn_fits = false;   // the per-head weight copy exists (qkv_attention_fits)
   struct Mark {
     hipEvent_t start, stop;
     int step;
@@ -100,11 +100,11 @@ ftx_status step(ftx_decoder* e, int cls, hipStream_t s, F&& launch) {
 }
 
 // The causal self-attention runs inside the self Q/K/V projection when the shape fits and,
-// in the default mode, when there are at least 256 decoder rows (one whole tile), as in the
-// encoder.
+// in the default mode, when there are at least 256 decoder rows (one whole tile) and 64
+// tiles, as in the encoder.
 bool use_fused_self_attention(const ftx_decoder* e) {
   if (!e->attn_fits || e->fused_attention == 0) return false;
-  return e->fused_attention == 2 || e->Td >= 256;
+  return e->fused_attention == 2 || (e->Td >= 256 && fused_attention_tiles(e->Td, e->H) >= 64);
 }
 
 ftx_status enqueue_decoder(ftx_decoder* e, const void* input, const void* memory,
@@ -252,7 +252,7 @@ ftx_status ftx_decoder_create(int batch_size, int tgt_len, int mem_len, int head
   // per layer: Wqkv 3HH + 3H, Wo HH + H, LN1 2H, Wq2 HH + H, Wkv2 2HH + 2H, Wo2 HH + H,
   // LN2 2H, W1 FH + F, W2 HF + H, LN3 2H
   // (+ 3HH + 3H in per-head order when the fused self-attention fits)
-  e->attn_fits = qkv_attention_fits(dtype, e->Sd, size_per_head);
+  e->attn_fits = qkv_attention_fits(dtype, e->Sd, head_num, size_per_head);
   const size_t per_layer = pad(3 * H * H * es) + pad(3 * H * es) + 3 * pad(H * H * es) +
                            pad(2 * H * H * es) + pad(2 * H * es) + pad(F * H * es) + pad(F * es) +
                            pad(H * F * es) + 10 * pad(H * es) +
@@ -417,7 +417,7 @@ ftx_status ftx_decoder_set_weights(ftx_decoder* e, int layer, const ftx_decoder_
   FTX_HIP(copy(lw.ln3_g, w->ln3_gamma, H));
   FTX_HIP(copy(lw.ln3_b, w->ln3_beta, H));
   if (lw.w_qkvh_t) {
-    // rows of head h of Q (K, V) go to rows 192 h .. (+64, +128): d = 64 here
+    // rows of head h of Q (K, V) go to rows 3 d h .. (+d, +2d)
     const size_t d = e->d;
     for (int part = 0; part < 3; ++part) {
       FTX_HIP(hipMemcpy2DAsync((char*)lw.w_qkvh_t + part * d * H * es, 3 * d * H * es,

@@ -83,7 +83,7 @@ struct ftx_encoder {
   size_t splitk_elems = 0;
   float* y1f = nullptr;  // fp32 copy of Y1, the residual of the second LayerNorm (bf16 only)
   int fused = 1;
-  int fused_attention = 1;  // 0 off, 1 from 256 rows (one whole tile), 2 whenever the shape fits
+  int fused_attention = 1;  // 0 off, 1 from 256 rows and 64 tiles, 2 whenever the shape fits
   bool attn_fits = false;   // the per-head weight copy exists (16-bit, S = 32, d = 64)
   int timing = 0;
   int graph_mode = 0;
@@ -148,12 +148,14 @@ void drop_graph(ftx_encoder* e) {
 
 // The projection with the attention in its epilogue replaces the projection + attention
 // pair when the shape fits and, in the default mode, when there are at least 256 tokens (one
-// whole tile of rows): below that its tile is mostly padding rows, while the separate path
-// splits K over many small blocks (measured at BERT-base S32: B1 0.585 ms fused against 0.516
-// separate, B8 0.656 against 0.664, B64 0.927 against 0.947; S64 B64 1.253 against 1.508).
+// whole tile of rows) and 64 tiles: with fewer, the tiles are mostly padding rows or the
+// long epilogue runs on few CUs, while the separate kernels spread the same work (measured,
+// fused against separate: BERT-base S32 B1 0.585 against 0.516 ms, B64 (96 tiles) 0.927
+// against 0.947, S64 B64 1.253 against 1.508; the 4 x 32 model B64 (16 tiles) 0.321 against
+// 0.298, B512 (128 tiles) 0.464 against 0.514).
 bool use_fused_attention(const ftx_encoder* e) {
   if (!e->fused || !e->attn_fits || e->fused_attention == 0) return false;
-  return e->fused_attention == 2 || e->T >= 256;
+  return e->fused_attention == 2 || (e->T >= 256 && fused_attention_tiles(e->T, e->H) >= 64);
 }
 
 // Enqueue the L-layer forward on `s` (arguments already validated).
@@ -303,7 +305,7 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
   e->es = dtype_size(dtype);
   e->device = dev;
 
-  e->attn_fits = qkv_attention_fits(dtype, e->S, size_per_head);
+  e->attn_fits = qkv_attention_fits(dtype, e->S, head_num, size_per_head);
 
   const size_t H = e->H, F = e->F, T = e->T, es = e->es;
   // weights: per layer 3H*H + 3H + H*H + H + 2H + F*H + F + H*F + H + 2H elements (plus a
@@ -438,7 +440,7 @@ ftx_status ftx_set_weights(ftx_encoder* e, int layer, const ftx_layer_weights* w
   FTX_HIP(hipMemcpyAsync(lw.ln2_g, w->ln2_gamma, H * es, hipMemcpyDeviceToDevice, s));
   FTX_HIP(hipMemcpyAsync(lw.ln2_b, w->ln2_beta, H * es, hipMemcpyDeviceToDevice, s));
   if (lw.w_qkvh_t) {
-    // rows of head h of Q (K, V) go to rows 192 h .. (+64, +128): d = 64 here
+    // rows of head h of Q (K, V) go to rows 3 d h .. (+d, +2d)
     const size_t d = e->d;
     for (int part = 0; part < 3; ++part) {
       FTX_HIP(hipMemcpy2DAsync((char*)lw.w_qkvh_t + part * d * H * es, 3 * d * H * es,
@@ -634,8 +636,10 @@ ftx_status ftx_step_qkv_attention(ftx_dtype dtype, int B, int S, int n, int d, c
   if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
   ftx_status st = check_shape(B, S, n, d);
   if (st != FTX_OK) return st;
-  if (!qkv_attention_fits(dtype, S, d))
-    return fail(FTX_ERR_UNSUPPORTED, "fused projection + attention needs fp16/bf16, S in {32, 64, 128, 256}, d = 64");
+  if (!qkv_attention_fits(dtype, S, n, d))
+    return fail(FTX_ERR_UNSUPPORTED,
+                "fused projection + attention needs fp16/bf16, S in {32, 64, 128, 256}, d = 64 "
+                "(or 32 with an even head count)");
   if (!x || !w_qkv_t || !b_qkv || !ctx) return fail(FTX_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned16(x) || !aligned16(w_qkv_t) || !aligned16(b_qkv) || !aligned16(ctx))
     return fail(FTX_ERR_INVALID_ARG, "pointers must be 16-byte aligned");

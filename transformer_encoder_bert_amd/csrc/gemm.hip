@@ -280,39 +280,46 @@ __device__ __forceinline__ void workgroup_barrier() {
 // only, so the 32-row tiles of a wave differ by a constant offset.
 __device__ __forceinline__ int swz(int R) { return (R & 7) ^ ((R >> 3) & 3); }
 
-// Q/K/V projection of SEQ-token sequences (SEQ = 32, 64, 128 or 256) with head size 64, and
-// the attention of each (sequence, head) in the epilogue (the layer's first steps, section
-// "Faster Transformer 优化原理" of the Faster Transformer article).  The weight rows (output
-// columns) are ordered per head, [Q_h | K_h | V_h] for h = 0 .. nh-1, so the 192 columns of
-// tile column h are exactly Q, K and V of head h, and the 256 rows of a tile are 256 / SEQ
-// whole sequences.  After the K loop the tile is biased, rounded to the storage type (as Q,
-// K and V are when they go through memory) and split in LDS into Q and K (rows of 64 d) and
-// V^T (rows of 256 tokens); then each wave takes one block of 32 queries (wave w: sequence
-// w / (SEQ/32), query block w % (SEQ/32)) and runs the chain of the attention kernel over
-// all keys of its sequence: S^T = K Q^T per 32-key tile (four MFMAs), the key mask at the
-// sequence's valid length and the exp2 softmax on the fp32 scores (key tiles wholly past it
-// are skipped: their probabilities are 0), C^T = V^T P^T with the probabilities rounded to
-// the storage type, and the division by the row sum; with the causal flag (a decoder's
-// self-attention) query i also ignores keys j > i and key tiles past its own block are
-// skipped.  The context is staged in the wave's own Q rows and stored as 128-byte rows of
-// ctx[b*SEQ + i][h*64 + e].  Q, K and V never
+// Q/K/V projection of SEQ-token sequences (SEQ = 32, 64, 128 or 256) with head size D (64,
+// or 32 with an even head count), and the attention of each (sequence, head) in the epilogue
+// (the layer's first steps, section "Faster Transformer 优化原理" of the Faster Transformer
+// article).  The weight rows (output columns) are ordered per head, [Q_h | K_h | V_h] for
+// h = 0 .. nh-1, so the 192 columns of a tile column are exactly Q, K and V of 64 / D heads,
+// and the 256 rows of a tile are 256 / SEQ whole sequences.  After the K loop the tile is
+// biased, rounded to the storage type (as Q, K and V are when they go through memory) and
+// split in LDS into Q and K (rows of the tile's 64 head columns) and V^T (one row per head
+// column, 256 tokens); then each wave takes one block of 32 queries (wave w: sequence
+// w / (SEQ/32), query block w % (SEQ/32)) and, for each head of the tile in turn, runs the
+// chain of the attention kernel over all keys of its sequence: S^T = K Q^T per 32-key tile
+// (D/16 MFMAs), the key mask at the sequence's valid length and the exp2 softmax on the fp32
+// scores (key tiles wholly past it are skipped: their probabilities are 0), C^T = V^T P^T
+// with the probabilities rounded to the storage type, and the division by the row sum; with
+// the causal flag (a decoder's self-attention) query i also ignores keys j > i and key tiles
+// past its own block are skipped.  Each head's context is staged in the wave's own Q rows
+// and columns of that head and stored as rows of ctx[b*SEQ + i][h*D + e].  Q, K and V never
 // reach global memory.
-template <typename T, int SEQ> struct EpiQKVAttn {
+template <typename T, int SEQ, int D> struct EpiQKVAttn {
   static_assert(SEQ == 32 || SEQ == 64 || SEQ == 128 || SEQ == 256, "whole sequences per tile");
+  static_assert(D == 32 || D == 64, "head size");
   static constexpr bool kBlock = true;
   static constexpr int NKT = SEQ / 32;  // key tiles (and query blocks) per sequence
+  static constexpr int HPT = 64 / D;    // heads per 192-column tile
+  static constexpr int NQF = D / 16;    // 16-wide fragments along d
+  static constexpr int DT = D / 32;     // 32-row tiles of the transposed context along d
+  static constexpr int VPR = D / 8;     // 16-byte vectors per context row of one head
   typedef T out_t;
   typedef typename VecT<T, 4>::type b4;
   typedef typename Vec16<T>::type vec;
   T* ctx;               // [M][N / 3]
   const T* bias;        // [N], ordered like the weight rows
   const int32_t* lens;  // [M / SEQ] valid lengths, or null
-  int M, N;             // M = SEQ * sequences, N = 3 * 64 * heads
+  int M, N;             // M = SEQ * sequences, N = 3 * D * heads
   int s_valid;          // keys at or past it are masked in every sequence
-  float scale_log2e;    // log2(e) / sqrt(64)
+  float scale_log2e;    // log2(e) / sqrt(D)
   int causal;           // non-zero: query i also ignores keys j > i
-  // LDS: Q and K rows padded to 72 elements, V^T rows (one per d) to 260 tokens, so the
-  // fragment reads of 32 consecutive rows fall in distinct banks
+  // LDS: Q and K rows (the tile's 64 head columns) padded to 72 elements, V^T rows (one per
+  // head column) to 260 tokens, so the fragment reads of 32 consecutive rows fall in
+  // distinct banks
   static constexpr int QLD = 72, VLD = 260;
   static constexpr int KOFF = 256 * QLD, VOFF = 2 * 256 * QLD;
   static constexpr size_t kLdsBytes = (size_t)(VOFF + 64 * VLD) * sizeof(T);
@@ -330,11 +337,12 @@ template <typename T, int SEQ> struct EpiQKVAttn {
     T* lds = (T*)smem;
     const int wm = wave / WN, wn = wave % WN, lr = lane % 32, g = lane / 32;
     // 1. register r of accumulator (j, i): tile column c0 + 8 (r / 4) + 4 g + r % 4 of row
-    //    (wm TM + i) 32 + lr; a 32-column tile lies inside one of Q, K, V
+    //    (wm TM + i) 32 + lr; a 32-column tile lies inside one of Q, K, V of one head hh, at
+    //    head column hh D + (c0 mod D) of the 64 the tile holds
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int c0 = (wn * TN + j) * 32;
-      const int part = c0 / 64, dd0 = c0 % 64;
+      const int blk = c0 / D, hh = blk / 3, part = blk % 3, dd0 = hh * D + c0 % D;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int row = (wm * TM + i) * 32 + lr;
@@ -366,92 +374,97 @@ template <typename T, int SEQ> struct EpiQKVAttn {
     int nkt = (len + 31) / 32;
     if (causal) nkt = min(nkt, qb + 1);  // later key tiles are entirely in the future
     const int query = qb * 32 + lr;
-    // query lr of Q: d = 16 f + 8 g .. + 7 of fragment f
-    frag qf[4];
+    const int H = N / 3;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) qf[f] = *(const frag*)(lds + (r0 + lr) * QLD + 8 * g + 16 * f);
-    // S^T = K Q^T per key tile: register r of sc[t] holds key 32 t + 8 (r / 4) + 4 g + r % 4
-    // of query lr
-    f32x16 sc[NKT];
-    float mx = -INFINITY;
+    for (int hh = 0; hh < HPT; ++hh) {
+      const int hc = hh * D;  // this head's first column in the tile's Q, K and V^T
+      // query lr of Q: d = 16 f + 8 g .. + 7 of fragment f
+      frag qf[NQF];
 #pragma unroll
-    for (int t = 0; t < NKT; ++t) {
+      for (int f = 0; f < NQF; ++f) qf[f] = *(const frag*)(lds + (r0 + lr) * QLD + hc + 8 * g + 16 * f);
+      // S^T = K Q^T per key tile: register r of sc[t] holds key 32 t + 8 (r / 4) + 4 g + r % 4
+      // of query lr
+      f32x16 sc[NKT];
+      float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[t][r] = -INFINITY;
-      if (t < nkt) {
+      for (int t = 0; t < NKT; ++t) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
-        const T* krow = lds + KOFF + (k0 + 32 * t + lr) * QLD + 8 * g;
+        for (int r = 0; r < 16; ++r) sc[t][r] = -INFINITY;
+        if (t < nkt) {
 #pragma unroll
-        for (int f = 0; f < 4; ++f) Mfma<T>::mma(*(const frag*)(krow + 16 * f), qf[f], sc[t]);
+          for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
+          const T* krow = lds + KOFF + (k0 + 32 * t + lr) * QLD + hc + 8 * g;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * t + 8 * (r / 4) + 4 * g + (r % 4);
-          if (key >= len || (causal && key > query)) sc[t][r] = -INFINITY;
-          mx = fmaxf(mx, sc[t][r]);
-        }
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));  // finite: key 0 is always valid
-    float sum = 0.f;
+          for (int f = 0; f < NQF; ++f) Mfma<T>::mma(*(const frag*)(krow + 16 * f), qf[f], sc[t]);
 #pragma unroll
-    for (int t = 0; t < NKT; ++t)
-      if (t < nkt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sc[t][r] = exp2f((sc[t][r] - mx) * scale_log2e);
-          sum += sc[t][r];
-        }
-      }
-    sum += __shfl_xor(sum, 32);
-    // C^T = V^T P^T; MFMA (t, u) takes P registers 8u .. 8u+7 of key tile t = keys
-    // 32 t + 16 u + {0..3, 8..11} + 4 g, against V^T rows d = 32 dt + lr at those keys
-    f32x16 o[2];
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-#pragma unroll
-    for (int t = 0; t < NKT; ++t)
-      if (t < nkt) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          frag pf;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pf[e] = from_f32<T>(sc[t][8 * u + e]);
-#pragma unroll
-          for (int dt = 0; dt < 2; ++dt) {
-            const T* vp = lds + VOFF + (32 * dt + lr) * VLD + k0 + 32 * t + 16 * u + 4 * g;
-            const b4 lo = *(const b4*)vp, hi = *(const b4*)(vp + 8);
-            frag vf;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              vf[e] = lo[e];
-              vf[e + 4] = hi[e];
-            }
-            Mfma<T>::mma(vf, pf, o[dt]);
+          for (int r = 0; r < 16; ++r) {
+            const int key = 32 * t + 8 * (r / 4) + 4 * g + (r % 4);
+            if (key >= len || (causal && key > query)) sc[t][r] = -INFINITY;
+            mx = fmaxf(mx, sc[t][r]);
           }
         }
       }
-    // register r of o[dt]: d = 32 dt + 8 (r / 4) + 4 g + r % 4 of query lr; staged in this
-    // wave's own Q rows (no other wave reads them; a wave's LDS accesses complete in order)
-    const float inv = 1.0f / sum;
-    T* st = lds + r0 * QLD;
+      mx = fmaxf(mx, __shfl_xor(mx, 32));  // finite: key 0 is always valid
+      float sum = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
+      for (int t = 0; t < NKT; ++t)
+        if (t < nkt) {
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        b4 vv;
+          for (int r = 0; r < 16; ++r) {
+            sc[t][r] = exp2f((sc[t][r] - mx) * scale_log2e);
+            sum += sc[t][r];
+          }
+        }
+      sum += __shfl_xor(sum, 32);
+      // C^T = V^T P^T; MFMA (t, u) takes P registers 8u .. 8u+7 of key tile t = keys
+      // 32 t + 16 u + {0..3, 8..11} + 4 g, against V^T rows hc + 32 dt + lr at those keys
+      f32x16 o[DT];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vv[e] = from_f32<T>(o[dt][4 * s4 + e] * inv);
-        *(b4*)(st + lr * QLD + 32 * dt + 8 * s4 + 4 * g) = vv;
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+#pragma unroll
+      for (int t = 0; t < NKT; ++t)
+        if (t < nkt) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            frag pf;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pf[e] = from_f32<T>(sc[t][8 * u + e]);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+              const T* vp = lds + VOFF + (hc + 32 * dt + lr) * VLD + k0 + 32 * t + 16 * u + 4 * g;
+              const b4 lo = *(const b4*)vp, hi = *(const b4*)(vp + 8);
+              frag vf;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                vf[e] = lo[e];
+                vf[e + 4] = hi[e];
+              }
+              Mfma<T>::mma(vf, pf, o[dt]);
+            }
+          }
+        }
+      // register r of o[dt]: d = 32 dt + 8 (r / 4) + 4 g + r % 4 of query lr; staged in this
+      // wave's own Q rows, this head's columns (no other wave reads them, this wave reads
+      // them no more; a wave's LDS accesses complete in order)
+      const float inv = 1.0f / sum;
+      T* st = lds + r0 * QLD + hc;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          b4 vv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vv[e] = from_f32<T>(o[dt][4 * s4 + e] * inv);
+          *(b4*)(st + lr * QLD + 32 * dt + 8 * s4 + 4 * g) = vv;
+        }
+      T* out = ctx + (size_t)(m0 + r0) * H + ((n0 / 192) * HPT + hh) * D;
+#pragma unroll
+      for (int p = 0; p < 32 * VPR / kWave; ++p) {
+        const int row = p * (kWave / VPR) + lane / VPR, c = (lane % VPR) * 8;
+        *(vec*)(out + (size_t)row * H + c) = *(const vec*)(st + row * QLD + c);
       }
-    const int H = N / 3;
-    T* out = ctx + (size_t)(m0 + r0) * H + (n0 / 192) * 64;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int row = 8 * p + lane / 8, c = (lane % 8) * 8;
-      *(vec*)(out + (size_t)row * H + c) = *(const vec*)(st + row * QLD + c);
     }
   }
 };
@@ -806,45 +819,54 @@ hipError_t launch_head_projection(ftx_dtype dt, int B, int S, int nh, int d, con
   return hipErrorInvalidValue;
 }
 
-bool qkv_attention_fits(ftx_dtype dt, int S, int d) {
-  return dt != FTX_FP32 && (S == 32 || S == 64 || S == 128 || S == 256) && d == 64;
+bool qkv_attention_fits(ftx_dtype dt, int S, int nh, int d) {
+  return dt != FTX_FP32 && (S == 32 || S == 64 || S == 128 || S == 256) &&
+         (d == 64 || (d == 32 && nh % 2 == 0));
 }
 
-template <typename T, int SEQ>
+template <typename T, int SEQ, int D>
 static hipError_t qkv_attention_t(int B, int nh, const void* x, const void* w_t, const void* bias,
                                   const int32_t* lens, int s_valid, int causal, void* ctx,
                                   hipStream_t s) {
-  const int M = SEQ * B, N = 3 * 64 * nh, K = 64 * nh;
+  const int M = SEQ * B, N = 3 * D * nh, K = D * nh;
   // log2(e) / sqrt(d), rounded once from double as the attention kernel does
-  const float scale_log2e = (float)(1.4426950408889634 / 8.0);
-  EpiQKVAttn<T, SEQ> epi{(T*)ctx, (const T*)bias, lens, M, N, s_valid, scale_log2e, causal};
+  const float scale_log2e = (float)(1.4426950408889634 / sqrt((double)D));
+  EpiQKVAttn<T, SEQ, D> epi{(T*)ctx, (const T*)bias, lens, M, N, s_valid, scale_log2e, causal};
   const int tiles = ((M + 255) / 256) * (N / 192);
-  gemm_kernel<T, 256, 192, 4, 2, EpiQKVAttn<T, SEQ>><<<tiles, 8 * kWave, 0, s>>>(
+  gemm_kernel<T, 256, 192, 4, 2, EpiQKVAttn<T, SEQ, D>><<<tiles, 8 * kWave, 0, s>>>(
       (const T*)x, (const T*)w_t, M, N, K, K, epi);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, int D>
 static hipError_t qkv_attention_s(int B, int S, int nh, const void* x, const void* w_t,
                                   const void* bias, const int32_t* lens, int s_valid, int causal,
                                   void* ctx, hipStream_t s) {
   switch (S) {
-    case 32: return qkv_attention_t<T, 32>(B, nh, x, w_t, bias, lens, s_valid, causal, ctx, s);
-    case 64: return qkv_attention_t<T, 64>(B, nh, x, w_t, bias, lens, s_valid, causal, ctx, s);
-    case 128: return qkv_attention_t<T, 128>(B, nh, x, w_t, bias, lens, s_valid, causal, ctx, s);
-    case 256: return qkv_attention_t<T, 256>(B, nh, x, w_t, bias, lens, s_valid, causal, ctx, s);
+    case 32: return qkv_attention_t<T, 32, D>(B, nh, x, w_t, bias, lens, s_valid, causal, ctx, s);
+    case 64: return qkv_attention_t<T, 64, D>(B, nh, x, w_t, bias, lens, s_valid, causal, ctx, s);
+    case 128: return qkv_attention_t<T, 128, D>(B, nh, x, w_t, bias, lens, s_valid, causal, ctx, s);
+    case 256: return qkv_attention_t<T, 256, D>(B, nh, x, w_t, bias, lens, s_valid, causal, ctx, s);
   }
   return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t qkv_attention_d(int B, int S, int nh, int d, const void* x, const void* w_t,
+                                  const void* bias, const int32_t* lens, int s_valid, int causal,
+                                  void* ctx, hipStream_t s) {
+  if (d == 64) return qkv_attention_s<T, 64>(B, S, nh, x, w_t, bias, lens, s_valid, causal, ctx, s);
+  return qkv_attention_s<T, 32>(B, S, nh, x, w_t, bias, lens, s_valid, causal, ctx, s);
 }
 
 hipError_t launch_qkv_attention(ftx_dtype dt, int B, int S, int nh, int d, const void* x,
                                 const void* w_qkv_t, const void* b_qkv, const int32_t* lens,
                                 int s_valid, void* ctx, hipStream_t s, bool causal) {
-  if (!qkv_attention_fits(dt, S, d) || B < 1 || nh < 1) return hipErrorInvalidValue;
+  if (!qkv_attention_fits(dt, S, nh, d) || B < 1 || nh < 1) return hipErrorInvalidValue;
   if (s_valid <= 0 || s_valid > S) s_valid = S;
   const int c = causal ? 1 : 0;
-  if (dt == FTX_FP16) return qkv_attention_s<f16>(B, S, nh, x, w_qkv_t, b_qkv, lens, s_valid, c, ctx, s);
-  return qkv_attention_s<bf16>(B, S, nh, x, w_qkv_t, b_qkv, lens, s_valid, c, ctx, s);
+  if (dt == FTX_FP16) return qkv_attention_d<f16>(B, S, nh, d, x, w_qkv_t, b_qkv, lens, s_valid, c, ctx, s);
+  return qkv_attention_d<bf16>(B, S, nh, d, x, w_qkv_t, b_qkv, lens, s_valid, c, ctx, s);
 }
 
 hipError_t launch_qkv_projection(ftx_dtype dt, int B, int S, int nh, int d, const void* x,

@@ -29,11 +29,16 @@ hipError_t launch_head_projection(ftx_dtype dt, int B, int S, int nh, int d, con
                                   float* ws = nullptr, size_t ws_elems = 0);
 
 // Whether the fused projection + attention below takes this shape: a 16-bit dtype, S (the
-// padded length) 32, 64, 128 or 256, d = 64.
-bool qkv_attention_fits(ftx_dtype dt, int S, int d);
+// padded length) 32, 64, 128 or 256, d = 64, or d = 32 with an even head count (a 192-column
+// tile holds Q, K and V of 64 / d whole heads).
+bool qkv_attention_fits(ftx_dtype dt, int S, int nh, int d);
+
+// Tiles of the fused projection + attention for T rows of hidden size H: 256 rows by 192
+// columns.
+inline long fused_attention_tiles(long T, long H) { return (T + 255) / 256 * (3 * H / 192); }
 
 // Q/K/V projection of x [B*S][H] with the attention of every (sequence, head) in the same
-// kernel: w_qkv_t [3H][H] and b_qkv [3H] ordered per head ([Q_h | K_h | V_h], 192 rows each),
+// kernel: w_qkv_t [3H][H] and b_qkv [3H] ordered per head ([Q_h | K_h | V_h], 3d rows each),
 // ctx [B*S][H] as launch_attention writes it.  Keys at or past min(lens[b], s_valid) are
 // masked (s_valid 1..S, default S; lens NULL: s_valid); causal: query i also ignores keys
 // j > i.  hipErrorInvalidValue when the shape does not fit.
