@@ -9,7 +9,8 @@
 //
 //   S^T = K Q^T       v_mfma 32x32 tiles, keys on rows, the wave's 32 queries on columns;
 //                     a lane then holds 16 of the 32 keys of one query per tile;
-//   mask, scale       keys j >= len_b get -inf; scores scaled by 1/sqrt(d) inside exp2;
+//   mask, scale       keys j >= len_b get -inf (only tiles reaching len_b are masked key by
+//                     key); scores scaled by 1/sqrt(d) inside the hardware exp2;
 //   softmax           row max and sum: the lane's own values, then one cross-lane step
 //                     (lane ^ 32) -- the wave64 form of the shuffle row reduction; fp32;
 //   C^T = V^T P^T     the probabilities stay in registers and are fed, converted to the
@@ -125,25 +126,32 @@ __global__ __launch_bounds__(256) void attention_global_kernel(const T* __restri
         for (int f = 0; f < NQF; ++f) MF::mma(*(const frag*)(kr + f * KF), qf[f], sc[t]);
       }
     }
-    // mask and chunk maximum (key of register r: tile*32 + 8*(r/4) + 4*g + r%4)
+    // mask and chunk maximum (key of register r: tile*32 + 8*(r/4) + 4*g + r%4); only a key
+    // tile that reaches the valid length or (causal) the query block's diagonal needs the
+    // per-key mask
     float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < CH; ++t)
+    for (int t = 0; t < CH; ++t) {
+      const int kb = (c0 + t) * 32;
+      if (kb + 32 > len || (causal && kb + 31 > qb * 32)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = (c0 + t) * 32 + 8 * (r / 4) + 4 * g + (r % 4);
-        if (key >= len || (causal && key > query)) sc[t][r] = -INFINITY;
-        mx = fmaxf(mx, sc[t][r]);
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + 8 * (r / 4) + 4 * g + (r % 4);
+          if (key >= len || (causal && key > query)) sc[t][r] = -INFINITY;
+        }
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);  // finite: the first chunk holds key 0 < len
-    const float alpha = exp2f((m_run - m_new) * scale_log2e);
+    const float alpha = exp2_flush((m_run - m_new) * scale_log2e);
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < CH; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f((sc[t][r] - m_new) * scale_log2e);
+        const float p = exp2_flush((sc[t][r] - m_new) * scale_log2e);
         sc[t][r] = p;
         psum += p;
       }
@@ -332,26 +340,33 @@ __global__ __launch_bounds__((AttnCfg<T, D, SMAX>::NW * kWave)) void attention_k
           for (int f = 0; f < NQF; ++f) MF::mma(*(const frag*)(kr + f * KF), qf[f], sc[t]);
         }
       }
-      // mask and chunk maximum (key of register r: tile*32 + 8*(r/4) + 4*g + r%4)
+      // mask and chunk maximum (key of register r: tile*32 + 8*(r/4) + 4*g + r%4); only a
+      // key tile that reaches the valid length or (causal) the query block's diagonal needs
+      // the per-key mask
       float mx = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < CH; ++t)
+      for (int t = 0; t < CH; ++t) {
+        const int kb = (c0 + t) * 32;
+        if (kb + 32 > len || (causal && kb + 31 > qb * 32)) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = (c0 + t) * 32 + 8 * (r / 4) + 4 * g + (r % 4);
-          if (key >= len || (causal && key > query)) sc[t][r] = -INFINITY;
-          mx = fmaxf(mx, sc[t][r]);
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb + 8 * (r / 4) + 4 * g + (r % 4);
+            if (key >= len || (causal && key > query)) sc[t][r] = -INFINITY;
+          }
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       // finite: every chunk's first key is below len and (causal) not after the query
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f((m_run - m_new) * scale_log2e);
+      const float alpha = exp2_flush((m_run - m_new) * scale_log2e);
       float psum = 0.f;
 #pragma unroll
       for (int t = 0; t < CH; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2f((sc[t][r] - m_new) * scale_log2e);
+          const float p = exp2_flush((sc[t][r] - m_new) * scale_log2e);
           sc[t][r] = p;
           psum += p;
         }
@@ -494,17 +509,20 @@ __global__ __launch_bounds__(256) void attention_s32_kernel(const T* __restrict_
 #pragma unroll
   for (int f = 0; f < NQF; ++f) MF::mma(kf[f], qf[f], sc);
   float mx = -INFINITY;
+  if (len < 32 || causal) {  // the per-key mask, only when some key is masked
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int key = 8 * (r / 4) + 4 * g + (r % 4);
-    if (key >= len || (causal && key > lr)) sc[r] = -INFINITY;
-    mx = fmaxf(mx, sc[r]);
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r / 4) + 4 * g + (r % 4);
+      if (key >= len || (causal && key > lr)) sc[r] = -INFINITY;
+    }
   }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
   mx = fmaxf(mx, __shfl_xor(mx, 32));  // finite: key 0 is always valid
   float sum = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    sc[r] = exp2f((sc[r] - mx) * scale_log2e);
+    sc[r] = exp2_flush((sc[r] - mx) * scale_log2e);
     sum += sc[r];
   }
   sum += __shfl_xor(sum, 32);

@@ -45,6 +45,11 @@ template <typename T> __device__ __forceinline__ T from_f32(float v) { return st
 // pow): one multiply-add, two multiplies, one add, and the hardware base-2 exponential and
 // reciprocal per element.  Large negative u gives 2^z -> inf, a reciprocal of 0 and a result
 // of -0; large positive u gives 2^z -> 0 and the result u.
+// 2^x on the hardware exp2 alone, for softmax probabilities 2^((s - max) * scale): results
+// below 2^-126 (probabilities that small against the row maximum) flush to 0, where the
+// library exp2f wraps the same instruction in a range fix-up (compare, select, ldexp).
+__device__ __forceinline__ float exp2_flush(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float gelu_tanh(float u) {
   constexpr float c1 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
   constexpr float c3 = c1 * 0.044715f;

@@ -396,12 +396,17 @@ template <typename T, int SEQ, int D> struct EpiQKVAttn {
           const T* krow = lds + KOFF + (k0 + 32 * t + lr) * QLD + hc + 8 * g;
 #pragma unroll
           for (int f = 0; f < NQF; ++f) Mfma<T>::mma(*(const frag*)(krow + 16 * f), qf[f], sc[t]);
+          // the per-key mask, only on a tile that reaches the valid length or (causal) the
+          // query block's diagonal
+          if (32 * t + 32 > len || (causal && 32 * t + 31 > qb * 32)) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = 32 * t + 8 * (r / 4) + 4 * g + (r % 4);
-            if (key >= len || (causal && key > query)) sc[t][r] = -INFINITY;
-            mx = fmaxf(mx, sc[t][r]);
+            for (int r = 0; r < 16; ++r) {
+              const int key = 32 * t + 8 * (r / 4) + 4 * g + (r % 4);
+              if (key >= len || (causal && key > query)) sc[t][r] = -INFINITY;
+            }
           }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
         }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));  // finite: key 0 is always valid
@@ -411,7 +416,7 @@ template <typename T, int SEQ, int D> struct EpiQKVAttn {
         if (t < nkt) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            sc[t][r] = exp2f((sc[t][r] - mx) * scale_log2e);
+            sc[t][r] = exp2_flush((sc[t][r] - mx) * scale_log2e);
             sum += sc[t][r];
           }
         }
