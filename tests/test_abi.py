@@ -114,6 +114,7 @@ def test_step_argument_checks(lib):
     assert lib.ftx_step_qkv_attention(2, 1, 32, 3, 32, 256, 512, 768, None, 0, 1024, None) == U  # odd n, d 32
     assert lib.ftx_step_qkv_attention(1, 1, 32, 2, 64, None, 512, 768, None, 0, 1024, None) == E
     assert lib.ftx_step_qkv_attention(1, 1, 32, 2, 64, 256, 512, 776, None, 1, 1024, None) == E
+    assert lib.ftx_step_qkv_attention(1, 1, 32, 2, 64, 4096, 1 << 20, 1 << 21, None, 0, 4096, None) == E  # ctx = x
     # layernorm: cols not a multiple of 4, above the limit, misaligned
     assert lib.ftx_step_bias_residual_layernorm(1, 4, 6, 256, 512, 768, 1024, 2048, 4096, None) == E
     assert lib.ftx_step_bias_residual_layernorm(1, 4, 8192, 256, 512, 768, 1024, 2048, 4096, None) == ftx.FTX_ERR_UNSUPPORTED

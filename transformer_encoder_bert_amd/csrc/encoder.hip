@@ -643,6 +643,10 @@ ftx_status ftx_step_qkv_attention(ftx_dtype dtype, int B, int S, int n, int d, c
   if (!x || !w_qkv_t || !b_qkv || !ctx) return fail(FTX_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned16(x) || !aligned16(w_qkv_t) || !aligned16(b_qkv) || !aligned16(ctx))
     return fail(FTX_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  // other tiles still read rows of x while a tile writes its context rows
+  const size_t es = dtype_size(dtype), H = (size_t)n * d, rows = (size_t)B * S;
+  if (overlap(x, rows * H * es, ctx, rows * H * es) || overlap(w_qkv_t, 3 * H * H * es, ctx, rows * H * es))
+    return fail(FTX_ERR_INVALID_ARG, "ctx overlaps an input");
   if (!all_device({x, w_qkv_t, b_qkv, seq_lens, ctx}))
     return fail(FTX_ERR_INVALID_ARG, "pointers must be device memory");
   hipError_t err = launch_qkv_attention(dtype, B, S, n, d, x, w_qkv_t, b_qkv, seq_lens, S, ctx,
