@@ -94,11 +94,17 @@ KERNEL_SOURCES = ("transformer_encoder_bert_amd/csrc/gemm.hip",
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: // comments and blank lines are dropped, so editing a
+    comment does not mark a measurement stale."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            for line in f:
+                code = re.sub(r"//.*$", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

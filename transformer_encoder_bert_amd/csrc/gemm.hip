@@ -13,7 +13,9 @@
 //   while the current one is multiplied; waves WM x WN each own a (BM/WM) x (BN/WN)
 //   sub-tile of 32x32 accumulators;
 //   the bias, the tanh GELU and the Q/K/V head split are applied in the epilogue on the
-//   fp32 accumulators, so U never makes a round trip through memory before its GELU.
+//   fp32 accumulators, so U never makes a round trip through memory before its GELU; for
+//   sequences of up to 256 tokens the Q/K/V projection can also run the attention of its
+//   tile in the epilogue (EpiQKVAttn), so Q, K and V never reach memory at all.
 //
 // MFMA operand layout used (32x32 output tile, 64 lanes, g = lane / 32):
 //   first operand: lane holds row (lane % 32), VEC consecutive K values at K-offset g * VEC;
