@@ -491,8 +491,8 @@ def main():
     if args.workload is None:
         args.workload = WORKLOAD_DEFAULT
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(f"bench.py runs on one GPU only: this encoder forward shards by data parallelism "
-              f"with no collective, and no multi-GPU run is part of this build (asked: --gpus {args.gpus})",
+        print(f"bench.py measures one GPU: the encoder forward shards by data parallelism with no "
+              f"collective, so the one-GPU figure times each GPU's share (asked: --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
 

@@ -57,7 +57,7 @@ typedef enum { FTX_FP32 = 0, FTX_FP16 = 1, FTX_BF16 = 2 } ftx_dtype;
 typedef enum {
   FTX_OK = 0,
   FTX_ERR_INVALID_ARG = 1,   /* NULL / misaligned / aliased pointer, value out of range */
-  FTX_ERR_UNSUPPORTED = 2,   /* a valid value this build does not implement */
+  FTX_ERR_UNSUPPORTED = 2,   /* a valid value this library does not implement */
   FTX_ERR_OUT_OF_MEMORY = 3, /* device allocation failed */
   FTX_ERR_DEVICE = 4,        /* a HIP runtime call failed (no device, launch failure...) */
   FTX_ERR_NOT_READY = 5      /* forward called before every layer's weights were set */

@@ -79,7 +79,7 @@ hipError_t launch_bias_gelu(ftx_dtype dt, int rows, int cols, const void* u, con
 hipError_t launch_transpose(ftx_dtype dt, int rows, int cols, const void* in, void* out,
                             hipStream_t s);
 
-// Largest LayerNorm row this build handles (4-element vectors, <= 16 per lane of a wave).
+// Largest LayerNorm row the library handles (4-element vectors, <= 16 per lane of a wave).
 constexpr int kMaxLayerNormCols = 4096;
 // largest inner dimension K of a projection: a 256-row panel of K elements stays below 2^31
 // bytes, the range of the buffer resources the GEMM loads through
