@@ -115,15 +115,18 @@ def classify_dispatches(names):
     steps, prev = [], None
     for n in names:
         st = None
-        if "gemm_kernel" in n and "EpiQKVAttn" in n:
+        # the projections run the two-buffer K loop (gemm_kernel) or, for long K, the
+        # ping-pong one (gemm_pp_kernel)
+        gemm = "gemm_kernel" in n or "gemm_pp_kernel" in n
+        if gemm and "EpiQKVAttn" in n:
             st = "qkv_attention"
-        elif "gemm_kernel" in n and "EpiQKV" in n:
+        elif gemm and "EpiQKV" in n:
             st = "qkv_gemm"
         elif "attention" in n and "ftx" in n:
             st = "attention"
         elif "layernorm_kernel" in n:
             st = "ln1" if prev in ("attn_out_gemm", "attention") else "ln2"
-        elif "gemm_kernel" in n and "EpiLinear" in n:
+        elif gemm and "EpiLinear" in n:
             m = re.search(r"EpiLinearI\w+?Lb([01])E", n)
             gelu = m is not None and m.group(1) == "1"
             if gelu or prev == "ln1":

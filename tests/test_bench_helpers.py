@@ -1,0 +1,32 @@
+"""Host logic of bench.py: the step class of each kernel dispatch of a forward, which the
+rocprofv3 summaries and the bench's traffic lookup are keyed on."""
+from __future__ import annotations
+
+import bench
+
+# kernel symbols of one BERT-base fp16 layer as the library launches them: the Q/K/V
+# projection with the attention in its epilogue, the attention-output projection, LN1,
+# FFN-in with GELU, FFN-out on the ping-pong K loop, LN2
+QKV_ATTN = "_ZN3ftx11gemm_kernelIDF16_Li256ELi192ELi4ELi2ENS_10EpiQKVAttnIDF16_Li32ELi64EEEEEvPKT_S5_iiiiT4_"
+LINEAR = "_ZN3ftx11gemm_kernelIDF16_Li256ELi192ELi4ELi2ENS_9EpiLinearIDF16_Lb0EDF16_EEEEvPKT_S5_iiiiT4_"
+LINEAR_PP = "_ZN3ftx14gemm_pp_kernelIDF16_Li256ELi192ENS_9EpiLinearIDF16_Lb0EDF16_EEEEvPKT_S5_iiiiT2_"
+GELU = "_ZN3ftx11gemm_kernelIDF16_Li256ELi256ELi4ELi2ENS_9EpiLinearIDF16_Lb1EDF16_EEEEvPKT_S5_iiiiT4_"
+LN = "_ZN3ftx16layernorm_kernelIDF16_DF16_DF16_Li8ELi32ELi3ELb1EEEvPKT0_PKT1_PKT_S9_S9_PS7_Pfii"
+QKV = "_ZN3ftx11gemm_kernelIDF16_Li256ELi192ELi4ELi2ENS_6EpiQKVIDF16_EEEEvPKT_S5_iiiiT4_"
+ATTN = "_ZN3ftx16attention_kernelIDF16_Li32ELi64ELi1EEEvPKT_S3_S3_PKiPS1_iiiif"
+
+
+def test_fused_layer_dispatches():
+    layer = [QKV_ATTN, LINEAR, LN, GELU, LINEAR_PP, LN]
+    assert bench.classify_dispatches(layer * 2) == [
+        "qkv_attention", "attn_out_gemm", "ln1", "ffn1_gemm", "ffn2_gemm", "ln2"] * 2
+
+
+def test_separate_attention_dispatches():
+    layer = [QKV, ATTN, LINEAR, LN, GELU, LINEAR, LN]
+    assert bench.classify_dispatches(layer) == [
+        "qkv_gemm", "attention", "attn_out_gemm", "ln1", "ffn1_gemm", "ffn2_gemm", "ln2"]
+
+
+def test_unknown_kernels_are_not_classified():
+    assert bench.classify_dispatches(["copy_kernel", LN]) == [None, "ln2"]
