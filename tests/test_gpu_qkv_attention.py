@@ -70,6 +70,9 @@ CASES = [
     (9, 32, 4, 32, "random"),       # d = 32: two heads per tile (the pruned model's 4 x 32)
     (3, 32, 2, 32, None),
     (3, 128, 6, 32, [128, 50, 1]),
+    # hidden size 1024 (16 K slabs): the ping-pong K loop
+    (3, 128, 16, 64, [128, 70, 1]),  # BERT-large heads
+    (9, 32, 32, 32, "random"),
 ]
 
 
@@ -92,7 +95,7 @@ def test_step_matches_oracle(dtype, B, S, n, d, lens):
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("B,S,n,d", [(2, 32, 2, 64), (3, 64, 2, 64), (2, 128, 1, 64), (1, 256, 2, 64),
-                                     (2, 64, 2, 32)])
+                                     (2, 64, 2, 32), (2, 128, 16, 64)])
 def test_step_causal_matches_oracle(dtype, B, S, n, d):
     """The decoder's self-attention: query i sees keys j <= i (no length vector)."""
     x, ws, bs = exact_case(B, S, n, 3000 + B + S + n + d, d)
@@ -172,6 +175,7 @@ STACK = [
     (2, 230, 2, 64, "fp16", None),        # padded to 256
     (9, 32, 4, 32, "fp16", (1, 32)),      # the pruned model's 4 x 32
     (3, 64, 4, 32, "bf16", None),
+    (3, 128, 16, 64, "bf16", (64, 128)),  # BERT-large heads: ping-pong K loop
 ]
 
 

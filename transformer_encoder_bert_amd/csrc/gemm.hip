@@ -899,10 +899,10 @@ size_t gemm_splitk_workspace(ftx_dtype dt, int M, int N, int K) {
   return p.splits > 1 ? (size_t)p.splits * M * N : 0;
 }
 
-// The ping-pong K loop pays off once a tile runs many slabs: measured on the 16384-row
-// projections, 7% faster at K = 3072 (48 slabs) and 9% at K = 24576, but 0-4% slower at
-// K = 768 (12 slabs), where its idle first and last phases weigh more.
-constexpr int kPingPongMinSlabs = 24;
+// The ping-pong K loop pays off once a tile runs enough slabs: measured at 16384-32768 rows,
+// 0-4% faster at K = 1024 (16 slabs), 7-15% at K = 3072-4096 and 9% at K = 24576, but up
+// to 4% slower at K = 768 (12 slabs), where its idle first and last phases weigh more.
+constexpr int kPingPongMinSlabs = 16;
 
 template <typename T, int BM, int BN, int WM, int WN, typename Epi>
 static hipError_t gemm_launch_cfg(int M, int N, int K, const void* a, const void* w_t, Epi epi,
@@ -1012,8 +1012,13 @@ static hipError_t qkv_attention_t(int B, int nh, const void* x, const void* w_t,
   const float scale_log2e = (float)(1.4426950408889634 / sqrt((double)D));
   EpiQKVAttn<T, SEQ, D> epi{(T*)ctx, (const T*)bias, lens, M, N, s_valid, scale_log2e, causal};
   const int tiles = ((M + 255) / 256) * (N / 192);
-  gemm_kernel<T, 256, 192, 4, 2, EpiQKVAttn<T, SEQ, D>><<<tiles, 8 * kWave, 0, s>>>(
-      (const T*)x, (const T*)w_t, M, N, K, K, epi);
+  constexpr int BK = GemmCfg<T, 256, 192, 4, 2>::BK;
+  if (K % BK == 0 && K / BK >= kPingPongMinSlabs)
+    gemm_pp_kernel<T, 256, 192, EpiQKVAttn<T, SEQ, D>><<<tiles, 8 * kWave, 0, s>>>(
+        (const T*)x, (const T*)w_t, M, N, K, K, epi);
+  else
+    gemm_kernel<T, 256, 192, 4, 2, EpiQKVAttn<T, SEQ, D>><<<tiles, 8 * kWave, 0, s>>>(
+        (const T*)x, (const T*)w_t, M, N, K, K, epi);
   return hipGetLastError();
 }
 
