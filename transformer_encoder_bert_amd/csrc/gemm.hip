@@ -541,7 +541,9 @@ __device__ __forceinline__ void gemm_epilogue(const Epi& epi, char* smem, int m0
 // K range of this block: [blockIdx.y * kchunk, min(K, (blockIdx.y + 1) * kchunk)); kchunk is
 // K (one range) or, under split-K, a multiple of the slab depth.  K * BM * sizeof(T) and
 // K * BN * sizeof(T) stay below 2^31 (callers bound K).
-template <typename T, int BM, int BN, int WM, int WN, typename Epi>
+// NST LDS buffers (slab stages): slab kt + NST - 1 is loaded while slab kt is multiplied, so
+// NST - 1 slabs are in flight; small tiles with a long K chain take more than two.
+template <typename T, int BM, int BN, int WM, int WN, typename Epi, int NST = 2>
 __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restrict__ A,
                                                                const T* __restrict__ Bt, int M,
                                                                int N, int K, int kchunk, Epi epi) {
@@ -549,7 +551,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
   typedef typename C::MF MF;
   typedef typename MF::frag frag;
   constexpr int TM = C::TM, TN = C::TN, AQ = C::AQ, BQ = C::BQ, ROWB = C::ROWB;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
+  static_assert(NST >= 2 && NST <= 8, "slab stages");
+  __shared__ __attribute__((aligned(1024))) char smem[NST * C::STAGE];
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
@@ -630,26 +633,32 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
     for (int j = 0; j < TN; ++j) fb[set][j] = *(const frag*)(Bs + j * 32 * ROWB);
   };
 
-  // Double-buffered slabs: at the top of step kt every wave waits for its own loads of slab
-  // kt, and the barrier makes all of them visible and tells that every wave is done with
-  // the other buffer, which then receives slab kt + 1 while slab kt is multiplied.  Inside
-  // a slab the fragments of sub-step s + 1 are read before the MFMAs of sub-step s; the
-  // scheduling barriers keep the compiler from regrouping them, so LDS latency hides
-  // behind the MFMAs.
-  if (nk > 0) load_slab(0, 0);
-  for (int k0 = 0; k0 < nk; k0 += 2) {
+  // Slab kt sits in buffer kt % NST.  At the top of step kt every wave waits for its own
+  // loads of slab kt (the loads of the NST - 2 later slabs may stay in flight: every wave
+  // issues exactly AQ + BQ loads per slab, and loads complete in order), and the barrier
+  // makes all of them visible and tells that every wave is done with buffer (kt - 1) % NST,
+  // which then receives slab kt + NST - 1 while slab kt is multiplied.  Inside a slab the
+  // fragments of sub-step s + 1 are read before the MFMAs of sub-step s; the scheduling
+  // barriers keep the compiler from regrouping them, so LDS latency hides behind the MFMAs.
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+  for (int p = 0; p < NST - 1; ++p)
+    if (p < nk) load_slab(p, p);
+  for (int k0 = 0; k0 < nk; k0 += NST) {
+#pragma unroll
+    for (int u = 0; u < NST; ++u) {
       const int kt = k0 + u;
       if (kt < nk) {
-        wait_vmcnt<0>();
+        if (kt + NST - 2 < nk)
+          wait_vmcnt<(NST - 2) * (AQ + BQ)>();
+        else
+          wait_vmcnt<0>();
         workgroup_barrier();
         if (kt == nk - 1 && kn - kt * C::BK < C::BK) {
           zero_k_tail(u, kn - kt * C::BK);
           __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's zero stores done
           workgroup_barrier();
         }
-        if (kt + 1 < nk) load_slab(kt + 1, u ^ 1);
+        if (kt + NST - 1 < nk) load_slab(kt + NST - 1, (u + NST - 1) % NST);
         read_frags(u, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -904,13 +913,35 @@ size_t gemm_splitk_workspace(ftx_dtype dt, int M, int N, int K) {
 // to 4% slower at K = 768 (12 slabs), where its idle first and last phases weigh more.
 constexpr int kPingPongMinSlabs = 16;
 
+// A 64x64 tile multiplies 64 x 64 x 64 per slab, far less than the latency of the slab's
+// loads: with 24 slabs or more per block it keeps two slabs in flight (three LDS stages,
+// 48 KB).  Measured on the BERT-base FFN-out projection at batch 64 (2048 x 768 x 3072):
+// 24.8 -> 20.6 us; at 12 slabs (the attention-output projection) the third stage costs
+// 4% instead.
+constexpr int kSmallTileDeepSlabs = 24;
+
+template <typename T, int BM, int BN, int WM, int WN, typename Epi>
+static void gemm_kernel_launch(dim3 grid, int kchunk, int M, int N, int K, const void* a,
+                               const void* w_t, Epi epi, hipStream_t s) {
+  constexpr int BK = GemmCfg<T, BM, BN, WM, WN>::BK;
+  if constexpr (BM == 64 && BN == 64) {
+    if ((kchunk + BK - 1) / BK >= kSmallTileDeepSlabs) {
+      gemm_kernel<T, BM, BN, WM, WN, Epi, 3><<<grid, WM * WN * kWave, 0, s>>>(
+          (const T*)a, (const T*)w_t, M, N, K, kchunk, epi);
+      return;
+    }
+  }
+  gemm_kernel<T, BM, BN, WM, WN, Epi><<<grid, WM * WN * kWave, 0, s>>>(
+      (const T*)a, (const T*)w_t, M, N, K, kchunk, epi);
+}
+
 template <typename T, int BM, int BN, int WM, int WN, typename Epi>
 static hipError_t gemm_launch_cfg(int M, int N, int K, const void* a, const void* w_t, Epi epi,
                                   const GemmPlan& plan, float* ws, hipStream_t s) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (plan.splits > 1) {
-    gemm_kernel<T, BM, BN, WM, WN, EpiPartial><<<dim3(tiles, plan.splits), WM * WN * kWave, 0, s>>>(
-        (const T*)a, (const T*)w_t, M, N, K, plan.kchunk, EpiPartial{ws, M, N});
+    gemm_kernel_launch<T, BM, BN, WM, WN, EpiPartial>(dim3(tiles, plan.splits), plan.kchunk, M, N,
+                                                      K, a, w_t, EpiPartial{ws, M, N}, s);
     const int64_t threads = (int64_t)M * (N / 4);
     splitk_reduce_kernel<Epi><<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(ws, plan.splits, M, N, epi);
     return hipGetLastError();
@@ -923,8 +954,7 @@ static hipError_t gemm_launch_cfg(int M, int N, int K, const void* a, const void
       return hipGetLastError();
     }
   }
-  gemm_kernel<T, BM, BN, WM, WN, Epi><<<tiles, WM * WN * kWave, 0, s>>>(
-      (const T*)a, (const T*)w_t, M, N, K, K, epi);
+  gemm_kernel_launch<T, BM, BN, WM, WN, Epi>(dim3(tiles), K, M, N, K, a, w_t, epi, s);
   return hipGetLastError();
 }
 
