@@ -171,6 +171,120 @@ hipError_t launch_bias_residual_layernorm_f32res(ftx_dtype dt, int rows, int col
   return hipErrorInvalidValue;
 }
 
+// Sum over the 256 threads of a workgroup in a fixed order (deterministic); `red` holds
+// four floats of LDS.
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = group_sum<kWave>(v);
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  const float t = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();  // every thread has read red before it is written again
+  return t;
+}
+
+// bias + residual + LayerNorm of a projection that was split over K (the small-batch path):
+// the branch a is the sum of the fp32 partials in split order -- the split-K reduction's
+// sum -- rounded to TA as the projection would have stored it, so one launch replaces the
+// reduction and the LayerNorm.  One workgroup of 256 threads per row, 4 columns per thread
+// and group (cols <= 4096, a multiple of 4): the partial reads of a row spread over a
+// whole CU.  Statistics as in layernorm_kernel (fp32, mean, then centred sum of squares).
+template <typename T, typename TX, typename TA>
+__global__ __launch_bounds__(256) void splitk_layernorm_kernel(const TX* __restrict__ x,
+                                                               const float* __restrict__ p,
+                                                               int splits,
+                                                               const T* __restrict__ bias,
+                                                               const T* __restrict__ gamma,
+                                                               const T* __restrict__ beta,
+                                                               T* y, float* yf, int rows,
+                                                               int cols) {
+  constexpr int G = kMaxLayerNormCols / (4 * 256);
+  typedef typename VecT<T, 4>::type t4;
+  typedef typename VecT<TX, 4>::type x4;
+  __shared__ float red[4];
+  const int row = blockIdx.x;
+  const size_t base = (size_t)row * cols, mn = (size_t)rows * cols;
+  float z[G][4];
+  float sum = 0.f;
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    const int c = 4 * (threadIdx.x + 256 * gi);
+    if (c < cols) {
+      f32x4 acc = *(const f32x4*)(p + base + c);
+      for (int k = 1; k < splits; ++k) acc += *(const f32x4*)(p + k * mn + base + c);
+      const x4 xv = *(const x4*)(x + base + c);
+      const t4 bv = *(const t4*)(bias + c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // the reduction's store: no projection bias (the LayerNorm adds it), rounded to TA
+        const float a = to_f32(from_f32<TA>(acc[e] + 0.0f));
+        z[gi][e] = to_f32(xv[e]) + a + to_f32(bv[e]);
+        sum += z[gi][e];
+      }
+    }
+  }
+  const float inv_n = 1.0f / (float)cols;
+  const float mean = block_sum256(sum, red) * inv_n;
+  float sq = 0.f;
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi)
+    if (4 * (threadIdx.x + 256 * gi) < cols)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float d = z[gi][e] - mean;
+        sq += d * d;
+      }
+  const float rs = rsqrtf(block_sum256(sq, red) * inv_n + FTX_LN_EPSILON);
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    const int c = 4 * (threadIdx.x + 256 * gi);
+    if (c < cols) {
+      const t4 gv = *(const t4*)(gamma + c), btv = *(const t4*)(beta + c);
+      f32x4 of;
+      t4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        of[e] = to_f32(gv[e]) * ((z[gi][e] - mean) * rs) + to_f32(btv[e]);
+        o[e] = from_f32<T>(of[e]);
+      }
+      *(t4*)(y + base + c) = o;
+      if (yf) *(f32x4*)(yf + base + c) = of;
+    }
+  }
+}
+
+template <typename T, typename TX, typename TA>
+static hipError_t splitk_ln_launch(int rows, int cols, const void* x, const float* p, int splits,
+                                   const void* bias, const void* gamma, const void* beta,
+                                   void* y, float* yf, hipStream_t s) {
+  splitk_layernorm_kernel<T, TX, TA><<<rows, 256, 0, s>>>(
+      (const TX*)x, p, splits, (const T*)bias, (const T*)gamma, (const T*)beta, (T*)y, yf, rows,
+      cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_bias_residual_layernorm(ftx_dtype dt, int rows, int cols,
+                                                 const void* x, bool x_f32, const float* p,
+                                                 int splits, bool a_f32, const void* bias,
+                                                 const void* gamma, const void* beta, void* y,
+                                                 float* yf, hipStream_t s) {
+  if (rows < 1 || cols < 4 || cols % 4 || cols > kMaxLayerNormCols || splits < 1)
+    return hipErrorInvalidValue;
+  if (x_f32 && !a_f32) return hipErrorInvalidValue;  // an fp32 residual comes with an fp32 branch
+  switch (dt) {
+    case FTX_FP32:
+      return splitk_ln_launch<float, float, float>(rows, cols, x, p, splits, bias, gamma, beta, y, yf, s);
+    case FTX_FP16:
+      if (x_f32) return splitk_ln_launch<f16, float, float>(rows, cols, x, p, splits, bias, gamma, beta, y, yf, s);
+      if (a_f32) return splitk_ln_launch<f16, f16, float>(rows, cols, x, p, splits, bias, gamma, beta, y, yf, s);
+      return splitk_ln_launch<f16, f16, f16>(rows, cols, x, p, splits, bias, gamma, beta, y, yf, s);
+    case FTX_BF16:
+      if (x_f32) return splitk_ln_launch<bf16, float, float>(rows, cols, x, p, splits, bias, gamma, beta, y, yf, s);
+      if (a_f32) return splitk_ln_launch<bf16, bf16, float>(rows, cols, x, p, splits, bias, gamma, beta, y, yf, s);
+      return splitk_ln_launch<bf16, bf16, bf16>(rows, cols, x, p, splits, bias, gamma, beta, y, yf, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 // ------------------------------------------------------------------------------------
 // bias + GELU over [rows][cols], 16-byte vectors, grid-stride.
 template <typename T>

@@ -206,17 +206,32 @@ ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq
       });
       if (st != FTX_OK) return st;
     }
-    st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
-      return launch_linear(dt, T, H, H, e->ctx, w.w_o_t, nullptr, false, e->abuf, s, e->y1f != nullptr,
-                           e->splitk, e->splitk_elems);
-    });
-    if (st != FTX_OK) return st;
-    st = run_step(e, FTX_STEP_LN1, s, [&] {
-      if (e->y1f)
-        return launch_bias_residual_layernorm_f32res(dt, T, H, x, false, (const float*)e->abuf, w.b_o, w.ln1_g,
-                                                     w.ln1_b, e->y1, e->y1f, s);
-      return launch_bias_residual_layernorm(dt, T, H, x, e->abuf, w.b_o, w.ln1_g, w.ln1_b, e->y1, s);
-    });
+    // A projection that splits K (small batches) leaves its fp32 partials to the LayerNorm
+    // that follows it, which sums them itself: one launch instead of reduction + LayerNorm.
+    const int o_splits = linear_splits(dt, T, H, H, e->splitk_elems);
+    if (o_splits > 1) {
+      st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
+        return launch_linear_partials(dt, T, H, H, e->ctx, w.w_o_t, e->splitk, e->splitk_elems, s);
+      });
+      if (st != FTX_OK) return st;
+      st = run_step(e, FTX_STEP_LN1, s, [&] {
+        return launch_splitk_bias_residual_layernorm(dt, T, H, x, false, e->splitk, o_splits,
+                                                     e->y1f != nullptr, w.b_o, w.ln1_g, w.ln1_b,
+                                                     e->y1, e->y1f, s);
+      });
+    } else {
+      st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
+        return launch_linear(dt, T, H, H, e->ctx, w.w_o_t, nullptr, false, e->abuf, s,
+                             e->y1f != nullptr, e->splitk, e->splitk_elems);
+      });
+      if (st != FTX_OK) return st;
+      st = run_step(e, FTX_STEP_LN1, s, [&] {
+        if (e->y1f)
+          return launch_bias_residual_layernorm_f32res(dt, T, H, x, false, (const float*)e->abuf, w.b_o,
+                                                       w.ln1_g, w.ln1_b, e->y1, e->y1f, s);
+        return launch_bias_residual_layernorm(dt, T, H, x, e->abuf, w.b_o, w.ln1_g, w.ln1_b, e->y1, s);
+      });
+    }
     if (st != FTX_OK) return st;
     if (e->fused) {
       st = run_step(e, FTX_STEP_FFN1_GEMM, s, [&] {
@@ -234,17 +249,31 @@ ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq
       });
     }
     if (st != FTX_OK) return st;
-    st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
-      return launch_linear(dt, T, H, F, e->u, w.w2_t, nullptr, false, e->abuf, s, e->y1f != nullptr,
-                           e->splitk, e->splitk_elems);
-    });
-    if (st != FTX_OK) return st;
-    st = run_step(e, FTX_STEP_LN2, s, [&] {
-      if (e->y1f)
-        return launch_bias_residual_layernorm_f32res(dt, T, H, e->y1f, true, (const float*)e->abuf, w.b2,
+    const int f_splits = linear_splits(dt, T, H, F, e->splitk_elems);
+    if (f_splits > 1) {
+      st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
+        return launch_linear_partials(dt, T, H, F, e->u, w.w2_t, e->splitk, e->splitk_elems, s);
+      });
+      if (st != FTX_OK) return st;
+      st = run_step(e, FTX_STEP_LN2, s, [&] {
+        const bool f32res = e->y1f != nullptr;
+        return launch_splitk_bias_residual_layernorm(dt, T, H, f32res ? (const void*)e->y1f : e->y1,
+                                                     f32res, e->splitk, f_splits, f32res, w.b2,
                                                      w.ln2_g, w.ln2_b, state, nullptr, s);
-      return launch_bias_residual_layernorm(dt, T, H, e->y1, e->abuf, w.b2, w.ln2_g, w.ln2_b, state, s);
-    });
+      });
+    } else {
+      st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
+        return launch_linear(dt, T, H, F, e->u, w.w2_t, nullptr, false, e->abuf, s,
+                             e->y1f != nullptr, e->splitk, e->splitk_elems);
+      });
+      if (st != FTX_OK) return st;
+      st = run_step(e, FTX_STEP_LN2, s, [&] {
+        if (e->y1f)
+          return launch_bias_residual_layernorm_f32res(dt, T, H, e->y1f, true, (const float*)e->abuf, w.b2,
+                                                       w.ln2_g, w.ln2_b, state, nullptr, s);
+        return launch_bias_residual_layernorm(dt, T, H, e->y1, e->abuf, w.b2, w.ln2_g, w.ln2_b, state, s);
+      });
+    }
     if (st != FTX_OK) return st;
   }
   if (e->xpad) {

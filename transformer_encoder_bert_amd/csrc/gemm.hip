@@ -935,15 +935,19 @@ static void gemm_kernel_launch(dim3 grid, int kchunk, int M, int N, int K, const
       (const T*)a, (const T*)w_t, M, N, K, kchunk, epi);
 }
 
+// reduce: under split-K, also launch the reduction that finishes the partials with `epi`
+// (false: the caller's next kernel consumes the partials itself).
 template <typename T, int BM, int BN, int WM, int WN, typename Epi>
 static hipError_t gemm_launch_cfg(int M, int N, int K, const void* a, const void* w_t, Epi epi,
-                                  const GemmPlan& plan, float* ws, hipStream_t s) {
+                                  const GemmPlan& plan, float* ws, hipStream_t s, bool reduce) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (plan.splits > 1) {
     gemm_kernel_launch<T, BM, BN, WM, WN, EpiPartial>(dim3(tiles, plan.splits), plan.kchunk, M, N,
                                                       K, a, w_t, EpiPartial{ws, M, N}, s);
-    const int64_t threads = (int64_t)M * (N / 4);
-    splitk_reduce_kernel<Epi><<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(ws, plan.splits, M, N, epi);
+    if (reduce) {
+      const int64_t threads = (int64_t)M * (N / 4);
+      splitk_reduce_kernel<Epi><<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(ws, plan.splits, M, N, epi);
+    }
     return hipGetLastError();
   }
   if constexpr (sizeof(T) == 2 && BM == 256 && WM == 4 && WN == 2) {
@@ -960,7 +964,8 @@ static hipError_t gemm_launch_cfg(int M, int N, int K, const void* a, const void
 
 template <typename T, typename Epi>
 static hipError_t gemm_launch(int M, int N, int K, const void* a, const void* w_t, Epi epi,
-                              hipStream_t s, float* ws = nullptr, size_t ws_elems = 0) {
+                              hipStream_t s, float* ws = nullptr, size_t ws_elems = 0,
+                              bool reduce = true) {
   constexpr bool wide = sizeof(T) == 2;
   GemmPlan plan = plan_gemm(M, N, K, (int)sizeof(T));
   if (plan.splits > 1 && (!ws || ws_elems < (size_t)plan.splits * M * N)) {
@@ -969,16 +974,36 @@ static hipError_t gemm_launch(int M, int N, int K, const void* a, const void* w_
   }
   switch (plan.cfg) {
     case TILE_256x256:
-      if constexpr (wide) return gemm_launch_cfg<T, 256, 256, 4, 2>(M, N, K, a, w_t, epi, plan, ws, s);
+      if constexpr (wide) return gemm_launch_cfg<T, 256, 256, 4, 2>(M, N, K, a, w_t, epi, plan, ws, s, reduce);
       break;
     case TILE_256x192:
-      if constexpr (wide) return gemm_launch_cfg<T, 256, 192, 4, 2>(M, N, K, a, w_t, epi, plan, ws, s);
+      if constexpr (wide) return gemm_launch_cfg<T, 256, 192, 4, 2>(M, N, K, a, w_t, epi, plan, ws, s, reduce);
       break;
-    case TILE_256x128: return gemm_launch_cfg<T, 256, 128, 4, 2>(M, N, K, a, w_t, epi, plan, ws, s);
-    case TILE_128x128: return gemm_launch_cfg<T, 128, 128, 2, 2>(M, N, K, a, w_t, epi, plan, ws, s);
-    case TILE_64x64: return gemm_launch_cfg<T, 64, 64, 2, 2>(M, N, K, a, w_t, epi, plan, ws, s);
-    case TILE_32x32: return gemm_launch_cfg<T, 32, 32, 1, 1>(M, N, K, a, w_t, epi, plan, ws, s);
+    case TILE_256x128: return gemm_launch_cfg<T, 256, 128, 4, 2>(M, N, K, a, w_t, epi, plan, ws, s, reduce);
+    case TILE_128x128: return gemm_launch_cfg<T, 128, 128, 2, 2>(M, N, K, a, w_t, epi, plan, ws, s, reduce);
+    case TILE_64x64: return gemm_launch_cfg<T, 64, 64, 2, 2>(M, N, K, a, w_t, epi, plan, ws, s, reduce);
+    case TILE_32x32: return gemm_launch_cfg<T, 32, 32, 1, 1>(M, N, K, a, w_t, epi, plan, ws, s, reduce);
     default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+int linear_splits(ftx_dtype dt, int M, int N, int K, size_t ws_elems) {
+  const GemmPlan p = plan_gemm(M, N, K, dt == FTX_FP32 ? 4 : 2);
+  return (p.splits > 1 && ws_elems >= (size_t)p.splits * M * N) ? p.splits : 1;
+}
+
+hipError_t launch_linear_partials(ftx_dtype dt, int M, int N, int K, const void* a,
+                                  const void* w_t, float* ws, size_t ws_elems, hipStream_t s) {
+  if (linear_splits(dt, M, N, K, ws_elems) < 2) return hipErrorInvalidValue;
+  // the epilogue only serves the reduction, which is not launched
+  switch (dt) {
+    case FTX_FP32:
+      return gemm_launch<float>(M, N, K, a, w_t, EpiLinear<float, false>{nullptr, nullptr, M, N}, s, ws, ws_elems, false);
+    case FTX_FP16:
+      return gemm_launch<f16>(M, N, K, a, w_t, EpiLinear<f16, false>{nullptr, nullptr, M, N}, s, ws, ws_elems, false);
+    case FTX_BF16:
+      return gemm_launch<bf16>(M, N, K, a, w_t, EpiLinear<bf16, false>{nullptr, nullptr, M, N}, s, ws, ws_elems, false);
   }
   return hipErrorInvalidValue;
 }

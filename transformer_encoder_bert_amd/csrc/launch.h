@@ -49,6 +49,15 @@ hipError_t launch_qkv_attention(ftx_dtype dt, int B, int S, int nh, int d, const
 // fp32 elements of split-K workspace the GEMM of this shape uses (0: it does not split).
 size_t gemm_splitk_workspace(ftx_dtype dt, int M, int N, int K);
 
+// K ranges launch_linear splits this shape into with ws_elems fp32 of workspace (1: none).
+int linear_splits(ftx_dtype dt, int M, int N, int K, size_t ws_elems);
+
+// The split-K partial products of the projection c = a w alone: ws[z][M][N] fp32 for the
+// linear_splits(...) ranges z, summed by nobody yet (launch_splitk_bias_residual_layernorm
+// consumes them).  hipErrorInvalidValue when the shape does not split.
+hipError_t launch_linear_partials(ftx_dtype dt, int M, int N, int K, const void* a,
+                                  const void* w_t, float* ws, size_t ws_elems, hipStream_t s);
+
 hipError_t launch_bias_qkv_split(ftx_dtype dt, int B, int S, int nh, int d, const void* qkv,
                                  const void* b_qkv, void* q, void* k, void* vt, hipStream_t s);
 
@@ -72,6 +81,16 @@ hipError_t launch_bias_residual_layernorm_f32res(ftx_dtype dt, int rows, int col
                                                  const void* bias, const void* gamma,
                                                  const void* beta, void* y, float* yf,
                                                  hipStream_t s);
+
+// The LayerNorm above after a projection split over K: a = the sum of the fp32 partials
+// p[0..splits-1][rows][cols] in split order (what the split-K reduction computes), rounded to
+// the storage type unless a_f32 (the projection's output would have been fp32); x is read
+// as fp32 when x_f32; yf (non-null) also receives y in fp32.  One workgroup per row.
+hipError_t launch_splitk_bias_residual_layernorm(ftx_dtype dt, int rows, int cols,
+                                                 const void* x, bool x_f32, const float* p,
+                                                 int splits, bool a_f32, const void* bias,
+                                                 const void* gamma, const void* beta, void* y,
+                                                 float* yf, hipStream_t s);
 
 hipError_t launch_bias_gelu(ftx_dtype dt, int rows, int cols, const void* u, const void* bias,
                             void* g, hipStream_t s);
