@@ -116,6 +116,32 @@ ftx_status enqueue_decoder(ftx_decoder* e, const void* input, const void* memory
   float* ws = e->splitk;
   const size_t wn = e->splitk_elems;
   ftx_status st;
+  // Projection a w_t (K = kin, N = H) and the add & LayerNorm after it: y = LN(xr + a w_t +
+  // bias) (xr read as fp32 when xr_f32), yf an fp32 copy.  A projection that splits K (small
+  // batches) leaves its fp32 partials to the LayerNorm, which sums them itself.
+  auto proj_ln = [&](int proj_step, int ln_step, const void* a, const void* w_t, int kin,
+                     const void* xr, bool xr_f32, const void* bias, const void* gamma,
+                     const void* beta, void* y, float* yf) -> ftx_status {
+    const int sp = linear_splits(dt, Td, H, kin, wn);
+    ftx_status r;
+    if (sp > 1) {
+      if ((r = step(e, proj_step, s, [&] {
+             return launch_linear_partials(dt, Td, H, kin, a, w_t, ws, wn, s);
+           })) != FTX_OK) return r;
+      return step(e, ln_step, s, [&] {
+        return launch_splitk_bias_residual_layernorm(dt, Td, H, xr, xr_f32, ws, sp, f32res, bias,
+                                                     gamma, beta, y, yf, s);
+      });
+    }
+    if ((r = step(e, proj_step, s, [&] {
+           return launch_linear(dt, Td, H, kin, a, w_t, nullptr, false, e->abuf, s, f32res, ws, wn);
+         })) != FTX_OK) return r;
+    return step(e, ln_step, s, [&] {
+      return f32res ? launch_bias_residual_layernorm_f32res(dt, Td, H, xr, xr_f32, (const float*)e->abuf,
+                                                            bias, gamma, beta, y, yf, s)
+                    : launch_bias_residual_layernorm(dt, Td, H, xr, e->abuf, bias, gamma, beta, y, s);
+    });
+  };
   // Caller lengths below the internal ones: rows 0..Sdv-1 (0..Sev-1) of each sequence go to
   // the padded copies, the layers run at Sd and Se, and rows 0..Sdv-1 come back at the end.
   // Padded decoder rows follow the valid ones, so the causal mask keeps them out of every
@@ -152,16 +178,8 @@ ftx_status enqueue_decoder(ftx_decoder* e, const void* input, const void* memory
                                      Sd, true);
            })) != FTX_OK) return st;
     }
-    if ((st = step(e, FTX_DEC_STEP_SELF_OUT_GEMM, s, [&] {
-           return launch_linear(dt, Td, H, H, e->ctx, w.w_o_t, nullptr, false, e->abuf, s, f32res,
-                                ws, wn);
-         })) != FTX_OK) return st;
-    if ((st = step(e, FTX_DEC_STEP_LN1, s, [&] {
-           return f32res ? launch_bias_residual_layernorm_f32res(dt, Td, H, x, false, (const float*)e->abuf,
-                                                                 w.b_o, w.ln1_g, w.ln1_b, e->y1, e->y1f, s)
-                         : launch_bias_residual_layernorm(dt, Td, H, x, e->abuf, w.b_o, w.ln1_g,
-                                                          w.ln1_b, e->y1, s);
-         })) != FTX_OK) return st;
+    if ((st = proj_ln(FTX_DEC_STEP_SELF_OUT_GEMM, FTX_DEC_STEP_LN1, e->ctx, w.w_o_t, H, x, false,
+                      w.b_o, w.ln1_g, w.ln1_b, e->y1, e->y1f)) != FTX_OK) return st;
     // cross-attention over the memory, add & LayerNorm 2
     if ((st = step(e, FTX_DEC_STEP_CROSS_Q_GEMM, s, [&] {
            return launch_head_projection(dt, B, Sd, nh, d, e->y1, w.w_q2_t, w.b_q2, 0, 1, e->q2,
@@ -175,30 +193,16 @@ ftx_status enqueue_decoder(ftx_decoder* e, const void* input, const void* memory
            return launch_attention(dt, B, Sd, Se, nh, d, e->q2, e->k2, e->vt2, mem_lens, e->ctx, s,
                                    e->Sev, false);
          })) != FTX_OK) return st;
-    if ((st = step(e, FTX_DEC_STEP_CROSS_OUT_GEMM, s, [&] {
-           return launch_linear(dt, Td, H, H, e->ctx, w.w_o2_t, nullptr, false, e->abuf, s, f32res,
-                                ws, wn);
-         })) != FTX_OK) return st;
-    if ((st = step(e, FTX_DEC_STEP_LN2, s, [&] {
-           return f32res ? launch_bias_residual_layernorm_f32res(dt, Td, H, e->y1f, true, (const float*)e->abuf,
-                                                                 w.b_o2, w.ln2_g, w.ln2_b, e->y2, e->y2f, s)
-                         : launch_bias_residual_layernorm(dt, Td, H, e->y1, e->abuf, w.b_o2, w.ln2_g,
-                                                          w.ln2_b, e->y2, s);
-         })) != FTX_OK) return st;
+    if ((st = proj_ln(FTX_DEC_STEP_CROSS_OUT_GEMM, FTX_DEC_STEP_LN2, e->ctx, w.w_o2_t, H,
+                      f32res ? (const void*)e->y1f : e->y1, f32res, w.b_o2, w.ln2_g, w.ln2_b,
+                      e->y2, e->y2f)) != FTX_OK) return st;
     // feed-forward, add & LayerNorm 3 (written to the output, the next layer's input)
     if ((st = step(e, FTX_DEC_STEP_FFN1_GEMM, s, [&] {
            return launch_linear(dt, Td, F, H, e->y2, w.w1_t, w.b1, true, e->u, s, false, ws, wn);
          })) != FTX_OK) return st;
-    if ((st = step(e, FTX_DEC_STEP_FFN2_GEMM, s, [&] {
-           return launch_linear(dt, Td, H, F, e->u, w.w2_t, nullptr, false, e->abuf, s, f32res, ws,
-                                wn);
-         })) != FTX_OK) return st;
-    if ((st = step(e, FTX_DEC_STEP_LN3, s, [&] {
-           return f32res ? launch_bias_residual_layernorm_f32res(dt, Td, H, e->y2f, true, (const float*)e->abuf,
-                                                                 w.b2, w.ln3_g, w.ln3_b, state, nullptr, s)
-                         : launch_bias_residual_layernorm(dt, Td, H, e->y2, e->abuf, w.b2, w.ln3_g,
-                                                          w.ln3_b, state, s);
-         })) != FTX_OK) return st;
+    if ((st = proj_ln(FTX_DEC_STEP_FFN2_GEMM, FTX_DEC_STEP_LN3, e->u, w.w2_t, F,
+                      f32res ? (const void*)e->y2f : e->y2, f32res, w.b2, w.ln3_g, w.ln3_b, state,
+                      nullptr)) != FTX_OK) return st;
   }
   if (e->xpad)
     FTX_HIP(hipMemcpy2DAsync(output, e->Sdv * row, state, Sd * row, e->Sdv * row, B,
