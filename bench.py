@@ -161,13 +161,17 @@ def profile_commands(wl, calib_mb, name):
 # what each ftx kernel symbol is, for the kernel-trace summaries (demangling by hand: the
 # host's c++filt predates the _Float16 mangling)
 KERNEL_ROLES = (
+    ("splitk_layernorm", "split-K partial sum + bias + residual + LayerNorm"),
+    ("splitk_reduce_kernelINS_6EpiQKV", "split-K reduction + bias + head split (Q/K/V)"),
+    ("splitk_reduce_kernelINS_9EpiLinearIDF16_Lb1", "split-K reduction + bias + GELU (FFN-in)"),
+    ("splitk_reduce_kernelINS_9EpiLinearIDF16bLb1", "split-K reduction + bias + GELU (FFN-in)"),
+    ("splitk_reduce", "split-K reduction + the projection's epilogue"),
     ("EpiQKVAttn", "Q/K/V projection with the attention in its epilogue"),
     ("EpiQKV", "Q/K/V (or Q-only, K/V-only) projection with bias + head split"),
     ("EpiLinearIDF16_Lb1", "projection with bias + GELU (FFN-in)"),
     ("EpiLinearIDF16bLb1", "projection with bias + GELU (FFN-in)"),
     ("EpiLinear", "projection (attention output, FFN-out)"),
     ("EpiPartial", "split-K partial products"),
-    ("splitk_reduce", "split-K reduction + epilogue"),
     ("attention", "attention (scores, masked softmax, context)"),
     ("layernorm", "bias + residual + LayerNorm"),
     ("transpose", "weight repacking (set_weights, not in the forward)"),
