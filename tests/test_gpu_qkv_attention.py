@@ -70,9 +70,11 @@ CASES = [
     (9, 32, 4, 32, "random"),       # d = 32: two heads per tile (the pruned model's 4 x 32)
     (3, 32, 2, 32, None),
     (3, 128, 6, 32, [128, 50, 1]),
-    # hidden size 1024 (16 K slabs): the ping-pong K loop
+    # hidden size 1024 (16 K slabs): 128-row tiles below 256 tiles of 256 rows ...
     (3, 128, 16, 64, [128, 70, 1]),  # BERT-large heads
     (9, 32, 32, 32, "random"),
+    # ... and 256-row tiles on the ping-pong K loop from there on
+    (32, 128, 16, 64, "random"),
 ]
 
 
@@ -209,8 +211,9 @@ def test_encoder_fused_and_separate_agree():
 
 def test_encoder_auto_mode_needs_64_tiles():
     """Default mode: fused from 64 tiles of 256 x 192 (BERT-base S32: B = 48 gives 6 x 12),
-    separate below (B = 40 gives 5 x 12)."""
-    for B, fused in ((40, False), (48, True)):
+    separate below (B = 40 gives 5 x 12, B = 16 gives 2 x 12) -- except where the separate
+    Q/K/V projection would split K (B = 8, 256 tokens)."""
+    for B, fused in ((8, True), (16, False), (40, False), (48, True)):
         c = si.make_case("bert_base_fp16_s32", B, params="bert", num_layers=1)
         enc = _encoder(c.shape, list(c.layers()), 1)
         enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)

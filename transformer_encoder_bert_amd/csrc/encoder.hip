@@ -147,15 +147,20 @@ void drop_graph(ftx_encoder* e) {
 }
 
 // The projection with the attention in its epilogue replaces the projection + attention
-// pair when the shape fits and, in the default mode, when there are at least 256 tokens (one
-// whole tile of rows) and 64 tiles: with fewer, the tiles are mostly padding rows or the
-// long epilogue runs on few CUs, while the separate kernels spread the same work (measured,
-// fused against separate: BERT-base S32 B1 0.585 against 0.516 ms, B64 (96 tiles) 0.927
-// against 0.947, S64 B64 1.253 against 1.508; the 4 x 32 model B64 (16 tiles) 0.321 against
-// 0.298, B512 (128 tiles) 0.464 against 0.514).
+// pair when the shape fits and, in the default mode, when there are at least 256 tokens and
+// either 64 tiles of 256 rows or a separate Q/K/V projection that would split K (three
+// launches: partials, reduction, attention).  Below that the tiles are mostly padding rows
+// or the long epilogue runs on few CUs, while the separate kernels spread the same work.
+// Measured, fused against separate (128-row tiles below 256 tiles of 256 rows): BERT-base
+// S32 B1 0.482 against 0.462 ms, B8 (split Q/K/V) 0.549 against 0.607, B16 0.691 against
+// 0.670, B64 0.805 against 0.867; S64 B64 1.253 against 1.508; the 4 x 32 model B64 0.294
+// against 0.296, B512 0.464 against 0.514.
 bool use_fused_attention(const ftx_encoder* e) {
   if (!e->fused || !e->attn_fits || e->fused_attention == 0) return false;
-  return e->fused_attention == 2 || (e->T >= 256 && fused_attention_tiles(e->T, e->H) >= 64);
+  if (e->fused_attention == 2) return true;
+  if (e->T < 256) return false;
+  return fused_attention_tiles(e->T, e->H) >= 64 ||
+         linear_splits(e->dt, e->T, 3 * e->H, e->H, e->splitk_elems) > 1;
 }
 
 // Enqueue the L-layer forward on `s` (arguments already validated).

@@ -287,10 +287,11 @@ __device__ __forceinline__ int swz(int R) { return (R & 7) ^ ((R >> 3) & 3); }
 // (the layer's first steps, section "Faster Transformer 优化原理" of the Faster Transformer
 // article).  The weight rows (output columns) are ordered per head, [Q_h | K_h | V_h] for
 // h = 0 .. nh-1, so the 192 columns of a tile column are exactly Q, K and V of 64 / D heads,
-// and the 256 rows of a tile are 256 / SEQ whole sequences.  After the K loop the tile is
+// and the R rows of a tile (256 with 8 waves, or 128 with 4 when the 256-row grid would
+// leave CUs idle) are R / SEQ whole sequences.  After the K loop the tile is
 // biased, rounded to the storage type (as Q, K and V are when they go through memory) and
 // split in LDS into Q and K (rows of the tile's 64 head columns) and V^T (one row per head
-// column, 256 tokens); then each wave takes one block of 32 queries (wave w: sequence
+// column, R tokens); then each of the R / 32 waves takes one block of 32 queries (wave w: sequence
 // w / (SEQ/32), query block w % (SEQ/32)) and, for each head of the tile in turn, runs the
 // chain of the attention kernel over all keys of its sequence: S^T = K Q^T per 32-key tile
 // (D/16 MFMAs), the key mask at the sequence's valid length and the exp2 softmax on the fp32
@@ -300,8 +301,9 @@ __device__ __forceinline__ int swz(int R) { return (R & 7) ^ ((R >> 3) & 3); }
 // past its own block are skipped.  Each head's context is staged in the wave's own Q rows
 // and columns of that head and stored as rows of ctx[b*SEQ + i][h*D + e].  Q, K and V never
 // reach global memory.
-template <typename T, int SEQ, int D> struct EpiQKVAttn {
-  static_assert(SEQ == 32 || SEQ == 64 || SEQ == 128 || SEQ == 256, "whole sequences per tile");
+template <typename T, int SEQ, int D, int R = 256> struct EpiQKVAttn {
+  static_assert(SEQ == 32 || SEQ == 64 || SEQ == 128 || SEQ == 256, "sequence length");
+  static_assert((R == 128 || R == 256) && R % SEQ == 0, "whole sequences per tile");
   static_assert(D == 32 || D == 64, "head size");
   static constexpr bool kBlock = true;
   static constexpr int NKT = SEQ / 32;  // key tiles (and query blocks) per sequence
@@ -320,10 +322,10 @@ template <typename T, int SEQ, int D> struct EpiQKVAttn {
   float scale_log2e;    // log2(e) / sqrt(D)
   int causal;           // non-zero: query i also ignores keys j > i
   // LDS: Q and K rows (the tile's 64 head columns) padded to 72 elements, V^T rows (one per
-  // head column) to 260 tokens, so the fragment reads of 32 consecutive rows fall in
+  // head column) to R + 4 tokens, so the fragment reads of 32 consecutive rows fall in
   // distinct banks
-  static constexpr int QLD = 72, VLD = 260;
-  static constexpr int KOFF = 256 * QLD, VOFF = 2 * 256 * QLD;
+  static constexpr int QLD = 72, VLD = R + 4;
+  static constexpr int KOFF = R * QLD, VOFF = 2 * R * QLD;
   static constexpr size_t kLdsBytes = (size_t)(VOFF + 64 * VLD) * sizeof(T);
   __device__ __forceinline__ b4 bias4(int n) const {
     b4 v = {};
@@ -334,7 +336,7 @@ template <typename T, int SEQ, int D> struct EpiQKVAttn {
   __device__ __forceinline__ void block(char* smem, int m0, int n0, int wave, int lane,
                                         const f32x16 (&acc)[TN][TM],
                                         const b4 (&bq)[TN][4]) const {
-    static_assert(TM == 2 && TN == 3 && WN == 2, "256 x 192 tile of 4 x 2 waves");
+    static_assert(TM == 2 && TN == 3 && WN == 2, "R x 192 tile of (R / 64) x 2 waves");
     typedef typename Mfma<T>::frag frag;
     T* lds = (T*)smem;
     const int wm = wave / WN, wn = wave % WN, lr = lane % 32, g = lane / 32;
@@ -1065,8 +1067,19 @@ static hipError_t qkv_attention_t(int B, int nh, const void* x, const void* w_t,
   const int M = SEQ * B, N = 3 * D * nh, K = D * nh;
   // log2(e) / sqrt(d), rounded once from double as the attention kernel does
   const float scale_log2e = (float)(1.4426950408889634 / sqrt((double)D));
-  EpiQKVAttn<T, SEQ, D> epi{(T*)ctx, (const T*)bias, lens, M, N, s_valid, scale_log2e, causal};
   const int tiles = ((M + 255) / 256) * (N / 192);
+  if constexpr (SEQ <= 128) {
+    // fewer 256-row tiles than CUs: 128-row tiles of 4 waves, twice the tiles and two
+    // blocks per CU (BERT-base at batch 64: 96 tiles of 256 rows, 192 of 128)
+    if (tiles < 256) {
+      typedef EpiQKVAttn<T, SEQ, D, 128> Epi128;
+      Epi128 epi{(T*)ctx, (const T*)bias, lens, M, N, s_valid, scale_log2e, causal};
+      gemm_kernel<T, 128, 192, 2, 2, Epi128><<<((M + 127) / 128) * (N / 192), 4 * kWave, 0, s>>>(
+          (const T*)x, (const T*)w_t, M, N, K, K, epi);
+      return hipGetLastError();
+    }
+  }
+  EpiQKVAttn<T, SEQ, D> epi{(T*)ctx, (const T*)bias, lens, M, N, s_valid, scale_log2e, causal};
   constexpr int BK = GemmCfg<T, 256, 192, 4, 2>::BK;
   if (K % BK == 0 && K / BK >= kPingPongMinSlabs)
     gemm_pp_kernel<T, 256, 192, EpiQKVAttn<T, SEQ, D>><<<tiles, 8 * kWave, 0, s>>>(
