@@ -40,7 +40,8 @@ def parse():
     p.add_argument("--graph", action="store_true", help="replay the forward as one HIP graph")
     p.add_argument("--fused-attention", type=int, default=1, choices=(0, 1, 2),
                    help="projection + attention in one kernel: 0 never, 1 from 256 tokens and "
-                        "64 tiles (default), 2 whenever the shape fits")
+                        "64 tiles of 256 rows or a split-K Q/K/V projection (default), 2 "
+                        "whenever the shape fits")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-kernel-times", action="store_true")
