@@ -141,8 +141,8 @@ const char *ftx_last_error(void);
  *     up to 256, rounded up to a multiple of 32 that is one of those), size_per_head 64 (or
  *     32 with an even head_num) and a 16-bit dtype, the Q/K/V projection and the attention
  *     run as one kernel that attends each 256 x 192 projection tile (256/S whole sequences,
- *     64/size_per_head heads; 128-row tiles when the 256-row grid has fewer tiles than the
- *     GPU has CUs) in its epilogue, so Q, K and V never reach memory
+ *     64/size_per_head heads; 128-row tiles when the 256-row grid has at most half as many
+ *     tiles as the GPU has CUs) in its epilogue, so Q, K and V never reach memory
  *     (ftx_step_qkv_attention).  0 = never; 1 = when batch*S >= 256 and either the 256-row
  *     grid has at least 64 tiles (ceil(batch*S/256) * 3*hidden/192) or the separate Q/K/V
  *     projection would split its K dimension (small batches), else the separate kernels;

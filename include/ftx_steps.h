@@ -66,7 +66,8 @@ ftx_status ftx_step_attention(ftx_dtype dtype, int B, int S, int n, int d, const
  *   seq_lens [B] int32 (clamped to [1, S]) or NULL; causal != 0: query i also ignores keys
  *   j > i (a decoder's self-attention).
  * Q, K and V stay on chip: each 256 x 192 output tile (256/S whole sequences, 64/d heads;
- * 128 x 192 tiles when the 256-row grid has fewer tiles than the GPU has CUs and S <= 128)
+ * 128 x 192 tiles when the 256-row grid has at most half as many tiles as the GPU has CUs
+ * and S <= 128)
  * is attended in the projection's epilogue.  ctx must not overlap x or w_qkv_t
  * (FTX_ERR_INVALID_ARG). */
 ftx_status ftx_step_qkv_attention(ftx_dtype dtype, int B, int S, int n, int d, const void *x,

@@ -288,7 +288,7 @@ __device__ __forceinline__ int swz(int R) { return (R & 7) ^ ((R >> 3) & 3); }
 // article).  The weight rows (output columns) are ordered per head, [Q_h | K_h | V_h] for
 // h = 0 .. nh-1, so the 192 columns of a tile column are exactly Q, K and V of 64 / D heads,
 // and the R rows of a tile (256 with 8 waves, or 128 with 4 when the 256-row grid would
-// leave CUs idle) are R / SEQ whole sequences.  After the K loop the tile is
+// leave half the CUs idle) are R / SEQ whole sequences.  After the K loop the tile is
 // biased, rounded to the storage type (as Q, K and V are when they go through memory) and
 // split in LDS into Q and K (rows of the tile's 64 head columns) and V^T (one row per head
 // column, R tokens); then each of the R / 32 waves takes one block of 32 queries (wave w: sequence
@@ -1069,9 +1069,10 @@ static hipError_t qkv_attention_t(int B, int nh, const void* x, const void* w_t,
   const float scale_log2e = (float)(1.4426950408889634 / sqrt((double)D));
   const int tiles = ((M + 255) / 256) * (N / 192);
   if constexpr (SEQ <= 128) {
-    // fewer 256-row tiles than CUs: 128-row tiles of 4 waves, twice the tiles and two
-    // blocks per CU (BERT-base at batch 64: 96 tiles of 256 rows, 192 of 128)
-    if (tiles < 256) {
+    // 128-row tiles of 4 waves while twice the tiles still fit one per CU (BERT-base S32
+    // at batch 64: 96 tiles of 256 rows -> 192 of 128, 0.849 -> 0.806 ms; at S64, 192 tiles
+    // of 256 rows would become 384 sharing CUs: 1.267 -> 1.287 ms, so they stay)
+    if (2 * tiles <= 256) {
       typedef EpiQKVAttn<T, SEQ, D, 128> Epi128;
       Epi128 epi{(T*)ctx, (const T*)bias, lens, M, N, s_valid, scale_log2e, causal};
       gemm_kernel<T, 128, 192, 2, 2, Epi128><<<((M + 127) / 128) * (N / 192), 4 * kWave, 0, s>>>(
