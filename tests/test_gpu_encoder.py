@@ -224,6 +224,25 @@ def test_max_hidden_and_odd_heads():
         check(out, ref, shape.dtype, tol, f"{shape}")
 
 
+@pytest.mark.parametrize("shape", [
+    si.Shape(1, 32, 24, 64, 1, "fp16"),  # hidden 1536, one sequence
+    si.Shape(2, 32, 24, 64, 1, "bf16"),  # the same with the fp32 residual stream
+    si.Shape(1, 32, 4, 64, 1, "fp32"),   # fp32, hidden 256
+])
+def test_split_k_paths(shape):
+    """The small-batch path: at these shapes every projection splits K; the Q/K/V head split
+    and the GELU finish their partials in the reduction, the attention-output and FFN-out
+    partials are summed by the LayerNorm after them.  One layer at the layer bar."""
+    c = si.custom_case(shape, 31, lens_range=(1, shape.seq_len), params="random_affine")
+    layers = list(c.layers())
+    ref = oracle.encoder(c.x, layers, c.lens, shape.head_num)
+    enc = _encoder(shape, layers)
+    enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)
+    out = to_f64(enc.forward(to_dev(c.x, shape.dtype), dev_lens(c.lens)))
+    enc.close()
+    check(out, ref, shape.dtype, layer_tol(shape.dtype), f"{shape}")
+
+
 @pytest.mark.parametrize("shape,with_lens", [
     (si.Shape(3, 100, 4, 32, 2, "fp16"), True),
     (si.Shape(2, 100, 4, 32, 2, "fp16"), False),   # no seq_lens: keys limited to 100

@@ -875,10 +875,14 @@ static TileCfg choose_tile(int M, int N, bool wide) {
 // Split-K (the small-batch path): when the chosen configuration has fewer tiles than there
 // are CUs, K is cut into up to 16 ranges of at least two slabs each, so that
 // about 512 blocks run; the partial products go to an fp32 workspace [splits][M][N] and a
-// reduction kernel finishes them.  The partials are capped at 16 MiB (fewer splits, or
-// none): their round trip through memory must stay small against what the split saves --
-// at 4096 rows a 6-way split of the 768-wide projections would move 75 MB and lose.
-// Without a workspace of the planned size the GEMM is not split.
+// reduction kernel (or the LayerNorm that follows) finishes them.  The partials are capped
+// at 16 MiB (fewer splits, or none): their round trip through memory must stay small
+// against what the split saves -- at 4096 rows a 6-way split of the 768-wide projections
+// would move 75 MB and lose.  Without a workspace of the planned size the GEMM is not
+// split.  Even a short K chain gains: the split spreads the reads of weights that arrive
+// cold from memory over six times the blocks (BERT-base batch 1, K = 768 unsplit: 0.481
+// against 0.463 ms per forward), although the same projection repeated on weights already
+// in L2 runs faster unsplit (4.6 against 7.5 us).
 struct GemmPlan {
   TileCfg cfg;
   int splits;  // 1 = no split
