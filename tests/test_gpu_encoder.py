@@ -243,6 +243,28 @@ def test_split_k_paths(shape):
     check(out, ref, shape.dtype, layer_tol(shape.dtype), f"{shape}")
 
 
+@pytest.mark.parametrize("shape", [
+    si.Shape(256, 32, 4, 32, 2, "fp16"),  # 8192 rows: 128 tiles of 64
+    si.Shape(257, 32, 4, 32, 1, "bf16"),  # the fp32 residual stream; a partial last tile
+    si.Shape(128, 64, 2, 64, 1, "fp32"),
+])
+def test_hidden_128_layernorm_in_the_projection(shape):
+    """Hidden size 128 with at least 128 row tiles: the attention-output and FFN-out
+    projections run the bias + residual + LayerNorm in their epilogue (a 64 x 128 tile holds
+    whole rows); against the oracle at the stack bar, and no LayerNorm launch of its own."""
+    c = si.custom_case(shape, 41, lens_range=(1, shape.seq_len), params="random_affine")
+    layers = list(c.layers())
+    ref = oracle.encoder(c.x, layers, c.lens, shape.head_num)
+    enc = _encoder(shape, layers)
+    enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)
+    out = to_f64(enc.forward(to_dev(c.x, shape.dtype), dev_lens(c.lens)))
+    t = enc.kernel_times()
+    enc.close()
+    assert t["ln1"][1] == 0 and t["ln2"][1] == 0
+    assert t["attn_out_gemm"][1] == shape.num_layers and t["ffn2_gemm"][1] == shape.num_layers
+    check(out, ref, shape.dtype, stack_tol(shape.dtype), f"{shape}")
+
+
 @pytest.mark.parametrize("shape,with_lens", [
     (si.Shape(3, 100, 4, 32, 2, "fp16"), True),
     (si.Shape(2, 100, 4, 32, 2, "fp16"), False),   # no seq_lens: keys limited to 100

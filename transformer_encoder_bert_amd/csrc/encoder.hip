@@ -211,10 +211,20 @@ ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq
       });
       if (st != FTX_OK) return st;
     }
-    // A projection that splits K (small batches) leaves its fp32 partials to the LayerNorm
-    // that follows it, which sums them itself: one launch instead of reduction + LayerNorm.
+    // Hidden size 128 with at least 128 row tiles: one 64 x 128 projection tile holds whole
+    // rows, and the projection runs the bias + residual + LayerNorm in its epilogue (the
+    // 4 x 32 model at batch 512: 0.445 -> 0.418 ms; with fewer tiles the unsplit K chain on
+    // few CUs loses -- batch 64 0.302 -> 0.338 ms).  Otherwise a projection that splits K
+    // (small batches) leaves its fp32 partials to the LayerNorm that follows it, which sums
+    // them itself: one launch instead of reduction + LayerNorm.
+    const bool row_ln = H == 128 && (T + 63) / 64 >= 128;
     const int o_splits = linear_splits(dt, T, H, H, e->splitk_elems);
-    if (o_splits > 1) {
+    if (row_ln) {
+      st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
+        return launch_linear_layernorm(dt, T, H, H, e->ctx, w.w_o_t, x, false, e->y1f != nullptr,
+                                       w.b_o, w.ln1_g, w.ln1_b, e->y1, e->y1f, s);
+      });
+    } else if (o_splits > 1) {
       st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
         return launch_linear_partials(dt, T, H, H, e->ctx, w.w_o_t, e->splitk, e->splitk_elems, s);
       });
@@ -255,7 +265,14 @@ ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq
     }
     if (st != FTX_OK) return st;
     const int f_splits = linear_splits(dt, T, H, F, e->splitk_elems);
-    if (f_splits > 1) {
+    if (row_ln) {
+      st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
+        const bool f32res = e->y1f != nullptr;
+        return launch_linear_layernorm(dt, T, H, F, e->u, w.w2_t,
+                                       f32res ? (const void*)e->y1f : e->y1, f32res, f32res,
+                                       w.b2, w.ln2_g, w.ln2_b, state, nullptr, s);
+      });
+    } else if (f_splits > 1) {
       st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
         return launch_linear_partials(dt, T, H, F, e->u, w.w2_t, e->splitk, e->splitk_elems, s);
       });

@@ -171,6 +171,93 @@ template <typename T> struct EpiQKV {
   }
 };
 
+// Projection + bias + residual + LayerNorm for a hidden size of 128, where a 64 x 128 tile
+// (4 waves, 2 x 2, each 32 rows x 64 columns) holds whole rows: y = LN(x + a + bias; gamma,
+// beta) with a the projection (rounded to the storage type as a separate projection's
+// store would be, unless A_F32: the fp32 residual stream of the 16-bit modes), the
+// statistics in fp32 -- mean, then the centred sum of squares -- with the two wave columns
+// of a row meeting in LDS.  TX: type of the residual x; yf (non-null): y in fp32 as well.
+template <typename T, typename TX, bool A_F32> struct EpiLinearLN {
+  static constexpr bool kBlock = true;
+  typedef T out_t;
+  typedef typename VecT<T, 4>::type b4;
+  typedef typename VecT<TX, 4>::type x4;
+  const TX* x;
+  const T* bias;
+  const T* gamma;
+  const T* beta;
+  T* y;
+  float* yf;
+  int M, N;
+  static constexpr size_t kLdsBytes = 2 * 64 * 2 * sizeof(float);  // row partials of 2 passes
+  __device__ __forceinline__ b4 bias4(int n) const {
+    b4 v = {};
+    if (n < N) v = *(const b4*)(bias + n);
+    return v;
+  }
+  template <int TM, int TN, int WN>
+  __device__ __forceinline__ void block(char* smem, int m0, int n0, int wave, int lane,
+                                        const f32x16 (&acc)[TN][TM],
+                                        const b4 (&bq)[TN][4]) const {
+    static_assert(TM == 1 && TN == 2 && WN == 2, "64 x 128 tile of 2 x 2 waves");
+    const int wm = wave / WN, wn = wave % WN, lr = lane % 32, g = lane / 32;
+    const int rl = wm * 32 + lr, row = m0 + rl;
+    const bool ok = row < M;
+    float* red = (float*)smem;  // [pass][64 rows][2 wave columns]
+    float z[TN][16];
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + (wn * TN + j) * 32 + 8 * q + 4 * g;
+        x4 xv = {};
+        if (ok) xv = *(const x4*)(x + (size_t)row * N + n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float av = acc[j][0][4 * q + e] + 0.0f;
+          const float a = A_F32 ? av : to_f32(from_f32<T>(av));
+          z[j][4 * q + e] = to_f32(xv[e]) + a + to_f32(bq[j][q][e]);
+          sum += z[j][4 * q + e];
+        }
+      }
+    sum += __shfl_xor(sum, 32);
+    if (g == 0) red[rl * 2 + wn] = sum;
+    __syncthreads();
+    const float inv_n = 1.0f / (float)N;
+    const float mean = (red[rl * 2] + red[rl * 2 + 1]) * inv_n;
+    float sq = 0.f;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float d = z[j][r] - mean;
+        sq += d * d;
+      }
+    sq += __shfl_xor(sq, 32);
+    if (g == 0) red[128 + rl * 2 + wn] = sq;
+    __syncthreads();
+    const float rs = rsqrtf((red[128 + rl * 2] + red[128 + rl * 2 + 1]) * inv_n + FTX_LN_EPSILON);
+    if (!ok) return;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + (wn * TN + j) * 32 + 8 * q + 4 * g;
+        const b4 gv = *(const b4*)(gamma + n), btv = *(const b4*)(beta + n);
+        f32x4 of;
+        b4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          of[e] = to_f32(gv[e]) * ((z[j][4 * q + e] - mean) * rs) + to_f32(btv[e]);
+          o[e] = from_f32<T>(of[e]);
+        }
+        *(b4*)(y + (size_t)row * N + n) = o;
+        if (yf) *(f32x4*)(yf + (size_t)row * N + n) = of;
+      }
+  }
+};
+
 // Split-K partial products: the tile of K range blockIdx.y is written, unscaled and in fp32,
 // to P[blockIdx.y][M][N]; splitk_reduce_kernel then sums the ranges in order and applies
 // the real epilogue.
@@ -1033,6 +1120,39 @@ hipError_t launch_linear(ftx_dtype dt, int M, int N, int K, const void* a, const
     case FTX_FP32: return linear_t<float>(M, N, K, a, w_t, bias, gelu, false, c, s, ws, ws_elems);
     case FTX_FP16: return linear_t<f16>(M, N, K, a, w_t, bias, gelu, out_f32, c, s, ws, ws_elems);
     case FTX_BF16: return linear_t<bf16>(M, N, K, a, w_t, bias, gelu, out_f32, c, s, ws, ws_elems);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, typename TX, bool A_F32>
+static hipError_t linear_ln_t(int M, int K, const void* a, const void* w_t, const void* x,
+                              const void* bias, const void* gamma, const void* beta, void* y,
+                              float* yf, hipStream_t s) {
+  constexpr int N = 128;
+  typedef EpiLinearLN<T, TX, A_F32> Epi;
+  Epi epi{(const TX*)x, (const T*)bias, (const T*)gamma, (const T*)beta, (T*)y, yf, M, N};
+  gemm_kernel<T, 64, 128, 2, 2, Epi><<<(M + 63) / 64, 4 * kWave, 0, s>>>(
+      (const T*)a, (const T*)w_t, M, N, K, K, epi);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_layernorm(ftx_dtype dt, int M, int N, int K, const void* a,
+                                   const void* w_t, const void* x, bool x_f32, bool a_f32,
+                                   const void* bias, const void* gamma, const void* beta,
+                                   void* y, float* yf, hipStream_t s) {
+  if (N != 128 || M < 1 || K < 8 || K % 8 || K > kMaxInnerDim) return hipErrorInvalidValue;
+  if (x_f32 && !a_f32) return hipErrorInvalidValue;
+  switch (dt) {
+    case FTX_FP32:
+      return linear_ln_t<float, float, true>(M, K, a, w_t, x, bias, gamma, beta, y, yf, s);
+    case FTX_FP16:
+      if (x_f32) return linear_ln_t<f16, float, true>(M, K, a, w_t, x, bias, gamma, beta, y, yf, s);
+      if (a_f32) return linear_ln_t<f16, f16, true>(M, K, a, w_t, x, bias, gamma, beta, y, yf, s);
+      return linear_ln_t<f16, f16, false>(M, K, a, w_t, x, bias, gamma, beta, y, yf, s);
+    case FTX_BF16:
+      if (x_f32) return linear_ln_t<bf16, float, true>(M, K, a, w_t, x, bias, gamma, beta, y, yf, s);
+      if (a_f32) return linear_ln_t<bf16, bf16, true>(M, K, a, w_t, x, bias, gamma, beta, y, yf, s);
+      return linear_ln_t<bf16, bf16, false>(M, K, a, w_t, x, bias, gamma, beta, y, yf, s);
   }
   return hipErrorInvalidValue;
 }

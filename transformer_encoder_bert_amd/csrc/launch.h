@@ -82,6 +82,16 @@ hipError_t launch_bias_residual_layernorm_f32res(ftx_dtype dt, int rows, int col
                                                  const void* beta, void* y, float* yf,
                                                  hipStream_t s);
 
+// Projection a w_t (N = 128: one 64 x 128 tile holds whole rows) with the bias + residual +
+// LayerNorm of launch_bias_residual_layernorm in its epilogue: y = LN(x + a w_t + bias).
+// a_f32: the projection's output counts unrounded (the fp32 residual stream of the 16-bit
+// modes); x_f32: x is fp32; yf (non-null) also receives y in fp32.
+// hipErrorInvalidValue when N != 128.
+hipError_t launch_linear_layernorm(ftx_dtype dt, int M, int N, int K, const void* a,
+                                   const void* w_t, const void* x, bool x_f32, bool a_f32,
+                                   const void* bias, const void* gamma, const void* beta,
+                                   void* y, float* yf, hipStream_t s);
+
 // The LayerNorm above after a projection split over K: a = the sum of the fp32 partials
 // p[0..splits-1][rows][cols] in split order (what the split-K reduction computes), rounded to
 // the storage type unless a_f32 (the projection's output would have been fp32); x is read
