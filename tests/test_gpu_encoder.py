@@ -228,6 +228,7 @@ def test_max_hidden_and_odd_heads():
     si.Shape(1, 32, 24, 64, 1, "fp16"),  # hidden 1536, one sequence
     si.Shape(2, 32, 24, 64, 1, "bf16"),  # the same with the fp32 residual stream
     si.Shape(1, 32, 4, 64, 1, "fp32"),   # fp32, hidden 256
+    si.Shape(3, 32, 48, 32, 1, "fp16"),  # size per head 32
 ])
 def test_split_k_paths(shape):
     """The small-batch path: at these shapes every projection splits K; the Q/K/V head split
