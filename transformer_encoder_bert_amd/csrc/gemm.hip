@@ -1003,8 +1003,11 @@ size_t gemm_splitk_workspace(ftx_dtype dt, int M, int N, int K) {
 
 // The ping-pong K loop pays off once a tile runs enough slabs: measured at 16384-32768 rows,
 // 0-4% faster at K = 1024 (16 slabs), 7-15% at K = 3072-4096 and 9% at K = 24576, but up
-// to 4% slower at K = 768 (12 slabs), where its idle first and last phases weigh more.
+// to 4% slower at K = 768 (12 slabs) on the 192- and 128-column tiles, where its idle first
+// and last phases weigh more.  The 256x256 tile (32 MFMAs per burst) takes it from 12
+// slabs: BERT-base FFN-in at batch 512 94.0 -> 91.2 us, the forward 3.310 -> 3.266 ms.
 constexpr int kPingPongMinSlabs = 16;
+constexpr int kPingPongMinSlabsWide = 12;  // 256x256 tiles
 
 // A 64x64 tile multiplies 64 x 64 x 64 per slab, far less than the latency of the slab's
 // loads: with 24 slabs or more per block it keeps two slabs in flight (three LDS stages,
@@ -1045,7 +1048,7 @@ static hipError_t gemm_launch_cfg(int M, int N, int K, const void* a, const void
   }
   if constexpr (sizeof(T) == 2 && BM == 256 && WM == 4 && WN == 2) {
     constexpr int BK = GemmCfg<T, BM, BN, WM, WN>::BK;
-    if (K % BK == 0 && K / BK >= kPingPongMinSlabs) {
+    if (K % BK == 0 && K / BK >= (BN == 256 ? kPingPongMinSlabsWide : kPingPongMinSlabs)) {
       gemm_pp_kernel<T, BM, BN, Epi><<<tiles, WM * WN * kWave, 0, s>>>(
           (const T*)a, (const T*)w_t, M, N, K, K, epi);
       return hipGetLastError();
