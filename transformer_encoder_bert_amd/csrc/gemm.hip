@@ -1001,13 +1001,13 @@ size_t gemm_splitk_workspace(ftx_dtype dt, int M, int N, int K) {
   return p.splits > 1 ? (size_t)p.splits * M * N : 0;
 }
 
-// The ping-pong K loop pays off once a tile runs enough slabs: measured at 16384-32768 rows,
-// 0-4% faster at K = 1024 (16 slabs), 7-15% at K = 3072-4096 and 9% at K = 24576, but up
-// to 4% slower at K = 768 (12 slabs) on the 192- and 128-column tiles, where its idle first
-// and last phases weigh more.  The 256x256 tile (32 MFMAs per burst) takes it from 12
-// slabs: BERT-base FFN-in at batch 512 94.0 -> 91.2 us, the forward 3.310 -> 3.266 ms.
-constexpr int kPingPongMinSlabs = 16;
-constexpr int kPingPongMinSlabsWide = 12;  // 256x256 tiles
+// The ping-pong K loop from 12 slabs (K >= 768 in 16-bit).  Measured in whole forwards,
+// against the two-buffer loop on the same box: BERT-base S32 B512 3.242 -> 3.215 ms (FFN-in
+// alone 94.0 -> 91.2 us), S128 B64 2.165 -> 2.128, S64 B64 1.222 -> 1.210, the decoder B512
+// 4.875 -> 4.777; BERT-large (K = 1024) Q/K/V 202 -> 195 us, FFN-out at K = 3072-4096 7-15%
+// faster.  (A 256x192 projection repeated alone on weights already in L2 runs 0-4% slower
+// at 12 slabs; in the forward it gains.)
+constexpr int kPingPongMinSlabs = 12;
 
 // A 64x64 tile multiplies 64 x 64 x 64 per slab, far less than the latency of the slab's
 // loads: with 24 slabs or more per block it keeps two slabs in flight (three LDS stages,
@@ -1048,7 +1048,7 @@ static hipError_t gemm_launch_cfg(int M, int N, int K, const void* a, const void
   }
   if constexpr (sizeof(T) == 2 && BM == 256 && WM == 4 && WN == 2) {
     constexpr int BK = GemmCfg<T, BM, BN, WM, WN>::BK;
-    if (K % BK == 0 && K / BK >= (BN == 256 ? kPingPongMinSlabsWide : kPingPongMinSlabs)) {
+    if (K % BK == 0 && K / BK >= kPingPongMinSlabs) {
       gemm_pp_kernel<T, BM, BN, Epi><<<tiles, WM * WN * kWave, 0, s>>>(
           (const T*)a, (const T*)w_t, M, N, K, K, epi);
       return hipGetLastError();
