@@ -70,7 +70,7 @@ CASES = [
     (9, 32, 4, 32, "random"),       # d = 32: two heads per tile (the pruned model's 4 x 32)
     (3, 32, 2, 32, None),
     (3, 128, 6, 32, [128, 50, 1]),
-    # hidden size 1024 (16 K slabs): 128-row tiles below 256 tiles of 256 rows ...
+    # hidden size 1024: 128-row tiles while 256-row tiles would number 128 or fewer ...
     (3, 128, 16, 64, [128, 70, 1]),  # BERT-large heads
     (9, 32, 32, 32, "random"),
     # ... and 256-row tiles on the ping-pong K loop from there on
@@ -177,7 +177,7 @@ STACK = [
     (2, 230, 2, 64, "fp16", None),        # padded to 256
     (9, 32, 4, 32, "fp16", (1, 32)),      # the pruned model's 4 x 32
     (3, 64, 4, 32, "bf16", None),
-    (3, 128, 16, 64, "bf16", (64, 128)),  # BERT-large heads: ping-pong K loop
+    (3, 128, 16, 64, "bf16", (64, 128)),  # BERT-large heads
 ]
 
 

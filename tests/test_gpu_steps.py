@@ -63,7 +63,8 @@ LINEAR_SHAPES = [
     (4096, 2312, 768),   # 256x192 tiles with a ragged N tail
     (16416, 768, 768),   # 256x128 tiles with a ragged M tail
     (16384, 3072, 768),  # 256x256 tiles (BERT-base FFN-in at batch 512)
-    # K of 24 slabs or more takes the ping-pong K loop (16-bit dtypes, 256-row tiles)
+    # 256-row tiles with 12 slabs or more take the ping-pong K loop (16-bit dtypes; so do the
+    # 256x256 and 256x192 shapes above)
     (16384, 768, 3072),  # 256x192 tiles (BERT-base FFN-out at batch 512)
     (16416, 768, 3072),  # 256x256 tiles with a ragged M tail
     (4000, 4040, 2048),  # 256x256 tiles with ragged M and N tails
