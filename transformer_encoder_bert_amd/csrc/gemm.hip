@@ -1010,11 +1010,11 @@ size_t gemm_splitk_workspace(ftx_dtype dt, int M, int N, int K) {
 constexpr int kPingPongMinSlabs = 12;
 
 // A 64x64 tile multiplies 64 x 64 x 64 per slab, far less than the latency of the slab's
-// loads: with 24 slabs or more per block it keeps two slabs in flight (three LDS stages,
-// 48 KB).  Measured on the BERT-base FFN-out projection at batch 64 (2048 x 768 x 3072):
-// 24.8 -> 20.6 us; at 12 slabs (the attention-output projection) the third stage costs
-// 4% instead.
-constexpr int kSmallTileDeepSlabs = 24;
+// loads: with 12 slabs or more per block it keeps two slabs in flight (three LDS stages,
+// 48 KB).  Measured on whole forwards against two stages (same box): BERT-base B64 0.814 ->
+// 0.805 ms, B16 0.670 -> 0.653, the decoder B64 1.516 -> 1.455; the FFN-out projection at
+// batch 64 (2048 x 768 x 3072) alone 24.8 -> 20.6 us.
+constexpr int kSmallTileDeepSlabs = 12;
 
 template <typename T, int BM, int BN, int WM, int WN, typename Epi>
 static void gemm_kernel_launch(dim3 grid, int kchunk, int M, int N, int K, const void* a,
