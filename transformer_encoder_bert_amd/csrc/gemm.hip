@@ -960,9 +960,15 @@ static TileCfg choose_tile(int M, int N, bool wide) {
 }
 
 // Split-K (the small-batch path): when the chosen configuration has fewer tiles than there
-// are CUs, K is cut into up to 16 ranges of at least two slabs each, so that
-// about 512 blocks run; the partial products go to an fp32 workspace [splits][M][N] and a
-// reduction kernel (or the LayerNorm that follows) finishes them.  The partials are capped
+// are CUs, K is cut into up to 16 ranges of at least two slabs each, so that about 512
+// blocks run.  When it has more tiles than CUs but fewer waves than SIMDs (only 32x32
+// tiles, one wave each, reach this), K is cut so that about one wave per SIMD runs.
+// Measured in whole forwards against splitting below 256 tiles only (same box): BERT-base
+// B12 0.683 -> 0.529 ms, B16 0.653 -> 0.520, the decoder B16 1.205 -> 1.029; splitting the
+// 384 four-wave 64x64 tiles at B64 in two instead lost (0.813 -> 0.845), and filling the
+// SIMDs below 256 tiles too (B8: 6 splits of two slabs, not 3 of four) lost 0.548 -> 0.561.
+// The partial products go to an fp32 workspace [splits][M][N] and a reduction kernel (or
+// the LayerNorm that follows) finishes them.  The partials are capped
 // at 16 MiB (fewer splits, or none): their round trip through memory must stay small
 // against what the split saves -- at 4096 rows a 6-way split of the 768-wide projections
 // would move 75 MB and lose.  Without a workspace of the planned size the GEMM is not
@@ -976,6 +982,8 @@ struct GemmPlan {
   int kchunk;  // K elements per split (K when splits == 1)
 };
 
+constexpr long kSIMDs = 1024;  // 256 CUs x 4 SIMDs
+
 static GemmPlan plan_gemm(int M, int N, int K, int elem_bytes) {
   static const int bm[TILE_COUNT] = {256, 256, 256, 128, 64, 32};
   static const int bn[TILE_COUNT] = {256, 192, 128, 128, 64, 32};
@@ -983,10 +991,13 @@ static GemmPlan plan_gemm(int M, int N, int K, int elem_bytes) {
   const int bk = 128 / elem_bytes;
   const long tiles = (long)((M + bm[p.cfg] - 1) / bm[p.cfg]) * ((N + bn[p.cfg] - 1) / bn[p.cfg]);
   const int nk = (K + bk - 1) / bk;
-  if (tiles < 256 && nk >= 4) {
+  static const int waves[TILE_COUNT] = {8, 8, 8, 4, 4, 1};
+  if ((tiles < 256 || tiles * waves[p.cfg] < kSIMDs) && nk >= 4) {
     constexpr size_t kMaxPartialBytes = 16u << 20;
     const long by_bytes = (long)(kMaxPartialBytes / ((size_t)M * N * sizeof(float)));
-    int sp = (int)std::min<long>(std::min<long>((512 + tiles - 1) / tiles, nk / 2),
+    const long wv = tiles * waves[p.cfg];
+    const long fill = tiles < 256 ? (512 + tiles - 1) / tiles : (kSIMDs + wv - 1) / wv;
+    int sp = (int)std::min<long>(std::min<long>(fill, nk / 2),
                                  std::min<long>(16, by_bytes));
     if (sp > 1) {
       p.kchunk = (nk + sp - 1) / sp * bk;
