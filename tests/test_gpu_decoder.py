@@ -89,6 +89,9 @@ CASES = [
     (2, 64, 32, 4, 32, 2, "fp16", (5, 32), "random_affine"),
     (3, 32, 96, 12, 64, 2, "fp16", (40, 96), "bert"),
     (2, 64, 128, 4, 64, 2, "bf16", (64, 128), "random_affine"),
+    # 512 target rows at hidden 768: the three projections before a LayerNorm split K over
+    # 384 tiles of 32 x 32, and the LayerNorms sum the partials
+    (16, 32, 32, 12, 64, 1, "fp16", (8, 32), "random_affine"),
 ]
 
 

@@ -231,11 +231,12 @@ def test_max_hidden_and_odd_heads():
     si.Shape(3, 32, 48, 32, 1, "fp16"),  # size per head 32
     si.Shape(16, 32, 12, 64, 1, "fp16"),  # BERT-base, 512 rows: 384 tiles of 32 x 32
     si.Shape(12, 32, 12, 64, 1, "bf16"),  # 384 rows: 288 tiles of 32 x 32
+    si.Shape(1, 512, 16, 64, 1, "bf16"),  # BERT-large, 512 rows: 512 tiles of 32 x 32
 ])
 def test_split_k_paths(shape):
     """The small-batch path: at the first four shapes every projection splits K; the Q/K/V
     head split and the GELU finish their partials in the reduction, the attention-output and
-    FFN-out partials are summed by the LayerNorm after them.  At the last two only the
+    FFN-out partials are summed by the LayerNorm after them.  At the last three only the
     attention-output and FFN-out projections split (more 32 x 32 tiles than CUs, fewer
     waves than SIMDs).  One layer at the layer bar."""
     c = si.custom_case(shape, 31, lens_range=(1, shape.seq_len), params="random_affine")

@@ -107,7 +107,7 @@ bool use_fused_self_attention(const ftx_decoder* e) {
   if (e->fused_attention == 2) return true;
   if (e->Td < 256) return false;
   return fused_attention_tiles(e->Td, e->H) >= 64 ||
-         linear_splits(e->dt, e->Td, 3 * e->H, e->H, e->splitk_elems) > 1;
+         linear_splits(e->dt, e->Td, 3 * e->H, e->H, e->splitk_elems, false) > 1;
 }
 
 ftx_status enqueue_decoder(ftx_decoder* e, const void* input, const void* memory,
@@ -125,7 +125,7 @@ ftx_status enqueue_decoder(ftx_decoder* e, const void* input, const void* memory
   auto proj_ln = [&](int proj_step, int ln_step, const void* a, const void* w_t, int kin,
                      const void* xr, bool xr_f32, const void* bias, const void* gamma,
                      const void* beta, void* y, float* yf) -> ftx_status {
-    const int sp = linear_splits(dt, Td, H, kin, wn);
+    const int sp = linear_splits(dt, Td, H, kin, wn, true);
     ftx_status r;
     if (sp > 1) {
       if ((r = step(e, proj_step, s, [&] {

@@ -160,7 +160,7 @@ bool use_fused_attention(const ftx_encoder* e) {
   if (e->fused_attention == 2) return true;
   if (e->T < 256) return false;
   return fused_attention_tiles(e->T, e->H) >= 64 ||
-         linear_splits(e->dt, e->T, 3 * e->H, e->H, e->splitk_elems) > 1;
+         linear_splits(e->dt, e->T, 3 * e->H, e->H, e->splitk_elems, false) > 1;
 }
 
 // Enqueue the L-layer forward on `s` (arguments already validated).
@@ -218,7 +218,7 @@ ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq
     // (small batches) leaves its fp32 partials to the LayerNorm that follows it, which sums
     // them itself: one launch instead of reduction + LayerNorm.
     const bool row_ln = H == 128 && (T + 63) / 64 >= 128;
-    const int o_splits = linear_splits(dt, T, H, H, e->splitk_elems);
+    const int o_splits = linear_splits(dt, T, H, H, e->splitk_elems, true);
     if (row_ln) {
       st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
         return launch_linear_layernorm(dt, T, H, H, e->ctx, w.w_o_t, x, false, e->y1f != nullptr,
@@ -264,7 +264,7 @@ ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq
       });
     }
     if (st != FTX_OK) return st;
-    const int f_splits = linear_splits(dt, T, H, F, e->splitk_elems);
+    const int f_splits = linear_splits(dt, T, H, F, e->splitk_elems, true);
     if (row_ln) {
       st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
         const bool f32res = e->y1f != nullptr;

@@ -962,11 +962,16 @@ static TileCfg choose_tile(int M, int N, bool wide) {
 // Split-K (the small-batch path): when the chosen configuration has fewer tiles than there
 // are CUs, K is cut into up to 16 ranges of at least two slabs each, so that about 512
 // blocks run.  When it has more tiles than CUs but fewer waves than SIMDs (only 32x32
-// tiles, one wave each, reach this), K is cut so that about one wave per SIMD runs.
-// Measured in whole forwards against splitting below 256 tiles only (same box): BERT-base
-// B12 0.683 -> 0.529 ms, B16 0.653 -> 0.520, the decoder B16 1.205 -> 1.029; splitting the
-// 384 four-wave 64x64 tiles at B64 in two instead lost (0.813 -> 0.845), and filling the
-// SIMDs below 256 tiles too (B8: 6 splits of two slabs, not 3 of four) lost 0.548 -> 0.561.
+// tiles, one wave each, reach this), K is cut so that about one wave per SIMD runs -- but
+// only where the LayerNorm after the projection sums the partials (no reduction launch)
+// and its rows are at least 256 wide.  Measured in whole forwards against splitting below
+// 256 tiles only (same box): BERT-base B12 0.683 -> 0.529 ms, B16 0.653 -> 0.518, BERT-large
+// S512 B1 2.346 -> 1.796, S128 B2 2.264 -> 1.436, the decoder B16 1.205 -> 1.029.  Losses
+// that set the conditions: the same split with a reduction launch (Q/K/V and FFN-in at 128
+// rows, S128 B1 0.500 -> 0.551), hidden size 128 (the 4x32 model B64 0.297 -> 0.317, B128
+// 0.328 -> 0.372), 384 four-wave 64x64 tiles at B64 cut in two (0.813 -> 0.845), and
+// filling the SIMDs below 256 tiles too (B8: 6 splits of two slabs, not 3 of four, 0.548 ->
+// 0.561).
 // The partial products go to an fp32 workspace [splits][M][N] and a reduction kernel (or
 // the LayerNorm that follows) finishes them.  The partials are capped
 // at 16 MiB (fewer splits, or none): their round trip through memory must stay small
@@ -984,7 +989,9 @@ struct GemmPlan {
 
 constexpr long kSIMDs = 1024;  // 256 CUs x 4 SIMDs
 
-static GemmPlan plan_gemm(int M, int N, int K, int elem_bytes) {
+// sums_partials: the kernel after this projection sums its partials itself (the split-K
+// LayerNorm), so a split costs no reduction launch.
+static GemmPlan plan_gemm(int M, int N, int K, int elem_bytes, bool sums_partials) {
   static const int bm[TILE_COUNT] = {256, 256, 256, 128, 64, 32};
   static const int bn[TILE_COUNT] = {256, 192, 128, 128, 64, 32};
   GemmPlan p{choose_tile(M, N, elem_bytes == 2), 1, K};
@@ -992,7 +999,8 @@ static GemmPlan plan_gemm(int M, int N, int K, int elem_bytes) {
   const long tiles = (long)((M + bm[p.cfg] - 1) / bm[p.cfg]) * ((N + bn[p.cfg] - 1) / bn[p.cfg]);
   const int nk = (K + bk - 1) / bk;
   static const int waves[TILE_COUNT] = {8, 8, 8, 4, 4, 1};
-  if ((tiles < 256 || tiles * waves[p.cfg] < kSIMDs) && nk >= 4) {
+  const bool fill_simds = sums_partials && N >= 256 && tiles * waves[p.cfg] < kSIMDs;
+  if ((tiles < 256 || fill_simds) && nk >= 4) {
     constexpr size_t kMaxPartialBytes = 16u << 20;
     const long by_bytes = (long)(kMaxPartialBytes / ((size_t)M * N * sizeof(float)));
     const long wv = tiles * waves[p.cfg];
@@ -1008,8 +1016,12 @@ static GemmPlan plan_gemm(int M, int N, int K, int elem_bytes) {
 }
 
 size_t gemm_splitk_workspace(ftx_dtype dt, int M, int N, int K) {
-  const GemmPlan p = plan_gemm(M, N, K, dt == FTX_FP32 ? 4 : 2);
-  return p.splits > 1 ? (size_t)p.splits * M * N : 0;
+  size_t need = 0;
+  for (bool sums : {false, true}) {
+    const GemmPlan p = plan_gemm(M, N, K, dt == FTX_FP32 ? 4 : 2, sums);
+    if (p.splits > 1) need = std::max(need, (size_t)p.splits * M * N);
+  }
+  return need;
 }
 
 // The ping-pong K loop from 12 slabs (K >= 768 in 16-bit).  Measured in whole forwards,
@@ -1074,7 +1086,7 @@ static hipError_t gemm_launch(int M, int N, int K, const void* a, const void* w_
                               hipStream_t s, float* ws = nullptr, size_t ws_elems = 0,
                               bool reduce = true) {
   constexpr bool wide = sizeof(T) == 2;
-  GemmPlan plan = plan_gemm(M, N, K, (int)sizeof(T));
+  GemmPlan plan = plan_gemm(M, N, K, (int)sizeof(T), !reduce);
   if (plan.splits > 1 && (!ws || ws_elems < (size_t)plan.splits * M * N)) {
     plan.splits = 1;
     plan.kchunk = K;
@@ -1095,14 +1107,14 @@ static hipError_t gemm_launch(int M, int N, int K, const void* a, const void* w_
   return hipErrorInvalidValue;
 }
 
-int linear_splits(ftx_dtype dt, int M, int N, int K, size_t ws_elems) {
-  const GemmPlan p = plan_gemm(M, N, K, dt == FTX_FP32 ? 4 : 2);
+int linear_splits(ftx_dtype dt, int M, int N, int K, size_t ws_elems, bool sums_partials) {
+  const GemmPlan p = plan_gemm(M, N, K, dt == FTX_FP32 ? 4 : 2, sums_partials);
   return (p.splits > 1 && ws_elems >= (size_t)p.splits * M * N) ? p.splits : 1;
 }
 
 hipError_t launch_linear_partials(ftx_dtype dt, int M, int N, int K, const void* a,
                                   const void* w_t, float* ws, size_t ws_elems, hipStream_t s) {
-  if (linear_splits(dt, M, N, K, ws_elems) < 2) return hipErrorInvalidValue;
+  if (linear_splits(dt, M, N, K, ws_elems, true) < 2) return hipErrorInvalidValue;
   // the epilogue only serves the reduction, which is not launched
   switch (dt) {
     case FTX_FP32:

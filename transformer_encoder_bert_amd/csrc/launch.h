@@ -49,8 +49,11 @@ hipError_t launch_qkv_attention(ftx_dtype dt, int B, int S, int nh, int d, const
 // fp32 elements of split-K workspace the GEMM of this shape uses (0: it does not split).
 size_t gemm_splitk_workspace(ftx_dtype dt, int M, int N, int K);
 
-// K ranges launch_linear splits this shape into with ws_elems fp32 of workspace (1: none).
-int linear_splits(ftx_dtype dt, int M, int N, int K, size_t ws_elems);
+// K ranges a projection of this shape is split into with ws_elems fp32 of workspace (1:
+// none).  sums_partials: the partials go to the kernel after it (launch_linear_partials,
+// then the split-K LayerNorm), which splits more shapes than a projection that finishes
+// its partials with a reduction launch of its own (launch_linear and the other GEMMs).
+int linear_splits(ftx_dtype dt, int M, int N, int K, size_t ws_elems, bool sums_partials);
 
 // The split-K partial products of the projection c = a w alone: ws[z][M][N] fp32 for the
 // linear_splits(...) ranges z, summed by nobody yet (launch_splitk_bias_residual_layernorm
