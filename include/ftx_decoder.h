@@ -80,8 +80,8 @@ ftx_status ftx_decoder_forward(ftx_decoder *dec, const void *input, const void *
  *     and an internal decoder length of 32, 64, 128 or 256, the self Q/K/V projection
  *     attends each of its 256 x 192 (or 128 x 192) tiles in its epilogue (step class
  *     FTX_DEC_STEP_SELF_QKV_ATTENTION); 0 never; 1 when batch*len >= 256 (len: the internal
- *     decoder length) and either the 256-row grid has at least 64 tiles or the separate
- *     Q/K/V projection would split its K dimension; 2 whenever the shape fits; other
+ *     decoder length) and the 256-row grid has at least 64 tiles; 2 whenever the shape
+ *     fits; other
  *     values -> FTX_ERR_INVALID_ARG. */
 ftx_status ftx_decoder_set_option(ftx_decoder *dec, ftx_option option, int value);
 

@@ -211,9 +211,8 @@ def test_encoder_fused_and_separate_agree():
 
 def test_encoder_auto_mode_needs_64_tiles():
     """Default mode: fused from 64 tiles of 256 x 192 (BERT-base S32: B = 48 gives 6 x 12),
-    separate below (B = 40 gives 5 x 12, B = 16 gives 2 x 12) -- except where the separate
-    Q/K/V projection would split K (B = 8, 256 tokens)."""
-    for B, fused in ((8, True), (16, False), (40, False), (48, True)):
+    separate below (B = 40 gives 5 x 12, B = 16 gives 2 x 12, B = 8 gives 1 x 12)."""
+    for B, fused in ((8, False), (16, False), (40, False), (48, True)):
         c = si.make_case("bert_base_fp16_s32", B, params="bert", num_layers=1)
         enc = _encoder(c.shape, list(c.layers()), 1)
         enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)

@@ -100,14 +100,13 @@ ftx_status step(ftx_decoder* e, int cls, hipStream_t s, F&& launch) {
 }
 
 // The causal self-attention runs inside the self Q/K/V projection when the shape fits and,
-// in the default mode, when there are at least 256 decoder rows and either 64 tiles of 256
-// rows or a separate Q/K/V projection that would split K, as in the encoder.
+// in the default mode, when there are at least 256 decoder rows and 64 tiles of 256 rows,
+// as in the encoder.
 bool use_fused_self_attention(const ftx_decoder* e) {
   if (!e->attn_fits || e->fused_attention == 0) return false;
   if (e->fused_attention == 2) return true;
   if (e->Td < 256) return false;
-  return fused_attention_tiles(e->Td, e->H) >= 64 ||
-         linear_splits(e->dt, e->Td, 3 * e->H, e->H, e->splitk_elems, false) > 1;
+  return fused_attention_tiles(e->Td, e->H) >= 64;
 }
 
 ftx_status enqueue_decoder(ftx_decoder* e, const void* input, const void* memory,

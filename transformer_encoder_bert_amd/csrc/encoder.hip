@@ -148,19 +148,19 @@ void drop_graph(ftx_encoder* e) {
 
 // The projection with the attention in its epilogue replaces the projection + attention
 // pair when the shape fits and, in the default mode, when there are at least 256 tokens and
-// either 64 tiles of 256 rows or a separate Q/K/V projection that would split K (three
-// launches: partials, reduction, attention).  Below that the tiles are mostly padding rows
-// or the long epilogue runs on few CUs, while the separate kernels spread the same work.
-// Measured, fused against separate (128-row tiles below 256 tiles of 256 rows): BERT-base
-// S32 B1 0.482 against 0.462 ms, B8 (split Q/K/V) 0.549 against 0.607, B16 0.691 against
-// 0.670, B64 0.805 against 0.867; S64 B64 1.253 against 1.508; the 4 x 32 model B64 0.294
-// against 0.296, B512 0.464 against 0.514.
+// 64 tiles of 256 rows.  Below that the tiles are mostly padding rows or the long epilogue
+// runs on few CUs, while the separate kernels spread the same work.  Measured, fused against
+// separate (128-row tiles below 256 tiles of 256 rows): BERT-base S32 B1 0.482 against 0.462
+// ms, B8 0.510 against 0.466, B12 0.529 against 0.482, B16 0.691 against 0.670, B64 0.805
+// against 0.867; S64 B4 0.522 against 0.485, S64 B64 1.253 against 1.508; BERT-large S128 B2
+// 1.431 against 1.280; the 4 x 32 model B64 0.294 against 0.296, B512 0.464 against 0.514.
+// (Small batches once took the fused kernel whenever the separate Q/K/V projection split
+// K; with that split capped it no longer pays.)
 bool use_fused_attention(const ftx_encoder* e) {
   if (!e->fused || !e->attn_fits || e->fused_attention == 0) return false;
   if (e->fused_attention == 2) return true;
   if (e->T < 256) return false;
-  return fused_attention_tiles(e->T, e->H) >= 64 ||
-         linear_splits(e->dt, e->T, 3 * e->H, e->H, e->splitk_elems, false) > 1;
+  return fused_attention_tiles(e->T, e->H) >= 64;
 }
 
 // Enqueue the L-layer forward on `s` (arguments already validated).

@@ -973,8 +973,8 @@ static TileCfg choose_tile(int M, int N, bool wide) {
 // filling the SIMDs below 256 tiles too (B8: 6 splits of two slabs, not 3 of four, 0.548 ->
 // 0.561).
 // The partial products go to an fp32 workspace [splits][M][N] and a reduction kernel (or
-// the LayerNorm that follows) finishes them.  The partials are capped
-// at 16 MiB (fewer splits, or none): their round trip through memory must stay small
+// the LayerNorm that follows) finishes them.  The partials are capped at 16 MiB, at 4 MiB
+// where a reduction launch finishes them (fewer splits, or none): their round trip through memory must stay small
 // against what the split saves -- at 4096 rows a 6-way split of the 768-wide projections
 // would move 75 MB and lose.  Without a workspace of the planned size the GEMM is not
 // split.  Even a short K chain gains: the split spreads the reads of weights that arrive
@@ -988,6 +988,12 @@ struct GemmPlan {
 };
 
 constexpr long kSIMDs = 1024;  // 256 CUs x 4 SIMDs
+constexpr size_t kMaxPartialBytes = 16u << 20;
+// A split finished by a reduction launch also pays that launch and the second read of the
+// partials: above 4 MiB of partials it lost in whole forwards (BERT-base B8, FFN-in at 256
+// rows cut in three, 9 MiB: 0.551 against 0.511 ms unsplit; S64 B4 0.563 against 0.523;
+// the decoder B8 0.987 against 0.911).
+constexpr size_t kMaxReducedPartialBytes = 4u << 20;
 
 // sums_partials: the kernel after this projection sums its partials itself (the split-K
 // LayerNorm), so a split costs no reduction launch.
@@ -1001,8 +1007,8 @@ static GemmPlan plan_gemm(int M, int N, int K, int elem_bytes, bool sums_partial
   static const int waves[TILE_COUNT] = {8, 8, 8, 4, 4, 1};
   const bool fill_simds = sums_partials && N >= 256 && tiles * waves[p.cfg] < kSIMDs;
   if ((tiles < 256 || fill_simds) && nk >= 4) {
-    constexpr size_t kMaxPartialBytes = 16u << 20;
-    const long by_bytes = (long)(kMaxPartialBytes / ((size_t)M * N * sizeof(float)));
+    const size_t max_partial_bytes = sums_partials ? kMaxPartialBytes : kMaxReducedPartialBytes;
+    const long by_bytes = (long)(max_partial_bytes / ((size_t)M * N * sizeof(float)));
     const long wv = tiles * waves[p.cfg];
     const long fill = tiles < 256 ? (512 + tiles - 1) / tiles : (kSIMDs + wv - 1) / wv;
     int sp = (int)std::min<long>(std::min<long>(fill, nk / 2),
