@@ -57,6 +57,26 @@ __device__ __forceinline__ float gelu_tanh(float u) {
   return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
 }
 
+// Sum of the split-K partials p[0], p[stride], ..., p[(splits - 1) * stride] (four floats
+// each) in split order.  The loads go out four at a time before their additions, so a long
+// split costs a quarter of the dependent memory round trips; the additions keep the order.
+__device__ __forceinline__ f32x4 sum_partials4(const float* p, size_t stride, int splits) {
+  f32x4 acc = *(const f32x4*)p;
+  int z = 1;
+  for (; z + 4 <= splits; z += 4) {
+    const f32x4 v0 = *(const f32x4*)(p + z * stride);
+    const f32x4 v1 = *(const f32x4*)(p + (z + 1) * stride);
+    const f32x4 v2 = *(const f32x4*)(p + (z + 2) * stride);
+    const f32x4 v3 = *(const f32x4*)(p + (z + 3) * stride);
+    acc += v0;
+    acc += v1;
+    acc += v2;
+    acc += v3;
+  }
+  for (; z < splits; ++z) acc += *(const f32x4*)(p + z * stride);
+  return acc;
+}
+
 // Sum / max over groups of `width` consecutive lanes (width a power of two <= 64).
 template <int width> __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll

@@ -209,8 +209,7 @@ __global__ __launch_bounds__(256) void splitk_layernorm_kernel(const TX* __restr
   for (int gi = 0; gi < G; ++gi) {
     const int c = 4 * (threadIdx.x + 256 * gi);
     if (c < cols) {
-      f32x4 acc = *(const f32x4*)(p + base + c);
-      for (int k = 1; k < splits; ++k) acc += *(const f32x4*)(p + k * mn + base + c);
+      const f32x4 acc = sum_partials4(p + base + c, mn, splits);
       const x4 xv = *(const x4*)(x + base + c);
       const t4 bv = *(const t4*)(bias + c);
 #pragma unroll

@@ -288,8 +288,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   if (idx >= (int64_t)M * q4) return;
   const int m = (int)(idx / q4), n = (int)(idx % q4) * 4;
   const size_t mn = (size_t)M * N;
-  f32x4 acc = *(const f32x4*)(P + (size_t)m * N + n);
-  for (int z = 1; z < splits; ++z) acc += *(const f32x4*)(P + z * mn + (size_t)m * N + n);
+  const f32x4 acc = sum_partials4(P + (size_t)m * N + n, mn, splits);
   const auto bv = epi.bias4(n);
   float v[4];
 #pragma unroll
