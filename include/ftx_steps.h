@@ -106,6 +106,19 @@ ftx_status ftx_step_bias_gelu(ftx_dtype dtype, int rows, int cols, const void *u
 ftx_status ftx_step_transpose(ftx_dtype dtype, int rows, int cols, const void *in, void *out,
                               void *stream);
 
+/* The launch plan of an M x N x K projection (ftx_step_linear and the encoder's
+ * projections) on a device with `cus` compute units: the block tile tile_m x tile_n and the
+ * number of ranges K is split into (1 = no split).  sums_partials != 0: the plan of a
+ * projection whose split-K partials the LayerNorm after it sums (the attention-output and
+ * FFN-out projections), else of one that finishes them with its own reduction.  The handles
+ * and the step entry points read `cus` from the device (hipGetDeviceProperties) and plan
+ * with it; the article tunes launch configurations to the shape (section "Faster
+ * Transformer 优化原理").  Host arithmetic only, no HIP call: usable without a GPU.
+ * M, N, K, cus >= 1 and tile_m, tile_n, splits non-NULL (host pointers), else
+ * FTX_ERR_INVALID_ARG. */
+ftx_status ftx_plan_linear(ftx_dtype dtype, int M, int N, int K, int cus, int sums_partials,
+                           int *tile_m, int *tile_n, int *splits);
+
 #ifdef __cplusplus
 }
 #endif

@@ -156,3 +156,48 @@ def test_masked_attention_argument_checks(lib):
     assert lib.ftx_step_masked_attention(1, 1, 32, 64, 2, 64, 256, 512, 768, None, 1, 1024, None) == E
     assert lib.ftx_step_masked_attention(1, 1, 32, 48, 2, 64, 256, 512, 768, None, 0, 1024, None) == ftx.FTX_ERR_UNSUPPORTED
     assert lib.ftx_step_masked_attention(1, 1, 32, 64, 2, 64, None, 512, 768, None, 0, 1024, None) == E
+
+
+# (dtype, M, N, K, sums_partials) -> (tile_m, tile_n, splits) on 256 CUs: the BERT-base
+# projections at batch 512, 64, 8 and 1 (S = 32), BERT-large FFN-in at S128 B256, and the
+# single-layer fp32 model's Q/K/V projection
+PLANS_256_CUS = [
+    (("fp16", 16384, 2304, 768, False), (256, 192, 1)),
+    (("fp16", 16384, 768, 768, True), (256, 192, 1)),
+    (("fp16", 16384, 3072, 768, False), (256, 256, 1)),
+    (("fp16", 16384, 768, 3072, True), (256, 192, 1)),
+    (("fp16", 2048, 2304, 768, False), (128, 128, 1)),
+    (("fp16", 2048, 768, 3072, True), (64, 64, 1)),
+    (("fp16", 256, 3072, 768, False), (64, 64, 1)),
+    (("fp16", 256, 768, 3072, True), (32, 32, 3)),
+    (("fp16", 32, 2304, 768, False), (32, 32, 6)),
+    (("fp16", 32, 768, 3072, True), (32, 32, 16)),
+    (("bf16", 32768, 3072, 1024, False), (256, 256, 1)),
+    (("fp32", 32, 384, 128, False), (32, 32, 2)),
+]
+
+
+@pytest.mark.parametrize("args,plan", PLANS_256_CUS)
+def test_plans_on_256_cus(lib, args, plan):
+    """The planner reads the CU count from the device; on MI355X's 256 CUs it gives the
+    launch configurations the forward was tuned with."""
+    dt, M, N, K, sums = args
+    assert ftx.ftx_plan_linear(dt, M, N, K, 256, sums) == plan
+
+
+def test_plans_follow_the_cu_count(lib):
+    """A smaller part (e.g. one XCD of 32 CUs, or a partitioned device) gets plans sized for
+    it: fewer blocks to fill, so larger tiles and fewer K splits."""
+    assert ftx.ftx_plan_linear("fp16", 32, 768, 3072, 256, True) == (32, 32, 16)
+    assert ftx.ftx_plan_linear("fp16", 32, 768, 3072, 32, True) == (32, 32, 3)
+    assert ftx.ftx_plan_linear("fp16", 2048, 768, 3072, 256, True) == (64, 64, 1)
+    assert ftx.ftx_plan_linear("fp16", 2048, 768, 3072, 32, True) == (256, 192, 1)
+    assert ftx.ftx_plan_linear("fp16", 256, 768, 3072, 64, True) == (64, 64, 3)
+    assert ftx.ftx_plan_linear("fp16", 16384, 768, 3072, 32, True) == (256, 256, 1)
+    changed = sum(ftx.ftx_plan_linear("fp16", M, N, K, 256, s) != ftx.ftx_plan_linear("fp16", M, N, K, 32, s)
+                  for (_, M, N, K, s), _ in PLANS_256_CUS[:10])
+    assert changed >= 6
+    for bad in ((0, 768, 768, 256), (32, 768, 768, 0)):
+        with pytest.raises(ftx.FtxError) as e:
+            ftx.ftx_plan_linear("fp16", *bad, False)
+        assert e.value.status == ftx.FTX_ERR_INVALID_ARG

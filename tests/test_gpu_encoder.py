@@ -308,6 +308,8 @@ def test_graph_mode_replays_match_eager(workload, batch, seq):
     x = to_dev(c.x, shape.dtype)
     lens = dev_lens(c.lens)
     ref = enc.forward(x, lens).clone()
+    oref = oracle.encoder(c.x, layers, c.lens, shape.head_num)
+    print("eager", check(to_f64(ref), oref, shape.dtype, stack_tol(shape.dtype), "eager"))
     enc.set_option(ftx.FTX_OPT_GRAPH, 1)
     out = torch.empty_like(ref)
     for i in range(4):
@@ -315,20 +317,23 @@ def test_graph_mode_replays_match_eager(workload, batch, seq):
         enc.forward(x, lens, out)
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {i}"
+        check(to_f64(out), oref, shape.dtype, stack_tol(shape.dtype), f"replay {i}")
         junk = (x.float() * 3).sum()  # eager work on the stream between replays
         torch.cuda.synchronize()
     out2 = torch.empty_like(ref)
     enc.forward(x, lens, out2)           # new output buffer: captured again
     torch.cuda.synchronize()
     assert torch.equal(out2, ref)
+    check(to_f64(out2), oref, shape.dtype, stack_tol(shape.dtype), "new capture")
     enc.set_option(ftx.FTX_OPT_GRAPH, 0)
     assert torch.equal(enc.forward(x, lens), ref)
     enc.close()
     del junk
 
 
-def test_torch_operator_matches_the_c_abi():
-    """torch.ops.ftx.encoder_forward (and the nn.Module around it) is ftx_forward."""
+def test_torch_operator_matches_the_oracle_and_the_c_abi():
+    """torch.ops.ftx.encoder_forward (and the nn.Module around it) against the fp64 oracle at
+    the stack bar, on padded lengths, and bitwise equal to ftx_forward."""
     from transformer_encoder_bert_amd import torch_op
     c, layers = _case("bert_base_fp16_s128_varlen", 4, "random_affine")
     enc = _encoder(c.shape, layers)
@@ -336,8 +341,15 @@ def test_torch_operator_matches_the_c_abi():
     lens = dev_lens(c.lens)
     ref = enc.forward(x, lens).clone()
     mod = torch_op.EncoderModule(enc)
-    assert torch.equal(mod(x, lens), ref)
-    assert torch.equal(torch.ops.ftx.encoder_forward(x, lens, mod.op_id), ref)
+    got = mod(x, lens)
+    oref = oracle.encoder(c.x, layers, c.lens, c.shape.head_num)
+    print(check(to_f64(got), oref, "fp16", stack_tol("fp16"), "torch operator"))
+    assert torch.equal(got, ref)
+    got2 = torch.ops.ftx.encoder_forward(x, lens, mod.op_id)
+    check(to_f64(got2), oref, "fp16", stack_tol("fp16"), "torch operator, direct call")
+    assert torch.equal(got2, ref)
+    with pytest.raises(ValueError):     # not [B][S][H]
+        torch.ops.ftx.encoder_forward(x.view(-1, x.shape[-1]), lens, mod.op_id)
     mod.close()
 
 
@@ -375,10 +387,37 @@ def test_kernel_timing_counts_launches():
 
 # ------------------------------------------------------------------ full sizes, sampled rows
 
+def tile_sample(batch: int, seq_len: int, seed: int):
+    """Sequences the oracle checks at a full batch: all of them up to 64 sequences; above,
+    one seeded sequence from every 256-row tile of the projections (256 / seq_len sequences
+    per tile, at least one), so every tile of the benchmark's grid is covered."""
+    if batch <= 64:
+        return list(range(batch))
+    per_tile = max(1, 256 // seq_len)
+    rng = np.random.default_rng(seed)
+    rows = []
+    for first in range(0, batch, per_tile):
+        rows.append(first + int(rng.integers(0, min(per_tile, batch - first))))
+    return rows
+
+
+# Every (workload, batch) the benchmark reports, in the launch configuration it times
+# (default options).  BERT-large checks two sequences: its oracle takes about a second per
+# sequence, where BERT-base takes 20 ms.
 FULL = [
-    ("bert_base_fp16_s32", 512, [0, 137, 511]),
-    ("pruned_fp16_s32", 512, [0, 255, 511]),
-    ("bert_base_fp16_s128_varlen", 64, [0, 31, 63]),
+    ("bert_base_fp16_s32", 512, None),
+    ("bert_base_fp16_s32", 256, None),
+    ("bert_base_fp16_s32", 128, None),
+    ("bert_base_fp16_s32", 64, None),
+    ("bert_base_fp16_s32", 8, None),
+    ("bert_base_fp16_s32", 1, None),
+    ("pruned_fp16_s32", 512, None),
+    ("pruned_fp16_s32", 64, None),
+    ("pruned_fp16_s32", 1, None),
+    ("bert_base_fp16_s64_varlen", 64, None),
+    ("bert_base_fp16_s64_varlen", 1, None),
+    ("bert_base_fp16_s128_varlen", 64, None),
+    ("bert_base_fp16_s128_varlen", 1, None),
     ("bert_large_bf16_s128", 256, [0, 200]),
     ("bert_large_bf16_s512", 32, [7, 31]),
 ]
@@ -387,12 +426,15 @@ FULL = [
 @pytest.mark.parametrize("workload,batch,rows", FULL)
 def test_full_size_sampled_rows(workload, batch, rows):
     """The whole batch at its full size, in the launch configuration the benchmark times;
-    the oracle checks a sample of sequences (sequences are independent)."""
+    the oracle checks the sampled sequences (sequences are independent)."""
     c, layers = _case(workload, batch)
+    if rows is None:
+        rows = tile_sample(batch, c.shape.seq_len, seed=batch + c.shape.seq_len)
     enc = _encoder(c.shape, layers)
     out = enc.forward(to_dev(c.x, c.shape.dtype), dev_lens(c.lens))
     got = to_f64(out[rows])
     enc.close()
     ref = oracle.encoder_rows(c.x, layers, c.lens, c.shape.head_num, rows)
-    rep = check(got, ref, c.shape.dtype, stack_tol(c.shape.dtype), f"{workload} B={batch} rows {rows}")
-    print(rep)
+    rep = check(got, ref, c.shape.dtype, stack_tol(c.shape.dtype),
+                f"{workload} B={batch} {len(rows)} sequences")
+    print(f"{workload} B={batch}: {len(rows)} of {batch} sequences checked, {rep}")

@@ -42,6 +42,7 @@ struct ftx_decoder {
   ftx_dtype dt;
   size_t es;
   int device;
+  DeviceInfo dev;  // CU and XCD counts, read at create
   void* weights = nullptr;
   void* ws = nullptr;
   std::vector<DecLayerW> layers;
@@ -100,13 +101,12 @@ ftx_status step(ftx_decoder* e, int cls, hipStream_t s, F&& launch) {
 }
 
 // The causal self-attention runs inside the self Q/K/V projection when the shape fits and,
-// in the default mode, when there are at least 256 decoder rows and 64 tiles of 256 rows,
-// as in the encoder.
+// in the default mode, under the encoder's rule (at least 256 decoder rows and a quarter as
+// many 256-row tiles as the device has CUs).
 bool use_fused_self_attention(const ftx_decoder* e) {
   if (!e->attn_fits || e->fused_attention == 0) return false;
   if (e->fused_attention == 2) return true;
-  if (e->Td < 256) return false;
-  return fused_attention_tiles(e->Td, e->H) >= 64;
+  return fused_attention_pays(e->Td, e->H, e->dev.cus);
 }
 
 ftx_status enqueue_decoder(ftx_decoder* e, const void* input, const void* memory,
@@ -252,6 +252,7 @@ ftx_status ftx_decoder_create(int batch_size, int tgt_len, int mem_len, int head
   e->dt = dtype;
   e->es = dtype_size(dtype);
   e->device = dev;
+  e->dev = device_info();
 
   const size_t H = e->H, F = e->F, Td = e->Td, Tm = e->Tm, es = e->es;
   auto pad = [](size_t bytes) { return (bytes + 255) / 256 * 256; };

@@ -72,6 +72,7 @@ struct ftx_encoder {
   ftx_dtype dt;
   size_t es;
   int device;
+  DeviceInfo dev;  // CU and XCD counts, read at create
   void* weights = nullptr;
   void* ws = nullptr;
   std::vector<LayerW> layers;
@@ -159,8 +160,7 @@ void drop_graph(ftx_encoder* e) {
 bool use_fused_attention(const ftx_encoder* e) {
   if (!e->fused || !e->attn_fits || e->fused_attention == 0) return false;
   if (e->fused_attention == 2) return true;
-  if (e->T < 256) return false;
-  return fused_attention_tiles(e->T, e->H) >= 64;
+  return fused_attention_pays(e->T, e->H, e->dev.cus);
 }
 
 // Enqueue the L-layer forward on `s` (arguments already validated).
@@ -355,6 +355,7 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
   e->dt = dtype;
   e->es = dtype_size(dtype);
   e->device = dev;
+  e->dev = device_info();
 
   e->attn_fits = qkv_attention_fits(dtype, e->S, head_num, size_per_head);
 
@@ -766,6 +767,16 @@ ftx_status ftx_step_transpose(ftx_dtype dtype, int rows, int cols, const void* i
   if (!all_device({in, out})) return fail(FTX_ERR_INVALID_ARG, "pointers must be device memory");
   hipError_t err = launch_transpose(dtype, rows, cols, in, out, (hipStream_t)stream);
   return err == hipSuccess ? FTX_OK : hip_fail(err, "transpose launch");
+}
+
+ftx_status ftx_plan_linear(ftx_dtype dtype, int M, int N, int K, int cus, int sums_partials,
+                           int* tile_m, int* tile_n, int* splits) {
+  last_error_slot().clear();
+  if (!dtype_ok(dtype)) return fail(FTX_ERR_INVALID_ARG, "unknown dtype");
+  if (M < 1 || N < 1 || K < 1 || cus < 1) return fail(FTX_ERR_INVALID_ARG, "M, N, K and cus must be >= 1");
+  if (!tile_m || !tile_n || !splits) return fail(FTX_ERR_INVALID_ARG, "NULL pointer");
+  plan_linear(dtype, M, N, K, cus, sums_partials != 0, tile_m, tile_n, splits);
+  return FTX_OK;
 }
 
 }  // extern "C"

@@ -30,6 +30,8 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "device_common.h"
 #include "launch.h"
@@ -582,15 +584,16 @@ template <typename T, int BM, int BN, int WM, int WN> struct GemmCfg {
   static_assert(AQ * 8 * NW == BM && BQ * 8 * NW == BN, "slab loads not divisible");
 };
 
-// Map the linear block id to a (tile_m, tile_n): blocks are handed to the 8 XCDs round
-// robin, so first give every XCD a contiguous range of tiles, then walk each range in
-// groups of GROUP_M tile rows so the blocks resident on one XCD share A and W panels in
-// that XCD's L2.
-__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int XCDS = 8, GROUP_M = 8;
+// Map the linear block id to a (tile_m, tile_n): blocks are handed to the device's xcds
+// XCDs round robin, so first give every XCD a contiguous range of tiles, then walk each
+// range in groups of GROUP_M tile rows so the blocks resident on one XCD share A and W
+// panels in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int xcds, int& tm,
+                                            int& tn) {
+  constexpr int GROUP_M = 8;
   const int nt = tiles_m * tiles_n;
   int L = bid;
-  if (nt % XCDS == 0) L = (bid % XCDS) * (nt / XCDS) + bid / XCDS;
+  if (xcds > 1 && nt % xcds == 0) L = (bid % xcds) * (nt / xcds) + bid / xcds;
   const int per_group = GROUP_M * tiles_n;
   const int group = L / per_group;
   const int first_m = group * GROUP_M;
@@ -634,7 +637,8 @@ __device__ __forceinline__ void gemm_epilogue(const Epi& epi, char* smem, int m0
 template <typename T, int BM, int BN, int WM, int WN, typename Epi, int NST = 2>
 __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restrict__ A,
                                                                const T* __restrict__ Bt, int M,
-                                                               int N, int K, int kchunk, Epi epi) {
+                                                               int N, int K, int kchunk, int xcds,
+                                                               Epi epi) {
   typedef GemmCfg<T, BM, BN, WM, WN> C;
   typedef typename C::MF MF;
   typedef typename MF::frag frag;
@@ -644,7 +648,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  tile_coords(blockIdx.x, tiles_m, tiles_n, xcds, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int wm = wave / WN, wn = wave % WN;
@@ -785,7 +789,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
 template <typename T, int BM, int BN, typename Epi>
 __global__ __launch_bounds__(8 * kWave) void gemm_pp_kernel(const T* __restrict__ A,
                                                             const T* __restrict__ Bt, int M,
-                                                            int N, int K, int kchunk, Epi epi) {
+                                                            int N, int K, int kchunk, int xcds,
+                                                            Epi epi) {
   constexpr int WM = 4, WN = 2;
   typedef GemmCfg<T, BM, BN, WM, WN> C;
   typedef typename C::MF MF;
@@ -797,7 +802,7 @@ __global__ __launch_bounds__(8 * kWave) void gemm_pp_kernel(const T* __restrict_
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  tile_coords(blockIdx.x, tiles_m, tiles_n, xcds, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   // wave-uniform, so the group's branches around barriers are scalar branches
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -927,18 +932,20 @@ __global__ __launch_bounds__(8 * kWave) void gemm_pp_kernel(const T* __restrict_
 //   128x128, 4 waves (2 x 2),  64 KB LDS: 0.36, 2 blocks per CU
 //    64x64,  4 waves (2 x 2),  32 KB LDS: 0.25, 4 blocks per CU
 //    32x32,  1 wave,           16 KB LDS: 0.18, 8 blocks per CU
-// The modelled time of a launch is (rounds of blocks over the 256 CUs) x (one block's
+// The modelled time of a launch is (rounds of blocks over the device's CUs) x (one block's
 // time, longer when several blocks share a CU); the candidate with the least modelled time
 // wins, so small batches get small tiles that still spread over every CU.  fp32 (twice the
 // register footprint per element) uses the table without its two largest tiles.
 
 enum TileCfg { TILE_256x256, TILE_256x192, TILE_256x128, TILE_128x128, TILE_64x64, TILE_32x32, TILE_COUNT };
+static const int kTileM[TILE_COUNT] = {256, 256, 256, 128, 64, 32};
+static const int kTileN[TILE_COUNT] = {256, 192, 128, 128, 64, 32};
 
-static TileCfg choose_tile(int M, int N, bool wide) {
+static TileCfg choose_tile(int M, int N, bool wide, int cus) {
   struct Cand { int bm, bn, per_cu; double eff; };
   static const Cand cand[TILE_COUNT] = {{256, 256, 1, 0.37}, {256, 192, 1, 0.36}, {256, 128, 1, 0.34},
                                         {128, 128, 2, 0.36}, {64, 64, 4, 0.25},   {32, 32, 8, 0.18}};
-  constexpr int kCUs = 256;
+  const long kCUs = std::max(cus, 1);
   int best = TILE_32x32;
   double best_t = 1e300;
   for (int c = wide ? 0 : TILE_256x128; c < TILE_COUNT; ++c) {
@@ -959,8 +966,8 @@ static TileCfg choose_tile(int M, int N, bool wide) {
 }
 
 // Split-K (the small-batch path): when the chosen configuration has fewer tiles than there
-// are CUs, K is cut into up to 16 ranges of at least two slabs each, so that about 512
-// blocks run.  When it has more tiles than CUs but fewer waves than SIMDs (only 32x32
+// are CUs, K is cut into up to 16 ranges of at least two slabs each, so that about twice as
+// many blocks as CUs run (512 on 256 CUs).  When it has more tiles than CUs but fewer waves than SIMDs (only 32x32
 // tiles, one wave each, reach this), K is cut so that about one wave per SIMD runs -- but
 // only where the LayerNorm after the projection sums the partials (no reduction launch)
 // and its rows are at least 256 wide.  Measured in whole forwards against splitting below
@@ -986,7 +993,6 @@ struct GemmPlan {
   int kchunk;  // K elements per split (K when splits == 1)
 };
 
-constexpr long kSIMDs = 1024;  // 256 CUs x 4 SIMDs
 constexpr size_t kMaxPartialBytes = 16u << 20;
 // A split finished by a reduction launch also pays that launch and the second read of the
 // partials: above 4 MiB of partials it lost in whole forwards (BERT-base B8, FFN-in at 256
@@ -996,20 +1002,19 @@ constexpr size_t kMaxReducedPartialBytes = 4u << 20;
 
 // sums_partials: the kernel after this projection sums its partials itself (the split-K
 // LayerNorm), so a split costs no reduction launch.
-static GemmPlan plan_gemm(int M, int N, int K, int elem_bytes, bool sums_partials) {
-  static const int bm[TILE_COUNT] = {256, 256, 256, 128, 64, 32};
-  static const int bn[TILE_COUNT] = {256, 192, 128, 128, 64, 32};
-  GemmPlan p{choose_tile(M, N, elem_bytes == 2), 1, K};
+static GemmPlan plan_gemm(int M, int N, int K, int elem_bytes, bool sums_partials, int cus) {
+  const long kCUs = std::max(cus, 1), kSIMDs = 4 * kCUs;
+  GemmPlan p{choose_tile(M, N, elem_bytes == 2, cus), 1, K};
   const int bk = 128 / elem_bytes;
-  const long tiles = (long)((M + bm[p.cfg] - 1) / bm[p.cfg]) * ((N + bn[p.cfg] - 1) / bn[p.cfg]);
+  const long tiles = (long)((M + kTileM[p.cfg] - 1) / kTileM[p.cfg]) * ((N + kTileN[p.cfg] - 1) / kTileN[p.cfg]);
   const int nk = (K + bk - 1) / bk;
   static const int waves[TILE_COUNT] = {8, 8, 8, 4, 4, 1};
   const bool fill_simds = sums_partials && N >= 256 && tiles * waves[p.cfg] < kSIMDs;
-  if ((tiles < 256 || fill_simds) && nk >= 4) {
+  if ((tiles < kCUs || fill_simds) && nk >= 4) {
     const size_t max_partial_bytes = sums_partials ? kMaxPartialBytes : kMaxReducedPartialBytes;
     const long by_bytes = (long)(max_partial_bytes / ((size_t)M * N * sizeof(float)));
     const long wv = tiles * waves[p.cfg];
-    const long fill = tiles < 256 ? (512 + tiles - 1) / tiles : (kSIMDs + wv - 1) / wv;
+    const long fill = tiles < kCUs ? (2 * kCUs + tiles - 1) / tiles : (kSIMDs + wv - 1) / wv;
     int sp = (int)std::min<long>(std::min<long>(fill, nk / 2),
                                  std::min<long>(16, by_bytes));
     if (sp > 1) {
@@ -1020,13 +1025,47 @@ static GemmPlan plan_gemm(int M, int N, int K, int elem_bytes, bool sums_partial
   return p;
 }
 
+DeviceInfo device_info() {
+  static std::mutex mu;
+  static std::vector<DeviceInfo> cache;  // per device id; cus == 0: not read yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return {1, 1};
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if ((size_t)dev < cache.size() && cache[dev].cus > 0) return cache[dev];
+  hipDeviceProp_t prop;
+  int xcds = 1;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess || prop.multiProcessorCount < 1) {
+    (void)hipGetLastError();
+    return {1, 1};
+  }
+  if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcds < 1) {
+    (void)hipGetLastError();
+    xcds = 1;
+  }
+  if ((size_t)dev >= cache.size()) cache.resize(dev + 1, DeviceInfo{0, 0});
+  cache[dev] = {prop.multiProcessorCount, xcds};
+  return cache[dev];
+}
+
 size_t gemm_splitk_workspace(ftx_dtype dt, int M, int N, int K) {
+  const int cus = device_info().cus;
   size_t need = 0;
   for (bool sums : {false, true}) {
-    const GemmPlan p = plan_gemm(M, N, K, dt == FTX_FP32 ? 4 : 2, sums);
+    const GemmPlan p = plan_gemm(M, N, K, dt == FTX_FP32 ? 4 : 2, sums, cus);
     if (p.splits > 1) need = std::max(need, (size_t)p.splits * M * N);
   }
   return need;
+}
+
+void plan_linear(ftx_dtype dt, int M, int N, int K, int cus, bool sums_partials, int* tile_m,
+                 int* tile_n, int* splits) {
+  const GemmPlan p = plan_gemm(M, N, K, dt == FTX_FP32 ? 4 : 2, sums_partials, cus);
+  *tile_m = kTileM[p.cfg];
+  *tile_n = kTileN[p.cfg];
+  *splits = p.splits;
 }
 
 // The ping-pong K loop from 12 slabs (K >= 768 in 16-bit).  Measured in whole forwards,
@@ -1046,28 +1085,29 @@ constexpr int kSmallTileDeepSlabs = 12;
 
 template <typename T, int BM, int BN, int WM, int WN, typename Epi>
 static void gemm_kernel_launch(dim3 grid, int kchunk, int M, int N, int K, const void* a,
-                               const void* w_t, Epi epi, hipStream_t s) {
+                               const void* w_t, Epi epi, int xcds, hipStream_t s) {
   constexpr int BK = GemmCfg<T, BM, BN, WM, WN>::BK;
   if constexpr (BM == 64 && BN == 64) {
     if ((kchunk + BK - 1) / BK >= kSmallTileDeepSlabs) {
       gemm_kernel<T, BM, BN, WM, WN, Epi, 3><<<grid, WM * WN * kWave, 0, s>>>(
-          (const T*)a, (const T*)w_t, M, N, K, kchunk, epi);
+          (const T*)a, (const T*)w_t, M, N, K, kchunk, xcds, epi);
       return;
     }
   }
   gemm_kernel<T, BM, BN, WM, WN, Epi><<<grid, WM * WN * kWave, 0, s>>>(
-      (const T*)a, (const T*)w_t, M, N, K, kchunk, epi);
+      (const T*)a, (const T*)w_t, M, N, K, kchunk, xcds, epi);
 }
 
 // reduce: under split-K, also launch the reduction that finishes the partials with `epi`
 // (false: the caller's next kernel consumes the partials itself).
 template <typename T, int BM, int BN, int WM, int WN, typename Epi>
 static hipError_t gemm_launch_cfg(int M, int N, int K, const void* a, const void* w_t, Epi epi,
-                                  const GemmPlan& plan, float* ws, hipStream_t s, bool reduce) {
+                                  const GemmPlan& plan, float* ws, int xcds, hipStream_t s,
+                                  bool reduce) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (plan.splits > 1) {
     gemm_kernel_launch<T, BM, BN, WM, WN, EpiPartial>(dim3(tiles, plan.splits), plan.kchunk, M, N,
-                                                      K, a, w_t, EpiPartial{ws, M, N}, s);
+                                                      K, a, w_t, EpiPartial{ws, M, N}, xcds, s);
     if (reduce) {
       const int64_t threads = (int64_t)M * (N / 4);
       splitk_reduce_kernel<Epi><<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(ws, plan.splits, M, N, epi);
@@ -1078,11 +1118,11 @@ static hipError_t gemm_launch_cfg(int M, int N, int K, const void* a, const void
     constexpr int BK = GemmCfg<T, BM, BN, WM, WN>::BK;
     if (K % BK == 0 && K / BK >= kPingPongMinSlabs) {
       gemm_pp_kernel<T, BM, BN, Epi><<<tiles, WM * WN * kWave, 0, s>>>(
-          (const T*)a, (const T*)w_t, M, N, K, K, epi);
+          (const T*)a, (const T*)w_t, M, N, K, K, xcds, epi);
       return hipGetLastError();
     }
   }
-  gemm_kernel_launch<T, BM, BN, WM, WN, Epi>(dim3(tiles), K, M, N, K, a, w_t, epi, s);
+  gemm_kernel_launch<T, BM, BN, WM, WN, Epi>(dim3(tiles), K, M, N, K, a, w_t, epi, xcds, s);
   return hipGetLastError();
 }
 
@@ -1091,29 +1131,30 @@ static hipError_t gemm_launch(int M, int N, int K, const void* a, const void* w_
                               hipStream_t s, float* ws = nullptr, size_t ws_elems = 0,
                               bool reduce = true) {
   constexpr bool wide = sizeof(T) == 2;
-  GemmPlan plan = plan_gemm(M, N, K, (int)sizeof(T), !reduce);
+  const DeviceInfo di = device_info();
+  GemmPlan plan = plan_gemm(M, N, K, (int)sizeof(T), !reduce, di.cus);
   if (plan.splits > 1 && (!ws || ws_elems < (size_t)plan.splits * M * N)) {
     plan.splits = 1;
     plan.kchunk = K;
   }
   switch (plan.cfg) {
     case TILE_256x256:
-      if constexpr (wide) return gemm_launch_cfg<T, 256, 256, 4, 2>(M, N, K, a, w_t, epi, plan, ws, s, reduce);
+      if constexpr (wide) return gemm_launch_cfg<T, 256, 256, 4, 2>(M, N, K, a, w_t, epi, plan, ws, di.xcds, s, reduce);
       break;
     case TILE_256x192:
-      if constexpr (wide) return gemm_launch_cfg<T, 256, 192, 4, 2>(M, N, K, a, w_t, epi, plan, ws, s, reduce);
+      if constexpr (wide) return gemm_launch_cfg<T, 256, 192, 4, 2>(M, N, K, a, w_t, epi, plan, ws, di.xcds, s, reduce);
       break;
-    case TILE_256x128: return gemm_launch_cfg<T, 256, 128, 4, 2>(M, N, K, a, w_t, epi, plan, ws, s, reduce);
-    case TILE_128x128: return gemm_launch_cfg<T, 128, 128, 2, 2>(M, N, K, a, w_t, epi, plan, ws, s, reduce);
-    case TILE_64x64: return gemm_launch_cfg<T, 64, 64, 2, 2>(M, N, K, a, w_t, epi, plan, ws, s, reduce);
-    case TILE_32x32: return gemm_launch_cfg<T, 32, 32, 1, 1>(M, N, K, a, w_t, epi, plan, ws, s, reduce);
+    case TILE_256x128: return gemm_launch_cfg<T, 256, 128, 4, 2>(M, N, K, a, w_t, epi, plan, ws, di.xcds, s, reduce);
+    case TILE_128x128: return gemm_launch_cfg<T, 128, 128, 2, 2>(M, N, K, a, w_t, epi, plan, ws, di.xcds, s, reduce);
+    case TILE_64x64: return gemm_launch_cfg<T, 64, 64, 2, 2>(M, N, K, a, w_t, epi, plan, ws, di.xcds, s, reduce);
+    case TILE_32x32: return gemm_launch_cfg<T, 32, 32, 1, 1>(M, N, K, a, w_t, epi, plan, ws, di.xcds, s, reduce);
     default: break;
   }
   return hipErrorInvalidValue;
 }
 
 int linear_splits(ftx_dtype dt, int M, int N, int K, size_t ws_elems, bool sums_partials) {
-  const GemmPlan p = plan_gemm(M, N, K, dt == FTX_FP32 ? 4 : 2, sums_partials);
+  const GemmPlan p = plan_gemm(M, N, K, dt == FTX_FP32 ? 4 : 2, sums_partials, device_info().cus);
   return (p.splits > 1 && ws_elems >= (size_t)p.splits * M * N) ? p.splits : 1;
 }
 
@@ -1163,7 +1204,7 @@ static hipError_t linear_ln_t(int M, int K, const void* a, const void* w_t, cons
   typedef EpiLinearLN<T, TX, A_F32> Epi;
   Epi epi{(const TX*)x, (const T*)bias, (const T*)gamma, (const T*)beta, (T*)y, yf, M, N};
   gemm_kernel<T, 64, 128, 2, 2, Epi><<<(M + 63) / 64, 4 * kWave, 0, s>>>(
-      (const T*)a, (const T*)w_t, M, N, K, K, epi);
+      (const T*)a, (const T*)w_t, M, N, K, K, device_info().xcds, epi);
   return hipGetLastError();
 }
 
@@ -1223,15 +1264,17 @@ static hipError_t qkv_attention_t(int B, int nh, const void* x, const void* w_t,
   // log2(e) / sqrt(d), rounded once from double as the attention kernel does
   const float scale_log2e = (float)(1.4426950408889634 / sqrt((double)D));
   const int tiles = ((M + 255) / 256) * (N / 192);
+  const DeviceInfo di = device_info();
   if constexpr (SEQ <= 128) {
     // 128-row tiles of 4 waves while twice the tiles still fit one per CU (BERT-base S32
-    // at batch 64: 96 tiles of 256 rows -> 192 of 128, 0.849 -> 0.806 ms; at S64, 192 tiles
-    // of 256 rows would become 384 sharing CUs: 1.267 -> 1.287 ms, so they stay)
-    if (2 * tiles <= 256) {
+    // at batch 64 on 256 CUs: 96 tiles of 256 rows -> 192 of 128, 0.849 -> 0.806 ms; at
+    // S64, 192 tiles of 256 rows would become 384 sharing CUs: 1.267 -> 1.287 ms, so they
+    // stay)
+    if (2 * tiles <= di.cus) {
       typedef EpiQKVAttn<T, SEQ, D, 128> Epi128;
       Epi128 epi{(T*)ctx, (const T*)bias, lens, M, N, s_valid, scale_log2e, causal};
       gemm_kernel<T, 128, 192, 2, 2, Epi128><<<((M + 127) / 128) * (N / 192), 4 * kWave, 0, s>>>(
-          (const T*)x, (const T*)w_t, M, N, K, K, epi);
+          (const T*)x, (const T*)w_t, M, N, K, K, di.xcds, epi);
       return hipGetLastError();
     }
   }
@@ -1239,10 +1282,10 @@ static hipError_t qkv_attention_t(int B, int nh, const void* x, const void* w_t,
   constexpr int BK = GemmCfg<T, 256, 192, 4, 2>::BK;
   if (K % BK == 0 && K / BK >= kPingPongMinSlabs)
     gemm_pp_kernel<T, 256, 192, EpiQKVAttn<T, SEQ, D>><<<tiles, 8 * kWave, 0, s>>>(
-        (const T*)x, (const T*)w_t, M, N, K, K, epi);
+        (const T*)x, (const T*)w_t, M, N, K, K, di.xcds, epi);
   else
     gemm_kernel<T, 256, 192, 4, 2, EpiQKVAttn<T, SEQ, D>><<<tiles, 8 * kWave, 0, s>>>(
-        (const T*)x, (const T*)w_t, M, N, K, K, epi);
+        (const T*)x, (const T*)w_t, M, N, K, K, di.xcds, epi);
   return hipGetLastError();
 }
 

@@ -8,6 +8,18 @@
 
 namespace ftx {
 
+// Compute units and XCDs (the dies the CUs are spread over, each with its own L2) of a
+// device.  The GEMM planner sizes grids and split-K from the CU count (4 SIMDs per CU) and
+// the kernels map block ids to tiles per XCD.
+struct DeviceInfo {
+  int cus;
+  int xcds;
+};
+// The current device's counts, read from the HIP runtime (hipGetDeviceProperties,
+// hipDeviceAttributeNumberOfXccs) on the first call for that device and cached; {1, 1} if
+// the runtime cannot be asked (the launch that follows then fails on its own).
+DeviceInfo device_info();
+
 // out_f32: c is written as fp32 (16-bit dtypes, without GELU; ignored in fp32 mode).
 // ws / ws_elems: fp32 workspace for split-K; a GEMM whose plan splits K runs unsplit when
 // the workspace is missing or smaller than gemm_splitk_workspace() says.
@@ -37,6 +49,14 @@ bool qkv_attention_fits(ftx_dtype dt, int S, int nh, int d);
 // columns.
 inline long fused_attention_tiles(long T, long H) { return (T + 255) / 256 * (3 * H / 192); }
 
+// Whether the automatic mode runs the projection + attention as one kernel: from 256 rows,
+// with at least a quarter as many 256-row tiles as the device has CUs (64 on 256 CUs).
+// Below that the tiles are mostly padding rows or the long epilogue runs on few CUs, while
+// the separate kernels spread the same work.
+inline bool fused_attention_pays(long T, long H, int cus) {
+  return T >= 256 && 4 * fused_attention_tiles(T, H) >= cus;
+}
+
 // Q/K/V projection of x [B*S][H] with the attention of every (sequence, head) in the same
 // kernel: w_qkv_t [3H][H] and b_qkv [3H] ordered per head ([Q_h | K_h | V_h], 3d rows each),
 // ctx [B*S][H] as launch_attention writes it.  Keys at or past min(lens[b], s_valid) are
@@ -48,6 +68,11 @@ hipError_t launch_qkv_attention(ftx_dtype dt, int B, int S, int nh, int d, const
 
 // fp32 elements of split-K workspace the GEMM of this shape uses (0: it does not split).
 size_t gemm_splitk_workspace(ftx_dtype dt, int M, int N, int K);
+
+// The launch plan of an M x N x K projection on a device with `cus` CUs: block tile
+// tile_m x tile_n and K ranges (1: no split).  sums_partials as for linear_splits.
+void plan_linear(ftx_dtype dt, int M, int N, int K, int cus, bool sums_partials, int* tile_m,
+                 int* tile_n, int* splits);
 
 // K ranges a projection of this shape is split into with ws_elems fp32 of workspace (1:
 // none).  sums_partials: the partials go to the kernel after it (launch_linear_partials,

@@ -40,7 +40,7 @@ EXPORTED = ("ftx_encoder_create", "ftx_set_weights", "ftx_forward", "ftx_destroy
             "ftx_step_linear", "ftx_step_qkv_projection", "ftx_step_qkv_attention",
             "ftx_step_bias_qkv_split",
             "ftx_step_attention", "ftx_step_masked_attention", "ftx_step_bias_residual_layernorm",
-            "ftx_step_bias_gelu", "ftx_step_transpose",
+            "ftx_step_bias_gelu", "ftx_step_transpose", "ftx_plan_linear",
             "ftx_decoder_create", "ftx_decoder_set_weights", "ftx_decoder_forward",
             "ftx_decoder_set_option", "ftx_decoder_kernel_times", "ftx_decoder_destroy")
 DEC_STEP_NAMES = ("self_qkv_gemm", "self_attention", "self_out_gemm", "ln1", "cross_q_gemm",
@@ -102,6 +102,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ftx_step_bias_residual_layernorm": (i, [i, i, i, p, p, p, p, p, p, v]),
         "ftx_step_bias_gelu": (i, [i, i, i, p, p, p, v]),
         "ftx_step_transpose": (i, [i, i, i, p, p, v]),
+        "ftx_plan_linear": (i, [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i),
+                                ctypes.POINTER(i)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -144,14 +146,14 @@ def _dt(x) -> int:
 
 
 def _need(t: torch.Tensor, name: str, dtype: torch.dtype, numel: Optional[int] = None) -> None:
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if numel is not None and t.numel() != numel:
         raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
 
 
 # ------------------------------------------------------------------------ the four calls
@@ -212,7 +214,12 @@ class Encoder:
 
     def forward(self, x: torch.Tensor, seq_lens: Optional[torch.Tensor] = None,
                 out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        # the kernels read seq_lens[b] for every sequence b of the batch
+        if seq_lens is not None:
+            _need(seq_lens, "seq_lens", torch.int32, self.shape[0])
         _need(x, "input", self.dtype, self.shape[0] * self.shape[1] * self.shape[2])
+        if seq_lens is not None and seq_lens.device != x.device:
+            raise ValueError(f"seq_lens is on {seq_lens.device}, input on {x.device}")
         if out is None:
             out = torch.empty(self.shape, dtype=self.dtype, device=x.device)
         _need(out, "output", self.dtype, x.numel())
@@ -444,3 +451,13 @@ def ftx_step_transpose(inp, out, stream=None) -> None:
     _need(out, "out", inp.dtype, rows * cols)
     _check(load_library().ftx_step_transpose(_dt(inp.dtype), rows, cols, _ptr(inp), _ptr(out),
                                              _stream(stream)), "ftx_step_transpose")
+
+
+def ftx_plan_linear(dtype, M: int, N: int, K: int, cus: int, sums_partials: bool = False):
+    """(tile_m, tile_n, splits) of an M x N x K projection on a device with `cus` CUs.
+    Host arithmetic in the library; needs no GPU."""
+    tm, tn, sp = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(load_library().ftx_plan_linear(_dt(dtype), M, N, K, cus, int(bool(sums_partials)),
+                                          ctypes.byref(tm), ctypes.byref(tn), ctypes.byref(sp)),
+           "ftx_plan_linear")
+    return tm.value, tn.value, sp.value

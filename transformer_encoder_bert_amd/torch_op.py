@@ -46,16 +46,23 @@ def _lookup(op_id: int) -> Encoder:
         raise ValueError(f"no ftx encoder registered under id {op_id}") from None
 
 
+def _checked(x: torch.Tensor, op_id: int) -> Encoder:
+    enc = _lookup(op_id)
+    if tuple(x.shape) != tuple(enc.shape):
+        raise ValueError(f"input has shape {tuple(x.shape)}, the encoder takes [B][S][H] = {enc.shape}")
+    return enc
+
+
 @torch.library.custom_op("ftx::encoder_forward", mutates_args=())
 def encoder_forward(x: torch.Tensor, seq_lens: Optional[torch.Tensor], op_id: int) -> torch.Tensor:
-    """[B][S][H] -> [B][S][H]: the L-layer encoder forward of the registered handle, on the
-    current stream."""
-    return _lookup(op_id).forward(x.contiguous(), seq_lens)
+    """[B][S][H] -> [B][S][H] (a new contiguous tensor): the L-layer encoder forward of the
+    registered handle, on the current stream."""
+    return _checked(x, op_id).forward(x.contiguous(), seq_lens)
 
 
 @encoder_forward.register_fake
 def _(x, seq_lens, op_id):
-    return torch.empty_like(x)
+    return x.new_empty(_checked(x, op_id).shape)
 
 
 class EncoderModule(torch.nn.Module):
