@@ -111,6 +111,29 @@ ftx_status ftx_set_weights(ftx_encoder *enc, int layer, const ftx_layer_weights 
 ftx_status ftx_forward(ftx_encoder *enc, const void *input, const int32_t *seq_lens,
                        void *output, void *stream);
 
+/* For callers that cannot allocate device memory while they run (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): ftx_forward with every
+ * intermediate tensor of the forward -- Q, K, V^T, the attention context, the projection
+ * outputs, the FFN hidden layer, the fp32 copies of FTX_BF16, the padded copies of a
+ * seq_len that is not a multiple of 32, the split-K partial products -- in the library's
+ * static scratch instead of the handle's workspace.  Same arguments, same kernels and
+ * launch plans, so the same result as ftx_forward, bit for bit.
+ *   The scratch is a fixed array of FTX_STATIC_SCRATCH_BYTES of device memory per GPU (the
+ *   library's code object holds it; each GPU the library runs on keeps its copy until the
+ *   process ends).  A handle whose workspace is larger -> FTX_ERR_UNSUPPORTED, nothing
+ *   enqueued (BERT-base fp16 at seq_len 32 fits up to about 100 sequences).
+ *   Allocates nothing: no hipMalloc/hipFree, no allocating library call; the padded input
+ *   copy is cleared with a kernel, not hipMemsetAsync, so the call can be captured.
+ *   FTX_OPT_GRAPH does not apply (the caller captures if it wishes); FTX_OPT_KERNEL_TIMING
+ *   does.
+ *   Every call on one GPU, from any handle or thread, uses that GPU's one scratch array and
+ *   leaves its contents behind: calls that overlap in time on one GPU (other streams, other
+ *   threads) race and give wrong results.  Order them on one stream or synchronize between
+ *   them.  Other errors as ftx_forward. */
+#define FTX_STATIC_SCRATCH_BYTES (64u << 20)
+ftx_status ftx_forward_static_workspace(ftx_encoder *enc, const void *input,
+                                        const int32_t *seq_lens, void *output, void *stream);
+
 /* Free the handle and its device memory (synchronizes the device first).  NULL -> FTX_OK. */
 ftx_status ftx_destroy(ftx_encoder *enc);
 

@@ -9,6 +9,8 @@
 // Here: 64-lane wavefronts, 8- or 16-byte vector accesses, fp32 statistics, and a
 // two-pass (mean, then centred sum of squares) variance held entirely in registers.
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -428,6 +430,23 @@ hipError_t launch_transpose(ftx_dtype dt, int rows, int cols, const void* in, vo
     case FTX_BF16: return transpose_launch<bf16>(rows, cols, in, out, s);
   }
   return hipErrorInvalidValue;
+}
+
+// Zero n16 16-byte vectors at p (grid-stride; the pointer is 16-byte aligned).  A kernel
+// rather than hipMemsetAsync, so a caller's HIP graph capture records a kernel node.
+__global__ __launch_bounds__(256) void zero16_kernel(uint4* __restrict__ p, size_t n16) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += stride)
+    p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  if (((uintptr_t)p & 15u) || (bytes & 15u)) return hipErrorInvalidValue;
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>((n16 + 255) / 256, 4096);
+  zero16_kernel<<<(unsigned)blocks, 256, 0, s>>>((uint4*)p, n16);
+  return hipGetLastError();
 }
 
 }  // namespace ftx

@@ -12,6 +12,7 @@
 
 #include <algorithm>
 #include <initializer_list>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -64,6 +65,17 @@ struct LayerW {
   void* ln2_b;
 };
 
+// Views of the forward's intermediate tensors, all carved from one block of device memory:
+// the handle's own workspace (ftx_forward) or the library's static scratch
+// (ftx_forward_static_workspace).
+struct Workspace {
+  void *q, *k, *vt, *ctx, *abuf, *y1, *u;
+  void *xpad = nullptr, *spad = nullptr;  // [B][S][H] input copy and layer state when Sv < S
+  float* y1f = nullptr;     // fp32 copy of Y1, the residual of the second LayerNorm (bf16 only)
+  float* splitk = nullptr;  // fp32 partial products of split-K projections
+  size_t splitk_elems = 0;
+};
+
 }  // namespace
 
 struct ftx_encoder {
@@ -74,15 +86,12 @@ struct ftx_encoder {
   int device;
   DeviceInfo dev;  // CU and XCD counts, read at create
   void* weights = nullptr;
-  void* ws = nullptr;
+  void* ws_mem = nullptr;  // the workspace allocation
+  size_t ws_bytes = 0;     // its size (the layout of layout_workspace)
+  size_t splitk_need = 0;  // fp32 elements of split-K partials the plans use
+  Workspace w;             // views into ws_mem
   std::vector<LayerW> layers;
   std::vector<char> ready;
-  // workspace views
-  void *q, *k, *vt, *ctx, *abuf, *y1, *u;
-  void *xpad = nullptr, *spad = nullptr;  // [B][S][H] input copy and layer state when Sv < S
-  float* splitk = nullptr;                 // fp32 partial products of split-K projections
-  size_t splitk_elems = 0;
-  float* y1f = nullptr;  // fp32 copy of Y1, the residual of the second LayerNorm (bf16 only)
   int fused = 1;
   int fused_attention = 1;  // 0 off, 1 from 256 rows and 64 tiles, 2 whenever the shape fits
   bool attn_fits = false;   // the per-head weight copy exists (16-bit, S = 32, d = 64)
@@ -163,9 +172,77 @@ bool use_fused_attention(const ftx_encoder* e) {
   return fused_attention_pays(e->T, e->H, e->dev.cus);
 }
 
-// Enqueue the L-layer forward on `s` (arguments already validated).
-ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq_lens,
-                           void* output, hipStream_t s) {
+// The workspace of ftx_forward_static_workspace: FTX_STATIC_SCRATCH_BYTES of device memory
+// per GPU, part of the library's code object (each device that runs the library holds its
+// own copy until the process ends).  Host code must not pass `scratch` itself to a kernel --
+// on the host the name stands for a host-side shadow, not the device array -- but the
+// address static_scratch() obtains for the current device.
+__device__ __align__(256) static char scratch[FTX_STATIC_SCRATCH_BYTES];
+
+// Device address of `scratch` on device `dev` (which must be current), looked up with
+// hipGetSymbolAddress the first time per device and kept; null if the lookup fails.
+void* static_scratch(int dev) {
+  static std::mutex mu;
+  static std::vector<void*> addr;  // per device id
+  if (dev < 0) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((size_t)dev < addr.size() && addr[dev]) return addr[dev];
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if ((size_t)dev >= addr.size()) addr.resize(dev + 1, nullptr);
+  addr[dev] = p;
+  return p;
+}
+
+// Lay the workspace of `e` out from `base` into `w` (base null: only measure); returns its
+// size in bytes.  Every view starts on a 256-byte boundary.
+size_t layout_workspace(const ftx_encoder* e, char* base, Workspace* w) {
+  auto pad = [](size_t bytes) { return (bytes + 255) / 256 * 256; };
+  const size_t H = e->H, F = e->F, T = e->T, es = e->es;
+  const size_t TH = pad(T * H * es);
+  // bf16 keeps what enters a LayerNorm un-normalised in fp32: the residual Y1 and the two
+  // projection outputs added to a residual (C Wo, G W2).  Half an ulp of bf16 at |v| in
+  // [2, 4) is 7.8e-3, and the LayerNorms pass such errors to the output with gain ~gamma.
+  const bool f32res = e->dt == FTX_BF16;
+  const bool padded = e->Sv != e->S;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* p = base ? base + off : nullptr;
+    off += pad(bytes);
+    return p;
+  };
+  Workspace v;
+  v.q = take(TH);
+  v.k = take(TH);
+  v.vt = take(TH);
+  v.ctx = take(TH);
+  v.abuf = take(f32res ? T * H * 4 : TH);
+  v.y1 = take(TH);
+  v.u = take(T * F * es);
+  if (f32res) v.y1f = (float*)take(T * H * 4);
+  if (padded) {
+    // the rows past Sv of each sequence are zero in the input copy and finite in the state;
+    // neither reaches a row below Sv
+    v.xpad = take(TH);
+    v.spad = take(TH);
+  }
+  if (e->splitk_need) {
+    v.splitk = (float*)take(e->splitk_need * sizeof(float));
+    v.splitk_elems = e->splitk_need;
+  }
+  if (w) *w = v;
+  return off;
+}
+
+// Enqueue the L-layer forward on `s` with the intermediate tensors of `ws` (arguments already
+// validated).  clear_pad: zero the padded input copy first (a workspace shared with other
+// forwards may hold anything there; the handle's own is zeroed once at create).
+ftx_status enqueue_forward(ftx_encoder* e, const Workspace& ws, const void* input,
+                           const int32_t* seq_lens, void* output, hipStream_t s,
+                           bool clear_pad = false) {
   const ftx_dtype dt = e->dt;
   const int B = e->B, S = e->S, nh = e->nh, d = e->d, H = e->H, F = e->F, T = e->T;
   // The stack's state lives in `output`, or -- when the caller's length Sv is not a multiple
@@ -173,12 +250,13 @@ ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq
   // S rows, the layers run at S, and rows 0..Sv-1 are copied back at the end.
   const void* x0 = input;
   void* state = output;
-  if (e->xpad) {
+  if (ws.xpad) {
     const size_t row = (size_t)H * e->es;
-    FTX_HIP(hipMemcpy2DAsync(e->xpad, S * row, input, e->Sv * row, e->Sv * row, B,
+    if (clear_pad) FTX_HIP(launch_zero(ws.xpad, (size_t)B * S * row, s));
+    FTX_HIP(hipMemcpy2DAsync(ws.xpad, S * row, input, e->Sv * row, e->Sv * row, B,
                              hipMemcpyDeviceToDevice, s));
-    x0 = e->xpad;
-    state = e->spad;
+    x0 = ws.xpad;
+    state = ws.spad;
   }
   for (int l = 0; l < e->L; ++l) {
     const LayerW& w = e->layers[l];
@@ -187,27 +265,27 @@ ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq
     if (use_fused_attention(e)) {
       st = run_step(e, FTX_STEP_QKV_ATTENTION, s, [&] {
         return launch_qkv_attention(dt, B, S, nh, d, x, w.w_qkvh_t, w.b_qkvh, seq_lens, e->Sv,
-                                    e->ctx, s);
+                                    ws.ctx, s);
       });
     } else if (e->fused) {
       st = run_step(e, FTX_STEP_QKV_GEMM, s, [&] {
-        return launch_qkv_projection(dt, B, S, nh, d, x, w.w_qkv_t, w.b_qkv, e->q, e->k, e->vt, s,
-                                     e->splitk, e->splitk_elems);
+        return launch_qkv_projection(dt, B, S, nh, d, x, w.w_qkv_t, w.b_qkv, ws.q, ws.k, ws.vt, s,
+                                     ws.splitk, ws.splitk_elems);
       });
     } else {
       st = run_step(e, FTX_STEP_QKV_GEMM, s, [&] {
-        return launch_linear(dt, T, 3 * H, H, x, w.w_qkv_t, nullptr, false, e->u, s, false,
-                             e->splitk, e->splitk_elems);
+        return launch_linear(dt, T, 3 * H, H, x, w.w_qkv_t, nullptr, false, ws.u, s, false,
+                             ws.splitk, ws.splitk_elems);
       });
       if (st != FTX_OK) return st;
       st = run_step(e, FTX_STEP_BIAS_QKV_SPLIT, s, [&] {
-        return launch_bias_qkv_split(dt, B, S, nh, d, e->u, w.b_qkv, e->q, e->k, e->vt, s);
+        return launch_bias_qkv_split(dt, B, S, nh, d, ws.u, w.b_qkv, ws.q, ws.k, ws.vt, s);
       });
     }
     if (st != FTX_OK) return st;
     if (!use_fused_attention(e)) {
       st = run_step(e, FTX_STEP_ATTENTION, s, [&] {
-        return launch_attention(dt, B, S, S, nh, d, e->q, e->k, e->vt, seq_lens, e->ctx, s, e->Sv);
+        return launch_attention(dt, B, S, S, nh, d, ws.q, ws.k, ws.vt, seq_lens, ws.ctx, s, e->Sv);
       });
       if (st != FTX_OK) return st;
     }
@@ -218,87 +296,87 @@ ftx_status enqueue_forward(ftx_encoder* e, const void* input, const int32_t* seq
     // (small batches) leaves its fp32 partials to the LayerNorm that follows it, which sums
     // them itself: one launch instead of reduction + LayerNorm.
     const bool row_ln = H == 128 && (T + 63) / 64 >= 128;
-    const int o_splits = linear_splits(dt, T, H, H, e->splitk_elems, true);
+    const int o_splits = linear_splits(dt, T, H, H, ws.splitk_elems, true);
     if (row_ln) {
       st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
-        return launch_linear_layernorm(dt, T, H, H, e->ctx, w.w_o_t, x, false, e->y1f != nullptr,
-                                       w.b_o, w.ln1_g, w.ln1_b, e->y1, e->y1f, s);
+        return launch_linear_layernorm(dt, T, H, H, ws.ctx, w.w_o_t, x, false, ws.y1f != nullptr,
+                                       w.b_o, w.ln1_g, w.ln1_b, ws.y1, ws.y1f, s);
       });
     } else if (o_splits > 1) {
       st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
-        return launch_linear_partials(dt, T, H, H, e->ctx, w.w_o_t, e->splitk, e->splitk_elems, s);
+        return launch_linear_partials(dt, T, H, H, ws.ctx, w.w_o_t, ws.splitk, ws.splitk_elems, s);
       });
       if (st != FTX_OK) return st;
       st = run_step(e, FTX_STEP_LN1, s, [&] {
-        return launch_splitk_bias_residual_layernorm(dt, T, H, x, false, e->splitk, o_splits,
-                                                     e->y1f != nullptr, w.b_o, w.ln1_g, w.ln1_b,
-                                                     e->y1, e->y1f, s);
+        return launch_splitk_bias_residual_layernorm(dt, T, H, x, false, ws.splitk, o_splits,
+                                                     ws.y1f != nullptr, w.b_o, w.ln1_g, w.ln1_b,
+                                                     ws.y1, ws.y1f, s);
       });
     } else {
       st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
-        return launch_linear(dt, T, H, H, e->ctx, w.w_o_t, nullptr, false, e->abuf, s,
-                             e->y1f != nullptr, e->splitk, e->splitk_elems);
+        return launch_linear(dt, T, H, H, ws.ctx, w.w_o_t, nullptr, false, ws.abuf, s,
+                             ws.y1f != nullptr, ws.splitk, ws.splitk_elems);
       });
       if (st != FTX_OK) return st;
       st = run_step(e, FTX_STEP_LN1, s, [&] {
-        if (e->y1f)
-          return launch_bias_residual_layernorm_f32res(dt, T, H, x, false, (const float*)e->abuf, w.b_o,
-                                                       w.ln1_g, w.ln1_b, e->y1, e->y1f, s);
-        return launch_bias_residual_layernorm(dt, T, H, x, e->abuf, w.b_o, w.ln1_g, w.ln1_b, e->y1, s);
+        if (ws.y1f)
+          return launch_bias_residual_layernorm_f32res(dt, T, H, x, false, (const float*)ws.abuf, w.b_o,
+                                                       w.ln1_g, w.ln1_b, ws.y1, ws.y1f, s);
+        return launch_bias_residual_layernorm(dt, T, H, x, ws.abuf, w.b_o, w.ln1_g, w.ln1_b, ws.y1, s);
       });
     }
     if (st != FTX_OK) return st;
     if (e->fused) {
       st = run_step(e, FTX_STEP_FFN1_GEMM, s, [&] {
-        return launch_linear(dt, T, F, H, e->y1, w.w1_t, w.b1, true, e->u, s, false, e->splitk,
-                             e->splitk_elems);
+        return launch_linear(dt, T, F, H, ws.y1, w.w1_t, w.b1, true, ws.u, s, false, ws.splitk,
+                             ws.splitk_elems);
       });
     } else {
       st = run_step(e, FTX_STEP_FFN1_GEMM, s, [&] {
-        return launch_linear(dt, T, F, H, e->y1, w.w1_t, nullptr, false, e->u, s, false, e->splitk,
-                             e->splitk_elems);
+        return launch_linear(dt, T, F, H, ws.y1, w.w1_t, nullptr, false, ws.u, s, false, ws.splitk,
+                             ws.splitk_elems);
       });
       if (st != FTX_OK) return st;
       st = run_step(e, FTX_STEP_BIAS_GELU, s, [&] {
-        return launch_bias_gelu(dt, T, F, e->u, w.b1, e->u, s);
+        return launch_bias_gelu(dt, T, F, ws.u, w.b1, ws.u, s);
       });
     }
     if (st != FTX_OK) return st;
-    const int f_splits = linear_splits(dt, T, H, F, e->splitk_elems, true);
+    const int f_splits = linear_splits(dt, T, H, F, ws.splitk_elems, true);
     if (row_ln) {
       st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
-        const bool f32res = e->y1f != nullptr;
-        return launch_linear_layernorm(dt, T, H, F, e->u, w.w2_t,
-                                       f32res ? (const void*)e->y1f : e->y1, f32res, f32res,
+        const bool f32res = ws.y1f != nullptr;
+        return launch_linear_layernorm(dt, T, H, F, ws.u, w.w2_t,
+                                       f32res ? (const void*)ws.y1f : ws.y1, f32res, f32res,
                                        w.b2, w.ln2_g, w.ln2_b, state, nullptr, s);
       });
     } else if (f_splits > 1) {
       st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
-        return launch_linear_partials(dt, T, H, F, e->u, w.w2_t, e->splitk, e->splitk_elems, s);
+        return launch_linear_partials(dt, T, H, F, ws.u, w.w2_t, ws.splitk, ws.splitk_elems, s);
       });
       if (st != FTX_OK) return st;
       st = run_step(e, FTX_STEP_LN2, s, [&] {
-        const bool f32res = e->y1f != nullptr;
-        return launch_splitk_bias_residual_layernorm(dt, T, H, f32res ? (const void*)e->y1f : e->y1,
-                                                     f32res, e->splitk, f_splits, f32res, w.b2,
+        const bool f32res = ws.y1f != nullptr;
+        return launch_splitk_bias_residual_layernorm(dt, T, H, f32res ? (const void*)ws.y1f : ws.y1,
+                                                     f32res, ws.splitk, f_splits, f32res, w.b2,
                                                      w.ln2_g, w.ln2_b, state, nullptr, s);
       });
     } else {
       st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
-        return launch_linear(dt, T, H, F, e->u, w.w2_t, nullptr, false, e->abuf, s,
-                             e->y1f != nullptr, e->splitk, e->splitk_elems);
+        return launch_linear(dt, T, H, F, ws.u, w.w2_t, nullptr, false, ws.abuf, s,
+                             ws.y1f != nullptr, ws.splitk, ws.splitk_elems);
       });
       if (st != FTX_OK) return st;
       st = run_step(e, FTX_STEP_LN2, s, [&] {
-        if (e->y1f)
-          return launch_bias_residual_layernorm_f32res(dt, T, H, e->y1f, true, (const float*)e->abuf, w.b2,
+        if (ws.y1f)
+          return launch_bias_residual_layernorm_f32res(dt, T, H, ws.y1f, true, (const float*)ws.abuf, w.b2,
                                                        w.ln2_g, w.ln2_b, state, nullptr, s);
-        return launch_bias_residual_layernorm(dt, T, H, e->y1, e->abuf, w.b2, w.ln2_g, w.ln2_b, state, s);
+        return launch_bias_residual_layernorm(dt, T, H, ws.y1, ws.abuf, w.b2, w.ln2_g, w.ln2_b, state, s);
       });
     }
     if (st != FTX_OK) return st;
   }
-  if (e->xpad) {
+  if (ws.xpad) {
     const size_t row = (size_t)H * e->es;
     FTX_HIP(hipMemcpy2DAsync(output, e->Sv * row, state, S * row, e->Sv * row, B,
                              hipMemcpyDeviceToDevice, s));
@@ -372,22 +450,19 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
     delete e;
     return hip_fail(err, "hipMalloc(weights)");
   }
-  const size_t TH = pad(T * H * es);
-  // bf16 keeps what enters a LayerNorm un-normalised in fp32: the residual Y1 and the two
-  // projection outputs added to a residual (C Wo, G W2).  Half an ulp of bf16 at |v| in
-  // [2, 4) is 7.8e-3, and the LayerNorms pass such errors to the output with gain ~gamma.
-  const bool f32res = dtype == FTX_BF16;
-  const size_t TA = f32res ? pad(T * H * 4) : TH;  // abuf
-  const bool padded = e->Sv != e->S;
-  const size_t ws_bytes = 3 * TH /*q,k,vt*/ + TH /*ctx*/ + TA /*abuf*/ + TH /*y1*/ +
-                          pad(T * F * es) /*u*/ + (f32res ? pad(T * H * 4) : 0) /*y1f*/ +
-                          (padded ? 2 * TH : 0) /*xpad, spad*/;
-  err = hipMalloc(&e->ws, ws_bytes);
+  // split-K workspace: the largest any of the four projections plans for
+  e->splitk_need = std::max(std::max(gemm_splitk_workspace(dtype, e->T, 3 * e->H, e->H),
+                                     gemm_splitk_workspace(dtype, e->T, e->H, e->H)),
+                            std::max(gemm_splitk_workspace(dtype, e->T, e->F, e->H),
+                                     gemm_splitk_workspace(dtype, e->T, e->H, e->F)));
+  e->ws_bytes = layout_workspace(e, nullptr, nullptr);
+  err = hipMalloc(&e->ws_mem, e->ws_bytes);
   if (err != hipSuccess) {
     hipFree(e->weights);
     delete e;
     return hip_fail(err, "hipMalloc(workspace)");
   }
+  layout_workspace(e, (char*)e->ws_mem, &e->w);
   char* w = (char*)e->weights;
   e->layers.resize(e->L);
   for (int l = 0; l < e->L; ++l) {
@@ -409,50 +484,23 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
     lw.b_qkvh = e->attn_fits ? take(3 * H * es) : nullptr;
   }
   e->ready.assign(e->L, 0);
-  char* p = (char*)e->ws;
-  e->q = p; p += TH;
-  e->k = p; p += TH;
-  e->vt = p; p += TH;
-  e->ctx = p; p += TH;
-  e->abuf = p; p += TA;
-  e->y1 = p; p += TH;
-  e->u = p; p += pad(T * F * es);
-  if (f32res) {
-    e->y1f = (float*)p;
-    p += pad(T * H * 4);
-  }
-  if (padded) {
-    // the rows past Sv of each sequence are zero in the input copy (they are never written
-    // again) and finite in the state; neither reaches a row below Sv
-    e->xpad = p; p += TH;
-    e->spad = p; p += TH;
-    err = hipMemset(e->xpad, 0, 2 * TH);
+  if (e->w.xpad) {
+    // the rows past Sv of each sequence stay zero in the handle's input copy (nothing else
+    // writes them)
+    const size_t TH = (size_t)T * H * es;
+    err = hipMemset(e->w.xpad, 0, TH);
+    if (err == hipSuccess) err = hipMemset(e->w.spad, 0, TH);
     if (err == hipSuccess) err = hipDeviceSynchronize();
     if (err != hipSuccess) {
-      hipFree(e->ws);
+      hipFree(e->ws_mem);
       hipFree(e->weights);
       delete e;
       return hip_fail(err, "hipMemset(padding)");
     }
   }
-  // split-K workspace: the largest any of the four projections plans for
-  {
-    const int Ti = e->T, Hi = e->H, Fi = e->F;
-    const size_t need = std::max(std::max(gemm_splitk_workspace(dtype, Ti, 3 * Hi, Hi),
-                                          gemm_splitk_workspace(dtype, Ti, Hi, Hi)),
-                                 std::max(gemm_splitk_workspace(dtype, Ti, Fi, Hi),
-                                          gemm_splitk_workspace(dtype, Ti, Hi, Fi)));
-    if (need) {
-      err = hipMalloc(&e->splitk, need * sizeof(float));
-      if (err != hipSuccess) {
-        hipFree(e->ws);
-        hipFree(e->weights);
-        delete e;
-        return hip_fail(err, "hipMalloc(split-K workspace)");
-      }
-      e->splitk_elems = need;
-    }
-  }
+  // the static scratch of ftx_forward_static_workspace, resolved once per device here (the
+  // regular forward does not need it: a failure is reported by that entry point)
+  (void)static_scratch(dev);
   *out = e;
   return FTX_OK;
 }
@@ -507,9 +555,9 @@ ftx_status ftx_set_weights(ftx_encoder* e, int layer, const ftx_layer_weights* w
   return FTX_OK;
 }
 
-ftx_status ftx_forward(ftx_encoder* e, const void* input, const int32_t* seq_lens, void* output,
-                       void* stream) {
-  last_error_slot().clear();
+// Argument checks of the two forward entry points.
+static ftx_status check_forward(const ftx_encoder* e, const void* input, const int32_t* seq_lens,
+                                const void* output) {
   if (!e) return fail(FTX_ERR_INVALID_ARG, "encoder is NULL");
   if (!input || !output) return fail(FTX_ERR_INVALID_ARG, "input or output is NULL");
   if (!aligned16(input) || !aligned16(output))
@@ -520,9 +568,17 @@ ftx_status ftx_forward(ftx_encoder* e, const void* input, const int32_t* seq_len
     if (!e->ready[l]) return fail(FTX_ERR_NOT_READY, "layer " + std::to_string(l) + " has no weights");
   if (!all_device({input, output, seq_lens}))
     return fail(FTX_ERR_INVALID_ARG, "input, output and seq_lens must be device memory");
+  return FTX_OK;
+}
+
+ftx_status ftx_forward(ftx_encoder* e, const void* input, const int32_t* seq_lens, void* output,
+                       void* stream) {
+  last_error_slot().clear();
+  ftx_status st0 = check_forward(e, input, seq_lens, output);
+  if (st0 != FTX_OK) return st0;
   hipStream_t s = (hipStream_t)stream;
   FTX_HIP(hipSetDevice(e->device));
-  if (!e->graph_mode || e->timing) return enqueue_forward(e, input, seq_lens, output, s);
+  if (!e->graph_mode || e->timing) return enqueue_forward(e, e->w, input, seq_lens, output, s);
 
   // graph mode: replay the captured forward if it was made for these buffers, else capture
   // one on the handle's own stream (the caller's may be the default stream, which cannot be
@@ -531,7 +587,7 @@ ftx_status ftx_forward(ftx_encoder* e, const void* input, const int32_t* seq_len
     drop_graph(e);
     if (!e->cap_stream) FTX_HIP(hipStreamCreateWithFlags(&e->cap_stream, hipStreamNonBlocking));
     FTX_HIP(hipStreamBeginCapture(e->cap_stream, hipStreamCaptureModeThreadLocal));
-    ftx_status st = enqueue_forward(e, input, seq_lens, output, e->cap_stream);
+    ftx_status st = enqueue_forward(e, e->w, input, seq_lens, output, e->cap_stream);
     hipGraph_t g = nullptr;
     hipError_t err = hipStreamEndCapture(e->cap_stream, &g);
     if (st != FTX_OK) {
@@ -553,6 +609,24 @@ ftx_status ftx_forward(ftx_encoder* e, const void* input, const int32_t* seq_len
   return FTX_OK;
 }
 
+ftx_status ftx_forward_static_workspace(ftx_encoder* e, const void* input,
+                                        const int32_t* seq_lens, void* output, void* stream) {
+  last_error_slot().clear();
+  ftx_status st = check_forward(e, input, seq_lens, output);
+  if (st != FTX_OK) return st;
+  if (e->ws_bytes > (size_t)FTX_STATIC_SCRATCH_BYTES)
+    return fail(FTX_ERR_UNSUPPORTED,
+                "this forward needs " + std::to_string(e->ws_bytes) +
+                    " bytes of workspace; the static scratch holds " +
+                    std::to_string((size_t)FTX_STATIC_SCRATCH_BYTES));
+  FTX_HIP(hipSetDevice(e->device));
+  char* base = (char*)static_scratch(e->device);
+  if (!base) return fail(FTX_ERR_DEVICE, "hipGetSymbolAddress of the static scratch failed");
+  Workspace w;
+  layout_workspace(e, base, &w);
+  return enqueue_forward(e, w, input, seq_lens, output, (hipStream_t)stream, true);
+}
+
 ftx_status ftx_destroy(ftx_encoder* e) {
   last_error_slot().clear();
   if (!e) return FTX_OK;
@@ -565,9 +639,8 @@ ftx_status ftx_destroy(ftx_encoder* e) {
   for (auto ev : e->pool) hipEventDestroy(ev);
   drop_graph(e);
   if (e->cap_stream) hipStreamDestroy(e->cap_stream);
-  if (e->splitk) hipFree(e->splitk);
   hipFree(e->weights);
-  hipFree(e->ws);
+  hipFree(e->ws_mem);
   delete e;
   return FTX_OK;
 }

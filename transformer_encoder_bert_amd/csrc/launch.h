@@ -136,6 +136,9 @@ hipError_t launch_bias_gelu(ftx_dtype dt, int rows, int cols, const void* u, con
 hipError_t launch_transpose(ftx_dtype dt, int rows, int cols, const void* in, void* out,
                             hipStream_t s);
 
+// Zero `bytes` bytes at p (16-byte aligned, a multiple of 16) with a kernel.
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
 // Largest LayerNorm row the library handles (4-element vectors, <= 16 per lane of a wave).
 constexpr int kMaxLayerNormCols = 4096;
 // largest inner dimension K of a projection: a 256-row panel of K elements stays below 2^31

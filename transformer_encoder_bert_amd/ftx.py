@@ -35,7 +35,8 @@ DECODER_WEIGHT_FIELDS = ("w_q", "b_q", "w_k", "b_k", "w_v", "b_v", "w_o", "b_o",
                          "ln3_gamma", "ln3_beta")
 
 
-EXPORTED = ("ftx_encoder_create", "ftx_set_weights", "ftx_forward", "ftx_destroy",
+EXPORTED = ("ftx_encoder_create", "ftx_set_weights", "ftx_forward", "ftx_forward_static_workspace",
+            "ftx_destroy",
             "ftx_status_string", "ftx_last_error", "ftx_set_option", "ftx_kernel_times",
             "ftx_step_linear", "ftx_step_qkv_projection", "ftx_step_qkv_attention",
             "ftx_step_bias_qkv_split",
@@ -82,6 +83,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ftx_encoder_create": (i, [i, i, i, i, i, i, ctypes.POINTER(p)]),
         "ftx_set_weights": (i, [p, i, ctypes.POINTER(ftx_layer_weights), v]),
         "ftx_forward": (i, [p, p, p, p, v]),
+        "ftx_forward_static_workspace": (i, [p, p, p, p, v]),
         "ftx_destroy": (i, [p]),
         "ftx_status_string": (ctypes.c_char_p, [i]),
         "ftx_last_error": (ctypes.c_char_p, []),
@@ -181,6 +183,15 @@ def ftx_forward(enc, x: torch.Tensor, seq_lens: Optional[torch.Tensor], out: tor
            "ftx_forward")
 
 
+def ftx_forward_static_workspace(enc, x: torch.Tensor, seq_lens: Optional[torch.Tensor],
+                                 out: torch.Tensor, stream=None) -> None:
+    if seq_lens is not None:
+        _need(seq_lens, "seq_lens", torch.int32)
+    _check(load_library().ftx_forward_static_workspace(enc, _ptr(x), _ptr(seq_lens), _ptr(out),
+                                                       _stream(stream)),
+           "ftx_forward_static_workspace")
+
+
 def ftx_destroy(enc) -> None:
     _check(load_library().ftx_destroy(enc), "ftx_destroy")
 
@@ -224,6 +235,17 @@ class Encoder:
             out = torch.empty(self.shape, dtype=self.dtype, device=x.device)
         _need(out, "output", self.dtype, x.numel())
         ftx_forward(self.handle, x, seq_lens, out, stream)
+        return out
+
+    def forward_static_workspace(self, x: torch.Tensor, seq_lens: Optional[torch.Tensor],
+                                 out: torch.Tensor, stream=None) -> torch.Tensor:
+        """ftx_forward_static_workspace: the forward with the library's static scratch as
+        workspace; ``out`` is the caller's (nothing is allocated)."""
+        if seq_lens is not None:
+            _need(seq_lens, "seq_lens", torch.int32, self.shape[0])
+        _need(x, "input", self.dtype, self.shape[0] * self.shape[1] * self.shape[2])
+        _need(out, "output", self.dtype, x.numel())
+        ftx_forward_static_workspace(self.handle, x, seq_lens, out, stream)
         return out
 
     def set_option(self, option: int, value: int) -> None:
