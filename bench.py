@@ -26,6 +26,14 @@ METRIC = "sequences/sec + TFLOPS (% MFMA peak), 12-layer BERT-base fp16, seq 32/
 WORKLOAD_DEFAULT = "bert_base_fp16_s32"
 PEAK_MFMA_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6, "fp32": 157.3}
 PEAK_HBM_GBS = 8000.0
+# MI355X: 256 CUs of 4 SIMDs at a 2.4 GHz peak engine clock (AMD's published figures); the
+# MFMA-busy fraction divides SQ_VALU_MFMA_BUSY_CYCLES (summed over every SIMD) by
+# SIMDs x clock x kernel time
+SIMDS = 1024
+CLOCK_HZ = 2.4e9
+# bytes written before each timed launch of the HBM measurement: four times the 256 MB
+# last-level cache (MALL), so every input of the timed kernel comes from HBM
+FLUSH_BYTES = 1 << 30
 DTYPE_TAG = {"fp16": "f16", "bf16": "bf16", "fp32": "f32"}
 
 
@@ -48,9 +56,13 @@ def parse():
     p.add_argument("--copy-calib-mb", type=int, default=0,
                    help="before the forwards, run a plain device copy kernel (torch.neg, fp16) over "
                         "this many MiB three times, so a counter run also sees a kernel of known traffic")
-    p.add_argument("--summarize-rocprof", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
-                   help="write profiles/<--summary-name>.md and _traffic.json from rocprofv3 output "
-                        "of this benchmark, then exit (no GPU needed)")
+    p.add_argument("--summarize-rocprof", nargs="+", metavar="DIR",
+                   help="TRACE_DIR FETCH_DIR WRITE_DIR [MFMA_DIR]: write profiles/<--summary-name>.md "
+                        "and _traffic.json from rocprofv3 output of this benchmark, then exit (no GPU "
+                        "needed)")
+    p.add_argument("--no-hbm", action="store_true",
+                   help="skip the HBM measurement of the element-wise kernels with the MALL flushed")
+    p.add_argument("--hbm-reps", type=int, default=20)
     p.add_argument("--summarize-trace", metavar="TRACE_DIR", default=None,
                    help="write profiles/<--summary-name>.md from a rocprofv3 kernel-trace run of "
                         "this benchmark (kernel stats only), then exit (no GPU needed)")
@@ -146,16 +158,19 @@ def classify_dispatches(names):
     return steps
 
 
-def profile_commands(wl, calib_mb, name):
-    """The three rocprofv3 runs a traffic summary is made from, and the summarizing call."""
-    w = "" if wl == WORKLOAD_DEFAULT else f" --workload {wl}"
-    run = f"python3 bench.py{w} --no-cpu-baseline --copy-calib-mb {calib_mb}"
+def profile_commands(wl, calib_mb, name, batch=None):
+    """The four rocprofv3 runs a summary is made from (kernel trace, FETCH_SIZE, WRITE_SIZE,
+    MFMA-busy counters), and the summarizing call."""
+    w = ("" if wl == WORKLOAD_DEFAULT else f" --workload {wl}") + (f" --batch {batch}" if batch else "")
+    run = f"python3 bench.py{w} --no-cpu-baseline --no-hbm --copy-calib-mb {calib_mb}"
+    short = "--steps 2 --warmup 1 --no-kernel-times"
     return [
         f"rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o trace -- {run} --steps 5 --warmup 2",
-        f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_fetch -o fetch -- {run} --steps 2 --warmup 1 --no-kernel-times",
-        f"rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_write -o write -- {run} --steps 2 --warmup 1 --no-kernel-times",
+        f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_fetch -o fetch -- {run} {short}",
+        f"rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_write -o write -- {run} {short}",
+        f"rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES -f csv -d gpurun_out/prof_mfma -o mfma -- {run} {short}",
         f"python3 bench.py{w} --copy-calib-mb {calib_mb} --summarize-rocprof gpurun_out/prof_trace "
-        f"gpurun_out/prof_fetch gpurun_out/prof_write --summary-name {name}",
+        f"gpurun_out/prof_fetch gpurun_out/prof_write gpurun_out/prof_mfma --summary-name {name}",
     ]
 
 
@@ -219,7 +234,10 @@ def summarize_rocprof(args):
     """Summarise a rocprofv3 kernel trace plus FETCH_SIZE / WRITE_SIZE counter runs of this
     benchmark (made with --copy-calib-mb) into profiles/<name>.md and profiles/<name>_traffic.json."""
     import csv
-    trace_dir, fetch_dir, write_dir = args.summarize_rocprof
+    if len(args.summarize_rocprof) not in (3, 4):
+        raise SystemExit("--summarize-rocprof takes TRACE_DIR FETCH_DIR WRITE_DIR [MFMA_DIR]")
+    trace_dir, fetch_dir, write_dir = args.summarize_rocprof[:3]
+    mfma_dir = args.summarize_rocprof[3] if len(args.summarize_rocprof) == 4 else None
     def one(d, suffix):
         fs = [os.path.join(d, f) for f in os.listdir(d) if f.endswith(suffix)]
         if len(fs) != 1:
@@ -251,21 +269,38 @@ def summarize_rocprof(args):
             if st is None:
                 continue
             counters.setdefault(st, {}).setdefault(name, []).append(float(r["Counter_Value"]) * 1024.0 * scale[name])
+    mfma = {}
+    if mfma_dir:
+        # one row per (dispatch, counter): MFMA-busy cycles summed over every SIMD
+        rows = one(mfma_dir, "_counter_collection.csv")
+        per_dispatch = {}
+        for r in rows:
+            if r["Counter_Name"] == "SQ_VALU_MFMA_BUSY_CYCLES":
+                per_dispatch[int(r["Dispatch_Id"])] = (r["Kernel_Name"], float(r["Counter_Value"]))
+        ids = sorted(per_dispatch)
+        for i, st in zip(ids, classify_dispatches([per_dispatch[i][0] for i in ids])):
+            if st is not None:
+                mfma.setdefault(st, []).append(per_dispatch[i][1])
     wl = WORKLOAD_DEFAULT if args.workload is None else args.workload
     import synthetic_inputs as si
     w = si.WORKLOADS[wl]
     shape = w.shape(args.batch or max(w.batches))
     out = {"workload": wl, "batch": shape.batch, "kernel_source_hash": kernel_source_hash(),
-           "scale": scale, "steps": {}}
-    commands = args.summary_commands or profile_commands(wl, args.copy_calib_mb, args.summary_name)
+           "scale": scale, "simds": SIMDS, "clock_hz": CLOCK_HZ, "steps": {}}
+    commands = args.summary_commands or profile_commands(wl, args.copy_calib_mb, args.summary_name,
+                                                         args.batch)
     lines = [f"# Kernel time and HBM traffic per step -- {wl}, batch {shape.batch}", "",
              "Commands (from the repository root, on one MI355X, with TMPDIR=/tmp):", "", "```",
              *commands, "```", "",
              f"FETCH_SIZE and WRITE_SIZE are scaled by what they read for a plain copy kernel "
              f"(torch.neg over {args.copy_calib_mb} MiB of fp16): true bytes per counted byte "
-             f"{scale['FETCH_SIZE']:.3f} (fetch) and {scale['WRITE_SIZE']:.3f} (write).", "",
-             "| step | launches | avg us | algorithmic MB | fetched MB | written MB | "
-             "algorithmic TFLOP/s | algorithmic GB/s |", "|---|---|---|---|---|---|---|---|"]
+             f"{scale['FETCH_SIZE']:.3f} (fetch) and {scale['WRITE_SIZE']:.3f} (write).",
+             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES (summed over the SIMDs) / "
+             f"({SIMDS} SIMDs x {CLOCK_HZ / 1e9:.1f} GHz x avg us); frac = algorithmic TFLOP/s / "
+             f"{PEAK_MFMA_TFLOPS[shape.dtype]} (dense MFMA peak).", "",
+             "| step | launches | avg us | algorithmic MB | fetched MB | written MB | traffic / algorithmic | "
+             "algorithmic TFLOP/s | frac of peak | MFMA busy % | algorithmic GB/s |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
     for st in ("qkv_attention", "qkv_gemm", "bias_qkv_split", "attention", "attn_out_gemm", "ln1", "ffn1_gemm",
                "bias_gelu", "ffn2_gemm", "ln2"):
         if st not in dur:
@@ -275,12 +310,18 @@ def summarize_rocprof(args):
         c = counters.get(st, {})
         fetch = sum(c.get("FETCH_SIZE", [0])) / max(1, len(c.get("FETCH_SIZE", [])))
         write = sum(c.get("WRITE_SIZE", [0])) / max(1, len(c.get("WRITE_SIZE", [])))
+        busy = None
+        if st in mfma:
+            busy = sum(mfma[st]) / len(mfma[st]) / (SIMDS * CLOCK_HZ * avg * 1e-6)
+        tfl = fl / (avg * 1e-6) / 1e12 if fl else 0.0
         out["steps"][st] = {"symbol": sym[st], "avg_us": avg, "launches": len(dur[st]),
                             "fetch_bytes": fetch, "write_bytes": write,
-                            "algorithmic_bytes": by, "flops": fl}
+                            "algorithmic_bytes": by, "flops": fl, "mfma_busy": busy,
+                            "frac": tfl / PEAK_MFMA_TFLOPS[shape.dtype] if fl else None}
         lines.append(f"| {st} | {len(dur[st])} | {avg:.1f} | {by / 1e6:.1f} | {fetch / 1e6:.1f} | "
-                     f"{write / 1e6:.1f} | {fl / (avg * 1e-6) / 1e12 if fl else 0:.1f} | "
-                     f"{by / (avg * 1e-6) / 1e9:.0f} |")
+                     f"{write / 1e6:.1f} | {(fetch + write) / by:.2f} | {tfl:.1f} | "
+                     f"{tfl / PEAK_MFMA_TFLOPS[shape.dtype]:.3f} | "
+                     f"{'' if busy is None else f'{100 * busy:.1f}'} | {by / (avg * 1e-6) / 1e9:.0f} |")
     lines += ["", "Kernel symbols:", ""]
     lines += [f"- {st}: `{v['symbol']}`" for st, v in out["steps"].items()]
     lines += ["", f"Kernel source hash: `{out['kernel_source_hash']}`"]
@@ -293,18 +334,22 @@ def summarize_rocprof(args):
     print(base + ".md")
 
 
-def measured_traffic(workload: str, batch: int, step: str):
-    """HBM bytes per launch of `step` from the committed counter summary of this workload,
-    or None when there is none or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"{workload}_b{batch}_traffic.json")
+def measured_profile(workload: str, batch: int, step: str):
+    """What the committed rocprofv3 summary of this workload says of `step` (kernel time,
+    HBM bytes, MFMA busy), or None when there is none or the kernel sources changed since it
+    was taken."""
+    rel = os.path.join("profiles", f"{workload}_b{batch}_traffic.json")
+    path = os.path.join(ROOT, rel)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
     if t.get("kernel_source_hash") != kernel_source_hash() or step not in t.get("steps", {}):
         return None
-    s = t["steps"][step]
-    return s["fetch_bytes"] + s["write_bytes"]
+    s = dict(t["steps"][step])
+    s["traffic"] = s["fetch_bytes"] + s["write_bytes"]
+    s["source"] = rel.replace("_traffic.json", ".md")
+    return s
 
 
 def blas_threads() -> int:
@@ -636,19 +681,96 @@ def main():
             achieved, peak, unit, bound = fl / avg_s / 1e12, PEAK_MFMA_TFLOPS[dt], "TFLOP/s", "mfma"
         else:
             achieved, peak, unit, bound = by / avg_s / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
-        traffic = measured_traffic(wl.name, shape.batch, dom)
-        result["roofline"] = {"kernel": dom, "bound": bound, "achieved": achieved, "peak": peak,
-                              "unit": unit, "frac": achieved / peak, "traffic": traffic,
-                              "traffic_gbs": None if traffic is None else traffic / avg_s / 1e9,
-                              "work_per_launch": fl if bound == "mfma" else by,
-                              "avg_launch_us": kernels[dom]["avg_us"]}
+        prof = measured_profile(wl.name, shape.batch, dom)
+        traffic = None if prof is None else prof["traffic"]
+        result["roofline"] = {
+            "kernel": dom, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak, "traffic": traffic,
+            "work_per_launch": fl if bound == "mfma" else by,
+            "avg_launch_us": kernels[dom]["avg_us"],
+            "timing": "HIP event pair around every launch on the forward's stream, "
+                      f"{args.steps} forwards after the timed region",
+            # the committed rocprofv3 summary of the same kernel code (null when the kernels
+            # changed since): its own kernel time, and HBM traffic and MFMA busy over that time
+            "profile": None if prof is None else {
+                "source": prof["source"], "avg_us": prof["avg_us"],
+                "frac": (fl if bound == "mfma" else by) / (prof["avg_us"] * 1e-6)
+                        / (1e12 if bound == "mfma" else 1e9) / peak,
+                "mfma_busy": prof.get("mfma_busy"),
+                "traffic_over_algorithmic": prof["traffic"] / prof["algorithmic_bytes"],
+                "traffic_gbs": prof["traffic"] / (prof["avg_us"] * 1e-6) / 1e9},
+        }
         result["kernels"] = kernels
         result["ms_per_step_with_kernel_events"] = 1e3 * timed_wall / args.steps
 
     enc.close()
+    if case.lens is not None:
+        # the same forward counted on the valid tokens only: projections on sum(len_b) rows,
+        # attention over len_b queries and keys
+        valid = shape.valid_flops(case.lens)
+        result["effective_tflops"] = valid / (ms_per_step * 1e-3) / 1e12
+        result["valid_token_fraction"] = float(np.sum(case.lens)) / shape.tokens
+    if not args.no_hbm:
+        result["elementwise_hbm"] = elementwise_hbm(shape, args.hbm_reps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def elementwise_hbm(shape, reps: int):
+    """HBM GB/s of the element-wise kernels (bias + residual + LayerNorm, standalone bias +
+    GELU, standalone bias + head split) at this workload's shape, each launch timed alone with
+    the last-level cache flushed first: FLUSH_BYTES are written before every timed launch, so
+    the kernel's inputs come from HBM, not from the 256 MB MALL or the L2s.  Algorithmic
+    bytes (inputs read once, output written once) over the median event time."""
+    import torch
+    from transformer_encoder_bert_amd import ftx
+    dev = "cuda:0"
+    dt = {"fp16": torch.float16, "bf16": torch.bfloat16, "fp32": torch.float32}[shape.dtype]
+    e = 4 if shape.dtype == "fp32" else 2
+    T, H, F = shape.tokens, shape.hidden, shape.ffn
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+
+    def rnd(*sz):
+        return torch.randn(*sz, generator=g, device=dev, dtype=torch.float32).to(dt)
+
+    x, a, y = rnd(T, H), rnd(T, H), torch.empty(T, H, dtype=dt, device=dev)
+    bias, gamma, beta = rnd(H), rnd(H), rnd(H)
+    u, bias_f, gel = rnd(T, F), rnd(F), torch.empty(T, F, dtype=dt, device=dev)
+    qkv, bias3 = rnd(T, 3 * H), rnd(3 * H)
+    q, k, vt = (torch.empty(T * H, dtype=dt, device=dev) for _ in range(3))
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    B, S, n, d = shape.batch, shape.seq_len, shape.head_num, shape.size_per_head
+    kernels = {
+        "bias_residual_layernorm": (lambda: ftx.ftx_step_bias_residual_layernorm(x, a, bias, gamma, beta, y),
+                                    3 * T * H * e),
+        "bias_gelu": (lambda: ftx.ftx_step_bias_gelu(u, bias_f, gel), 2 * T * F * e),
+        "bias_qkv_split": (lambda: ftx.ftx_step_bias_qkv_split(B, S, n, d, qkv, bias3, q, k, vt),
+                           6 * T * H * e),
+    }
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, (fn, nbytes) in kernels.items():
+        fn()
+        torch.cuda.synchronize()
+        times = []
+        for r in range(reps):
+            flush.fill_(r & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        med = float(np.median(times))
+        out[name] = {"bytes": nbytes, "median_us": med * 1e6, "min_us": min(times) * 1e6,
+                     "gbs": nbytes / med / 1e9, "frac_of_hbm_peak": nbytes / med / 1e9 / PEAK_HBM_GBS}
+    out["method"] = (f"each launch alone after writing {FLUSH_BYTES >> 20} MiB (4x the MALL); "
+                     f"HIP events around the launch, median of {reps}; algorithmic bytes")
+    del flush
+    torch.cuda.synchronize()
+    return out
 
 
 if __name__ == "__main__":

@@ -99,6 +99,13 @@ class Shape:
         T, S, H = self.tokens, self.seq_len, self.hidden
         return float(self.num_layers) * (24.0 * T * H * H + 4.0 * T * S * H)
 
+    def valid_flops(self, lens) -> float:
+        """The same count on the valid tokens only: the projections on sum(len_b) rows, scores
+        and context over len_b queries and len_b keys per sequence."""
+        ln = np.asarray(lens, dtype=np.float64)
+        H = self.hidden
+        return float(self.num_layers) * (24.0 * ln.sum() * H * H + 4.0 * (ln * ln).sum() * H)
+
 
 @dataclass(frozen=True)
 class Workload:

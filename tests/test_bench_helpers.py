@@ -30,3 +30,28 @@ def test_separate_attention_dispatches():
 
 def test_unknown_kernels_are_not_classified():
     assert bench.classify_dispatches(["copy_kernel", LN]) == [None, "ln2"]
+
+
+def test_valid_token_flops():
+    """Full lengths give the padded count; the count falls with the valid tokens (projections
+    linearly, attention quadratically)."""
+    import numpy as np
+    import synthetic_inputs as si
+    sh = si.Shape(4, 64, 12, 64, 12, "fp16")
+    assert sh.valid_flops(np.full(4, 64)) == sh.flops()
+    half = sh.valid_flops(np.full(4, 32))
+    H, L = 768, 12
+    assert half == L * (24.0 * 128 * H * H + 4.0 * 4 * 32 * 32 * H)
+
+
+def test_profile_commands_run_the_program_directly():
+    """Every rocprofv3 command puts python3 right after `--` (no shell or env hop) and keeps
+    counter passes apart from the kernel trace."""
+    cmds = bench.profile_commands("bert_base_fp16_s32", 512, "x", 64)
+    prof = [c for c in cmds if c.startswith("rocprofv3")]
+    assert len(prof) == 4
+    for c in prof:
+        assert " -- python3 bench.py" in c
+        assert not ("--pmc" in c and "--kernel-trace" in c)
+    assert any("SQ_VALU_MFMA_BUSY_CYCLES" in c for c in prof)
+    assert all("--batch 64" in c for c in cmds)
