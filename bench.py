@@ -31,8 +31,10 @@ PEAK_HBM_GBS = 8000.0
 # SIMDs x clock x kernel time
 SIMDS = 1024
 CLOCK_HZ = 2.4e9
-# bytes written before each timed launch of the HBM measurement: four times the 256 MB
-# last-level cache (MALL), so every input of the timed kernel comes from HBM
+# bytes read before each timed launch of the HBM measurement: four times the 256 MB
+# last-level cache (MALL), so every input of the timed kernel comes from HBM (read, not
+# written: written lines would leave the caches dirty, and their write-back would land in the
+# timed kernel)
 FLUSH_BYTES = 1 << 30
 DTYPE_TAG = {"fp16": "f16", "bf16": "bf16", "fp32": "f32"}
 
@@ -63,6 +65,11 @@ def parse():
     p.add_argument("--no-hbm", action="store_true",
                    help="skip the HBM measurement of the element-wise kernels with the MALL flushed")
     p.add_argument("--hbm-reps", type=int, default=20)
+    p.add_argument("--hbm-only", action="store_true",
+                   help="only the element-wise HBM measurement (one JSON line), e.g. under a kernel trace")
+    p.add_argument("--summarize-hbm", metavar="TRACE_DIR", default=None,
+                   help="write profiles/<--summary-name>.md from a rocprofv3 --kernel-trace run of "
+                        "--hbm-only, then exit (no GPU needed)")
     p.add_argument("--summarize-trace", metavar="TRACE_DIR", default=None,
                    help="write profiles/<--summary-name>.md from a rocprofv3 kernel-trace run of "
                         "this benchmark (kernel stats only), then exit (no GPU needed)")
@@ -334,6 +341,54 @@ def summarize_rocprof(args):
     print(base + ".md")
 
 
+HBM_KERNELS = (("layernorm_kernel", "bias_residual_layernorm", lambda T, H, F, e: 3 * T * H * e),
+               ("bias_gelu_kernel", "bias_gelu", lambda T, H, F, e: 2 * T * F * e),
+               ("bias_qkv_split_kernel", "bias_qkv_split", lambda T, H, F, e: 6 * T * H * e))
+
+
+def summarize_hbm(args):
+    """Kernel times of the element-wise kernels in a rocprofv3 --kernel-trace run of
+    --hbm-only (each launch after the MALL flush) into profiles/<name>.md: algorithmic bytes
+    over the traced kernel time, against 8 TB/s."""
+    import csv
+    fs = [os.path.join(args.summarize_hbm, f) for f in os.listdir(args.summarize_hbm)
+          if f.endswith("_kernel_trace.csv")]
+    if len(fs) != 1:
+        raise SystemExit(f"expected one *_kernel_trace.csv in {args.summarize_hbm}")
+    rows = sorted(csv.DictReader(open(fs[0])), key=lambda r: int(r["Dispatch_Id"]))
+    import synthetic_inputs as si
+    wl = args.workload or WORKLOAD_DEFAULT
+    shape = si.WORKLOADS[wl].shape(args.batch)
+    e = 4 if shape.dtype == "fp32" else 2
+    d = os.path.relpath(os.path.abspath(args.summarize_hbm), ROOT)
+    flags = (f" --workload {wl}" if wl != WORKLOAD_DEFAULT else "") + (f" --batch {args.batch}" if args.batch else "")
+    lines = [f"# Element-wise kernels from HBM (MALL flushed) -- {wl}, batch {shape.batch}", "",
+             "Commands (from the repository root, on one MI355X, with TMPDIR=/tmp):", "", "```",
+             f"rocprofv3 --kernel-trace -f csv -d {d} -o hbm -- python3 bench.py{flags} --hbm-only",
+             f"python3 bench.py{flags} --summarize-hbm {d} --summary-name {args.summary_name}",
+             "```", "",
+             f"Each launch runs alone after a reduction that reads {FLUSH_BYTES >> 20} MiB (four times the "
+             "256 MB MALL), so its inputs come from HBM.  The first launch of each kernel (a warm-up "
+             "without the flush) is left out.  GB/s = algorithmic bytes (inputs once, output once) / "
+             "traced kernel time.", "",
+             "| kernel | launches | algorithmic MB | median us | min us | GB/s (median) | % of 8 TB/s |",
+             "|---|---|---|---|---|---|---|"]
+    for sym_part, name, nbytes in HBM_KERNELS:
+        t = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3 for r in rows
+             if sym_part in r["Kernel_Name"] and "ftx" in r["Kernel_Name"]][1:]
+        if not t:
+            continue
+        by = nbytes(shape.tokens, shape.hidden, shape.ffn, e)
+        med = float(np.median(t))
+        lines.append(f"| {name} | {len(t)} | {by / 1e6:.1f} | {med:.1f} | {min(t):.1f} | "
+                     f"{by / (med * 1e-6) / 1e9:.0f} | {100 * by / (med * 1e-6) / 1e9 / PEAK_HBM_GBS:.1f} |")
+    lines += ["", f"Kernel source hash: `{kernel_source_hash()}`"]
+    path = os.path.join(ROOT, "profiles", args.summary_name + ".md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+
+
 def measured_profile(workload: str, batch: int, step: str):
     """What the committed rocprofv3 summary of this workload says of `step` (kernel time,
     HBM bytes, MFMA busy), or None when there is none or the kernel sources changed since it
@@ -533,11 +588,13 @@ def bench_decoder(args):
 
 def main():
     args = parse()
-    if args.summarize_rocprof or args.summarize_trace:
+    if args.summarize_rocprof or args.summarize_trace or args.summarize_hbm:
         if not args.summary_name:
             raise SystemExit("--summary-name is required")
         if args.summarize_rocprof:
             summarize_rocprof(args)
+        elif args.summarize_hbm:
+            summarize_hbm(args)
         else:
             summarize_trace(args)
         return
@@ -560,6 +617,11 @@ def main():
         sys.exit(1)
     wl = si.WORKLOADS[args.workload]
     batch = args.batch or max(wl.batches)
+    if args.hbm_only:
+        shape = wl.shape(batch)
+        res = {"workload": wl.name, "batch": batch, "elementwise_hbm": elementwise_hbm(shape, args.hbm_reps)}
+        print(json.dumps(res), flush=True)
+        return
     case = si.make_case(wl, batch)
     shape = case.shape
     dt = shape.dtype
@@ -720,9 +782,11 @@ def main():
 def elementwise_hbm(shape, reps: int):
     """HBM GB/s of the element-wise kernels (bias + residual + LayerNorm, standalone bias +
     GELU, standalone bias + head split) at this workload's shape, each launch timed alone with
-    the last-level cache flushed first: FLUSH_BYTES are written before every timed launch, so
+    the last-level cache flushed first: FLUSH_BYTES are read before every timed launch, so
     the kernel's inputs come from HBM, not from the 256 MB MALL or the L2s.  Algorithmic
-    bytes (inputs read once, output written once) over the median event time."""
+    bytes (inputs read once, output written once) over the median event time.  An event pair
+    around one launch adds a few microseconds; the kernel trace of --hbm-only
+    (--summarize-hbm) gives the kernel time itself."""
     import torch
     from transformer_encoder_bert_amd import ftx
     dev = "cuda:0"
@@ -740,7 +804,8 @@ def elementwise_hbm(shape, reps: int):
     u, bias_f, gel = rnd(T, F), rnd(F), torch.empty(T, F, dtype=dt, device=dev)
     qkv, bias3 = rnd(T, 3 * H), rnd(3 * H)
     q, k, vt = (torch.empty(T * H, dtype=dt, device=dev) for _ in range(3))
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
     B, S, n, d = shape.batch, shape.seq_len, shape.head_num, shape.size_per_head
     kernels = {
         "bias_residual_layernorm": (lambda: ftx.ftx_step_bias_residual_layernorm(x, a, bias, gamma, beta, y),
@@ -756,7 +821,7 @@ def elementwise_hbm(shape, reps: int):
         torch.cuda.synchronize()
         times = []
         for r in range(reps):
-            flush.fill_(r & 0xFF)
+            torch.sum(flush, dim=0, out=sink)  # reads FLUSH_BYTES
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             fn()
@@ -766,7 +831,7 @@ def elementwise_hbm(shape, reps: int):
         med = float(np.median(times))
         out[name] = {"bytes": nbytes, "median_us": med * 1e6, "min_us": min(times) * 1e6,
                      "gbs": nbytes / med / 1e9, "frac_of_hbm_peak": nbytes / med / 1e9 / PEAK_HBM_GBS}
-    out["method"] = (f"each launch alone after writing {FLUSH_BYTES >> 20} MiB (4x the MALL); "
+    out["method"] = (f"each launch alone after reading {FLUSH_BYTES >> 20} MiB (4x the MALL); "
                      f"HIP events around the launch, median of {reps}; algorithmic bytes")
     del flush
     torch.cuda.synchronize()
