@@ -920,6 +920,96 @@ __global__ __launch_bounds__(8 * kWave) void gemm_pp_kernel(const T* __restrict_
   gemm_epilogue<C, Epi>(epi, smem, m0, n0, wave, lane, acc, bq);
 }
 
+// Small-M projection (the rows of one or two short sequences): one workgroup of
+// kSmallWaves waves per 32 x 32 output tile, the waves splitting K.  Each wave issues the
+// global-to-LDS loads of its whole K range at once (at most kSmallMaxSlabs slabs, so one
+// round trip of memory latency instead of a chain of slab steps), multiplies its slabs, and
+// the waves' fp32 partial tiles are summed in wave order through LDS (deterministic) and
+// finished by the projection's own epilogue.  One launch where the split-K path takes a
+// partial-product launch and a reduction launch.  K is a whole number of slabs.
+constexpr int kSmallWaves = 4, kSmallMaxSlabs = 4;
+
+template <typename T, typename Epi>
+__global__ __launch_bounds__(kSmallWaves * kWave) void gemm_small_kernel(const T* __restrict__ A,
+                                                                         const T* __restrict__ Bt,
+                                                                         int M, int N, int K,
+                                                                         Epi epi) {
+  typedef GemmCfg<T, 32, 32, 1, 1> Cg;  // one slab: 32 rows of A and 32 rows of W^T
+  typedef typename Cg::MF MF;
+  typedef typename MF::frag frag;
+  constexpr int ROWB = Cg::ROWB, SLAB = Cg::STAGE, REGION = kSmallMaxSlabs * SLAB;
+  __shared__ __attribute__((aligned(1024))) char smem[kSmallWaves * REGION];
+  const int tiles_n = (N + 31) / 32;
+  const int m0 = (blockIdx.x / tiles_n) * 32, n0 = (blockIdx.x % tiles_n) * 32;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave, lr = lane % 32, g = lane / 32;
+  const int nk = K / Cg::BK;
+  const int spw = (nk + kSmallWaves - 1) / kSmallWaves;  // slabs per wave (<= kSmallMaxSlabs)
+  const int k0 = wave * spw, k1 = min(nk, k0 + spw);
+  char* const mine = smem + wave * REGION;
+
+  typename Epi::b4 bq[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) bq[q] = epi.bias4(n0 + 8 * q + 4 * g);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A + (size_t)m0 * K), (short)0, min(32, M - m0) * K * (int)sizeof(T), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Bt + (size_t)n0 * K), (short)0, min(32, N - n0) * K * (int)sizeof(T), 0x00020000);
+  // load q (of 4) of a slab fills rows 8 q .. 8 q + 7: lane l lands at position l % 8 of row
+  // 8 q + l / 8 and so fetches chunk (l % 8) ^ swz(row)
+  for (int kt = k0; kt < k1; ++kt) {
+    char* base = mine + (kt - k0) * SLAB;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int R = q * 8 + lane / 8;
+      const int off = (R * K + kt * Cg::BK + ((lane & 7) ^ swz(R)) * Cg::VEC) * (int)sizeof(T);
+      lds_dma16(ra, off, base + q * 1024);
+      lds_dma16(rb, off, base + 32 * ROWB + q * 1024);
+    }
+  }
+  wait_vmcnt<0>();  // this wave's slabs are in LDS (no other wave reads them)
+
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const int hl = swz(lr);
+  for (int kt = k0; kt < k1; ++kt) {
+    const char* base = mine + (kt - k0) * SLAB;
+#pragma unroll
+    for (int st = 0; st < Cg::NS; ++st) {
+      const int pos = ((2 * st + g) ^ hl) * 16;
+      const frag fa = *(const frag*)(base + lr * ROWB + pos);
+      const frag fb = *(const frag*)(base + 32 * ROWB + lr * ROWB + pos);
+      MF::mma(fb, fa, acc);
+    }
+  }
+  // partial tiles through LDS: register r of lane l at float r * 64 + l of the wave's region
+  // (after its own reads, in order), summed by wave 0 in wave order
+  float* red = (float*)mine;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) red[r * kWave + lane] = acc[r];
+  __syncthreads();
+  if (wave != 0) return;
+  f32x16 sum;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sum[r] = 0.f;
+  for (int w = 0; w < kSmallWaves; ++w) {
+    const float* pw = (const float*)(smem + w * REGION);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum[r] += pw[r * kWave + lane];
+  }
+  // epilogue scratch past wave 0's partials, inside its own region
+  typedef typename Epi::out_t TO;
+  epilogue_tile(epi, (TO*)(smem + 16 * kWave * sizeof(float)), m0, n0, lane, sum, bq);
+}
+
+template <typename T>
+static bool small_gemm_fits(int M, int N, int K, int cus) {
+  constexpr int BK = GemmCfg<T, 32, 32, 1, 1>::BK;
+  const long tiles = (long)((M + 31) / 32) * ((N + 31) / 32);
+  return K % BK == 0 && K / BK <= kSmallWaves * kSmallMaxSlabs && tiles <= cus;
+}
+
 // --------------------------------------------------------------------------- tile choice
 // The launch configuration is chosen per shape (the article tunes grid and block sizes to
 // the number of input rows, which ranges from tens at batch 1 to thousands at batch in the
@@ -1133,6 +1223,16 @@ static hipError_t gemm_launch(int M, int N, int K, const void* a, const void* w_
   constexpr bool wide = sizeof(T) == 2;
   const DeviceInfo di = device_info();
   GemmPlan plan = plan_gemm(M, N, K, (int)sizeof(T), !reduce, di.cus);
+  // where the plan splits K and finishes with a reduction launch, few rows take the
+  // small-M kernel instead (one launch, no workspace)
+  if constexpr (!Epi::kBlock) {
+    if (reduce && plan.splits > 1 && small_gemm_fits<T>(M, N, K, di.cus)) {
+      const int tiles = ((M + 31) / 32) * ((N + 31) / 32);
+      gemm_small_kernel<T, Epi><<<tiles, kSmallWaves * kWave, 0, s>>>((const T*)a, (const T*)w_t, M, N,
+                                                                      K, epi);
+      return hipGetLastError();
+    }
+  }
   if (plan.splits > 1 && (!ws || ws_elems < (size_t)plan.splits * M * N)) {
     plan.splits = 1;
     plan.kchunk = K;
