@@ -249,6 +249,33 @@ def test_split_k_paths(shape):
     check(out, ref, shape.dtype, layer_tol(shape.dtype), f"{shape}")
 
 
+@pytest.mark.parametrize("shape,fused", [
+    (si.Shape(1, 32, 12, 64, 2, "fp16"), True),    # BERT-base heads, one sequence
+    (si.Shape(2, 32, 12, 64, 1, "bf16"), True),    # the fp32 residual stream
+    (si.Shape(1, 32, 24, 32, 1, "fp16"), True),    # size per head 32, hidden 768
+    (si.Shape(1, 20, 16, 64, 1, "bf16"), True),    # hidden 1024 (four workgroups per head), S padded
+    (si.Shape(8, 32, 12, 64, 1, "fp16"), False),   # 9 MiB of per-head partials: separate kernels
+])
+def test_attention_with_output_projection_partials(shape, fused):
+    """Small batches at S = 32: the attention kernel also computes each head's share of the
+    attention-output projection (split-K partials split by head, summed by the LayerNorm in
+    head order); one launch replaces the attention and the projection (while the per-head
+    partials stay within 4 MiB).  Against the oracle at the layer (one layer) or stack bar,
+    with padded lengths."""
+    c = si.custom_case(shape, 61 + shape.batch, lens_range=(1, shape.seq_len), params="random_affine")
+    layers = list(c.layers())
+    ref = oracle.encoder(c.x, layers, c.lens, shape.head_num)
+    enc = _encoder(shape, layers)
+    enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)
+    out = to_f64(enc.forward(to_dev(c.x, shape.dtype), dev_lens(c.lens)))
+    t = enc.kernel_times()
+    enc.close()
+    assert t["attention"][1] == shape.num_layers and t["ln1"][1] == shape.num_layers
+    assert t["attn_out_gemm"][1] == (0 if fused else shape.num_layers)
+    tol = stack_tol(shape.dtype) if shape.num_layers > 1 else layer_tol(shape.dtype)
+    print(check(out, ref, shape.dtype, tol, f"{shape}"))
+
+
 @pytest.mark.parametrize("shape", [
     si.Shape(256, 32, 4, 32, 2, "fp16"),  # 8192 rows: 128 tiles of 64
     si.Shape(257, 32, 4, 32, 1, "bf16"),  # the fp32 residual stream; a partial last tile

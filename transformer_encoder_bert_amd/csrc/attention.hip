@@ -556,6 +556,177 @@ __global__ __launch_bounds__(256) void attention_s32_kernel(const T* __restrict_
     }
 }
 
+// The S = 32 attention of one (sequence, head) followed by that head's share of the
+// attention-output projection, for small batches where that projection splits K and the
+// LayerNorm after it sums the split partials: the projection's K range is the merged-heads
+// dimension, so head h's slice of it is exactly C_h (the head's context, 32 x D) times rows
+// h*D .. h*D+D-1 of Wo.  ceil(H / 256) workgroups of 8 waves per (b, h), one 32-column
+// output tile per wave (tile j = 8 part + wave): every wave first issues the loads of its Wo
+// fragments (the weight is given transposed, wo_t[n][k], so a fragment row is 4 consecutive
+// k twice; wave 0 after its Q, K, V loads), wave 0 runs
+// attention_s32_kernel's chain and leaves C_h, rounded to the storage type as the context
+// would be stored, in LDS in its own register order; after one barrier each wave multiplies
+// its tiles, C_h fragments taken lane by lane in that register order (the K order of an
+// MFMA only has to agree between its operands, and the Wo fragments are loaded in the same
+// order), and stores the fp32 partial tile to p[h][b*32 + i][n].  One launch for what the
+// attention kernel and the split-K partial products of the projection did in two.
+constexpr int kAttnOutMaxHidden = 1024;
+
+template <typename T, int D>
+__global__ __launch_bounds__(512) void attention_oproj_s32_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt,
+    const int32_t* __restrict__ lens, const T* __restrict__ wo_t, float* __restrict__ p, int B,
+    int nh, float scale_log2e, int s_valid) {
+  typedef AttnMfma<T> MF;
+  typedef typename MF::frag frag;
+  typedef typename VecT<T, 4>::type v4;
+  constexpr int VEC = MF::VEC;
+  static_assert(VEC == 8, "16-bit data");
+  constexpr int S = 32, KF = 2 * VEC, NQF = D / KF, DT = D / 32;
+  constexpr int NST = D / 16;  // MFMA K steps over the head's D columns
+  __shared__ __attribute__((aligned(16))) T cs[kWave * 16 * DT];  // C_h, lane by lane
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int lr = lane % 32, g = lane / 32;
+  const int H = nh * D, ntiles = H / 32, parts = (ntiles + 7) / 8;
+  const int bh = blockIdx.x / parts, part = blockIdx.x % parts, b = bh / nh, h = bh % nh;
+  const int j = 8 * part + wave;  // this wave's output column tile
+
+  // step st of an MFMA over the head's columns takes register pairs 2 st and 2 st + 1 of a
+  // lane (pair i: dt = i / 4, q = i % 4, i.e. d = 32 dt + 8 q + 4 g + 0..3)
+  frag wf[NST];
+  auto load_wo = [&]() {
+    if (j < ntiles) {
+      const T* wr = wo_t + (size_t)(32 * j + lr) * H + h * D + 4 * g;
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const int i0 = 2 * st, i1 = 2 * st + 1;
+        const v4 lo = *(const v4*)(wr + 32 * (i0 / 4) + 8 * (i0 % 4));
+        const v4 hi = *(const v4*)(wr + 32 * (i1 / 4) + 8 * (i1 % 4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wf[st][e] = lo[e];
+          wf[st][e + 4] = hi[e];
+        }
+      }
+    }
+  };
+  if (wave != 0) load_wo();
+
+  if (wave == 0) {
+    int len = lens ? lens[b] : s_valid;
+    len = min(max(len, 1), s_valid);
+    frag qf[NQF], kf[NQF];
+    const T* qp = q + ((size_t)bh * S + lr) * D + g * VEC;
+    const T* kp = k + ((size_t)bh * S + lr) * D + g * VEC;
+#pragma unroll
+    for (int f = 0; f < NQF; ++f) {
+      qf[f] = *(const frag*)(qp + f * KF);
+      kf[f] = *(const frag*)(kp + f * KF);
+    }
+    frag vf[DT][2];
+    const T* vp = vt + ((size_t)bh * D + lr) * S + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const v4 lo = *(const v4*)(vp + (size_t)dt * 32 * S + 16 * u);
+        const v4 hi = *(const v4*)(vp + (size_t)dt * 32 * S + 16 * u + 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vf[dt][u][e] = lo[e];
+          vf[dt][u][e + 4] = hi[e];
+        }
+      }
+    load_wo();
+    f32x16 sc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+    for (int f = 0; f < NQF; ++f) MF::mma(kf[f], qf[f], sc);
+    float mx = -INFINITY;
+    if (len < 32) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r / 4) + 4 * g + (r % 4);
+        if (key >= len) sc[r] = -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));  // finite: key 0 is always valid
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sc[r] = exp2_flush((sc[r] - mx) * scale_log2e);
+      sum += sc[r];
+    }
+    sum += __shfl_xor(sum, 32);
+    f32x16 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      frag pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = from_f32<T>(sc[8 * u + e]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) MF::mma(vf[dt][u], pf, o[dt]);
+    }
+    // register r of o[dt]: d = 32 dt + 8 (r / 4) + 4 g + r % 4 of query lr; pair i = 4 dt + r / 4
+    const float inv = 1.0f / sum;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cs[(16 * dt + r) * kWave + lane] = from_f32<T>(o[dt][r] * inv);
+  }
+  __syncthreads();
+  // C_h fragment of step st for lane (query lr, g): pairs 2 st, 2 st + 1 of that lane
+  frag cf[NST];
+#pragma unroll
+  for (int st = 0; st < NST; ++st)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cf[st][e] = cs[(8 * st + e) * kWave + lane];
+  // partial tile j: register r of a lane is column 32 j + 8 (r / 4) + 4 g + r % 4 of query lr
+  if (j >= ntiles) return;
+  float* pr = p + ((size_t)h * B * S + (size_t)b * S + lr) * H;
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int st = 0; st < NST; ++st) MF::mma(wf[st], cf[st], acc);
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq)
+    *(f32x4*)(pr + 32 * j + 8 * qq + 4 * g) =
+        f32x4{acc[4 * qq], acc[4 * qq + 1], acc[4 * qq + 2], acc[4 * qq + 3]};
+}
+
+bool attention_out_partials_fit(ftx_dtype dt, int S, int nh, int d) {
+  return dt != FTX_FP32 && S == 32 && (d == 32 || d == 64) && nh * d % 32 == 0 &&
+         nh * d <= kAttnOutMaxHidden;
+}
+
+hipError_t launch_attention_out_partials(ftx_dtype dt, int B, int nh, int d, const void* q,
+                                         const void* k, const void* vt, const int32_t* lens,
+                                         int s_valid, const void* wo_t, float* p, hipStream_t s) {
+  if (!attention_out_partials_fit(dt, 32, nh, d) || B < 1) return hipErrorInvalidValue;
+  if (s_valid <= 0 || s_valid > 32) s_valid = 32;
+  const float scale_log2e = (float)(1.4426950408889634 / sqrt((double)d));
+  const unsigned grid = (unsigned)(B * nh * ((nh * d / 32 + 7) / 8));
+#define FTX_AOP(T, D)                                                                            \
+  attention_oproj_s32_kernel<T, D><<<grid, 512, 0, s>>>((const T*)q, (const T*)k, (const T*)vt,  \
+                                                        lens, (const T*)wo_t, p, B, nh,         \
+                                                        scale_log2e, s_valid)
+  if (dt == FTX_FP16) {
+    if (d == 64) FTX_AOP(f16, 64); else FTX_AOP(f16, 32);
+  } else {
+    if (d == 64) FTX_AOP(bf16, 64); else FTX_AOP(bf16, 32);
+  }
+#undef FTX_AOP
+  return hipGetLastError();
+}
+
 constexpr size_t kMaxLdsBytes = 160 * 1024;  // per workgroup on gfx950
 
 template <typename T, int D, int SMAX>

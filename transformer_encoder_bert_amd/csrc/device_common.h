@@ -77,6 +77,21 @@ __device__ __forceinline__ f32x4 sum_partials4(const float* p, size_t stride, in
   return acc;
 }
 
+// The same sum with every load issued before the first addition (splits <= MAXS): one
+// memory round trip for the whole split, the additions still in split order.
+template <int MAXS>
+__device__ __forceinline__ f32x4 sum_partials_all(const float* p, size_t stride, int splits) {
+  f32x4 v[MAXS];
+#pragma unroll
+  for (int z = 0; z < MAXS; ++z)
+    if (z < splits) v[z] = *(const f32x4*)(p + z * stride);
+  f32x4 acc = v[0];
+#pragma unroll
+  for (int z = 1; z < MAXS; ++z)
+    if (z < splits) acc += v[z];
+  return acc;
+}
+
 // Sum / max over groups of `width` consecutive lanes (width a power of two <= 64).
 template <int width> __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll

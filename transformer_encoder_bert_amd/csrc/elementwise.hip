@@ -16,6 +16,10 @@
 
 namespace ftx {
 
+// the most split partials the split-K LayerNorm loads all at once (the planner splits K at
+// most 16 ways; the attention-output partials split by head, up to 16 heads here)
+constexpr int kMaxSplitsAll = 16;
+
 // ------------------------------------------------------------------------------------
 // bias + residual + LayerNorm: y = gamma * (z - mean) * rsqrt(var + eps) + beta,
 // z = x + a + bias.  LPR lanes own one row; each lane holds MAXV vectors of EV elements,
@@ -189,8 +193,11 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 // sum -- rounded to TA as the projection would have stored it, so one launch replaces the
 // reduction and the LayerNorm.  One workgroup of 256 threads per row, 4 columns per thread
 // and group (cols <= 4096, a multiple of 4): the partial reads of a row spread over a
-// whole CU.  Statistics as in layernorm_kernel (fp32, mean, then centred sum of squares).
-template <typename T, typename TX, typename TA>
+// whole CU.  ALL (5 to kMaxSplitsAll splits): a thread issues the loads of all the splits of
+// its columns before adding them (one memory round trip; at batch 1 the FFN-out projection
+// is cut in 16), a variant of its own so that fewer splits keep the smaller kernel.  Statistics
+// as in layernorm_kernel (fp32, mean, then centred sum of squares).
+template <typename T, typename TX, typename TA, bool ALL>
 __global__ __launch_bounds__(256) void splitk_layernorm_kernel(const TX* __restrict__ x,
                                                                const float* __restrict__ p,
                                                                int splits,
@@ -211,7 +218,8 @@ __global__ __launch_bounds__(256) void splitk_layernorm_kernel(const TX* __restr
   for (int gi = 0; gi < G; ++gi) {
     const int c = 4 * (threadIdx.x + 256 * gi);
     if (c < cols) {
-      const f32x4 acc = sum_partials4(p + base + c, mn, splits);
+      const f32x4 acc = ALL ? sum_partials_all<kMaxSplitsAll>(p + base + c, mn, splits)
+                            : sum_partials4(p + base + c, mn, splits);
       const x4 xv = *(const x4*)(x + base + c);
       const t4 bv = *(const t4*)(bias + c);
 #pragma unroll
@@ -257,9 +265,14 @@ template <typename T, typename TX, typename TA>
 static hipError_t splitk_ln_launch(int rows, int cols, const void* x, const float* p, int splits,
                                    const void* bias, const void* gamma, const void* beta,
                                    void* y, float* yf, hipStream_t s) {
-  splitk_layernorm_kernel<T, TX, TA><<<rows, 256, 0, s>>>(
-      (const TX*)x, p, splits, (const T*)bias, (const T*)gamma, (const T*)beta, (T*)y, yf, rows,
-      cols);
+  if (splits > 4 && splits <= kMaxSplitsAll)
+    splitk_layernorm_kernel<T, TX, TA, true><<<rows, 256, 0, s>>>(
+        (const TX*)x, p, splits, (const T*)bias, (const T*)gamma, (const T*)beta, (T*)y, yf, rows,
+        cols);
+  else
+    splitk_layernorm_kernel<T, TX, TA, false><<<rows, 256, 0, s>>>(
+        (const TX*)x, p, splits, (const T*)bias, (const T*)gamma, (const T*)beta, (T*)y, yf, rows,
+        cols);
   return hipGetLastError();
 }
 

@@ -95,6 +95,8 @@ struct ftx_encoder {
   int fused = 1;
   int fused_attention = 1;  // 0 off, 1 from 256 rows and 64 tiles, 2 whenever the shape fits
   bool attn_fits = false;   // the per-head weight copy exists (16-bit, S = 32, d = 64)
+  bool attn_out = false;    // small batch at S = 32: the attention also yields the
+                            // attention-output projection's partials, split by head
   int timing = 0;
   int graph_mode = 0;
   // graph of one whole forward, captured for the (input, seq_lens, output) it was made with
@@ -283,47 +285,64 @@ ftx_status enqueue_forward(ftx_encoder* e, const Workspace& ws, const void* inpu
       });
     }
     if (st != FTX_OK) return st;
-    if (!use_fused_attention(e)) {
-      st = run_step(e, FTX_STEP_ATTENTION, s, [&] {
-        return launch_attention(dt, B, S, S, nh, d, ws.q, ws.k, ws.vt, seq_lens, ws.ctx, s, e->Sv);
-      });
-      if (st != FTX_OK) return st;
-    }
     // Hidden size 128 with at least 128 row tiles: one 64 x 128 projection tile holds whole
     // rows, and the projection runs the bias + residual + LayerNorm in its epilogue (the
     // 4 x 32 model at batch 512: 0.445 -> 0.418 ms; with fewer tiles the unsplit K chain on
     // few CUs loses -- batch 64 0.302 -> 0.338 ms).  Otherwise a projection that splits K
     // (small batches) leaves its fp32 partials to the LayerNorm that follows it, which sums
-    // them itself: one launch instead of reduction + LayerNorm.
+    // them itself: one launch instead of reduction + LayerNorm.  At S = 32 such a split runs
+    // by head inside the attention kernel instead (its K range is the merged-heads dimension):
+    // one launch for the attention and the projection.
     const bool row_ln = H == 128 && (T + 63) / 64 >= 128;
     const int o_splits = linear_splits(dt, T, H, H, ws.splitk_elems, true);
-    if (row_ln) {
-      st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
-        return launch_linear_layernorm(dt, T, H, H, ws.ctx, w.w_o_t, x, false, ws.y1f != nullptr,
-                                       w.b_o, w.ln1_g, w.ln1_b, ws.y1, ws.y1f, s);
-      });
-    } else if (o_splits > 1) {
-      st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
-        return launch_linear_partials(dt, T, H, H, ws.ctx, w.w_o_t, ws.splitk, ws.splitk_elems, s);
+    const bool attn_out = e->attn_out && !use_fused_attention(e) && e->fused && !row_ln &&
+                          o_splits > 1 && (size_t)nh * T * H <= ws.splitk_elems;
+    if (attn_out) {
+      st = run_step(e, FTX_STEP_ATTENTION, s, [&] {
+        return launch_attention_out_partials(dt, B, nh, d, ws.q, ws.k, ws.vt, seq_lens, e->Sv,
+                                             w.w_o_t, ws.splitk, s);
       });
       if (st != FTX_OK) return st;
       st = run_step(e, FTX_STEP_LN1, s, [&] {
-        return launch_splitk_bias_residual_layernorm(dt, T, H, x, false, ws.splitk, o_splits,
+        return launch_splitk_bias_residual_layernorm(dt, T, H, x, false, ws.splitk, nh,
                                                      ws.y1f != nullptr, w.b_o, w.ln1_g, w.ln1_b,
                                                      ws.y1, ws.y1f, s);
       });
     } else {
-      st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
-        return launch_linear(dt, T, H, H, ws.ctx, w.w_o_t, nullptr, false, ws.abuf, s,
-                             ws.y1f != nullptr, ws.splitk, ws.splitk_elems);
-      });
-      if (st != FTX_OK) return st;
-      st = run_step(e, FTX_STEP_LN1, s, [&] {
-        if (ws.y1f)
-          return launch_bias_residual_layernorm_f32res(dt, T, H, x, false, (const float*)ws.abuf, w.b_o,
-                                                       w.ln1_g, w.ln1_b, ws.y1, ws.y1f, s);
-        return launch_bias_residual_layernorm(dt, T, H, x, ws.abuf, w.b_o, w.ln1_g, w.ln1_b, ws.y1, s);
-      });
+      if (!use_fused_attention(e)) {
+        st = run_step(e, FTX_STEP_ATTENTION, s, [&] {
+          return launch_attention(dt, B, S, S, nh, d, ws.q, ws.k, ws.vt, seq_lens, ws.ctx, s, e->Sv);
+        });
+        if (st != FTX_OK) return st;
+      }
+      if (row_ln) {
+        st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
+          return launch_linear_layernorm(dt, T, H, H, ws.ctx, w.w_o_t, x, false, ws.y1f != nullptr,
+                                         w.b_o, w.ln1_g, w.ln1_b, ws.y1, ws.y1f, s);
+        });
+      } else if (o_splits > 1) {
+        st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
+          return launch_linear_partials(dt, T, H, H, ws.ctx, w.w_o_t, ws.splitk, ws.splitk_elems, s);
+        });
+        if (st != FTX_OK) return st;
+        st = run_step(e, FTX_STEP_LN1, s, [&] {
+          return launch_splitk_bias_residual_layernorm(dt, T, H, x, false, ws.splitk, o_splits,
+                                                       ws.y1f != nullptr, w.b_o, w.ln1_g, w.ln1_b,
+                                                       ws.y1, ws.y1f, s);
+        });
+      } else {
+        st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
+          return launch_linear(dt, T, H, H, ws.ctx, w.w_o_t, nullptr, false, ws.abuf, s,
+                               ws.y1f != nullptr, ws.splitk, ws.splitk_elems);
+        });
+        if (st != FTX_OK) return st;
+        st = run_step(e, FTX_STEP_LN1, s, [&] {
+          if (ws.y1f)
+            return launch_bias_residual_layernorm_f32res(dt, T, H, x, false, (const float*)ws.abuf,
+                                                         w.b_o, w.ln1_g, w.ln1_b, ws.y1, ws.y1f, s);
+          return launch_bias_residual_layernorm(dt, T, H, x, ws.abuf, w.b_o, w.ln1_g, w.ln1_b, ws.y1, s);
+        });
+      }
     }
     if (st != FTX_OK) return st;
     if (e->fused) {
@@ -450,11 +469,22 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
     delete e;
     return hip_fail(err, "hipMalloc(weights)");
   }
-  // split-K workspace: the largest any of the four projections plans for
+  // split-K workspace: the largest any of the four projections plans for, and the per-head
+  // partials of the attention-output projection where the attention produces them (S = 32,
+  // the projection splits, and the partials stay within 4 MiB: BERT-base up to 3 sequences;
+  // at batch 8, 9 MiB of partials made the forward slower than the separate projection,
+  // 0.474 against 0.467 ms)
   e->splitk_need = std::max(std::max(gemm_splitk_workspace(dtype, e->T, 3 * e->H, e->H),
                                      gemm_splitk_workspace(dtype, e->T, e->H, e->H)),
                             std::max(gemm_splitk_workspace(dtype, e->T, e->F, e->H),
                                      gemm_splitk_workspace(dtype, e->T, e->H, e->F)));
+  {
+    const size_t per_head = (size_t)head_num * e->T * e->H;
+    e->attn_out = attention_out_partials_fit(dtype, e->S, head_num, size_per_head) &&
+                  linear_splits(dtype, e->T, e->H, e->H, (size_t)1 << 40, true) > 1 &&
+                  per_head * sizeof(float) <= (4u << 20);
+    if (e->attn_out) e->splitk_need = std::max(e->splitk_need, per_head);
+  }
   e->ws_bytes = layout_workspace(e, nullptr, nullptr);
   err = hipMalloc(&e->ws_mem, e->ws_bytes);
   if (err != hipSuccess) {

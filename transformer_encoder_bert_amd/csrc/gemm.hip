@@ -1184,6 +1184,15 @@ static void gemm_kernel_launch(dim3 grid, int kchunk, int M, int N, int K, const
       return;
     }
   }
+  if constexpr (BM == 32 && BN == 32) {
+    // a split-K block of at most three slabs loads them all before its first multiply (four
+    // 8 KB stages): one memory round trip instead of one per slab
+    if (grid.y > 1 && (kchunk + BK - 1) / BK <= 3) {
+      gemm_kernel<T, BM, BN, WM, WN, Epi, 4><<<grid, WM * WN * kWave, 0, s>>>(
+          (const T*)a, (const T*)w_t, M, N, K, kchunk, xcds, epi);
+      return;
+    }
+  }
   gemm_kernel<T, BM, BN, WM, WN, Epi><<<grid, WM * WN * kWave, 0, s>>>(
       (const T*)a, (const T*)w_t, M, N, K, kchunk, xcds, epi);
 }

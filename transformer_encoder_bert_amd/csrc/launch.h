@@ -97,6 +97,17 @@ hipError_t launch_attention(ftx_dtype dt, int B, int Sq, int Sk, int nh, int d, 
                             const void* k, const void* vt, const int32_t* lens, void* ctx,
                             hipStream_t s, int s_valid = 0, bool causal = false);
 
+// The S = 32 attention of every (sequence, head) with that head's share of the
+// attention-output projection: p[h][b*32 + i][n] = sum over d < D of C_h[b*32 + i][d] *
+// wo_t[n][h*D + d] (fp32; C_h rounded to the storage type first), the split-K partials of the
+// projection split by head, for the split-K LayerNorm (nh splits).  16-bit data, S = 32,
+// hidden size a multiple of 32 and at most 1024 (attention_out_partials_fit); q, k, vt as for
+// launch_attention; keys at or past min(lens[b], s_valid) masked.
+bool attention_out_partials_fit(ftx_dtype dt, int S, int nh, int d);
+hipError_t launch_attention_out_partials(ftx_dtype dt, int B, int nh, int d, const void* q,
+                                         const void* k, const void* vt, const int32_t* lens,
+                                         int s_valid, const void* wo_t, float* p, hipStream_t s);
+
 hipError_t launch_bias_residual_layernorm(ftx_dtype dt, int rows, int cols, const void* x,
                                           const void* a, const void* bias, const void* gamma,
                                           const void* beta, void* y, hipStream_t s);
