@@ -72,6 +72,15 @@ LINEAR_SHAPES = [
     (2048, 768, 768),    # BERT-base attention output at batch 64 (12 slabs)
     (2048, 768, 3072),   # BERT-base FFN-out at batch 64
     (2000, 776, 1576),   # ragged M, N and K tails (the last slab is partly zeroed)
+    # the small-M kernel (K split over the 4 waves of one workgroup per tile, whole slabs):
+    # 32-row tiles ...
+    (32, 2304, 768),     # BERT-base Q/K/V at batch 1
+    (31, 3072, 768),     # FFN-in with a ragged last row tile
+    (64, 768, 1024),     # 16 slabs: four per wave
+    # ... and 64-row tiles where 32-row tiles would outnumber the CUs
+    (128, 2304, 768),    # Q/K/V at 128 rows (BERT-base S128 batch 1)
+    (96, 3072, 768),     # 64-row tiles with an empty second row tile in the last one
+    (160, 2304, 512),    # three row tiles of 64, the last one half empty
 ]
 
 

@@ -783,9 +783,13 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
 // reads it in phase 2k and computes it in phase 2k + 1, group 1 one phase later.  Group 0
 // loads its share of slab k + 1 at the start of phase 2k (the buffer's previous slab was
 // read by both groups by then) and waits for it at the end of phase 2k + 1; group 1 loads
-// its share of slab k + 2 in phase 2k + 1 once its own reads of slab k are done, and waits
-// for it one slab later.  Every wave passes 2 nk + 2 barriers.  The sums are those of
-// gemm_kernel, in the same order.  Needs the block's K range to be whole slabs.
+// its share of slab k + 2 in phase 2k + 1, into the buffer of slab k, and waits for it one
+// slab later.  Group 0 read slab k before the barrier that opens phase 2k + 1, but the
+// other waves of group 1 read it during that phase (a wave's fragment reads span rows that
+// the other waves of its group load), so each group-1 wave, its reads done, adds one to an
+// LDS counter and issues its loads only once all four have (a wait inside group 1 alone;
+// bounded, so that it cannot hang).  Every wave passes 2 nk + 3 barriers.  The sums are those
+// of gemm_kernel, in the same order.  Needs the block's K range to be whole slabs.
 template <typename T, int BM, int BN, typename Epi>
 __global__ __launch_bounds__(8 * kWave) void gemm_pp_kernel(const T* __restrict__ A,
                                                             const T* __restrict__ Bt, int M,
@@ -798,7 +802,13 @@ __global__ __launch_bounds__(8 * kWave) void gemm_pp_kernel(const T* __restrict_
   constexpr int TM = C::TM, TN = C::TN, AQ = C::AQ, BQ = C::BQ, ROWB = C::ROWB, NS = C::NS;
   constexpr int LQ = AQ + BQ;  // loads per wave and slab
   static_assert(sizeof(T) == 2 && BM == 256, "16-bit, 8-wave tiles");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
+  // the two slab buffers, then a counter of the group-1 waves done reading their current slab
+  // (one LDS object: a second one gives the compiler alias scopes under which it waits for
+  // every slab load in flight before any LDS read)
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE + 16];
+  unsigned* const g1_reads_done = (unsigned*)(smem + 2 * C::STAGE);
+  if (threadIdx.x == 0) *g1_reads_done = 0;
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the store lands before the prologue's barrier
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
@@ -888,6 +898,23 @@ __global__ __launch_bounds__(8 * kWave) void gemm_pp_kernel(const T* __restrict_
       read_slab(buf);
       __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's reads of the buffer are done
       if (kt + 2 < nk) {
+        // every group-1 wave's reads of slab kt are done before any of them loads into its
+        // buffer (the counter only grows: 4 (kt + 1) arrivals by now).  Relaxed LDS atomics:
+        // this wave's reads completed (lgkmcnt(0) above) before its add, and its loads issue
+        // only after the count it waits for has been read; release/acquire would also wait
+        // for its loads in flight (vmcnt(0)), the very loads the early issue is for.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        if (lane == 0)
+          __hip_atomic_fetch_add(g1_reads_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const unsigned target = 4u * (unsigned)(kt + 1);
+        for (int spin = 0; spin < (1 << 16); ++spin) {
+          if (__hip_atomic_load(g1_reads_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target)
+            break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
         load_slab(kt + 2, buf);
         wait_vmcnt<LQ>();  // its share of slab kt + 1 has landed
       } else {
@@ -920,31 +947,36 @@ __global__ __launch_bounds__(8 * kWave) void gemm_pp_kernel(const T* __restrict_
   gemm_epilogue<C, Epi>(epi, smem, m0, n0, wave, lane, acc, bq);
 }
 
-// Small-M projection (the rows of one or two short sequences): one workgroup of
-// kSmallWaves waves per 32 x 32 output tile, the waves splitting K.  Each wave issues the
-// global-to-LDS loads of its whole K range at once (at most kSmallMaxSlabs slabs, so one
-// round trip of memory latency instead of a chain of slab steps), multiplies its slabs, and
-// the waves' fp32 partial tiles are summed in wave order through LDS (deterministic) and
-// finished by the projection's own epilogue.  One launch where the split-K path takes a
-// partial-product launch and a reduction launch.  K is a whole number of slabs.
-constexpr int kSmallWaves = 4, kSmallMaxSlabs = 4;
+// Small-M projection (the rows of a few short sequences): one workgroup of kSmallWaves
+// waves per (32 TM) x 32 output tile, the waves splitting K.  Each wave issues the
+// global-to-LDS loads of its whole K range at once (at most small_max_slabs(TM) slabs, so one
+// round trip of memory latency instead of a chain of slab steps), multiplies its slabs (TM
+// row tiles against one weight fragment), and the waves' fp32 partial tiles are summed in
+// wave order through LDS (deterministic) and finished by the projection's own epilogue.  One
+// launch where the split-K path takes a partial-product launch and a reduction launch.  K is
+// a whole number of slabs.  TM = 2 (64-row tiles) where 32-row tiles would outnumber the CUs.
+constexpr int kSmallWaves = 4;
+// slabs a wave holds: four of 8 KB for 32-row tiles, three of 12 KB for 64-row tiles
+constexpr int small_max_slabs(int tm) { return tm == 1 ? 4 : 3; }
 
-template <typename T, typename Epi>
+template <typename T, typename Epi, int TM>
 __global__ __launch_bounds__(kSmallWaves * kWave) void gemm_small_kernel(const T* __restrict__ A,
                                                                          const T* __restrict__ Bt,
                                                                          int M, int N, int K,
                                                                          Epi epi) {
-  typedef GemmCfg<T, 32, 32, 1, 1> Cg;  // one slab: 32 rows of A and 32 rows of W^T
+  typedef GemmCfg<T, 32 * TM, 32, 1, 1> Cg;  // one slab: 32 TM rows of A and 32 rows of W^T
   typedef typename Cg::MF MF;
   typedef typename MF::frag frag;
-  constexpr int ROWB = Cg::ROWB, SLAB = Cg::STAGE, REGION = kSmallMaxSlabs * SLAB;
+  constexpr int BM = 32 * TM, ROWB = Cg::ROWB, SLAB = Cg::STAGE;
+  constexpr int REGION = small_max_slabs(TM) * SLAB;
+  static_assert(16 * kWave * sizeof(float) * TM + 32 * 40 * 4 <= REGION, "reduction and epilogue scratch");
   __shared__ __attribute__((aligned(1024))) char smem[kSmallWaves * REGION];
   const int tiles_n = (N + 31) / 32;
-  const int m0 = (blockIdx.x / tiles_n) * 32, n0 = (blockIdx.x % tiles_n) * 32;
+  const int m0 = (blockIdx.x / tiles_n) * BM, n0 = (blockIdx.x % tiles_n) * 32;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave, lr = lane % 32, g = lane / 32;
   const int nk = K / Cg::BK;
-  const int spw = (nk + kSmallWaves - 1) / kSmallWaves;  // slabs per wave (<= kSmallMaxSlabs)
+  const int spw = (nk + kSmallWaves - 1) / kSmallWaves;  // slabs per wave (<= small_max_slabs)
   const int k0 = wave * spw, k1 = min(nk, k0 + spw);
   char* const mine = smem + wave * REGION;
 
@@ -952,62 +984,84 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void gemm_small_kernel(const T
 #pragma unroll
   for (int q = 0; q < 4; ++q) bq[q] = epi.bias4(n0 + 8 * q + 4 * g);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(A + (size_t)m0 * K), (short)0, min(32, M - m0) * K * (int)sizeof(T), 0x00020000);
+      (void*)(A + (size_t)m0 * K), (short)0, min(BM, M - m0) * K * (int)sizeof(T), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(Bt + (size_t)n0 * K), (short)0, min(32, N - n0) * K * (int)sizeof(T), 0x00020000);
-  // load q (of 4) of a slab fills rows 8 q .. 8 q + 7: lane l lands at position l % 8 of row
-  // 8 q + l / 8 and so fetches chunk (l % 8) ^ swz(row)
+  // load q of a slab fills rows 8 q .. 8 q + 7 (of A, then of W^T): lane l lands at position
+  // l % 8 of row 8 q + l / 8 and so fetches chunk (l % 8) ^ swz(row)
   for (int kt = k0; kt < k1; ++kt) {
     char* base = mine + (kt - k0) * SLAB;
 #pragma unroll
+    for (int q = 0; q < 4 * TM; ++q) {
+      const int R = q * 8 + lane / 8;
+      lds_dma16(ra, (R * K + kt * Cg::BK + ((lane & 7) ^ swz(R)) * Cg::VEC) * (int)sizeof(T),
+                base + q * 1024);
+    }
+#pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int R = q * 8 + lane / 8;
-      const int off = (R * K + kt * Cg::BK + ((lane & 7) ^ swz(R)) * Cg::VEC) * (int)sizeof(T);
-      lds_dma16(ra, off, base + q * 1024);
-      lds_dma16(rb, off, base + 32 * ROWB + q * 1024);
+      lds_dma16(rb, (R * K + kt * Cg::BK + ((lane & 7) ^ swz(R)) * Cg::VEC) * (int)sizeof(T),
+                base + BM * ROWB + q * 1024);
     }
   }
   wait_vmcnt<0>();  // this wave's slabs are in LDS (no other wave reads them)
 
-  f32x16 acc;
+  f32x16 acc[TM];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
   const int hl = swz(lr);
   for (int kt = k0; kt < k1; ++kt) {
     const char* base = mine + (kt - k0) * SLAB;
 #pragma unroll
     for (int st = 0; st < Cg::NS; ++st) {
       const int pos = ((2 * st + g) ^ hl) * 16;
-      const frag fa = *(const frag*)(base + lr * ROWB + pos);
-      const frag fb = *(const frag*)(base + 32 * ROWB + lr * ROWB + pos);
-      MF::mma(fb, fa, acc);
+      const frag fb = *(const frag*)(base + BM * ROWB + lr * ROWB + pos);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const frag fa = *(const frag*)(base + (32 * i + lr) * ROWB + pos);
+        MF::mma(fb, fa, acc[i]);
+      }
     }
   }
-  // partial tiles through LDS: register r of lane l at float r * 64 + l of the wave's region
-  // (after its own reads, in order), summed by wave 0 in wave order
+  // partial tiles through LDS: register r of row tile i of lane l at float (16 i + r) * 64 + l
+  // of the wave's region (after its own reads, in order), summed by wave 0 in wave order
   float* red = (float*)mine;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) red[r * kWave + lane] = acc[r];
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[(16 * i + r) * kWave + lane] = acc[i][r];
   __syncthreads();
   if (wave != 0) return;
-  f32x16 sum;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) sum[r] = 0.f;
-  for (int w = 0; w < kSmallWaves; ++w) {
-    const float* pw = (const float*)(smem + w * REGION);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sum[r] += pw[r * kWave + lane];
-  }
   // epilogue scratch past wave 0's partials, inside its own region
   typedef typename Epi::out_t TO;
-  epilogue_tile(epi, (TO*)(smem + 16 * kWave * sizeof(float)), m0, n0, lane, sum, bq);
+  TO* scratch = (TO*)(smem + 16 * kWave * sizeof(float) * TM);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    f32x16 sum;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum[r] = 0.f;
+    for (int w = 0; w < kSmallWaves; ++w) {
+      const float* pw = (const float*)(smem + w * REGION);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum[r] += pw[(16 * i + r) * kWave + lane];
+    }
+    if (m0 + 32 * i < M) epilogue_tile(epi, scratch, m0 + 32 * i, n0, lane, sum, bq);
+  }
 }
 
+// Row tiles of 32 (TM) rows per small-M workgroup for this shape, 0 where the small kernel
+// does not take it: K a whole number of slabs within the waves' reach, and the workgroups no
+// more than the CUs (32-row tiles first, then 64-row tiles).
 template <typename T>
-static bool small_gemm_fits(int M, int N, int K, int cus) {
+static int small_gemm_tm(int M, int N, int K, int cus) {
   constexpr int BK = GemmCfg<T, 32, 32, 1, 1>::BK;
-  const long tiles = (long)((M + 31) / 32) * ((N + 31) / 32);
-  return K % BK == 0 && K / BK <= kSmallWaves * kSmallMaxSlabs && tiles <= cus;
+  if (K % BK != 0) return 0;
+  const long tn = (N + 31) / 32;
+  if ((long)((M + 31) / 32) * tn <= cus && K / BK <= kSmallWaves * small_max_slabs(1)) return 1;
+  if ((long)((M + 63) / 64) * tn <= cus && K / BK <= kSmallWaves * small_max_slabs(2)) return 2;
+  return 0;
 }
 
 // --------------------------------------------------------------------------- tile choice
@@ -1232,13 +1286,20 @@ static hipError_t gemm_launch(int M, int N, int K, const void* a, const void* w_
   constexpr bool wide = sizeof(T) == 2;
   const DeviceInfo di = device_info();
   GemmPlan plan = plan_gemm(M, N, K, (int)sizeof(T), !reduce, di.cus);
-  // where the plan splits K and finishes with a reduction launch, few rows take the
-  // small-M kernel instead (one launch, no workspace)
+  // where the plan splits K and finishes with a reduction launch, or runs one-wave 32x32
+  // blocks each through its whole K chain, few rows take the small-M kernel instead (one
+  // launch, one round trip of loads, no workspace)
   if constexpr (!Epi::kBlock) {
-    if (reduce && plan.splits > 1 && small_gemm_fits<T>(M, N, K, di.cus)) {
-      const int tiles = ((M + 31) / 32) * ((N + 31) / 32);
-      gemm_small_kernel<T, Epi><<<tiles, kSmallWaves * kWave, 0, s>>>((const T*)a, (const T*)w_t, M, N,
-                                                                      K, epi);
+    const bool small = reduce && (plan.splits > 1 || plan.cfg == TILE_32x32);
+    const int tm = small ? small_gemm_tm<T>(M, N, K, di.cus) : 0;
+    if (tm) {
+      const int tiles = ((M + 32 * tm - 1) / (32 * tm)) * ((N + 31) / 32);
+      if (tm == 1)
+        gemm_small_kernel<T, Epi, 1><<<tiles, kSmallWaves * kWave, 0, s>>>((const T*)a, (const T*)w_t,
+                                                                           M, N, K, epi);
+      else
+        gemm_small_kernel<T, Epi, 2><<<tiles, kSmallWaves * kWave, 0, s>>>((const T*)a, (const T*)w_t,
+                                                                           M, N, K, epi);
       return hipGetLastError();
     }
   }
