@@ -57,6 +57,8 @@ ATTN = [
     (2, 128, 32, 2, 64, False, [32, 7]),     # cross: more queries than keys
     (1, 64, 512, 2, 64, False, [300]),       # cross, long memory
     (70, 32, 32, 32, 64, True, None),        # causal, over 2048 heads: the LDS kernel at S = 32
+    (8, 512, 512, 2, 64, True, None),        # causal, 16 heads: query groups renumbered by XCD
+    (4, 512, 256, 2, 32, False, [256, 1, 129, 200]),  # cross: four query groups over two key chunks
 ]
 
 

@@ -161,6 +161,8 @@ ATTN_CASES = [
     (2, 96, 2, 64, [96, 40]),        # S not a power of two
     (2, 32, 3, 64, [32, 9]),         # S = 32, few heads: the kernel without LDS
     (172, 32, 12, 64, None),         # S = 32, over 2048 heads: the LDS kernel
+    (9, 512, 1, 32, [1, 127, 128, 129, 256, 257, 384, 385, 512]),  # every count of 128-key chunks
+    (8, 256, 2, 64, [256, 1, 100, 129, 200, 33, 255, 64]),          # 16 heads: query groups renumbered by XCD
 ]
 
 

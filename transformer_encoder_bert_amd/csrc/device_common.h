@@ -92,6 +92,43 @@ __device__ __forceinline__ f32x4 sum_partials_all(const float* p, size_t stride,
   return acc;
 }
 
+// The value of the lane 32 away (lane ^ 32), by one v_permlane32_swap in registers instead
+// of an LDS round trip.  With both operands x, the swap's first result holds x of lane
+// l % 32 and its second x of lane l % 32 + 32, in every lane l.  Only the selected integer
+// is cast back to float: casting both results to float and combining them compiled, with
+// this toolchain, into code that read the first result twice.
+__device__ __forceinline__ float half_swap(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// 16 bytes per lane from byte offset voff + soff of buffer resource r into LDS at
+// lds + 16 * lane (buffer_load_dwordx4 ... lds: the LDS address is wave-uniform, the lane
+// offset implicit; soff is a wave-uniform byte offset).  An offset at or past the resource's
+// byte count reads as zero and touches no memory.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, int voff, void* lds,
+                                          int soff = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, soff, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding; LDS and
+// scalar counters unconstrained.  The loads into LDS are only tracked by this counter.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads() (which would also wait for
+// every outstanding load); the empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void workgroup_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Sum / max over groups of `width` consecutive lanes (width a power of two <= 64).
 template <int width> __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll

@@ -338,30 +338,6 @@ __device__ __forceinline__ void epilogue_tile(const Epi& epi, typename Epi::out_
 
 // ---------------------------------------------------------------------------------- kernel
 
-// 16 bytes per lane from byte offset voff of buffer resource r into LDS at lds + 16 * lane
-// (buffer_load_dwordx4 ... lds: the LDS address is wave-uniform, the lane offset implicit).
-// An offset at or past the resource's byte count reads as zero and touches no memory.
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, int voff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voff, 0, 0, 0);
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding; LDS and
-// scalar counters unconstrained.  The loads into LDS are only tracked by this counter.
-template <int N> __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier without the memory fence of __syncthreads() (which would also wait for
-// every outstanding load); the empty asm statements keep the compiler from moving memory
-// accesses across it.
-__device__ __forceinline__ void workgroup_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // LDS row of a slab: 128 bytes of K (8 chunks of 16 bytes).  Chunk c of tile row R sits at
 // position c ^ swz(R).  A wave's fragment read takes one 16-byte chunk from each of 32
 // consecutive rows; with this swizzle any 8 consecutive rows hit 8 different positions and
