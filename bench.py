@@ -73,6 +73,13 @@ def parse():
     p.add_argument("--summarize-trace", metavar="TRACE_DIR", default=None,
                    help="write profiles/<--summary-name>.md from a rocprofv3 kernel-trace run of "
                         "this benchmark (kernel stats only), then exit (no GPU needed)")
+    p.add_argument("--calibrate-gemm", action="store_true",
+                   help="time the workload's four projection shapes with the ftx GEMM (plain, and "
+                        "FFN-in with its bias + GELU epilogue) and with the vendor library GEMM "
+                        "(torch.matmul, same weight layout) for comparison; one JSON line")
+    p.add_argument("--summarize-calibration", metavar="JSON_FILE", default=None,
+                   help="write profiles/<--summary-name>.md from the saved output of --calibrate-gemm, "
+                        "then exit (no GPU needed)")
     p.add_argument("--summary-name", default=None)
     p.add_argument("--summary-commands", nargs="*", default=[])
     return p.parse_args()
@@ -588,10 +595,12 @@ def bench_decoder(args):
 
 def main():
     args = parse()
-    if args.summarize_rocprof or args.summarize_trace or args.summarize_hbm:
+    if args.summarize_rocprof or args.summarize_trace or args.summarize_hbm or args.summarize_calibration:
         if not args.summary_name:
             raise SystemExit("--summary-name is required")
-        if args.summarize_rocprof:
+        if args.summarize_calibration:
+            summarize_calibration(args)
+        elif args.summarize_rocprof:
             summarize_rocprof(args)
         elif args.summarize_hbm:
             summarize_hbm(args)
@@ -617,6 +626,8 @@ def main():
         sys.exit(1)
     wl = si.WORKLOADS[args.workload]
     batch = args.batch or max(wl.batches)
+    if args.calibrate_gemm:
+        return calibrate_gemm(args, wl, batch)
     if args.hbm_only:
         shape = wl.shape(batch)
         res = {"workload": wl.name, "batch": batch, "elementwise_hbm": elementwise_hbm(shape, args.hbm_reps)}
@@ -777,6 +788,83 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def calibrate_gemm(args, wl, batch):
+    """The projection GEMMs of one layer, alone: the ftx kernel against the vendor library
+    (torch.matmul, which calls hipBLASLt) on the same operands in the same layout (W^T, N x K),
+    as a practical ceiling next to the MFMA peak.  The library runs without an epilogue; ftx
+    runs plain and, for FFN-in, with its fused bias + GELU.  Each time is the mean of 50
+    back-to-back launches after a warm-up of at least 150 ms, from stream events."""
+    import torch
+    from transformer_encoder_bert_amd import ftx
+    shape = wl.shape(batch)
+    T, H, F = shape.tokens, shape.hidden, shape.ffn
+    tdt = {"fp16": torch.float16, "bf16": torch.bfloat16, "fp32": torch.float32}[shape.dtype]
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(7)
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.15:
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+        e0.record()
+        for _ in range(50):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / 50
+
+    rows = []
+    for name, M, N, K in (("Q/K/V projection", T, 3 * H, H), ("attention-output projection", T, H, H),
+                          ("FFN-in", T, F, H), ("FFN-out", T, H, F)):
+        a = torch.randn(M, K, device=dev, dtype=tdt, generator=g)
+        w_t = torch.randn(N, K, device=dev, dtype=tdt, generator=g) * 0.05
+        bias = torch.randn(N, device=dev, dtype=tdt, generator=g) * 0.1
+        c = torch.empty(M, N, device=dev, dtype=tdt)
+        flops = 2.0 * M * N * K
+        r = {"gemm": name, "M": M, "N": N, "K": K,
+             "ftx_plain_us": timed(lambda: ftx.ftx_step_linear(a, w_t, None, False, c)),
+             "library_plain_us": timed(lambda: torch.matmul(a, w_t.t()))}
+        if name == "FFN-in":
+            r["ftx_bias_gelu_us"] = timed(lambda: ftx.ftx_step_linear(a, w_t, bias, True, c))
+        for k in [k for k in r if k.endswith("_us")]:
+            r[k.replace("_us", "_tflops")] = flops / r[k] * 1e-6
+        rows.append(r)
+        del a, w_t, bias, c
+    res = {"workload": wl.name, "batch": batch, "dtype": shape.dtype, "library": "torch.matmul (hipBLASLt)",
+           "kernel_source_hash": kernel_source_hash(), "gemm_calibration": rows}
+    print(json.dumps(res), flush=True)
+
+
+def summarize_calibration(args):
+    """profiles/<name>.md from the JSON line of a --calibrate-gemm run."""
+    res = json.loads([l for l in open(args.summarize_calibration) if l.startswith("{")][-1])
+    wl, batch = res["workload"], res["batch"]
+    flags = (f" --workload {wl}" if wl != WORKLOAD_DEFAULT else "") + f" --batch {batch}"
+    src = os.path.relpath(os.path.abspath(args.summarize_calibration), ROOT)
+    lines = [f"# Projection GEMMs alone: ftx against the library -- {wl}, batch {batch}, {res['dtype']}", "",
+             "Commands (from the repository root, on one MI355X):", "", "```",
+             f"python3 bench.py{flags} --calibrate-gemm > {src}",
+             f"python3 bench.py --summarize-calibration {src} --summary-name {args.summary_name}", "```", "",
+             "Mean of 50 back-to-back launches after a 150 ms warm-up, stream events.  The library",
+             "(torch.matmul, which calls hipBLASLt) multiplies the same operands in the same layout",
+             "(A row-major M x K, weights as W^T, N x K) without an epilogue; ftx runs plain and, for",
+             "FFN-in, with its fused bias + GELU.  TFLOP/s against the 2516.6 dense peak.", "",
+             "| GEMM | M x N x K | ftx plain us (TFLOP/s) | library us (TFLOP/s) | ftx with bias+GELU us (TFLOP/s) |",
+             "|---|---|---|---|---|"]
+    for r in res["gemm_calibration"]:
+        gl = (f"{r['ftx_bias_gelu_us']:.1f} ({r['ftx_bias_gelu_tflops']:.0f})" if "ftx_bias_gelu_us" in r else "")
+        lines.append(f"| {r['gemm']} | {r['M']} x {r['N']} x {r['K']} | {r['ftx_plain_us']:.1f} "
+                     f"({r['ftx_plain_tflops']:.0f}) | {r['library_plain_us']:.1f} ({r['library_plain_tflops']:.0f}) | {gl} |")
+    lines += ["", f"Kernel source hash: `{res['kernel_source_hash']}`"]
+    path = os.path.join(ROOT, "profiles", args.summary_name + ".md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
 
 
 def elementwise_hbm(shape, reps: int):
