@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--workload", default=None, help=f"default {WORKLOAD_DEFAULT}")
     p.add_argument("--batch", type=int, default=None)
     p.add_argument("--unfused", action="store_true", help="standalone bias+split and bias+GELU kernels")
+    p.add_argument("--no-fold-layernorm", action="store_true",
+                   help="the first LayerNorm of each layer as its own kernel (not folded into "
+                        "the FFN-in projection)")
     p.add_argument("--graph", action="store_true", help="replay the forward as one HIP graph")
     p.add_argument("--fused-attention", type=int, default=1, choices=(0, 1, 2),
                    help="projection + attention in one kernel: 0 never, 1 from 256 tokens and "
@@ -652,6 +655,8 @@ def main():
     if args.unfused:
         enc.set_option(ftx.FTX_OPT_FUSED_EPILOGUES, 0)
     enc.set_option(ftx.FTX_OPT_FUSED_ATTENTION, args.fused_attention)
+    if args.no_fold_layernorm:
+        enc.set_option(ftx.FTX_OPT_FOLD_LAYERNORM, 0)
     if args.graph:
         enc.set_option(ftx.FTX_OPT_GRAPH, 1)
     x = up(case.x)
@@ -675,7 +680,10 @@ def main():
     # which attention path the handle takes (one forward with launch counts, untimed)
     enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)
     enc.forward(x, lens, out)
-    attn_fused = enc.kernel_times()["qkv_attention"][1] > 0
+    counts = enc.kernel_times()
+    attn_fused = counts["qkv_attention"][1] > 0
+    # (hidden 128 also has no LayerNorm-1 launch: it runs in the projection's epilogue)
+    ln_folded = counts["ln1"][1] == 0 and shape.hidden in (768, 1024)
     enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 0)
     torch.cuda.synchronize()
 
@@ -705,6 +713,7 @@ def main():
                    "parallelism": "none (1 GPU)",
                    "epilogues": "standalone" if args.unfused else "fused",
                    "attention": "in the Q/K/V projection's epilogue" if attn_fused else "own kernel",
+                   "layernorm1": "folded into the FFN-in projection" if ln_folded else "own kernel",
                    "launch": "hip graph" if args.graph else "stream"},
         "tflops": tflops, "frac_mfma_peak": tflops / PEAK_MFMA_TFLOPS[dt],
         "gpu_event_ms_per_step": gpu_ms / args.steps,

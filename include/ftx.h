@@ -170,12 +170,20 @@ const char *ftx_last_error(void);
  *     has at least 64 tiles (ceil(batch*S/256) * 3*hidden/192), else the separate kernels;
  *     2 = whenever the shape fits.  Needs FTX_OPT_FUSED_EPILOGUES = 1.
  *     Values outside 0..2 -> FTX_ERR_INVALID_ARG.
+ *   FTX_OPT_FOLD_LAYERNORM (default 1): for fp16, hidden size 768 or 1024 and a batch at
+ *     which the attention-output and FFN projections do not split K, the first LayerNorm of
+ *     each layer is folded into the first FFN projection (its gamma into that projection's
+ *     weights, its beta into the bias; the row statistics come from the attention-output
+ *     projection's epilogue), and the second LayerNorm rebuilds its residual from the same
+ *     statistics: one launch per layer fewer (no FTX_STEP_LN1).  Same result up to rounding
+ *     order.  0 = the LayerNorm runs as its own step.  Needs FTX_OPT_FUSED_EPILOGUES = 1.
  * Unknown option -> FTX_ERR_INVALID_ARG. */
 typedef enum {
   FTX_OPT_FUSED_EPILOGUES = 0,
   FTX_OPT_KERNEL_TIMING = 1,
   FTX_OPT_GRAPH = 2,
-  FTX_OPT_FUSED_ATTENTION = 3
+  FTX_OPT_FUSED_ATTENTION = 3,
+  FTX_OPT_FOLD_LAYERNORM = 4
 } ftx_option;
 ftx_status ftx_set_option(ftx_encoder *enc, ftx_option option, int value);
 

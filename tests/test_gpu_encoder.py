@@ -298,6 +298,47 @@ def test_hidden_128_layernorm_in_the_projection(shape):
     check(out, ref, shape.dtype, stack_tol(shape.dtype), f"{shape}")
 
 
+@pytest.mark.parametrize("shape", [
+    si.Shape(64, 32, 12, 64, 2, "fp16"),   # 2048 rows: 64 x 64 attention-output tiles, 12 per row
+    si.Shape(33, 64, 16, 64, 1, "fp16"),   # hidden 1024, 2112 rows: 128 x 128 tiles, last one partial
+    si.Shape(20, 200, 12, 64, 1, "fp16"),  # padded length 224, ragged lengths, 4480 rows
+])
+def test_layernorm_fold(shape):
+    """FTX_OPT_FOLD_LAYERNORM: the first LayerNorm folded into the FFN-in projection (gamma in
+    the weights, beta in the bias, the row statistics from the attention-output projection's
+    per-tile pairs) and rebuilt by the second LayerNorm.  No LayerNorm-1 launch; against the
+    oracle at the layer / stack bar; with the fold off the LayerNorm runs on its own and the
+    two agree within the stack bar.  New weights set on the handle are folded again."""
+    c = si.custom_case(shape, 91 + shape.batch, lens_range=(1, shape.seq_len), params="random_affine")
+    layers = list(c.layers())
+    ref = oracle.encoder(c.x, layers, c.lens, shape.head_num)
+    enc = _encoder(shape, layers)
+    enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)
+    x, lens = to_dev(c.x, shape.dtype), dev_lens(c.lens)
+    out = to_f64(enc.forward(x, lens))
+    t = enc.kernel_times()
+    assert t["ln1"][1] == 0 and t["ln2"][1] == shape.num_layers
+    assert t["attn_out_gemm"][1] == shape.num_layers and t["ffn1_gemm"][1] == shape.num_layers
+    tol = stack_tol(shape.dtype) if shape.num_layers > 1 else layer_tol(shape.dtype)
+    print("fold", check(out, ref, shape.dtype, tol, f"{shape} fold"))
+    enc.set_option(ftx.FTX_OPT_FOLD_LAYERNORM, 0)
+    plain = to_f64(enc.forward(x, lens))
+    t = enc.kernel_times()
+    assert t["ln1"][1] == shape.num_layers
+    check(plain, ref, shape.dtype, tol, f"{shape} no fold")
+    assert_within(out, plain, 5e-2, 0.0, "fold vs no fold")
+    # other weights into the same handle: folded again at set_weights
+    c2 = si.custom_case(shape, 191 + shape.batch, lens_range=(1, shape.seq_len), params="random_affine")
+    layers2 = list(c2.layers())
+    for l, w in enumerate(layers2):
+        enc.set_weights(l, dev_layer(w, shape.dtype))
+    enc.set_option(ftx.FTX_OPT_FOLD_LAYERNORM, 1)
+    out2 = to_f64(enc.forward(x, lens))
+    enc.close()
+    check(out2, oracle.encoder(c.x, layers2, c.lens, shape.head_num), shape.dtype, tol,
+          f"{shape} fold, new weights")
+
+
 @pytest.mark.parametrize("shape,with_lens", [
     (si.Shape(3, 100, 4, 32, 2, "fp16"), True),
     (si.Shape(2, 100, 4, 32, 2, "fp16"), False),   # no seq_lens: keys limited to 100

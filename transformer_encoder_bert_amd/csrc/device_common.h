@@ -129,6 +129,33 @@ __device__ __forceinline__ void workgroup_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Row statistics of z from per-tile pairs (mean, centred sum of squares) over tiles of bn
+// columns covering a width of h (ntn <= MAXT tiles; st a pointer or a register array):
+// r = 1 / sqrt(var + eps) and s = -mean * r, so that the normalised row is r z + s (before
+// gamma and beta).  Chan's merge of the groups, in tile order; the loops are unrolled to
+// MAXT so that a register array is indexed by constants only.
+template <int MAXT, typename S>
+__device__ __forceinline__ float2 merge_row_stats(const S& st, int ntn, int bn, int h, float eps) {
+  float mean = 0.f;
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t)
+    if (t < ntn) mean += st[t].x * (float)min(bn, h - t * bn);
+  mean /= (float)h;
+  float m2 = 0.f;
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t)
+    if (t < ntn) {
+      const float d = st[t].x - mean;
+      m2 += st[t].y + (float)min(bn, h - t * bn) * d * d;
+    }
+  const float r = rsqrtf(m2 / (float)h + eps);
+  return make_float2(r, -mean * r);
+}
+
+// Most per-tile statistics pairs a row of a folded LayerNorm may have (hidden 1024 in
+// 64-column tiles).
+constexpr int kMaxStatTiles = 16;
+
 // Sum / max over groups of `width` consecutive lanes (width a power of two <= 64).
 template <int width> __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll

@@ -28,13 +28,23 @@ constexpr int kMaxSplitsAll = 16;
 // EV = 8 for 16-bit data (16-byte vectors) when rows allow it, else 4.
 // TX and TA are the types of the residual x and the branch a (T, or float when the
 // residual stream is kept in fp32); yf, when non-null, receives an fp32 copy of y.
-template <typename T, typename TX, typename TA, int EV, int LPR, int MAXV, bool EXACT>
+// The residual given un-normalised (a LayerNorm folded into its consumers): x = LN(zx) with
+// per-tile row statistics of zx (merge_row_stats) and the first LayerNorm's gamma and beta.
+template <typename T> struct ResidualNorm {
+  const float2* stats = nullptr;  // [rows][ntn]
+  int ntn = 0, bn = 0;
+  const T* gamma = nullptr;
+  const T* beta = nullptr;
+};
+
+template <typename T, typename TX, typename TA, int EV, int LPR, int MAXV, bool EXACT, bool XN = false>
 __global__ __launch_bounds__(256) void layernorm_kernel(const TX* __restrict__ x,
                                                         const TA* __restrict__ a,
                                                         const T* __restrict__ bias,
                                                         const T* __restrict__ gamma,
                                                         const T* __restrict__ beta,
-                                                        T* y, float* yf, int rows, int cols) {
+                                                        T* y, float* yf, int rows, int cols,
+                                                        ResidualNorm<T> xn) {
   typedef typename VecT<T, EV>::type tv;
   typedef typename VecT<TX, EV>::type xv_t;
   typedef typename VecT<TA, EV>::type av_t;
@@ -47,6 +57,8 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const TX* __restrict__ x
   const int nvec = cols / EV;
   const size_t base = (size_t)row * cols;
 
+  float2 xrs = make_float2(1.f, 0.f);
+  if constexpr (XN) xrs = merge_row_stats<kMaxStatTiles>(xn.stats + (size_t)row * xn.ntn, xn.ntn, xn.bn, cols, FTX_LN_EPSILON);
   float z[MAXV][EV];
   float sum = 0.f;
 #pragma unroll
@@ -56,9 +68,16 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const TX* __restrict__ x
       const xv_t xv = *(const xv_t*)(x + base + EV * vi);
       const av_t av = *(const av_t*)(a + base + EV * vi);
       const tv bv = *(const tv*)(bias + EV * vi);
+      tv xg = {}, xb = {};
+      if constexpr (XN) {
+        xg = *(const tv*)(xn.gamma + EV * vi);
+        xb = *(const tv*)(xn.beta + EV * vi);
+      }
 #pragma unroll
       for (int e = 0; e < EV; ++e) {
-        z[v][e] = to_f32(xv[e]) + to_f32(av[e]) + to_f32(bv[e]);
+        float xe = to_f32(xv[e]);
+        if constexpr (XN) xe = fmaf(to_f32(xg[e]), fmaf(xe, xrs.x, xrs.y), to_f32(xb[e]));
+        z[v][e] = xe + to_f32(av[e]) + to_f32(bv[e]);
         sum += z[v][e];
       }
     }
@@ -98,16 +117,31 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const TX* __restrict__ x
   }
 }
 
-template <typename T, typename TX, typename TA, int EV, int LPR, int MAXV, bool EXACT>
+template <typename T, typename TX, typename TA, int EV, int LPR, int MAXV, bool EXACT, bool XN = false>
 static hipError_t ln_launch(int rows, int cols, const void* x, const void* a, const void* bias,
                             const void* gamma, const void* beta, void* y, float* yf,
-                            hipStream_t s) {
+                            hipStream_t s, ResidualNorm<T> xn = {}) {
   constexpr int rows_per_block = (256 / kWave) * (kWave / LPR);
   const int grid = (rows + rows_per_block - 1) / rows_per_block;
-  layernorm_kernel<T, TX, TA, EV, LPR, MAXV, EXACT><<<grid, 256, 0, s>>>(
+  layernorm_kernel<T, TX, TA, EV, LPR, MAXV, EXACT, XN><<<grid, 256, 0, s>>>(
       (const TX*)x, (const TA*)a, (const T*)bias, (const T*)gamma, (const T*)beta, (T*)y, yf,
-      rows, cols);
+      rows, cols, xn);
   return hipGetLastError();
+}
+
+// The folded-LayerNorm residual (16-bit, the exact tilings of the common hidden sizes only)
+template <typename T>
+static hipError_t ln_xnorm_dispatch(int rows, int cols, const void* x, const void* a,
+                                    const void* bias, const void* gamma, const void* beta,
+                                    void* y, ResidualNorm<T> xn, hipStream_t s) {
+  for (const void* p : {x, a, bias, gamma, beta, (const void*)y, (const void*)xn.gamma, (const void*)xn.beta})
+    if (!p || ((uintptr_t)p & 15)) return hipErrorInvalidValue;
+  switch (cols) {
+    case 768: return ln_launch<T, T, T, 8, 32, 3, true, true>(rows, cols, x, a, bias, gamma, beta, y, nullptr, s, xn);
+    case 1024: return ln_launch<T, T, T, 8, 32, 4, true, true>(rows, cols, x, a, bias, gamma, beta, y, nullptr, s, xn);
+    default: break;
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename T, typename TX, typename TA>
@@ -156,6 +190,74 @@ hipError_t launch_bias_residual_layernorm(ftx_dtype dt, int rows, int cols, cons
     case FTX_FP32: return ln_dispatch<float, float, float>(rows, cols, x, a, bias, gamma, beta, y, nullptr, s);
     case FTX_FP16: return ln_dispatch<f16, f16, f16>(rows, cols, x, a, bias, gamma, beta, y, nullptr, s);
     case FTX_BF16: return ln_dispatch<bf16, bf16, bf16>(rows, cols, x, a, bias, gamma, beta, y, nullptr, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bias_residual_layernorm_xnorm(ftx_dtype dt, int rows, int cols, const void* zx,
+                                                const float* xstats, int ntn, int bn,
+                                                const void* xgamma, const void* xbeta,
+                                                const void* a, const void* bias, const void* gamma,
+                                                const void* beta, void* y, hipStream_t s) {
+  if (ntn < 1 || ntn > kMaxStatTiles || bn < 1 || (cols + bn - 1) / bn != ntn) return hipErrorInvalidValue;
+  switch (dt) {
+    case FTX_FP16: {
+      const ResidualNorm<f16> xn{(const float2*)xstats, ntn, bn, (const f16*)xgamma, (const f16*)xbeta};
+      return ln_xnorm_dispatch<f16>(rows, cols, zx, a, bias, gamma, beta, y, xn, s);
+    }
+    case FTX_BF16: {
+      const ResidualNorm<bf16> xn{(const float2*)xstats, ntn, bn, (const bf16*)xgamma, (const bf16*)xbeta};
+      return ln_xnorm_dispatch<bf16>(rows, cols, zx, a, bias, gamma, beta, y, xn, s);
+    }
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+// A LayerNorm (gamma, beta over the K index) folded into the projection after it, W^T [N][K]:
+// w'[n][k] = w[n][k] gamma[k] rounded to T, csum[n] = the fp32 sum over k of the rounded
+// w'[n][k], bias'[n] = b[n] + sum_k beta[k] w[n][k] in fp32, so that LN(z) W + b =
+// r (z W') + s csum + bias' for the row's r, s.  One wave per row n, sums in a fixed order.
+// Weight preparation only (set_weights), not on the forward's path.
+template <typename T>
+__global__ __launch_bounds__(256) void fold_ln_weights_kernel(const T* __restrict__ w,
+                                                              const T* __restrict__ gamma,
+                                                              const T* __restrict__ beta,
+                                                              const T* __restrict__ b, T* wf,
+                                                              float* csum, float* bf, int N,
+                                                              int K) {
+  const int n = blockIdx.x * (256 / kWave) + threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if (n >= N) return;
+  float cs = 0.f, bs = 0.f;
+  for (int k = lane; k < K; k += kWave) {
+    const float wv = to_f32(w[(size_t)n * K + k]);
+    const T wr = from_f32<T>(wv * to_f32(gamma[k]));
+    wf[(size_t)n * K + k] = wr;
+    cs += to_f32(wr);
+    bs += to_f32(beta[k]) * wv;
+  }
+  cs = group_sum<kWave>(cs);
+  bs = group_sum<kWave>(bs);
+  if (lane == 0) {
+    csum[n] = cs;
+    bf[n] = to_f32(b[n]) + bs;
+  }
+}
+
+hipError_t launch_fold_layernorm_weights(ftx_dtype dt, int N, int K, const void* w_t,
+                                         const void* gamma, const void* beta, const void* b,
+                                         void* wf_t, float* csum, float* bias_f, hipStream_t s) {
+  const int blocks = (N + 3) / 4;
+  switch (dt) {
+    case FTX_FP16:
+      fold_ln_weights_kernel<f16><<<blocks, 256, 0, s>>>((const f16*)w_t, (const f16*)gamma, (const f16*)beta,
+                                                          (const f16*)b, (f16*)wf_t, csum, bias_f, N, K);
+      return hipGetLastError();
+    case FTX_BF16:
+      fold_ln_weights_kernel<bf16><<<blocks, 256, 0, s>>>((const bf16*)w_t, (const bf16*)gamma, (const bf16*)beta,
+                                                           (const bf16*)b, (bf16*)wf_t, csum, bias_f, N, K);
+      return hipGetLastError();
+    default: break;
   }
   return hipErrorInvalidValue;
 }

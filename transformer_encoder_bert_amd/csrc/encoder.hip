@@ -63,6 +63,12 @@ struct LayerW {
   void* b2;
   void* ln2_g;
   void* ln2_b;
+  // the first LayerNorm folded into the first FFN projection (null when the shape does not
+  // allow it): W1^T with its columns scaled by ln1 gamma, the fp32 column sums of that
+  // matrix and the fp32 bias b1 + beta W1
+  void* w1g_t = nullptr;  // [F][H]
+  float* c1 = nullptr;    // [F]
+  float* b1f = nullptr;   // [F]
 };
 
 // Views of the forward's intermediate tensors, all carved from one block of device memory:
@@ -72,6 +78,7 @@ struct Workspace {
   void *q, *k, *vt, *ctx, *abuf, *y1, *u;
   void *xpad = nullptr, *spad = nullptr;  // [B][S][H] input copy and layer state when Sv < S
   float* y1f = nullptr;     // fp32 copy of Y1, the residual of the second LayerNorm (bf16 only)
+  float* st1 = nullptr;     // [T][ntn] (mean, M2) pairs of Z1 per projection tile (folded LN1)
   float* splitk = nullptr;  // fp32 partial products of split-K projections
   size_t splitk_elems = 0;
 };
@@ -97,6 +104,9 @@ struct ftx_encoder {
   bool attn_fits = false;   // the per-head weight copy exists (16-bit, S = 32, d = 64)
   bool attn_out = false;    // small batch at S = 32: the attention also yields the
                             // attention-output projection's partials, split by head
+  bool fold_fits = false;   // the first LayerNorm can fold into the first FFN projection
+  int fold = 1;             // FTX_OPT_FOLD_LAYERNORM
+  int ln1_bn = 0, ln1_ntn = 0;  // attention-output tile width and tiles per row (fold)
   int timing = 0;
   int graph_mode = 0;
   // graph of one whole forward, captured for the (input, seq_lens, output) it was made with
@@ -225,6 +235,7 @@ size_t layout_workspace(const ftx_encoder* e, char* base, Workspace* w) {
   v.y1 = take(TH);
   v.u = take(T * F * es);
   if (f32res) v.y1f = (float*)take(T * H * 4);
+  if (e->fold_fits) v.st1 = (float*)take(T * e->ln1_ntn * 2 * sizeof(float));
   if (padded) {
     // the rows past Sv of each sequence are zero in the input copy and finite in the state;
     // neither reaches a row below Sv
@@ -294,6 +305,43 @@ ftx_status enqueue_forward(ftx_encoder* e, const Workspace& ws, const void* inpu
     // by head inside the attention kernel instead (its K range is the merged-heads dimension):
     // one launch for the attention and the projection.
     const bool row_ln = H == 128 && (T + 63) / 64 >= 128;
+    // The first LayerNorm folded into the first FFN projection (fp16 at batches whose
+    // projections do not split K): LN1(z) W1 + b1 = r (z (gamma o W1)) + s colsum(gamma o W1)
+    // + (b1 + beta W1) with the row's r = 1/sigma and s = -mean/sigma.  The attention-output
+    // projection stores Z1 = x + C Wo + bo and per-tile (mean, M2) of each row; the FFN-in
+    // projection merges the pairs and applies r, s in its epilogue; the second LayerNorm
+    // rebuilds its residual Y1 = LN1(Z1) from Z1 and the same pairs.  Four launches after
+    // the attention instead of five.
+    if (e->fold && e->fold_fits && e->fused && !row_ln) {
+      if (!use_fused_attention(e)) {
+        st = run_step(e, FTX_STEP_ATTENTION, s, [&] {
+          return launch_attention(dt, B, S, S, nh, d, ws.q, ws.k, ws.vt, seq_lens, ws.ctx, s, e->Sv);
+        });
+        if (st != FTX_OK) return st;
+      }
+      st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
+        return launch_linear_residual_stats(dt, T, H, H, ws.ctx, w.w_o_t, w.b_o, x, ws.y1,
+                                            ws.st1, e->ln1_ntn, s);
+      });
+      if (st != FTX_OK) return st;
+      st = run_step(e, FTX_STEP_FFN1_GEMM, s, [&] {
+        return launch_linear_norm_in(dt, T, F, H, ws.y1, w.w1g_t, w.b1f, w.c1, ws.st1,
+                                     e->ln1_ntn, e->ln1_bn, true, ws.u, s);
+      });
+      if (st != FTX_OK) return st;
+      st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
+        return launch_linear(dt, T, H, F, ws.u, w.w2_t, nullptr, false, ws.abuf, s, false,
+                             ws.splitk, ws.splitk_elems);
+      });
+      if (st != FTX_OK) return st;
+      st = run_step(e, FTX_STEP_LN2, s, [&] {
+        return launch_bias_residual_layernorm_xnorm(dt, T, H, ws.y1, ws.st1, e->ln1_ntn,
+                                                    e->ln1_bn, w.ln1_g, w.ln1_b, ws.abuf, w.b2,
+                                                    w.ln2_g, w.ln2_b, state, s);
+      });
+      if (st != FTX_OK) return st;
+      continue;
+    }
     const int o_splits = linear_splits(dt, T, H, H, ws.splitk_elems, true);
     const bool attn_out = e->attn_out && !use_fused_attention(e) && e->fused && !row_ln &&
                           o_splits > 1 && (size_t)nh * T * H <= ws.splitk_elems;
@@ -457,18 +505,6 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
   e->attn_fits = qkv_attention_fits(dtype, e->S, head_num, size_per_head);
 
   const size_t H = e->H, F = e->F, T = e->T, es = e->es;
-  // weights: per layer 3H*H + 3H + H*H + H + 2H + F*H + F + H*F + H + 2H elements (plus a
-  // second 3H*H + 3H in per-head order for the fused attention), each tensor padded to 256
-  // bytes
-  auto pad = [](size_t bytes) { return (bytes + 255) / 256 * 256; };
-  const size_t per_layer = pad(3 * H * H * es) + pad(3 * H * es) + pad(H * H * es) + 5 * pad(H * es) +
-                           pad(F * H * es) + pad(F * es) + pad(H * F * es) + pad(H * es) +
-                           (e->attn_fits ? pad(3 * H * H * es) + pad(3 * H * es) : 0);
-  hipError_t err = hipMalloc(&e->weights, per_layer * e->L);
-  if (err != hipSuccess) {
-    delete e;
-    return hip_fail(err, "hipMalloc(weights)");
-  }
   // split-K workspace: the largest any of the four projections plans for, and the per-head
   // partials of the attention-output projection where the attention produces them (S = 32,
   // the projection splits, and the partials stay within 4 MiB: BERT-base up to 3 sequences;
@@ -484,6 +520,35 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
                   linear_splits(dtype, e->T, e->H, e->H, (size_t)1 << 40, true) > 1 &&
                   per_head * sizeof(float) <= (4u << 20);
     if (e->attn_out) e->splitk_need = std::max(e->splitk_need, per_head);
+  }
+  {
+    // the LayerNorm fold: fp16 (bf16 keeps the un-normalised residual in fp32), the hidden
+    // sizes the rebuilding LayerNorm tiles exactly, and unsplit projections on multi-wave
+    // tiles for the attention output, FFN-in and FFN-out
+    int tm, tn, sp, tm1, tn1, sp1;
+    plan_linear(dtype, e->T, e->H, e->H, e->dev.cus, false, &tm, &tn, &sp);
+    plan_linear(dtype, e->T, e->F, e->H, e->dev.cus, false, &tm1, &tn1, &sp1);
+    e->fold_fits = dtype == FTX_FP16 && (e->H == 768 || e->H == 1024) && !e->attn_out &&
+                   sp == 1 && tm > 32 && sp1 == 1 && tm1 > 32 &&
+                   linear_splits(dtype, e->T, e->H, e->H, (size_t)1 << 40, true) == 1 &&
+                   linear_splits(dtype, e->T, e->H, e->F, (size_t)1 << 40, true) == 1;
+    if (e->fold_fits) {
+      e->ln1_bn = tn;
+      e->ln1_ntn = (e->H + tn - 1) / tn;
+    }
+  }
+  // weights: per layer 3H*H + 3H + H*H + H + 2H + F*H + F + H*F + H + 2H elements (plus a
+  // second 3H*H + 3H in per-head order for the fused attention, and for the LayerNorm fold
+  // F*H more plus 2F fp32), each tensor padded to 256 bytes
+  auto pad = [](size_t bytes) { return (bytes + 255) / 256 * 256; };
+  const size_t per_layer = pad(3 * H * H * es) + pad(3 * H * es) + pad(H * H * es) + 5 * pad(H * es) +
+                           pad(F * H * es) + pad(F * es) + pad(H * F * es) + pad(H * es) +
+                           (e->attn_fits ? pad(3 * H * H * es) + pad(3 * H * es) : 0) +
+                           (e->fold_fits ? pad(F * H * es) + 2 * pad(F * 4) : 0);
+  hipError_t err = hipMalloc(&e->weights, per_layer * e->L);
+  if (err != hipSuccess) {
+    delete e;
+    return hip_fail(err, "hipMalloc(weights)");
   }
   e->ws_bytes = layout_workspace(e, nullptr, nullptr);
   err = hipMalloc(&e->ws_mem, e->ws_bytes);
@@ -512,6 +577,11 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
     lw.ln2_b = take(H * es);
     lw.w_qkvh_t = e->attn_fits ? take(3 * H * H * es) : nullptr;
     lw.b_qkvh = e->attn_fits ? take(3 * H * es) : nullptr;
+    if (e->fold_fits) {
+      lw.w1g_t = take(F * H * es);
+      lw.c1 = (float*)take(F * 4);
+      lw.b1f = (float*)take(F * 4);
+    }
   }
   e->ready.assign(e->L, 0);
   if (e->w.xpad) {
@@ -580,6 +650,9 @@ ftx_status ftx_set_weights(ftx_encoder* e, int layer, const ftx_layer_weights* w
                                d * es, d * es, e->nh, hipMemcpyDeviceToDevice, s));
     }
   }
+  if (lw.w1g_t)
+    FTX_HIP(launch_fold_layernorm_weights(e->dt, e->F, e->H, lw.w1_t, lw.ln1_g, lw.ln1_b, lw.b1,
+                                          lw.w1g_t, lw.c1, lw.b1f, s));
   FTX_HIP(hipStreamSynchronize(s));
   e->ready[layer] = 1;
   return FTX_OK;
@@ -692,6 +765,10 @@ ftx_status ftx_set_option(ftx_encoder* e, ftx_option option, int value) {
     case FTX_OPT_GRAPH:
       e->graph_mode = value ? 1 : 0;
       if (!e->graph_mode) drop_graph(e);
+      return FTX_OK;
+    case FTX_OPT_FOLD_LAYERNORM:
+      if (e->fold != (value ? 1 : 0)) drop_graph(e);
+      e->fold = value ? 1 : 0;
       return FTX_OK;
   }
   return fail(FTX_ERR_INVALID_ARG, "unknown option");

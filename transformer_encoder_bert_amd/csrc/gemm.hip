@@ -260,6 +260,312 @@ template <typename T, typename TX, bool A_F32> struct EpiLinearLN {
   }
 };
 
+// Projection + bias + residual, with the statistics the LayerNorm after it needs, for a
+// LayerNorm folded into the next projection: z = x + a + bias is stored (rounded to the
+// storage type) and, for each row, the mean and the centred sum of squares of the fp32 z
+// over this tile's columns go to stats[row][tile column] -- the LayerNorm's own two-pass
+// statistics, taken per tile; a consumer merges the tiles' pairs (equal-count groups:
+// mean of means, sum of M2 plus the spread of the means).  Whole-tile epilogue: the wave
+// columns of a row meet in LDS.  Tiles up to 256 rows, two wave columns at most.
+template <typename T> struct EpiLinearResStats {
+  static constexpr bool kBlock = true;
+  typedef T out_t;
+  typedef typename VecT<T, 4>::type b4;
+  const T* x;       // residual [M][N]
+  const T* bias;    // [N]
+  T* z;             // [M][N]
+  float2* stats;    // [M][ntn]
+  int M, N, ntn;
+  static constexpr size_t kLdsBytes = 2 * 256 * 2 * sizeof(float);  // [pass][row][wave column]
+  __device__ __forceinline__ b4 bias4(int n) const {
+    b4 v = {};
+    if (n < N) v = *(const b4*)(bias + n);
+    return v;
+  }
+  template <int TM, int TN, int WN, int BM>
+  __device__ __forceinline__ void block(char* smem, int m0, int n0, int wave, int lane,
+                                        const f32x16 (&acc)[TN][TM],
+                                        const b4 (&bq)[TN][4]) const {
+    constexpr int BN = TN * 32 * WN;
+    if constexpr ((size_t)BM * BN * sizeof(T) + 2 * BM * 2 * sizeof(float) <= 2 * (BM + BN) * 128)
+      block_staged<TM, TN, WN, BM>(smem, m0, n0, wave, lane, acc, bq);
+    else
+      block_direct<TM, TN, WN>(smem, m0, n0, wave, lane, acc, bq);
+  }
+
+  // The residual tile x comes into LDS by DMA (16-byte chunks, row-contiguous; chunk c of
+  // tile row R at position c ^ (R & 7) of the row) while the accumulators take the bias; each
+  // lane adds its elements of x from LDS in the accumulator layout and writes z back over
+  // them in place (no other lane touches those bytes), and the block then stores z from LDS
+  // as 16-byte row-contiguous chunks.  The row statistics meet in LDS after the tile.  Needs
+  // the tile (BM x BN, 16-bit) plus 2 x BM x 2 floats within the two slab buffers.
+  template <int TM, int TN, int WN, int BM>
+  __device__ __forceinline__ void block_staged(char* smem, int m0, int n0, int wave, int lane,
+                                               const f32x16 (&acc)[TN][TM],
+                                               const b4 (&bq)[TN][4]) const {
+    static_assert(sizeof(T) == 2 && WN <= 2, "16-bit tiles, two wave columns at most");
+    constexpr int BN = TN * 32 * WN;
+    constexpr int CPR = BN / 8;         // 16-byte chunks per tile row
+    constexpr int NCH = BM * CPR;       // chunks in the tile
+    static_assert(NCH % kWave == 0, "whole wave loads");
+    constexpr int ROWB = BN * 2;        // LDS bytes per tile row
+    const int nth = blockDim.x;
+    const int wm = wave / WN, wn = wave % WN, lr = lane % 32, g = lane / 32;
+    float* red = (float*)(smem + BM * ROWB);  // [pass][BM rows][2 wave columns]
+    const int cnt = min(BN, N - n0);
+    const float inv = 1.0f / (float)cnt;
+    // x rows m0 .. m0 + BM - 1 (rows past M and columns past N read as zero)
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(x + (size_t)m0 * N), (short)0, min(BM, M - m0) * N * (int)sizeof(T), 0x00020000);
+    for (int c0 = wave * kWave; c0 < NCH; c0 += nth) {
+      const int c = c0 + lane, R = c / CPR, pos = c % CPR;
+      const int col = n0 + ((pos ^ (R & 7)) * 8);
+      const int voff = col < N ? (R * N + col) * (int)sizeof(T) : 0x7ffffff0;
+      lds_dma16(rx, voff, smem + c0 * 16);
+    }
+    float zv[TM][TN][16];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) zv[i][j][4 * q + e] = acc[j][i][4 * q + e] + to_f32(bq[j][q][e]);
+    wait_vmcnt<0>();   // this wave's share of x is in LDS
+    workgroup_barrier();
+    // LDS byte address of this lane's 4 elements (row rl, columns 8 q + 4 g of column tile j)
+    auto lds_at = [&](int rl, int j, int q) {
+      const int chunk = (wn * TN + j) * 4 + q;
+      return rl * ROWB + ((chunk ^ (rl & 7)) * 16) + g * 8;
+    };
+    float mean[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int rl = (wm * TM + i) * 32 + lr, row = m0 + rl;
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + (wn * TN + j) * 32 + 8 * q + 4 * g;
+          const bool ok = row < M && n < N;
+          const b4 xv = *(const b4*)(smem + lds_at(rl, j, q));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = ok ? zv[i][j][4 * q + e] + to_f32(xv[e]) : 0.f;
+            zv[i][j][4 * q + e] = v;
+            sum += v;
+          }
+        }
+      sum += __shfl_xor(sum, 32);
+      if (g == 0) red[rl * 2 + wn] = sum;
+    }
+    __syncthreads();  // LDS writes (not only the barrier) complete first
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int rl = (wm * TM + i) * 32 + lr;
+      mean[i] = (WN == 2 ? red[rl * 2] + red[rl * 2 + 1] : red[rl * 2]) * inv;
+      float sq = 0.f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + (wn * TN + j) * 32 + 8 * q + 4 * g;
+          b4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[e] = from_f32<T>(zv[i][j][4 * q + e]);
+            if (n < N) {
+              const float d = zv[i][j][4 * q + e] - mean[i];
+              sq += d * d;
+            }
+          }
+          *(b4*)(smem + lds_at(rl, j, q)) = o;  // z over this lane's own x
+        }
+      sq += __shfl_xor(sq, 32);
+      if (g == 0) red[2 * BM + rl * 2 + wn] = sq;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int rl = (wm * TM + i) * 32 + lr, row = m0 + rl;
+      if (row < M && wn == 0 && g == 0) {
+        const float m2 = WN == 2 ? red[2 * BM + rl * 2] + red[2 * BM + rl * 2 + 1] : red[2 * BM + rl * 2];
+        stats[(size_t)row * ntn + n0 / BN] = make_float2(mean[i], m2);
+      }
+    }
+    typedef typename Vec16<T>::type vec;
+    for (int c = threadIdx.x; c < NCH; c += nth) {
+      const int R = c / CPR, ch = c % CPR, col = n0 + ch * 8;
+      if (m0 + R < M && col < N)
+        *(vec*)(z + (size_t)(m0 + R) * N + col) = *(const vec*)(smem + R * ROWB + ((ch ^ (R & 7)) * 16));
+    }
+  }
+
+  // The same with x read and z written straight from the accumulator layout (4 elements
+  // per lane and row): tiles too large to stage.
+  template <int TM, int TN, int WN>
+  __device__ __forceinline__ void block_direct(char* smem, int m0, int n0, int wave, int lane,
+                                               const f32x16 (&acc)[TN][TM],
+                                               const b4 (&bq)[TN][4]) const {
+    static_assert(WN <= 2 && TM * 32 <= 256, "tile");
+    constexpr int BN = TN * 32 * WN;
+    const int wm = wave / WN, wn = wave % WN, lr = lane % 32, g = lane / 32;
+    float* red = (float*)smem;  // [pass][256 rows][2]
+    const int cnt = min(BN, N - n0);
+    const float inv = 1.0f / (float)cnt;
+    float zv[TM][TN][16];
+    float mean[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int rl = (wm * TM + i) * 32 + lr, row = m0 + rl;
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + (wn * TN + j) * 32 + 8 * q + 4 * g;
+          const bool ok = row < M && n < N;
+          b4 xv = {};
+          if (ok) xv = *(const b4*)(x + (size_t)row * N + n);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = ok ? acc[j][i][4 * q + e] + to_f32(bq[j][q][e]) + to_f32(xv[e]) : 0.f;
+            zv[i][j][4 * q + e] = v;
+            sum += v;
+          }
+        }
+      sum += __shfl_xor(sum, 32);
+      if (g == 0) red[rl * 2 + wn] = sum;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int rl = (wm * TM + i) * 32 + lr;
+      mean[i] = (WN == 2 ? red[rl * 2] + red[rl * 2 + 1] : red[rl * 2]) * inv;
+      float sq = 0.f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + (wn * TN + j) * 32 + 8 * q + 4 * g;
+          if (n < N)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float d = zv[i][j][4 * q + e] - mean[i];
+              sq += d * d;
+            }
+        }
+      sq += __shfl_xor(sq, 32);
+      if (g == 0) red[512 + rl * 2 + wn] = sq;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int rl = (wm * TM + i) * 32 + lr, row = m0 + rl;
+      if (row >= M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + (wn * TN + j) * 32 + 8 * q + 4 * g;
+          if (n >= N) continue;
+          b4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(zv[i][j][4 * q + e]);
+          *(b4*)(z + (size_t)row * N + n) = o;
+        }
+      if (wn == 0 && g == 0) {
+        const float m2 = WN == 2 ? red[512 + rl * 2] + red[512 + rl * 2 + 1] : red[512 + rl * 2];
+        stats[(size_t)row * ntn + n0 / BN] = make_float2(mean[i], m2);
+      }
+    }
+  }
+};
+
+// Projection of un-normalised rows z whose LayerNorm is folded in: with W' = gamma o W
+// (gamma scaling the rows of W, i.e. the K index), LN(z) W + b = r (z W') + s colsum(W') +
+// (b + beta W) for each row's r, s (merge_row_stats).  The weights arrive folded; csum holds
+// colsum(W') of the folded, rounded weights, bias the fp32 b + beta W.  Then the activation.
+template <typename T, bool GELU> struct EpiLinearNormIn {
+  static constexpr bool kBlock = false;
+  typedef T out_t;
+  typedef typename Vec16<T>::type vec;
+  typedef f32x4 b4;
+  T* c;
+  const float* bias;   // [N]: b + beta W
+  const float* csum;   // [N]: colsum(gamma o W)
+  const float2* stats; // [M][ntn]
+  int ntn, bn, h;      // the producer's tile width and the normalised width (K)
+  int M, N;
+  __device__ __forceinline__ b4 bias4(int n) const {
+    b4 v = {};
+    if (n < N) v = *(const f32x4*)(bias + n);
+    return v;
+  }
+  __device__ __forceinline__ float act(float v) const { return GELU ? gelu_tanh(v) : v; }
+  // The block's row factors (r, s) and column sums, staged in LDS after the slab buffers:
+  // thread t < BM loads the stats pairs of row m0 + t, thread BM + c the column sum of
+  // column n0 + c (pre_load, issued before the first slab loads), and after the prologue's
+  // wait it merges and stores them (pre_store); the LDS wait and barrier every wave passes
+  // before the epilogue publish them, and the epilogue reads LDS only.  Needs BM + BN <= the
+  // block's threads.
+  template <int BM, int BN> static constexpr int pre_bytes() { return BM * 8 + BN * 4; }
+  struct PreRegs {
+    float2 st[kMaxStatTiles];
+    float c;
+  };
+  template <int BM, int BN>
+  __device__ __forceinline__ PreRegs pre_load(int m0, int n0, int tid) const {
+    PreRegs p;
+    p.c = 0.f;
+#pragma unroll
+    for (int u = 0; u < kMaxStatTiles; ++u) p.st[u] = make_float2(0.f, 0.f);
+    if (tid < BM) {
+      const int m = m0 + tid;
+      if (m < M) {
+        const float2* st = stats + (size_t)m * ntn;
+#pragma unroll
+        for (int u = 0; u < kMaxStatTiles; ++u)
+          if (u < ntn) p.st[u] = st[u];
+      }
+    } else if (tid < BM + BN) {
+      const int n = n0 + tid - BM;
+      if (n < N) p.c = csum[n];
+    }
+    return p;
+  }
+  template <int BM, int BN>
+  __device__ __forceinline__ void pre_store(const PreRegs& p, char* lds, int m0, int tid) const {
+    if (tid < BM) {
+      ((float2*)lds)[tid] = m0 + tid < M ? merge_row_stats<kMaxStatTiles>(p.st, ntn, bn, h, FTX_LN_EPSILON)
+                                         : make_float2(0.f, 0.f);
+    } else if (tid < BM + BN) {
+      ((float*)(lds + BM * 8))[tid - BM] = p.c;
+    }
+  }
+  __device__ __forceinline__ TileDst<T> tile(int mt, int nt) const {
+    return {c + (size_t)mt * N + nt, N, false};
+  }
+  __device__ __forceinline__ bool valid(int mt, int nt, int r, int col) const {
+    return mt + r < M && nt + col < N;
+  }
+};
+template <typename E> struct is_res_stats { static constexpr bool value = false; };
+template <typename T> struct is_res_stats<EpiLinearResStats<T>> { static constexpr bool value = true; };
+template <typename E> struct is_norm_in { static constexpr bool value = false; };
+template <typename T, bool G> struct is_norm_in<EpiLinearNormIn<T, G>> { static constexpr bool value = true; };
+// LDS bytes an epilogue stages at the start of a BM x BN block (after the slab buffers), and
+// the registers that carry its loads across the prologue
+template <typename Epi, int BM, int BN> constexpr int epi_pre_bytes() {
+  if constexpr (is_norm_in<Epi>::value) return Epi::template pre_bytes<BM, BN>();
+  else return 0;
+}
+struct NoPre {};
+template <typename Epi, bool = is_norm_in<Epi>::value> struct PreOf { typedef NoPre type; };
+template <typename Epi> struct PreOf<Epi, true> { typedef typename Epi::PreRegs type; };
+
 // Split-K partial products: the tile of K range blockIdx.y is written, unscaled and in fp32,
 // to P[blockIdx.y][M][N]; splitk_reduce_kernel then sums the ranges in order and applies
 // the real epilogue.
@@ -301,10 +607,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // Stage one C^T tile (columns nt.., rows mt..) through this wave's LDS scratch `ws`
 // (32 x (32 + pad) elements of the output type) and store it as 16-byte vectors.
 // Wave-private: LDS accesses of one wave complete in order.
+// A normalising epilogue (is_norm_in) also takes the LDS row factors rsl[32] and column sums
+// csl[32] of this tile.
 template <typename Epi>
 __device__ __forceinline__ void epilogue_tile(const Epi& epi, typename Epi::out_t* ws, int mt,
                                               int nt, int lane, const f32x16& acc,
-                                              const typename Epi::b4 (&bq)[4]) {
+                                              const typename Epi::b4 (&bq)[4],
+                                              const float2* rsl = nullptr,
+                                              const float* csl = nullptr) {
   typedef typename Epi::out_t TO;
   typedef typename Epi::vec vec;
   constexpr int EV = 16 / sizeof(TO);       // elements per 16-byte vector
@@ -314,12 +624,21 @@ __device__ __forceinline__ void epilogue_tile(const Epi& epi, typename Epi::out_
   const int lr = lane % 32, g = lane / 32;
   const TileDst<TO> dst = epi.tile(mt, nt);
   typedef typename VecT<TO, 4>::type t4;
+  float2 rs = make_float2(1.f, 0.f);
+  if constexpr (is_norm_in<Epi>::value) rs = rsl[lr];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int nl = 8 * q + 4 * g;           // local column of register 4q
     t4 o;
+    if constexpr (is_norm_in<Epi>::value) {
+      const f32x4 cs = *(const f32x4*)(csl + nl);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = from_f32<TO>(epi.act(acc[4 * q + e] + to_f32(bq[q][e])));
+      for (int e = 0; e < 4; ++e)
+        o[e] = from_f32<TO>(epi.act(fmaf(rs.x, acc[4 * q + e], fmaf(rs.y, cs[e], to_f32(bq[q][e])))));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = from_f32<TO>(epi.act(acc[4 * q + e] + to_f32(bq[q][e])));
+    }
     if (dst.tr) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) ws[(nl + e) * LDW + lr] = o[e];  // LDS rows run along n
@@ -542,7 +861,8 @@ template <typename T, int SEQ, int D, int R = 256> struct EpiQKVAttn {
   }
 };
 
-template <typename T, int BM, int BN, int WM, int WN> struct GemmCfg {
+template <typename T, int BM_, int BN_, int WM, int WN> struct GemmCfg {
+  static constexpr int BM = BM_, BN = BN_;
   typedef Mfma<T> MF;
   static constexpr int VEC = MF::VEC;               // elements per 16-byte chunk
   static constexpr int ROWB = 128;                  // bytes of K per tile row and slab
@@ -585,11 +905,15 @@ template <typename C, typename Epi>
 __device__ __forceinline__ void gemm_epilogue(const Epi& epi, char* smem, int m0, int n0,
                                               int wave, int lane,
                                               const f32x16 (&acc)[C::TN][C::TM],
-                                              const typename Epi::b4 (&bq)[C::TN][4]) {
+                                              const typename Epi::b4 (&bq)[C::TN][4],
+                                              const char* pre = nullptr) {
   constexpr int TM = C::TM, TN = C::TN, WN = C::kWN;
   if constexpr (Epi::kBlock) {
     static_assert(Epi::kLdsBytes <= 2 * C::STAGE, "block epilogue LDS");
-    epi.template block<TM, TN, WN>(smem, m0, n0, wave, lane, acc, bq);
+    if constexpr (is_res_stats<Epi>::value)
+      epi.template block<TM, TN, WN, C::BM>(smem, m0, n0, wave, lane, acc, bq);
+    else
+      epi.template block<TM, TN, WN>(smem, m0, n0, wave, lane, acc, bq);
   } else {
     typedef typename Epi::out_t TO;
     constexpr int SCRATCH = 32 * (32 + 16 / sizeof(TO));  // elements of TO per wave
@@ -599,9 +923,16 @@ __device__ __forceinline__ void gemm_epilogue(const Epi& epi, char* smem, int m0
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i) {
+        const float2* rsl = nullptr;
+        const float* csl = nullptr;
+        if constexpr (is_norm_in<Epi>::value) {
+          rsl = (const float2*)pre + (wm * TM + i) * 32;
+          csl = (const float*)(pre + C::BM * 8) + (wn * TN + j) * 32;
+        }
         epilogue_tile(epi, ws, m0 + (wm * TM + i) * 32, n0 + (wn * TN + j) * 32, lane, acc[j][i],
-                      bq[j]);
+                      bq[j], rsl, csl);
+      }
   }
 }
 
@@ -620,7 +951,9 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
   typedef typename MF::frag frag;
   constexpr int TM = C::TM, TN = C::TN, AQ = C::AQ, BQ = C::BQ, ROWB = C::ROWB;
   static_assert(NST >= 2 && NST <= 8, "slab stages");
-  __shared__ __attribute__((aligned(1024))) char smem[NST * C::STAGE];
+  constexpr int PRE = epi_pre_bytes<Epi, BM, BN>();
+  static_assert(BM + BN <= C::NW * kWave || PRE == 0, "one staged row or column per thread");
+  __shared__ __attribute__((aligned(1024))) char smem[NST * C::STAGE + PRE];
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
@@ -644,6 +977,9 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
   for (int j = 0; j < TN; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) bq[j][q] = epi.bias4(n0 + (wn * TN + j) * 32 + 8 * q + 4 * g);
+  char* const pre = smem + NST * C::STAGE;
+  [[maybe_unused]] typename PreOf<Epi>::type pre_regs;
+  if constexpr (PRE > 0) pre_regs = epi.template pre_load<BM, BN>(m0, n0, threadIdx.x);
 
   const int kb = blockIdx.y * kchunk;
   const int kn = min(K - kb, kchunk);
@@ -711,6 +1047,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p)
     if (p < nk) load_slab(p, p);
+  if constexpr (PRE > 0) epi.template pre_store<BM, BN>(pre_regs, pre, m0, threadIdx.x);
   for (int k0 = 0; k0 < nk; k0 += NST) {
 #pragma unroll
     for (int u = 0; u < NST; ++u) {
@@ -746,7 +1083,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
   // every wave is done with both buffers before the LDS is reused as epilogue scratch
   __builtin_amdgcn_s_waitcnt(0xC07F);
   workgroup_barrier();
-  gemm_epilogue<C, Epi>(epi, smem, m0, n0, wave, lane, acc, bq);
+  gemm_epilogue<C, Epi>(epi, smem, m0, n0, wave, lane, acc, bq, pre);
 }
 
 // Ping-pong K loop for the 8-wave tiles in 16-bit types (BM = 256, waves 4 x 2).  Waves w
@@ -781,8 +1118,11 @@ __global__ __launch_bounds__(8 * kWave) void gemm_pp_kernel(const T* __restrict_
   // the two slab buffers, then a counter of the group-1 waves done reading their current slab
   // (one LDS object: a second one gives the compiler alias scopes under which it waits for
   // every slab load in flight before any LDS read)
-  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE + 16];
+  constexpr int PRE = epi_pre_bytes<Epi, BM, BN>();
+  static_assert(BM + BN <= 8 * kWave || PRE == 0, "one staged row or column per thread");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE + 16 + PRE];
   unsigned* const g1_reads_done = (unsigned*)(smem + 2 * C::STAGE);
+  char* const pre = smem + 2 * C::STAGE + 16;
   if (threadIdx.x == 0) *g1_reads_done = 0;
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the store lands before the prologue's barrier
 
@@ -853,7 +1193,10 @@ __global__ __launch_bounds__(8 * kWave) void gemm_pp_kernel(const T* __restrict_
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // prologue: slab 0 from every wave, group 1's share of slab 1 as well
+  // prologue: slab 0 from every wave, group 1's share of slab 1 as well (after the epilogue's
+  // staged loads, which the waits below then cover)
+  [[maybe_unused]] typename PreOf<Epi>::type pre_regs;
+  if constexpr (PRE > 0) pre_regs = epi.template pre_load<BM, BN>(m0, n0, threadIdx.x);
   if (nk > 0) load_slab(0, 0);
   if (grp == 1 && nk > 1) {
     load_slab(1, 1);
@@ -861,6 +1204,7 @@ __global__ __launch_bounds__(8 * kWave) void gemm_pp_kernel(const T* __restrict_
   } else {
     wait_vmcnt<0>();
   }
+  if constexpr (PRE > 0) epi.template pre_store<BM, BN>(pre_regs, pre, m0, threadIdx.x);
   barrier();
   if (grp == 1) barrier();
   for (int kt = 0; kt < nk; ++kt) {
@@ -920,7 +1264,7 @@ __global__ __launch_bounds__(8 * kWave) void gemm_pp_kernel(const T* __restrict_
   if (grp == 0) barrier();
   __builtin_amdgcn_s_waitcnt(0xC07F);
   barrier();
-  gemm_epilogue<C, Epi>(epi, smem, m0, n0, wave, lane, acc, bq);
+  gemm_epilogue<C, Epi>(epi, smem, m0, n0, wave, lane, acc, bq, pre);
 }
 
 // Small-M projection (the rows of a few short sequences): one workgroup of kSmallWaves
@@ -1338,6 +1682,77 @@ hipError_t launch_linear(ftx_dtype dt, int M, int N, int K, const void* a, const
     case FTX_FP32: return linear_t<float>(M, N, K, a, w_t, bias, gelu, false, c, s, ws, ws_elems);
     case FTX_FP16: return linear_t<f16>(M, N, K, a, w_t, bias, gelu, out_f32, c, s, ws, ws_elems);
     case FTX_BF16: return linear_t<bf16>(M, N, K, a, w_t, bias, gelu, out_f32, c, s, ws, ws_elems);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int BM_, int BN_, int WM_, int WN_> struct TileShape {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+};
+
+// The projection on the tile the planner picks, unsplit (for epilogues that have no split-K
+// form); hipErrorInvalidValue where the plan would split K.
+template <typename T, typename Epi>
+static hipError_t gemm_launch_whole(int M, int N, int K, const void* a, const void* w_t, Epi epi,
+                                    hipStream_t s) {
+  const DeviceInfo di = device_info();
+  const GemmPlan plan = plan_gemm(M, N, K, (int)sizeof(T), false, di.cus);
+  if (plan.splits > 1) return hipErrorInvalidValue;
+  auto run = [&](auto cfg) -> hipError_t {
+    constexpr int BM = decltype(cfg)::BM, BN = decltype(cfg)::BN, WM = decltype(cfg)::WM, WN = decltype(cfg)::WN;
+    const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    if constexpr (sizeof(T) == 2 && BM == 256 && WM == 4 && WN == 2) {
+      constexpr int BK = GemmCfg<T, BM, BN, WM, WN>::BK;
+      if (K % BK == 0 && K / BK >= kPingPongMinSlabs) {
+        gemm_pp_kernel<T, BM, BN, Epi><<<tiles, WM * WN * kWave, 0, s>>>(
+            (const T*)a, (const T*)w_t, M, N, K, K, di.xcds, epi);
+        return hipGetLastError();
+      }
+    }
+    gemm_kernel_launch<T, BM, BN, WM, WN, Epi>(dim3(tiles), K, M, N, K, a, w_t, epi, di.xcds, s);
+    return hipGetLastError();
+  };
+  switch (plan.cfg) {
+    case TILE_256x256: if constexpr (sizeof(T) == 2) return run(TileShape<256, 256, 4, 2>{}); break;
+    case TILE_256x192: if constexpr (sizeof(T) == 2) return run(TileShape<256, 192, 4, 2>{}); break;
+    case TILE_256x128: return run(TileShape<256, 128, 4, 2>{});
+    case TILE_128x128: return run(TileShape<128, 128, 2, 2>{});
+    case TILE_64x64: return run(TileShape<64, 64, 2, 2>{});
+    default: break;  // 32x32 tiles: one wave holds a row's columns alone, not supported here
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_linear_residual_stats(ftx_dtype dt, int M, int N, int K, const void* a,
+                                        const void* w_t, const void* bias, const void* x,
+                                        void* z, float* stats, int ntn, hipStream_t s) {
+  int tm, tn, sp;
+  plan_linear(dt, M, N, K, device_info().cus, false, &tm, &tn, &sp);
+  if (sp != 1 || ntn != (N + tn - 1) / tn || ntn > kMaxStatTiles || N % 8) return hipErrorInvalidValue;
+  switch (dt) {
+    case FTX_FP16: return gemm_launch_whole<f16>(M, N, K, a, w_t,
+        EpiLinearResStats<f16>{(const f16*)x, (const f16*)bias, (f16*)z, (float2*)stats, M, N, ntn}, s);
+    case FTX_BF16: return gemm_launch_whole<bf16>(M, N, K, a, w_t,
+        EpiLinearResStats<bf16>{(const bf16*)x, (const bf16*)bias, (bf16*)z, (float2*)stats, M, N, ntn}, s);
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_linear_norm_in(ftx_dtype dt, int M, int N, int K, const void* z,
+                                 const void* w_t, const float* bias, const float* csum,
+                                 const float* stats, int ntn, int bn, bool gelu, void* c,
+                                 hipStream_t s) {
+  if (ntn < 1 || ntn > kMaxStatTiles || bn < 1 || (K + bn - 1) / bn != ntn) return hipErrorInvalidValue;
+  const float2* st = (const float2*)stats;
+  switch (dt) {
+    case FTX_FP16:
+      if (gelu) return gemm_launch_whole<f16>(M, N, K, z, w_t, EpiLinearNormIn<f16, true>{(f16*)c, bias, csum, st, ntn, bn, K, M, N}, s);
+      return gemm_launch_whole<f16>(M, N, K, z, w_t, EpiLinearNormIn<f16, false>{(f16*)c, bias, csum, st, ntn, bn, K, M, N}, s);
+    case FTX_BF16:
+      if (gelu) return gemm_launch_whole<bf16>(M, N, K, z, w_t, EpiLinearNormIn<bf16, true>{(bf16*)c, bias, csum, st, ntn, bn, K, M, N}, s);
+      return gemm_launch_whole<bf16>(M, N, K, z, w_t, EpiLinearNormIn<bf16, false>{(bf16*)c, bias, csum, st, ntn, bn, K, M, N}, s);
+    default: break;
   }
   return hipErrorInvalidValue;
 }

@@ -141,6 +141,39 @@ hipError_t launch_splitk_bias_residual_layernorm(ftx_dtype dt, int rows, int col
                                                  const void* gamma, const void* beta, void* y,
                                                  float* yf, hipStream_t s);
 
+// LayerNorm folded into the projection after it (16-bit data).  The projection before it
+// stores z = x + a w_t + bias (rounded to the storage type) and, per row and per tile of
+// the planner's tile width tn, the mean and centred sum of squares of the fp32 z over the
+// tile's columns: stats[row][tile] as float2 pairs, ntn = ceil(N / tn) tiles.
+// hipErrorInvalidValue when the planner would split K or ntn does not match.
+hipError_t launch_linear_residual_stats(ftx_dtype dt, int M, int N, int K, const void* a,
+                                        const void* w_t, const void* bias, const void* x,
+                                        void* z, float* stats, int ntn, hipStream_t s);
+
+// The projection of LN(z) through the folded weights w_t = (gamma o W)^T [N][K]:
+// c = act(r (z w_t) + s csum + bias) per row, with r, s from the row's ntn stats pairs
+// (tiles of bn columns of the K-wide rows), csum and bias fp32 (launch_fold_layernorm_weights).
+hipError_t launch_linear_norm_in(ftx_dtype dt, int M, int N, int K, const void* z,
+                                 const void* w_t, const float* bias, const float* csum,
+                                 const float* stats, int ntn, int bn, bool gelu, void* c,
+                                 hipStream_t s);
+
+// y = LN(x + a + bias) with x = LN_x(zx) rebuilt from zx and its stats (the folded
+// LayerNorm's gamma xgamma and beta xbeta): the layer's second LayerNorm after a folded
+// first.  cols 768 or 1024, every pointer 16-byte aligned; else hipErrorInvalidValue.
+hipError_t launch_bias_residual_layernorm_xnorm(ftx_dtype dt, int rows, int cols, const void* zx,
+                                                const float* xstats, int ntn, int bn,
+                                                const void* xgamma, const void* xbeta,
+                                                const void* a, const void* bias, const void* gamma,
+                                                const void* beta, void* y, hipStream_t s);
+
+// Folded weights of a LayerNorm (gamma, beta) followed by the projection w_t [N][K], bias b:
+// wf_t[n][k] = w_t[n][k] gamma[k] rounded, csum[n] = sum_k wf_t[n][k] (fp32), bias_f[n] =
+// b[n] + sum_k beta[k] w_t[n][k] (fp32).  16-bit data.
+hipError_t launch_fold_layernorm_weights(ftx_dtype dt, int N, int K, const void* w_t,
+                                         const void* gamma, const void* beta, const void* b,
+                                         void* wf_t, float* csum, float* bias_f, hipStream_t s);
+
 hipError_t launch_bias_gelu(ftx_dtype dt, int rows, int cols, const void* u, const void* bias,
                             void* g, hipStream_t s);
 
