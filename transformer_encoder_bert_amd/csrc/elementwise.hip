@@ -57,28 +57,49 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const TX* __restrict__ x
   const int nvec = cols / EV;
   const size_t base = (size_t)row * cols;
 
-  float2 xrs = make_float2(1.f, 0.f);
-  if constexpr (XN) xrs = merge_row_stats<kMaxStatTiles>(xn.stats + (size_t)row * xn.ntn, xn.ntn, xn.bn, cols, FTX_LN_EPSILON);
   float z[MAXV][EV];
   float sum = 0.f;
+  if constexpr (XN) {
+    // every load of the row first (the stats pairs with the vectors), then the merge
+    static_assert(EXACT, "the rebuilt residual takes the exact tilings");
+    float2 st[kMaxStatTiles];
 #pragma unroll
-  for (int v = 0; v < MAXV; ++v) {
-    const int vi = v * LPR + sub;
-    if (EXACT || vi < nvec) {
-      const xv_t xv = *(const xv_t*)(x + base + EV * vi);
-      const av_t av = *(const av_t*)(a + base + EV * vi);
-      const tv bv = *(const tv*)(bias + EV * vi);
-      tv xg = {}, xb = {};
-      if constexpr (XN) {
-        xg = *(const tv*)(xn.gamma + EV * vi);
-        xb = *(const tv*)(xn.beta + EV * vi);
-      }
+    for (int t = 0; t < kMaxStatTiles; ++t)
+      st[t] = t < xn.ntn ? xn.stats[(size_t)row * xn.ntn + t] : make_float2(0.f, 0.f);
+    xv_t xv[MAXV];
+    av_t av[MAXV];
+    tv bv[MAXV], xg[MAXV], xb[MAXV];
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v) {
+      const int vi = v * LPR + sub;
+      xv[v] = *(const xv_t*)(x + base + EV * vi);
+      av[v] = *(const av_t*)(a + base + EV * vi);
+      bv[v] = *(const tv*)(bias + EV * vi);
+      xg[v] = *(const tv*)(xn.gamma + EV * vi);
+      xb[v] = *(const tv*)(xn.beta + EV * vi);
+    }
+    const float2 xrs = merge_row_stats<kMaxStatTiles>(st, xn.ntn, xn.bn, cols, FTX_LN_EPSILON);
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v)
 #pragma unroll
       for (int e = 0; e < EV; ++e) {
-        float xe = to_f32(xv[e]);
-        if constexpr (XN) xe = fmaf(to_f32(xg[e]), fmaf(xe, xrs.x, xrs.y), to_f32(xb[e]));
-        z[v][e] = xe + to_f32(av[e]) + to_f32(bv[e]);
+        const float xe = fmaf(to_f32(xg[v][e]), fmaf(to_f32(xv[v][e]), xrs.x, xrs.y), to_f32(xb[v][e]));
+        z[v][e] = xe + to_f32(av[v][e]) + to_f32(bv[v][e]);
         sum += z[v][e];
+      }
+  } else {
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v) {
+      const int vi = v * LPR + sub;
+      if (EXACT || vi < nvec) {
+        const xv_t xv = *(const xv_t*)(x + base + EV * vi);
+        const av_t av = *(const av_t*)(a + base + EV * vi);
+        const tv bv = *(const tv*)(bias + EV * vi);
+#pragma unroll
+        for (int e = 0; e < EV; ++e) {
+          z[v][e] = to_f32(xv[e]) + to_f32(av[e]) + to_f32(bv[e]);
+          sum += z[v][e];
+        }
       }
     }
   }

@@ -607,14 +607,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // Stage one C^T tile (columns nt.., rows mt..) through this wave's LDS scratch `ws`
 // (32 x (32 + pad) elements of the output type) and store it as 16-byte vectors.
 // Wave-private: LDS accesses of one wave complete in order.
-// A normalising epilogue (is_norm_in) also takes the LDS row factors rsl[32] and column sums
-// csl[32] of this tile.
+// A normalising epilogue (is_norm_in) also takes this lane's row factors rs and the column
+// sums cs of its columns 8 q + 4 g.
 template <typename Epi>
 __device__ __forceinline__ void epilogue_tile(const Epi& epi, typename Epi::out_t* ws, int mt,
                                               int nt, int lane, const f32x16& acc,
                                               const typename Epi::b4 (&bq)[4],
-                                              const float2* rsl = nullptr,
-                                              const float* csl = nullptr) {
+                                              float2 rs = make_float2(1.f, 0.f),
+                                              const f32x4* cs = nullptr) {
   typedef typename Epi::out_t TO;
   typedef typename Epi::vec vec;
   constexpr int EV = 16 / sizeof(TO);       // elements per 16-byte vector
@@ -624,17 +624,14 @@ __device__ __forceinline__ void epilogue_tile(const Epi& epi, typename Epi::out_
   const int lr = lane % 32, g = lane / 32;
   const TileDst<TO> dst = epi.tile(mt, nt);
   typedef typename VecT<TO, 4>::type t4;
-  float2 rs = make_float2(1.f, 0.f);
-  if constexpr (is_norm_in<Epi>::value) rs = rsl[lr];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int nl = 8 * q + 4 * g;           // local column of register 4q
     t4 o;
     if constexpr (is_norm_in<Epi>::value) {
-      const f32x4 cs = *(const f32x4*)(csl + nl);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        o[e] = from_f32<TO>(epi.act(fmaf(rs.x, acc[4 * q + e], fmaf(rs.y, cs[e], to_f32(bq[q][e])))));
+        o[e] = from_f32<TO>(epi.act(fmaf(rs.x, acc[4 * q + e], fmaf(rs.y, cs[q][e], to_f32(bq[q][e])))));
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = from_f32<TO>(epi.act(acc[4 * q + e] + to_f32(bq[q][e])));
@@ -920,19 +917,28 @@ __device__ __forceinline__ void gemm_epilogue(const Epi& epi, char* smem, int m0
     static_assert(SCRATCH * sizeof(TO) * C::NW <= 2 * C::STAGE, "epilogue scratch");
     const int wm = wave / WN, wn = wave % WN;
     TO* ws = (TO*)smem + wave * SCRATCH;
+    // the normalising epilogue's row factors and column sums, read from LDS once per row
+    // tile and column tile of the wave
+    const int lr = lane % 32, g = lane / 32;
+    float2 rsv[TM];
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int i = 0; i < TM; ++i) {
+      rsv[i] = make_float2(1.f, 0.f);
+      if constexpr (is_norm_in<Epi>::value) rsv[i] = ((const float2*)pre)[(wm * TM + i) * 32 + lr];
+    }
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const float2* rsl = nullptr;
-        const float* csl = nullptr;
-        if constexpr (is_norm_in<Epi>::value) {
-          rsl = (const float2*)pre + (wm * TM + i) * 32;
-          csl = (const float*)(pre + C::BM * 8) + (wn * TN + j) * 32;
-        }
-        epilogue_tile(epi, ws, m0 + (wm * TM + i) * 32, n0 + (wn * TN + j) * 32, lane, acc[j][i],
-                      bq[j], rsl, csl);
+    for (int j = 0; j < TN; ++j) {
+      f32x4 csv[4] = {};
+      if constexpr (is_norm_in<Epi>::value) {
+        const float* csl = (const float*)(pre + C::BM * 8) + (wn * TN + j) * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) csv[q] = *(const f32x4*)(csl + 8 * q + 4 * g);
       }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        epilogue_tile(epi, ws, m0 + (wm * TM + i) * 32, n0 + (wn * TN + j) * 32, lane, acc[j][i],
+                      bq[j], rsv[i], csv);
+    }
   }
 }
 
