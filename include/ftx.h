@@ -170,7 +170,7 @@ const char *ftx_last_error(void);
  *     has at least 64 tiles (ceil(batch*S/256) * 3*hidden/192), else the separate kernels;
  *     2 = whenever the shape fits.  Needs FTX_OPT_FUSED_EPILOGUES = 1.
  *     Values outside 0..2 -> FTX_ERR_INVALID_ARG.
- *   FTX_OPT_FOLD_LAYERNORM (default 1): for fp16, hidden size 768 or 1024 and a batch at
+ *   FTX_OPT_FOLD_LAYERNORM (default 1): for fp16/bf16, hidden size 768 or 1024 and a batch at
  *     which the attention-output and FFN projections do not split K, the first LayerNorm of
  *     each layer is folded into the first FFN projection (its gamma into that projection's
  *     weights, its beta into the bias; the row statistics come from the attention-output

@@ -150,18 +150,28 @@ static hipError_t ln_launch(int rows, int cols, const void* x, const void* a, co
   return hipGetLastError();
 }
 
-// The folded-LayerNorm residual (16-bit, the exact tilings of the common hidden sizes only)
-template <typename T>
+// The folded-LayerNorm residual (16-bit, the exact tilings of the common hidden sizes only;
+// TX, TA: T or float)
+template <typename T, typename TX, typename TA>
 static hipError_t ln_xnorm_dispatch(int rows, int cols, const void* x, const void* a,
                                     const void* bias, const void* gamma, const void* beta,
                                     void* y, ResidualNorm<T> xn, hipStream_t s) {
   for (const void* p : {x, a, bias, gamma, beta, (const void*)y, (const void*)xn.gamma, (const void*)xn.beta})
     if (!p || ((uintptr_t)p & 15)) return hipErrorInvalidValue;
   switch (cols) {
-    case 768: return ln_launch<T, T, T, 8, 32, 3, true, true>(rows, cols, x, a, bias, gamma, beta, y, nullptr, s, xn);
-    case 1024: return ln_launch<T, T, T, 8, 32, 4, true, true>(rows, cols, x, a, bias, gamma, beta, y, nullptr, s, xn);
+    case 768: return ln_launch<T, TX, TA, 8, 32, 3, true, true>(rows, cols, x, a, bias, gamma, beta, y, nullptr, s, xn);
+    case 1024: return ln_launch<T, TX, TA, 8, 32, 4, true, true>(rows, cols, x, a, bias, gamma, beta, y, nullptr, s, xn);
     default: break;
   }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t ln_xnorm_types(bool x_f32, bool a_f32, int rows, int cols, const void* x,
+                                 const void* a, const void* bias, const void* gamma,
+                                 const void* beta, void* y, ResidualNorm<T> xn, hipStream_t s) {
+  if (x_f32 && a_f32) return ln_xnorm_dispatch<T, float, float>(rows, cols, x, a, bias, gamma, beta, y, xn, s);
+  if (!x_f32 && !a_f32) return ln_xnorm_dispatch<T, T, T>(rows, cols, x, a, bias, gamma, beta, y, xn, s);
   return hipErrorInvalidValue;
 }
 
@@ -216,19 +226,20 @@ hipError_t launch_bias_residual_layernorm(ftx_dtype dt, int rows, int cols, cons
 }
 
 hipError_t launch_bias_residual_layernorm_xnorm(ftx_dtype dt, int rows, int cols, const void* zx,
-                                                const float* xstats, int ntn, int bn,
+                                                bool zx_f32, const float* xstats, int ntn, int bn,
                                                 const void* xgamma, const void* xbeta,
-                                                const void* a, const void* bias, const void* gamma,
-                                                const void* beta, void* y, hipStream_t s) {
+                                                const void* a, bool a_f32, const void* bias,
+                                                const void* gamma, const void* beta, void* y,
+                                                hipStream_t s) {
   if (ntn < 1 || ntn > kMaxStatTiles || bn < 1 || (cols + bn - 1) / bn != ntn) return hipErrorInvalidValue;
   switch (dt) {
     case FTX_FP16: {
       const ResidualNorm<f16> xn{(const float2*)xstats, ntn, bn, (const f16*)xgamma, (const f16*)xbeta};
-      return ln_xnorm_dispatch<f16>(rows, cols, zx, a, bias, gamma, beta, y, xn, s);
+      return ln_xnorm_types<f16>(zx_f32, a_f32, rows, cols, zx, a, bias, gamma, beta, y, xn, s);
     }
     case FTX_BF16: {
       const ResidualNorm<bf16> xn{(const float2*)xstats, ntn, bn, (const bf16*)xgamma, (const bf16*)xbeta};
-      return ln_xnorm_dispatch<bf16>(rows, cols, zx, a, bias, gamma, beta, y, xn, s);
+      return ln_xnorm_types<bf16>(zx_f32, a_f32, rows, cols, zx, a, bias, gamma, beta, y, xn, s);
     }
     default: break;
   }

@@ -305,13 +305,14 @@ ftx_status enqueue_forward(ftx_encoder* e, const Workspace& ws, const void* inpu
     // by head inside the attention kernel instead (its K range is the merged-heads dimension):
     // one launch for the attention and the projection.
     const bool row_ln = H == 128 && (T + 63) / 64 >= 128;
-    // The first LayerNorm folded into the first FFN projection (fp16 at batches whose
+    // The first LayerNorm folded into the first FFN projection (16-bit data at batches whose
     // projections do not split K): LN1(z) W1 + b1 = r (z (gamma o W1)) + s colsum(gamma o W1)
     // + (b1 + beta W1) with the row's r = 1/sigma and s = -mean/sigma.  The attention-output
-    // projection stores Z1 = x + C Wo + bo and per-tile (mean, M2) of each row; the FFN-in
-    // projection merges the pairs and applies r, s in its epilogue; the second LayerNorm
-    // rebuilds its residual Y1 = LN1(Z1) from Z1 and the same pairs.  Four launches after
-    // the attention instead of five.
+    // projection stores Z1 = x + C Wo + bo (bf16: also in fp32) and per-tile (mean, M2) of
+    // each row; the FFN-in projection merges the pairs and applies r, s in its epilogue; the
+    // second LayerNorm rebuilds its residual Y1 = LN1(Z1) from Z1 (bf16: the fp32 copy, with
+    // the FFN-out branch in fp32 as in the unfolded path) and the same pairs.  Four launches
+    // after the attention instead of five.
     if (e->fold && e->fold_fits && e->fused && !row_ln) {
       if (!use_fused_attention(e)) {
         st = run_step(e, FTX_STEP_ATTENTION, s, [&] {
@@ -321,7 +322,7 @@ ftx_status enqueue_forward(ftx_encoder* e, const Workspace& ws, const void* inpu
       }
       st = run_step(e, FTX_STEP_ATTN_OUT_GEMM, s, [&] {
         return launch_linear_residual_stats(dt, T, H, H, ws.ctx, w.w_o_t, w.b_o, x, ws.y1,
-                                            ws.st1, e->ln1_ntn, s);
+                                            ws.y1f, ws.st1, e->ln1_ntn, s);
       });
       if (st != FTX_OK) return st;
       st = run_step(e, FTX_STEP_FFN1_GEMM, s, [&] {
@@ -330,13 +331,15 @@ ftx_status enqueue_forward(ftx_encoder* e, const Workspace& ws, const void* inpu
       });
       if (st != FTX_OK) return st;
       st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
-        return launch_linear(dt, T, H, F, ws.u, w.w2_t, nullptr, false, ws.abuf, s, false,
-                             ws.splitk, ws.splitk_elems);
+        return launch_linear(dt, T, H, F, ws.u, w.w2_t, nullptr, false, ws.abuf, s,
+                             ws.y1f != nullptr, ws.splitk, ws.splitk_elems);
       });
       if (st != FTX_OK) return st;
       st = run_step(e, FTX_STEP_LN2, s, [&] {
-        return launch_bias_residual_layernorm_xnorm(dt, T, H, ws.y1, ws.st1, e->ln1_ntn,
-                                                    e->ln1_bn, w.ln1_g, w.ln1_b, ws.abuf, w.b2,
+        const bool f32res = ws.y1f != nullptr;  // bf16: Z1 and the FFN-out branch in fp32
+        return launch_bias_residual_layernorm_xnorm(dt, T, H, f32res ? (const void*)ws.y1f : ws.y1,
+                                                    f32res, ws.st1, e->ln1_ntn, e->ln1_bn,
+                                                    w.ln1_g, w.ln1_b, ws.abuf, f32res, w.b2,
                                                     w.ln2_g, w.ln2_b, state, s);
       });
       if (st != FTX_OK) return st;
@@ -522,13 +525,13 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
     if (e->attn_out) e->splitk_need = std::max(e->splitk_need, per_head);
   }
   {
-    // the LayerNorm fold: fp16 (bf16 keeps the un-normalised residual in fp32), the hidden
-    // sizes the rebuilding LayerNorm tiles exactly, and unsplit projections on multi-wave
-    // tiles for the attention output, FFN-in and FFN-out
+    // the LayerNorm fold: 16-bit data, the hidden sizes the rebuilding LayerNorm tiles
+    // exactly, and unsplit projections on multi-wave tiles for the attention output, FFN-in
+    // and FFN-out
     int tm, tn, sp, tm1, tn1, sp1;
     plan_linear(dtype, e->T, e->H, e->H, e->dev.cus, false, &tm, &tn, &sp);
     plan_linear(dtype, e->T, e->F, e->H, e->dev.cus, false, &tm1, &tn1, &sp1);
-    e->fold_fits = dtype == FTX_FP16 && (e->H == 768 || e->H == 1024) && !e->attn_out &&
+    e->fold_fits = (dtype == FTX_FP16 || dtype == FTX_BF16) && (e->H == 768 || e->H == 1024) && !e->attn_out &&
                    sp == 1 && tm > 32 && sp1 == 1 && tm1 > 32 &&
                    linear_splits(dtype, e->T, e->H, e->H, (size_t)1 << 40, true) == 1 &&
                    linear_splits(dtype, e->T, e->H, e->F, (size_t)1 << 40, true) == 1;

@@ -262,11 +262,18 @@ template <typename T, typename TX, bool A_F32> struct EpiLinearLN {
 
 // Projection + bias + residual, with the statistics the LayerNorm after it needs, for a
 // LayerNorm folded into the next projection: z = x + a + bias is stored (rounded to the
-// storage type) and, for each row, the mean and the centred sum of squares of the fp32 z
-// over this tile's columns go to stats[row][tile column] -- the LayerNorm's own two-pass
-// statistics, taken per tile; a consumer merges the tiles' pairs (equal-count groups:
-// mean of means, sum of M2 plus the spread of the means).  Whole-tile epilogue: the wave
-// columns of a row meet in LDS.  Tiles up to 256 rows, two wave columns at most.
+// storage type, and in fp32 as well when zf is set) and, for each row, the mean and the
+// centred sum of squares of the fp32 z over this tile's columns go to stats[row][tile
+// column] -- the LayerNorm's own two-pass statistics, taken per tile; a consumer merges the
+// tiles' pairs (equal-count groups: mean of means, sum of M2 plus the spread of the means).
+// Whole-tile epilogue.  The residual tile comes into LDS by DMA (16-byte chunks,
+// row-contiguous; chunk c of tile row R at position c ^ (R & 7) of the row) while the
+// accumulators take the bias; each lane adds its elements of x from LDS in the accumulator
+// layout and writes z back over them in place (no other lane touches those bytes), and the
+// block then stores z from LDS as 16-byte row-contiguous chunks.  The wave columns of a row
+// meet in `red`, an LDS area of 2 x BM x 2 floats past the slab buffers (pre_bytes).  The
+// fp32 copy goes out through a per-wave LDS scratch, 32 x 32 tiles at a time.  16-bit data,
+// two wave columns at most.
 template <typename T> struct EpiLinearResStats {
   static constexpr bool kBlock = true;
   typedef T out_t;
@@ -274,44 +281,29 @@ template <typename T> struct EpiLinearResStats {
   const T* x;       // residual [M][N]
   const T* bias;    // [N]
   T* z;             // [M][N]
+  float* zf;        // [M][N] fp32 copy of z, or null
   float2* stats;    // [M][ntn]
   int M, N, ntn;
-  static constexpr size_t kLdsBytes = 2 * 256 * 2 * sizeof(float);  // [pass][row][wave column]
+  static constexpr size_t kLdsBytes = 0;  // the tile uses the slab buffers, `red` its own area
+  template <int BM, int BN> static constexpr int pre_bytes() { return 2 * BM * 2 * 4; }
   __device__ __forceinline__ b4 bias4(int n) const {
     b4 v = {};
     if (n < N) v = *(const b4*)(bias + n);
     return v;
   }
   template <int TM, int TN, int WN, int BM>
-  __device__ __forceinline__ void block(char* smem, int m0, int n0, int wave, int lane,
+  __device__ __forceinline__ void block(char* smem, float* red, int m0, int n0, int wave, int lane,
                                         const f32x16 (&acc)[TN][TM],
                                         const b4 (&bq)[TN][4]) const {
-    constexpr int BN = TN * 32 * WN;
-    if constexpr ((size_t)BM * BN * sizeof(T) + 2 * BM * 2 * sizeof(float) <= 2 * (BM + BN) * 128)
-      block_staged<TM, TN, WN, BM>(smem, m0, n0, wave, lane, acc, bq);
-    else
-      block_direct<TM, TN, WN>(smem, m0, n0, wave, lane, acc, bq);
-  }
-
-  // The residual tile x comes into LDS by DMA (16-byte chunks, row-contiguous; chunk c of
-  // tile row R at position c ^ (R & 7) of the row) while the accumulators take the bias; each
-  // lane adds its elements of x from LDS in the accumulator layout and writes z back over
-  // them in place (no other lane touches those bytes), and the block then stores z from LDS
-  // as 16-byte row-contiguous chunks.  The row statistics meet in LDS after the tile.  Needs
-  // the tile (BM x BN, 16-bit) plus 2 x BM x 2 floats within the two slab buffers.
-  template <int TM, int TN, int WN, int BM>
-  __device__ __forceinline__ void block_staged(char* smem, int m0, int n0, int wave, int lane,
-                                               const f32x16 (&acc)[TN][TM],
-                                               const b4 (&bq)[TN][4]) const {
     static_assert(sizeof(T) == 2 && WN <= 2, "16-bit tiles, two wave columns at most");
     constexpr int BN = TN * 32 * WN;
     constexpr int CPR = BN / 8;         // 16-byte chunks per tile row
     constexpr int NCH = BM * CPR;       // chunks in the tile
     static_assert(NCH % kWave == 0, "whole wave loads");
     constexpr int ROWB = BN * 2;        // LDS bytes per tile row
+    static_assert(BM * ROWB <= 2 * (BM + BN) * 128, "the tile fits the two slab buffers");
     const int nth = blockDim.x;
     const int wm = wave / WN, wn = wave % WN, lr = lane % 32, g = lane / 32;
-    float* red = (float*)(smem + BM * ROWB);  // [pass][BM rows][2 wave columns]
     const int cnt = min(BN, N - n0);
     const float inv = 1.0f / (float)cnt;
     // x rows m0 .. m0 + BM - 1 (rows past M and columns past N read as zero)
@@ -361,7 +353,7 @@ template <typename T> struct EpiLinearResStats {
       sum += __shfl_xor(sum, 32);
       if (g == 0) red[rl * 2 + wn] = sum;
     }
-    __syncthreads();  // LDS writes (not only the barrier) complete first
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int rl = (wm * TM + i) * 32 + lr;
@@ -386,7 +378,7 @@ template <typename T> struct EpiLinearResStats {
       sq += __shfl_xor(sq, 32);
       if (g == 0) red[2 * BM + rl * 2 + wn] = sq;
     }
-    __syncthreads();
+    __syncthreads();  // LDS writes (not only the barrier) complete first
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int rl = (wm * TM + i) * 32 + lr, row = m0 + rl;
@@ -401,86 +393,30 @@ template <typename T> struct EpiLinearResStats {
       if (m0 + R < M && col < N)
         *(vec*)(z + (size_t)(m0 + R) * N + col) = *(const vec*)(smem + R * ROWB + ((ch ^ (R & 7)) * 16));
     }
-  }
-
-  // The same with x read and z written straight from the accumulator layout (4 elements
-  // per lane and row): tiles too large to stage.
-  template <int TM, int TN, int WN>
-  __device__ __forceinline__ void block_direct(char* smem, int m0, int n0, int wave, int lane,
-                                               const f32x16 (&acc)[TN][TM],
-                                               const b4 (&bq)[TN][4]) const {
-    static_assert(WN <= 2 && TM * 32 <= 256, "tile");
-    constexpr int BN = TN * 32 * WN;
-    const int wm = wave / WN, wn = wave % WN, lr = lane % 32, g = lane / 32;
-    float* red = (float*)smem;  // [pass][256 rows][2]
-    const int cnt = min(BN, N - n0);
-    const float inv = 1.0f / (float)cnt;
-    float zv[TM][TN][16];
-    float mean[TM];
+    if (!zf) return;
+    // fp32 copy: each 32 x 32 tile of the wave through its own LDS scratch (32 rows of 36
+    // floats), then 8 lanes per 128-byte row segment
+    __syncthreads();  // every wave's reads of the tile above are done
+    float* ws = (float*)smem + wave * 32 * 36;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int rl = (wm * TM + i) * 32 + lr, row = m0 + rl;
-      float sum = 0.f;
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j) {
+        const int mt = m0 + (wm * TM + i) * 32, nt = n0 + (wn * TN + j) * 32;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int n = n0 + (wn * TN + j) * 32 + 8 * q + 4 * g;
-          const bool ok = row < M && n < N;
-          b4 xv = {};
-          if (ok) xv = *(const b4*)(x + (size_t)row * N + n);
+          f32x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float v = ok ? acc[j][i][4 * q + e] + to_f32(bq[j][q][e]) + to_f32(xv[e]) : 0.f;
-            zv[i][j][4 * q + e] = v;
-            sum += v;
-          }
+          for (int e = 0; e < 4; ++e) v[e] = zv[i][j][4 * q + e];
+          *(f32x4*)(ws + lr * 36 + 8 * q + 4 * g) = v;
         }
-      sum += __shfl_xor(sum, 32);
-      if (g == 0) red[rl * 2 + wn] = sum;
-    }
-    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int rl = (wm * TM + i) * 32 + lr;
-      mean[i] = (WN == 2 ? red[rl * 2] + red[rl * 2 + 1] : red[rl * 2]) * inv;
-      float sq = 0.f;
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + (wn * TN + j) * 32 + 8 * q + 4 * g;
-          if (n < N)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float d = zv[i][j][4 * q + e] - mean[i];
-              sq += d * d;
-            }
+        for (int p = 0; p < 4; ++p) {
+          const int r = p * 8 + lane / 8, cc = (lane % 8) * 4;
+          const f32x4 v = *(const f32x4*)(ws + r * 36 + cc);
+          if (mt + r < M && nt + cc < N) *(f32x4*)(zf + (size_t)(mt + r) * N + nt + cc) = v;
         }
-      sq += __shfl_xor(sq, 32);
-      if (g == 0) red[512 + rl * 2 + wn] = sq;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int rl = (wm * TM + i) * 32 + lr, row = m0 + rl;
-      if (row >= M) continue;
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + (wn * TN + j) * 32 + 8 * q + 4 * g;
-          if (n >= N) continue;
-          b4 o;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(zv[i][j][4 * q + e]);
-          *(b4*)(z + (size_t)row * N + n) = o;
-        }
-      if (wn == 0 && g == 0) {
-        const float m2 = WN == 2 ? red[512 + rl * 2] + red[512 + rl * 2 + 1] : red[512 + rl * 2];
-        stats[(size_t)row * ntn + n0 / BN] = make_float2(mean[i], m2);
       }
-    }
   }
 };
 
@@ -559,7 +495,8 @@ template <typename T, bool G> struct is_norm_in<EpiLinearNormIn<T, G>> { static 
 // LDS bytes an epilogue stages at the start of a BM x BN block (after the slab buffers), and
 // the registers that carry its loads across the prologue
 template <typename Epi, int BM, int BN> constexpr int epi_pre_bytes() {
-  if constexpr (is_norm_in<Epi>::value) return Epi::template pre_bytes<BM, BN>();
+  if constexpr (is_norm_in<Epi>::value || is_res_stats<Epi>::value)
+    return Epi::template pre_bytes<BM, BN>();
   else return 0;
 }
 struct NoPre {};
@@ -908,7 +845,7 @@ __device__ __forceinline__ void gemm_epilogue(const Epi& epi, char* smem, int m0
   if constexpr (Epi::kBlock) {
     static_assert(Epi::kLdsBytes <= 2 * C::STAGE, "block epilogue LDS");
     if constexpr (is_res_stats<Epi>::value)
-      epi.template block<TM, TN, WN, C::BM>(smem, m0, n0, wave, lane, acc, bq);
+      epi.template block<TM, TN, WN, C::BM>(smem, (float*)pre, m0, n0, wave, lane, acc, bq);
     else
       epi.template block<TM, TN, WN>(smem, m0, n0, wave, lane, acc, bq);
   } else {
@@ -958,7 +895,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
   constexpr int TM = C::TM, TN = C::TN, AQ = C::AQ, BQ = C::BQ, ROWB = C::ROWB;
   static_assert(NST >= 2 && NST <= 8, "slab stages");
   constexpr int PRE = epi_pre_bytes<Epi, BM, BN>();
-  static_assert(BM + BN <= C::NW * kWave || PRE == 0, "one staged row or column per thread");
+  static_assert(BM + BN <= C::NW * kWave || !is_norm_in<Epi>::value, "one staged row or column per thread");
   __shared__ __attribute__((aligned(1024))) char smem[NST * C::STAGE + PRE];
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -985,7 +922,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
     for (int q = 0; q < 4; ++q) bq[j][q] = epi.bias4(n0 + (wn * TN + j) * 32 + 8 * q + 4 * g);
   char* const pre = smem + NST * C::STAGE;
   [[maybe_unused]] typename PreOf<Epi>::type pre_regs;
-  if constexpr (PRE > 0) pre_regs = epi.template pre_load<BM, BN>(m0, n0, threadIdx.x);
+  if constexpr (is_norm_in<Epi>::value) pre_regs = epi.template pre_load<BM, BN>(m0, n0, threadIdx.x);
 
   const int kb = blockIdx.y * kchunk;
   const int kn = min(K - kb, kchunk);
@@ -1053,7 +990,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_kernel(const T* __restri
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p)
     if (p < nk) load_slab(p, p);
-  if constexpr (PRE > 0) epi.template pre_store<BM, BN>(pre_regs, pre, m0, threadIdx.x);
+  if constexpr (is_norm_in<Epi>::value) epi.template pre_store<BM, BN>(pre_regs, pre, m0, threadIdx.x);
   for (int k0 = 0; k0 < nk; k0 += NST) {
 #pragma unroll
     for (int u = 0; u < NST; ++u) {
@@ -1125,7 +1062,7 @@ __global__ __launch_bounds__(8 * kWave) void gemm_pp_kernel(const T* __restrict_
   // (one LDS object: a second one gives the compiler alias scopes under which it waits for
   // every slab load in flight before any LDS read)
   constexpr int PRE = epi_pre_bytes<Epi, BM, BN>();
-  static_assert(BM + BN <= 8 * kWave || PRE == 0, "one staged row or column per thread");
+  static_assert(BM + BN <= 8 * kWave || !is_norm_in<Epi>::value, "one staged row or column per thread");
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE + 16 + PRE];
   unsigned* const g1_reads_done = (unsigned*)(smem + 2 * C::STAGE);
   char* const pre = smem + 2 * C::STAGE + 16;
@@ -1202,7 +1139,7 @@ __global__ __launch_bounds__(8 * kWave) void gemm_pp_kernel(const T* __restrict_
   // prologue: slab 0 from every wave, group 1's share of slab 1 as well (after the epilogue's
   // staged loads, which the waits below then cover)
   [[maybe_unused]] typename PreOf<Epi>::type pre_regs;
-  if constexpr (PRE > 0) pre_regs = epi.template pre_load<BM, BN>(m0, n0, threadIdx.x);
+  if constexpr (is_norm_in<Epi>::value) pre_regs = epi.template pre_load<BM, BN>(m0, n0, threadIdx.x);
   if (nk > 0) load_slab(0, 0);
   if (grp == 1 && nk > 1) {
     load_slab(1, 1);
@@ -1210,7 +1147,7 @@ __global__ __launch_bounds__(8 * kWave) void gemm_pp_kernel(const T* __restrict_
   } else {
     wait_vmcnt<0>();
   }
-  if constexpr (PRE > 0) epi.template pre_store<BM, BN>(pre_regs, pre, m0, threadIdx.x);
+  if constexpr (is_norm_in<Epi>::value) epi.template pre_store<BM, BN>(pre_regs, pre, m0, threadIdx.x);
   barrier();
   if (grp == 1) barrier();
   for (int kt = 0; kt < nk; ++kt) {
@@ -1731,15 +1668,15 @@ static hipError_t gemm_launch_whole(int M, int N, int K, const void* a, const vo
 
 hipError_t launch_linear_residual_stats(ftx_dtype dt, int M, int N, int K, const void* a,
                                         const void* w_t, const void* bias, const void* x,
-                                        void* z, float* stats, int ntn, hipStream_t s) {
+                                        void* z, float* zf, float* stats, int ntn, hipStream_t s) {
   int tm, tn, sp;
   plan_linear(dt, M, N, K, device_info().cus, false, &tm, &tn, &sp);
   if (sp != 1 || ntn != (N + tn - 1) / tn || ntn > kMaxStatTiles || N % 8) return hipErrorInvalidValue;
   switch (dt) {
     case FTX_FP16: return gemm_launch_whole<f16>(M, N, K, a, w_t,
-        EpiLinearResStats<f16>{(const f16*)x, (const f16*)bias, (f16*)z, (float2*)stats, M, N, ntn}, s);
+        EpiLinearResStats<f16>{(const f16*)x, (const f16*)bias, (f16*)z, zf, (float2*)stats, M, N, ntn}, s);
     case FTX_BF16: return gemm_launch_whole<bf16>(M, N, K, a, w_t,
-        EpiLinearResStats<bf16>{(const bf16*)x, (const bf16*)bias, (bf16*)z, (float2*)stats, M, N, ntn}, s);
+        EpiLinearResStats<bf16>{(const bf16*)x, (const bf16*)bias, (bf16*)z, zf, (float2*)stats, M, N, ntn}, s);
     default: break;
   }
   return hipErrorInvalidValue;

@@ -142,13 +142,14 @@ hipError_t launch_splitk_bias_residual_layernorm(ftx_dtype dt, int rows, int col
                                                  float* yf, hipStream_t s);
 
 // LayerNorm folded into the projection after it (16-bit data).  The projection before it
-// stores z = x + a w_t + bias (rounded to the storage type) and, per row and per tile of
-// the planner's tile width tn, the mean and centred sum of squares of the fp32 z over the
-// tile's columns: stats[row][tile] as float2 pairs, ntn = ceil(N / tn) tiles.
-// hipErrorInvalidValue when the planner would split K or ntn does not match.
+// stores z = x + a w_t + bias (rounded to the storage type; zf non-null: also in fp32) and,
+// per row and per tile of the planner's tile width tn, the mean and centred sum of squares
+// of the fp32 z over the tile's columns: stats[row][tile] as float2 pairs, ntn =
+// ceil(N / tn) tiles.  hipErrorInvalidValue when the planner would split K, ntn does not
+// match or N is not a multiple of 8.
 hipError_t launch_linear_residual_stats(ftx_dtype dt, int M, int N, int K, const void* a,
                                         const void* w_t, const void* bias, const void* x,
-                                        void* z, float* stats, int ntn, hipStream_t s);
+                                        void* z, float* zf, float* stats, int ntn, hipStream_t s);
 
 // The projection of LN(z) through the folded weights w_t = (gamma o W)^T [N][K]:
 // c = act(r (z w_t) + s csum + bias) per row, with r, s from the row's ntn stats pairs
@@ -160,12 +161,14 @@ hipError_t launch_linear_norm_in(ftx_dtype dt, int M, int N, int K, const void* 
 
 // y = LN(x + a + bias) with x = LN_x(zx) rebuilt from zx and its stats (the folded
 // LayerNorm's gamma xgamma and beta xbeta): the layer's second LayerNorm after a folded
-// first.  cols 768 or 1024, every pointer 16-byte aligned; else hipErrorInvalidValue.
+// first.  zx and a both in the storage type, or both fp32 (zx_f32 = a_f32 = true).  cols
+// 768 or 1024, every pointer 16-byte aligned; else hipErrorInvalidValue.
 hipError_t launch_bias_residual_layernorm_xnorm(ftx_dtype dt, int rows, int cols, const void* zx,
-                                                const float* xstats, int ntn, int bn,
+                                                bool zx_f32, const float* xstats, int ntn, int bn,
                                                 const void* xgamma, const void* xbeta,
-                                                const void* a, const void* bias, const void* gamma,
-                                                const void* beta, void* y, hipStream_t s);
+                                                const void* a, bool a_f32, const void* bias,
+                                                const void* gamma, const void* beta, void* y,
+                                                hipStream_t s);
 
 // Folded weights of a LayerNorm (gamma, beta) followed by the projection w_t [N][K], bias b:
 // wf_t[n][k] = w_t[n][k] gamma[k] rounded, csum[n] = sum_k wf_t[n][k] (fp32), bias_f[n] =
