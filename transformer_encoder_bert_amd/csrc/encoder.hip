@@ -48,6 +48,10 @@ ftx_status ftx::check_shape(int B, int S, int nh, int d, bool any_len) {
 
 namespace {
 
+// Largest FFN intermediate (rows x F) the folded path keeps in one piece: two thirds of the
+// 256 MB last-level cache, which then also holds the chunk's other operands.
+constexpr size_t kFfnChunkBytes = (size_t)160 << 20;
+
 struct LayerW {
   void* w_qkv_t;  // [3H][H]
   void* b_qkv;    // [3H]
@@ -107,6 +111,7 @@ struct ftx_encoder {
   bool fold_fits = false;   // the first LayerNorm can fold into the first FFN projection
   int fold = 1;             // FTX_OPT_FOLD_LAYERNORM
   int ln1_bn = 0, ln1_ntn = 0;  // attention-output tile width and tiles per row (fold)
+  int ffn_rows = 0;             // rows per FFN chunk on the folded path (T: one chunk)
   int timing = 0;
   int graph_mode = 0;
   // graph of one whole forward, captured for the (input, seq_lens, output) it was made with
@@ -325,24 +330,34 @@ ftx_status enqueue_forward(ftx_encoder* e, const Workspace& ws, const void* inpu
                                             ws.y1f, ws.st1, e->ln1_ntn, s);
       });
       if (st != FTX_OK) return st;
-      st = run_step(e, FTX_STEP_FFN1_GEMM, s, [&] {
-        return launch_linear_norm_in(dt, T, F, H, ws.y1, w.w1g_t, w.b1f, w.c1, ws.st1,
-                                     e->ln1_ntn, e->ln1_bn, true, ws.u, s);
-      });
-      if (st != FTX_OK) return st;
-      st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
-        return launch_linear(dt, T, H, F, ws.u, w.w2_t, nullptr, false, ws.abuf, s,
-                             ws.y1f != nullptr, ws.splitk, ws.splitk_elems);
-      });
-      if (st != FTX_OK) return st;
-      st = run_step(e, FTX_STEP_LN2, s, [&] {
-        const bool f32res = ws.y1f != nullptr;  // bf16: Z1 and the FFN-out branch in fp32
-        return launch_bias_residual_layernorm_xnorm(dt, T, H, f32res ? (const void*)ws.y1f : ws.y1,
-                                                    f32res, ws.st1, e->ln1_ntn, e->ln1_bn,
-                                                    w.ln1_g, w.ln1_b, ws.abuf, f32res, w.b2,
-                                                    w.ln2_g, w.ln2_b, state, s);
-      });
-      if (st != FTX_OK) return st;
+      // FFN-in, FFN-out and the second LayerNorm in row chunks (ffn_rows rows; all rows but at
+      // the largest batches), so that a chunk's F-wide intermediate stays in the last-level
+      // cache between the two projections
+      const bool f32res = ws.y1f != nullptr;  // bf16: Z1 and the FFN-out branch in fp32
+      const size_t eh = f32res ? sizeof(float) : e->es;
+      for (int r0 = 0; r0 < T; r0 += e->ffn_rows) {
+        const int m = std::min(e->ffn_rows, T - r0);
+        const size_t ro = (size_t)r0 * H;
+        const float* st1 = ws.st1 + (size_t)r0 * e->ln1_ntn * 2;
+        st = run_step(e, FTX_STEP_FFN1_GEMM, s, [&] {
+          return launch_linear_norm_in(dt, m, F, H, (const char*)ws.y1 + ro * e->es, w.w1g_t, w.b1f,
+                                       w.c1, st1, e->ln1_ntn, e->ln1_bn, true, ws.u, s);
+        });
+        if (st != FTX_OK) return st;
+        st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
+          return launch_linear(dt, m, H, F, ws.u, w.w2_t, nullptr, false, (char*)ws.abuf + ro * eh,
+                               s, f32res, ws.splitk, ws.splitk_elems);
+        });
+        if (st != FTX_OK) return st;
+        st = run_step(e, FTX_STEP_LN2, s, [&] {
+          const void* zx = f32res ? (const void*)((const char*)ws.y1f + ro * eh) : (const char*)ws.y1 + ro * e->es;
+          return launch_bias_residual_layernorm_xnorm(dt, m, H, zx, f32res, st1, e->ln1_ntn, e->ln1_bn,
+                                                      w.ln1_g, w.ln1_b, (const char*)ws.abuf + ro * eh,
+                                                      f32res, w.b2, w.ln2_g, w.ln2_b,
+                                                      (char*)state + ro * e->es, s);
+        });
+        if (st != FTX_OK) return st;
+      }
       continue;
     }
     const int o_splits = linear_splits(dt, T, H, H, ws.splitk_elems, true);
@@ -538,6 +553,18 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
     if (e->fold_fits) {
       e->ln1_bn = tn;
       e->ln1_ntn = (e->H + tn - 1) / tn;
+      // FFN chunks: the F-wide intermediate of a chunk within kFfnChunkBytes, chunks of whole
+      // 256-row tiles, each still planned unsplit
+      e->ffn_rows = e->T;
+      const size_t u_bytes = (size_t)e->T * e->F * e->es;
+      if (u_bytes > kFfnChunkBytes) {
+        const int n = (int)((u_bytes + kFfnChunkBytes - 1) / kFfnChunkBytes);
+        const int rows = ((e->T + n - 1) / n + 255) / 256 * 256;
+        int tm2, tn2, sp2;
+        plan_linear(dtype, rows, e->F, e->H, e->dev.cus, false, &tm2, &tn2, &sp2);
+        if (sp2 == 1 && tm2 > 32 && linear_splits(dtype, rows, e->H, e->F, (size_t)1 << 40, true) == 1)
+          e->ffn_rows = rows;
+      }
     }
   }
   // weights: per layer 3H*H + 3H + H*H + H + 2H + F*H + F + H*F + H + 2H elements (plus a
