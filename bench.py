@@ -156,6 +156,10 @@ def classify_dispatches(names):
             st = "attention"
         elif "layernorm_kernel" in n:
             st = "ln1" if prev in ("attn_out_gemm", "attention") else "ln2"
+        elif gemm and "EpiLinearResStats" in n:
+            st = "attn_out_gemm"  # with the first LayerNorm folded into FFN-in
+        elif gemm and "EpiLinearNormIn" in n:
+            st = "ffn1_gemm"
         elif gemm and "EpiLinear" in n:
             m = re.search(r"EpiLinearI\w+?Lb([01])E", n)
             gelu = m is not None and m.group(1) == "1"
@@ -201,11 +205,15 @@ KERNEL_ROLES = (
     ("splitk_reduce", "split-K reduction + the projection's epilogue"),
     ("EpiQKVAttn", "Q/K/V projection with the attention in its epilogue"),
     ("EpiQKV", "Q/K/V (or Q-only, K/V-only) projection with bias + head split"),
+    ("EpiLinearResStats", "attention-output projection + bias + residual, with per-tile row statistics (LayerNorm 1 folded)"),
+    ("EpiLinearNormIn", "FFN-in on the un-normalised rows, LayerNorm 1 applied in the epilogue, + bias + GELU"),
+    ("fold_ln_weights", "LayerNorm weight folding (set_weights, not in the forward)"),
     ("EpiLinearIDF16_Lb1", "projection with bias + GELU (FFN-in)"),
     ("EpiLinearIDF16bLb1", "projection with bias + GELU (FFN-in)"),
     ("EpiLinear", "projection (attention output, FFN-out)"),
     ("EpiPartial", "split-K partial products"),
     ("attention", "attention (scores, masked softmax, context)"),
+    ("ELb1ELb1EEEvPKT0_", "bias + residual + LayerNorm (LayerNorm 2, residual rebuilt from the folded LayerNorm 1)"),
     ("layernorm", "bias + residual + LayerNorm"),
     ("transpose", "weight repacking (set_weights, not in the forward)"),
 )

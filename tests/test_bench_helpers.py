@@ -28,6 +28,27 @@ def test_separate_attention_dispatches():
         "qkv_gemm", "attention", "attn_out_gemm", "ln1", "ffn1_gemm", "ffn2_gemm", "ln2"]
 
 
+# the same layer with the first LayerNorm folded into FFN-in
+RES_STATS = "_ZN3ftx14gemm_pp_kernelIDF16_Li256ELi192ENS_17EpiLinearResStatsIDF16_EEEEvPKT_S5_iiiiiT2_"
+NORM_IN = "_ZN3ftx14gemm_pp_kernelIDF16_Li256ELi256ENS_15EpiLinearNormInIDF16_Lb1EEEEEvPKT_S5_iiiiiT2_"
+LN_XN = ("_ZN3ftx16layernorm_kernelIDF16_DF16_DF16_Li8ELi32ELi3ELb1ELb1EEEvPKT0_PKT1_PKT_S9_S9_PS7_"
+         "PfiiNS_12ResidualNormIS7_EE")
+
+
+def test_folded_layer_dispatches():
+    layer = [QKV_ATTN, RES_STATS, NORM_IN, LINEAR_PP, LN_XN]
+    assert bench.classify_dispatches(layer * 2) == [
+        "qkv_attention", "attn_out_gemm", "ffn1_gemm", "ffn2_gemm", "ln2"] * 2
+    # the FFN block in two row chunks
+    chunked = [QKV_ATTN, RES_STATS, NORM_IN, LINEAR_PP, LN_XN, NORM_IN, LINEAR_PP, LN_XN]
+    assert bench.classify_dispatches(chunked) == [
+        "qkv_attention", "attn_out_gemm", "ffn1_gemm", "ffn2_gemm", "ln2", "ffn1_gemm",
+        "ffn2_gemm", "ln2"]
+    roles = [next((v for k, v in bench.KERNEL_ROLES if k in n), "") for n in (RES_STATS, NORM_IN, LN_XN, LN)]
+    assert "statistics" in roles[0] and "FFN-in" in roles[1] and "rebuilt" in roles[2]
+    assert roles[3] == "bias + residual + LayerNorm"
+
+
 def test_unknown_kernels_are_not_classified():
     assert bench.classify_dispatches(["copy_kernel", LN]) == [None, "ln2"]
 
