@@ -88,25 +88,55 @@ def parse():
     return p.parse_args()
 
 
-def step_work(shape, step: str):
+def launches_per_layer(counts, step) -> int:
+    """Launches of `step` per layer, from launch counts per step class (the Q/K/V step runs once
+    per layer; the FFN block may run in row chunks, each chunk a launch per step)."""
+    ref = next((counts[k] for k in ("qkv_attention", "qkv_gemm") if counts.get(k)), 0)
+    if not ref or step not in ("ffn1_gemm", "ffn2_gemm", "ln2", "bias_gelu"):
+        return 1
+    return max(1, round(counts.get(step, 0) / ref))
+
+
+def fold_stats_bytes(shape) -> int:
+    """Bytes of the per-tile row statistics of the folded LayerNorm: one (mean, M2) float pair
+    per row and attention-output tile column (the planner's tile width at 256 CUs)."""
+    from transformer_encoder_bert_amd import ftx
+    tn = ftx.ftx_plan_linear(shape.dtype, shape.tokens, shape.hidden, shape.hidden, 256)[1]
+    return shape.tokens * -(-shape.hidden // tn) * 8
+
+
+def step_work(shape, step: str, folded: bool = False):
     """Algorithmic work of ONE launch of a step class: (flops, bytes).
-    Bytes are the minimum HBM traffic (each operand read once, result written once)."""
+    Bytes are the minimum HBM traffic (each operand read once, result written once), with
+    the fp32 tensors of the bf16 mode (the attention-output and FFN-out results, the fp32 copy
+    of Y1) at 4 bytes.  folded: the first LayerNorm folded into FFN-in (the attention-output
+    projection also reads the residual and writes Z1 and its row statistics, the second
+    LayerNorm reads them back)."""
     T, S, H, F, B = shape.tokens, shape.seq_len, shape.hidden, shape.ffn, shape.batch
     e = 4 if shape.dtype == "fp32" else 2
+    f32res = shape.dtype == "bf16"
+    ea = 4 if f32res else e  # the attention-output and FFN-out results
     if step == "qkv_gemm":
         return 2.0 * T * 3 * H * H, (T * H + 3 * H * H + 3 * T * H) * e
     if step == "attn_out_gemm":
-        return 2.0 * T * H * H, (T * H + H * H + T * H) * e
+        if folded:
+            return 2.0 * T * H * H, ((3 * T * H + H * H) * e + (T * H * 4 if f32res else 0)
+                                     + fold_stats_bytes(shape))
+        return 2.0 * T * H * H, (T * H + H * H) * e + T * H * ea
     if step == "ffn1_gemm":
-        return 2.0 * T * F * H, (T * H + F * H + T * F) * e
+        return 2.0 * T * F * H, ((T * H + F * H + T * F) * e
+                                 + (fold_stats_bytes(shape) + 2 * F * 4 if folded else 0))
     if step == "ffn2_gemm":
-        return 2.0 * T * H * F, (T * F + H * F + T * H) * e
+        return 2.0 * T * H * F, (T * F + H * F) * e + T * H * ea
     if step == "attention":
         return 4.0 * B * S * S * H, 4 * T * H * e
     if step == "qkv_attention":  # Q, K and V stay on chip
         return 2.0 * T * 3 * H * H + 4.0 * B * S * S * H, (T * H + 3 * H * H + T * H) * e
-    if step in ("ln1", "ln2"):
-        return 0.0, 3 * T * H * e
+    if step == "ln1":  # bf16: the fp32 branch in, Y1 out in bf16 and fp32
+        return 0.0, (T * H * (2 * e + 8) if f32res else 3 * T * H * e)
+    if step == "ln2":  # bf16: Y1 (or Z1) and the branch in fp32
+        return 0.0, ((T * H * (8 + e) if f32res else 3 * T * H * e)
+                     + (fold_stats_bytes(shape) if folded else 0))
     if step == "bias_gelu":
         return 0.0, 2 * T * F * e
     if step == "bias_qkv_split":
@@ -326,12 +356,16 @@ def summarize_rocprof(args):
              "| step | launches | avg us | algorithmic MB | fetched MB | written MB | traffic / algorithmic | "
              "algorithmic TFLOP/s | frac of peak | MFMA busy % | algorithmic GB/s |",
              "|---|---|---|---|---|---|---|---|---|---|---|"]
+    folded = "EpiLinearResStats" in sym.get("attn_out_gemm", "")
+    per_layer = {k: len(v) for k, v in dur.items()}
     for st in ("qkv_attention", "qkv_gemm", "bias_qkv_split", "attention", "attn_out_gemm", "ln1", "ffn1_gemm",
                "bias_gelu", "ffn2_gemm", "ln2"):
         if st not in dur:
             continue
         avg = sum(dur[st]) / len(dur[st])
-        fl, by = step_work(shape, st)
+        fl, by = step_work(shape, st, folded)
+        ch = launches_per_layer(per_layer, st)  # the FFN block in row chunks: work per launch
+        fl, by = fl / ch, by / ch
         c = counters.get(st, {})
         fetch = sum(c.get("FETCH_SIZE", [0])) / max(1, len(c.get("FETCH_SIZE", [])))
         write = sum(c.get("WRITE_SIZE", [0])) / max(1, len(c.get("WRITE_SIZE", [])))
@@ -753,11 +787,14 @@ def main():
         times = enc.kernel_times()
         enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 0)
         kernels = {}
+        counts = {name: cnt for name, (ms, cnt) in times.items()}
         for name, (ms, cnt) in times.items():
             if cnt == 0:
                 continue
             avg = ms / cnt
-            fl, by = step_work(shape, name)
+            fl, by = step_work(shape, name, ln_folded)
+            ch = launches_per_layer(counts, name)
+            fl, by = fl / ch, by / ch
             kernels[name] = {"avg_us": 1e3 * avg, "launches": cnt, "share": 0.0,
                              "tflops": fl / (avg * 1e-3) / 1e12 if fl else None,
                              "gbs_algorithmic": by / (avg * 1e-3) / 1e9}
@@ -765,7 +802,9 @@ def main():
         for v in kernels.values():
             v["share"] = v["avg_us"] * v["launches"] / total
         dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
-        fl, by = step_work(shape, dom)
+        fl, by = step_work(shape, dom, ln_folded)
+        ch = launches_per_layer(counts, dom)
+        fl, by = fl / ch, by / ch
         avg_s = kernels[dom]["avg_us"] * 1e-6
         if fl > 0 and dom != "attention":
             achieved, peak, unit, bound = fl / avg_s / 1e12, PEAK_MFMA_TFLOPS[dt], "TFLOP/s", "mfma"

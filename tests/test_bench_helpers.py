@@ -76,3 +76,23 @@ def test_profile_commands_run_the_program_directly():
         assert not ("--pmc" in c and "--kernel-trace" in c)
     assert any("SQ_VALU_MFMA_BUSY_CYCLES" in c for c in prof)
     assert all("--batch 64" in c for c in cmds)
+
+
+def test_launches_per_layer_and_folded_work():
+    """The FFN block in row chunks launches its steps once per chunk: the work of one launch
+    is the layer's work over the chunks.  The folded attention-output step also moves the
+    residual, Z1 and the statistics; bf16 moves its fp32 tensors at 4 bytes."""
+    counts = {"qkv_attention": 48, "attn_out_gemm": 48, "ffn1_gemm": 96, "ffn2_gemm": 96, "ln2": 96}
+    assert bench.launches_per_layer(counts, "ffn1_gemm") == 2
+    assert bench.launches_per_layer(counts, "ln2") == 2
+    assert bench.launches_per_layer(counts, "attn_out_gemm") == 1
+    assert bench.launches_per_layer({"ffn1_gemm": 12}, "ffn1_gemm") == 1
+    import synthetic_inputs as si
+    sh = si.Shape(512, 32, 12, 64, 12, "fp16")
+    T, H = sh.tokens, sh.hidden
+    fl, plain = bench.step_work(sh, "attn_out_gemm")
+    fl2, folded = bench.step_work(sh, "attn_out_gemm", folded=True)
+    assert fl == fl2 == 2.0 * T * H * H
+    assert folded - plain == T * H * 2 + bench.fold_stats_bytes(sh)  # the residual in, the pairs out
+    bf = si.Shape(32, 512, 16, 64, 24, "bf16")
+    assert bench.step_work(bf, "ln1")[1] == bf.tokens * bf.hidden * (2 * 2 + 8)
