@@ -75,6 +75,35 @@ def test_static_workspace_matches_forward_on_two_calls():
         enc.close()
 
 
+def test_static_workspace_with_the_folded_layernorm():
+    """Shapes where the first LayerNorm folds into FFN-in (2048 rows, hidden 768 fp16 and
+    hidden 1024 bf16): the per-tile row statistics and Z1 live in the scratch too.  Two calls
+    in a row, the second on a different handle; each equals ftx_forward bitwise and meets the
+    oracle's stack bar."""
+    cases = [(si.Shape(64, 32, 12, 64, 1, "fp16"), 911, (1, 32)),
+             (si.Shape(16, 128, 16, 64, 1, "bf16"), 912, (1, 128))]
+    handles = [_handle(sh, seed, lr) for sh, seed, lr in cases]
+    outs = []
+    for (sh, _, _), (c, layers, enc) in zip(cases, handles):
+        x, lens = to_dev(c.x, sh.dtype), dev_lens(c.lens)
+        out = torch.full_like(x, float("nan"))
+        enc.forward_static_workspace(x, lens, out)
+        outs.append(out)
+    torch.cuda.synchronize()
+    for (sh, _, _), (c, layers, enc), got in zip(cases, handles, outs):
+        x, lens = to_dev(c.x, sh.dtype), dev_lens(c.lens)
+        enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)
+        ref = enc.forward(x, lens)
+        t = enc.kernel_times()
+        enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 0)
+        assert t["ln1"][1] == 0, f"{sh}: the LayerNorm did not fold"
+        assert torch.equal(got, ref), f"{sh}: static workspace differs from ftx_forward"
+        oref = oracle.encoder(c.x, layers, c.lens, sh.head_num)
+        print(sh, assert_within(to_f64(got), oref, *_bar(sh.dtype), f"{sh} vs oracle"))
+    for _, _, enc in handles:
+        enc.close()
+
+
 def test_static_workspace_refuses_a_larger_forward():
     """A handle whose workspace exceeds the static scratch is refused before anything is
     enqueued: BERT-base fp16 at 256 sequences of 32 needs about 120 MiB."""
