@@ -26,7 +26,10 @@
  * that FTX_BF16 keeps what enters a LayerNorm un-normalised in fp32 -- the residual Y1 (the
  * first LayerNorm's output, added back before the second) and the attention-output and
  * FFN-output projections -- because bf16's rounding of those (up to 7.8e-3 at |v| in
- * [2, 4)) reaches the layer output almost unattenuated.
+ * [2, 4)) reaches the layer output almost unattenuated.  With the first LayerNorm folded
+ * (FTX_OPT_FOLD_LAYERNORM) its un-normalised input Z1 takes Y1's place: stored in the 16-bit
+ * format as the FFN-in operand (and, for FTX_BF16, in fp32 as the second LayerNorm's
+ * residual), with its row statistics in fp32.
  *
  * Conventions.
  *  - All tensors are row-major.  All tensor pointers are DEVICE pointers on the device
@@ -177,6 +180,8 @@ const char *ftx_last_error(void);
  *     projection's epilogue), and the second LayerNorm rebuilds its residual from the same
  *     statistics: one launch per layer fewer (no FTX_STEP_LN1).  Same result up to rounding
  *     order.  0 = the LayerNorm runs as its own step.  Needs FTX_OPT_FUSED_EPILOGUES = 1.
+ *     When the FFN intermediate (batch*S x 4*hidden) exceeds 160 MB the folded path runs
+ *     FFN-in, FFN-out and the second LayerNorm in row chunks, one launch each per chunk.
  * Unknown option -> FTX_ERR_INVALID_ARG. */
 typedef enum {
   FTX_OPT_FUSED_EPILOGUES = 0,
@@ -192,9 +197,11 @@ typedef enum {
   FTX_STEP_QKV_GEMM = 0,        /* Q/K/V projection (with bias + head split when fused) */
   FTX_STEP_BIAS_QKV_SPLIT = 1,  /* bias + head split as its own kernel */
   FTX_STEP_ATTENTION = 2,       /* scores, masked softmax, context: one fused kernel */
-  FTX_STEP_ATTN_OUT_GEMM = 3,   /* attention-output projection */
+  FTX_STEP_ATTN_OUT_GEMM = 3,   /* attention-output projection (folded LN1: + bias, residual,
+                                   row statistics) */
   FTX_STEP_LN1 = 4,             /* bias + residual + LayerNorm after attention */
-  FTX_STEP_FFN1_GEMM = 5,       /* first FFN projection (with bias + GELU when fused) */
+  FTX_STEP_FFN1_GEMM = 5,       /* first FFN projection (with bias + GELU when fused; folded
+                                   LN1 applied in its epilogue) */
   FTX_STEP_BIAS_GELU = 6,       /* bias + GELU as its own kernel */
   FTX_STEP_FFN2_GEMM = 7,       /* second FFN projection */
   FTX_STEP_LN2 = 8,             /* bias + residual + LayerNorm after the FFN */
