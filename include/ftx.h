@@ -149,9 +149,10 @@ const char *ftx_last_error(void);
 /* ---------------------------------------------------------------------------------
  * Options of a handle.
  *   FTX_OPT_FUSED_EPILOGUES (default 1): 1 = bias+QKV split and bias+GELU run inside the
- *     projection kernels' epilogues (7 launches per layer); 0 = they run as standalone
- *     element-wise kernels after plain projections (9 launches per layer).  Same result
- *     up to rounding order.
+ *     projection kernels' epilogues; 0 = they run as standalone element-wise kernels after
+ *     plain projections (two launches per layer more: 9 instead of 7 with the attention as
+ *     its own kernel and neither LayerNorm folded; the fused attention and the LayerNorm
+ *     fold need 1 and take a layer down to 5).  Same result up to rounding order.
  *   FTX_OPT_KERNEL_TIMING (default 0): 1 = every forward records a HIP event pair around
  *     each launch, on the forward's stream, and accumulates per-step durations that
  *     ftx_kernel_times() returns.
