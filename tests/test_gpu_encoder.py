@@ -367,7 +367,8 @@ def test_ragged_sequence_lengths(shape, with_lens):
 
 @pytest.mark.parametrize("workload,batch,seq", [("bert_base_fp16_s32", 8, None),
                                                 ("bert_base_fp16_s128_varlen", 2, None),
-                                                ("bert_base_fp16_s32", 3, 100)])
+                                                ("bert_base_fp16_s32", 3, 100),
+                                                ("bert_base_fp16_s32", 64, None)])  # folded LN
 def test_graph_mode_replays_match_eager(workload, batch, seq):
     """FTX_OPT_GRAPH: every replay equals the eager forward bitwise, with eager work on the
     same stream between replays; new buffers trigger a new capture."""
