@@ -405,6 +405,29 @@ def test_graph_mode_replays_match_eager(workload, batch, seq):
     del junk
 
 
+def test_fold_option_under_graph_replay():
+    """Switching FTX_OPT_FOLD_LAYERNORM while graph replay is on drops the captured forward:
+    each replay equals the eager forward of the path the option selects, bit for bit."""
+    c, layers = _case("bert_base_fp16_s32", 64, "random_affine")
+    enc = _encoder(c.shape, layers)
+    x, lens = to_dev(c.x, "fp16"), dev_lens(c.lens)
+    folded = enc.forward(x, lens).clone()
+    enc.set_option(ftx.FTX_OPT_FOLD_LAYERNORM, 0)
+    plain = enc.forward(x, lens).clone()
+    assert not torch.equal(folded, plain)  # the two paths round differently
+    enc.set_option(ftx.FTX_OPT_FOLD_LAYERNORM, 1)
+    enc.set_option(ftx.FTX_OPT_GRAPH, 1)
+    out = torch.empty_like(folded)
+    for fold, ref in ((1, folded), (0, plain), (1, folded)):
+        enc.set_option(ftx.FTX_OPT_FOLD_LAYERNORM, fold)
+        for _ in range(2):
+            out.fill_(float("nan"))
+            enc.forward(x, lens, out)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), f"fold={fold}"
+    enc.close()
+
+
 def test_torch_operator_matches_the_oracle_and_the_c_abi():
     """torch.ops.ftx.encoder_forward (and the nn.Module around it) against the fp64 oracle at
     the stack bar, on padded lengths, and bitwise equal to ftx_forward."""
