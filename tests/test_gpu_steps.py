@@ -68,6 +68,9 @@ LINEAR_SHAPES = [
     (16384, 768, 3072),  # 256x192 tiles (BERT-base FFN-out at batch 512)
     (16416, 768, 3072),  # 256x256 tiles with a ragged M tail
     (4000, 4040, 2048),  # 256x256 tiles with ragged M and N tails
+    # 128x128 tiles with no more blocks than CUs and 12 slabs or more: three LDS stages
+    (4096, 768, 3072),   # BERT-base FFN-out at 4096 rows (192 tiles)
+    (4000, 776, 1576),   # ragged M, N and K tails (224 tiles)
     # 64x64 tiles with 12 slabs or more keep two slabs in flight (three LDS stages)
     (2048, 768, 768),    # BERT-base attention output at batch 64 (12 slabs)
     (2048, 768, 3072),   # BERT-base FFN-out at batch 64

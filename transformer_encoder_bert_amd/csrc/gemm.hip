@@ -1490,12 +1490,28 @@ constexpr int kPingPongMinSlabs = 12;
 // batch 64 (2048 x 768 x 3072) alone 24.8 -> 20.6 us.
 constexpr int kSmallTileDeepSlabs = 12;
 
+// A 128x128 grid with no more blocks than the GPU has CUs runs one block per CU whatever its
+// LDS, so from 12 slabs it takes three stages (96 KB) instead of two (64 KB, which would let
+// two blocks share a CU).  Measured on whole forwards against two stages (same box):
+// BERT-base S32 B128 1.203 -> 1.129 ms and S64 B64 1.232 -> 1.147 (4096 rows: the
+// attention-output and FFN-out projections on 192 tiles).  With more tiles than CUs three
+// stages lose (6144 rows 1.82 -> 2.03 ms, 8192 rows 2.19 -> 2.33): a second round of blocks
+// replaces the second block per CU.
+
 template <typename T, int BM, int BN, int WM, int WN, typename Epi>
 static void gemm_kernel_launch(dim3 grid, int kchunk, int M, int N, int K, const void* a,
                                const void* w_t, Epi epi, int xcds, hipStream_t s) {
   constexpr int BK = GemmCfg<T, BM, BN, WM, WN>::BK;
   if constexpr (BM == 64 && BN == 64) {
     if ((kchunk + BK - 1) / BK >= kSmallTileDeepSlabs) {
+      gemm_kernel<T, BM, BN, WM, WN, Epi, 3><<<grid, WM * WN * kWave, 0, s>>>(
+          (const T*)a, (const T*)w_t, M, N, K, kchunk, xcds, epi);
+      return;
+    }
+  }
+  if constexpr (BM == 128 && BN == 128) {
+    if ((kchunk + BK - 1) / BK >= kSmallTileDeepSlabs &&
+        (int64_t)grid.x * grid.y <= device_info().cus) {
       gemm_kernel<T, BM, BN, WM, WN, Epi, 3><<<grid, WM * WN * kWave, 0, s>>>(
           (const T*)a, (const T*)w_t, M, N, K, kchunk, xcds, epi);
       return;
