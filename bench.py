@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--no-fold-layernorm", action="store_true",
                    help="the first LayerNorm of each layer as its own kernel (not folded into "
                         "the FFN-in projection)")
+    p.add_argument("--no-prefetch-weights", action="store_true",
+                   help="never read W2 into the last-level cache ahead of the second FFN projection")
     p.add_argument("--graph", action="store_true", help="replay the forward as one HIP graph")
     p.add_argument("--fused-attention", type=int, default=1, choices=(0, 1, 2),
                    help="projection + attention in one kernel: 0 never, 1 from 256 tokens and "
@@ -141,6 +143,8 @@ def step_work(shape, step: str, folded: bool = False):
         return 0.0, 2 * T * F * e
     if step == "bias_qkv_split":
         return 0.0, 2 * 3 * T * H * e
+    if step == "weight_prefetch":  # W2 read once, nothing written
+        return 0.0, H * F * e
     raise KeyError(step)
 
 
@@ -203,6 +207,8 @@ def classify_dispatches(names):
             st = "bias_gelu"
         elif "bias_qkv_split_kernel" in n:
             st = "bias_qkv_split"
+        elif "prefetch16_kernel" in n:
+            st = "weight_prefetch"
         steps.append(st)
         if st is not None:
             prev = st
@@ -246,6 +252,7 @@ KERNEL_ROLES = (
     ("ELb1ELb1EEEvPKT0_", "bias + residual + LayerNorm (LayerNorm 2, residual rebuilt from the folded LayerNorm 1)"),
     ("layernorm", "bias + residual + LayerNorm"),
     ("transpose", "weight repacking (set_weights, not in the forward)"),
+    ("prefetch16_kernel", "read of the FFN-out weights into the last-level cache"),
 )
 
 
@@ -359,7 +366,7 @@ def summarize_rocprof(args):
     folded = "EpiLinearResStats" in sym.get("attn_out_gemm", "")
     per_layer = {k: len(v) for k, v in dur.items()}
     for st in ("qkv_attention", "qkv_gemm", "bias_qkv_split", "attention", "attn_out_gemm", "ln1", "ffn1_gemm",
-               "bias_gelu", "ffn2_gemm", "ln2"):
+               "bias_gelu", "weight_prefetch", "ffn2_gemm", "ln2"):
         if st not in dur:
             continue
         avg = sum(dur[st]) / len(dur[st])
@@ -699,6 +706,8 @@ def main():
     enc.set_option(ftx.FTX_OPT_FUSED_ATTENTION, args.fused_attention)
     if args.no_fold_layernorm:
         enc.set_option(ftx.FTX_OPT_FOLD_LAYERNORM, 0)
+    if args.no_prefetch_weights:
+        enc.set_option(ftx.FTX_OPT_PREFETCH_WEIGHTS, 0)
     if args.graph:
         enc.set_option(ftx.FTX_OPT_GRAPH, 1)
     x = up(case.x)
@@ -726,6 +735,7 @@ def main():
     attn_fused = counts["qkv_attention"][1] > 0
     # (hidden 128 also has no LayerNorm-1 launch: it runs in the projection's epilogue)
     ln_folded = counts["ln1"][1] == 0 and shape.hidden in (768, 1024)
+    w2_prefetch = counts["weight_prefetch"][1] > 0
     enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 0)
     torch.cuda.synchronize()
 
@@ -756,6 +766,7 @@ def main():
                    "epilogues": "standalone" if args.unfused else "fused",
                    "attention": "in the Q/K/V projection's epilogue" if attn_fused else "own kernel",
                    "layernorm1": "folded into the FFN-in projection" if ln_folded else "own kernel",
+                   "w2_prefetch": w2_prefetch,
                    "launch": "hip graph" if args.graph else "stream"},
         "tflops": tflops, "frac_mfma_peak": tflops / PEAK_MFMA_TFLOPS[dt],
         "gpu_event_ms_per_step": gpu_ms / args.steps,

@@ -183,13 +183,21 @@ const char *ftx_last_error(void);
  *     order.  0 = the LayerNorm runs as its own step.  Needs FTX_OPT_FUSED_EPILOGUES = 1.
  *     When the FFN intermediate (batch*S x 4*hidden) exceeds 160 MB the folded path runs
  *     FFN-in, FFN-out and the second LayerNorm in row chunks, one launch each per chunk.
+ *   FTX_OPT_PREFETCH_WEIGHTS (default 1): on the folded path, a kernel that only reads the
+ *     layer's second FFN weight matrix (FTX_STEP_PREFETCH) runs just before the second FFN
+ *     projection, so that the projection finds W2 in the last-level cache instead of HBM.
+ *     1 = where that projection runs on 128 x 128 tiles with more tiles than the GPU has CUs
+ *     (BERT-base from 6144 to 10240 rows, BERT-large at 8192); 2 = before every second FFN
+ *     projection of the folded path; 0 = never.  Writes nothing: the result is the same
+ *     bit for bit.  Values outside 0..2 -> FTX_ERR_INVALID_ARG.
  * Unknown option -> FTX_ERR_INVALID_ARG. */
 typedef enum {
   FTX_OPT_FUSED_EPILOGUES = 0,
   FTX_OPT_KERNEL_TIMING = 1,
   FTX_OPT_GRAPH = 2,
   FTX_OPT_FUSED_ATTENTION = 3,
-  FTX_OPT_FOLD_LAYERNORM = 4
+  FTX_OPT_FOLD_LAYERNORM = 4,
+  FTX_OPT_PREFETCH_WEIGHTS = 5
 } ftx_option;
 ftx_status ftx_set_option(ftx_encoder *enc, ftx_option option, int value);
 
@@ -207,7 +215,8 @@ typedef enum {
   FTX_STEP_FFN2_GEMM = 7,       /* second FFN projection */
   FTX_STEP_LN2 = 8,             /* bias + residual + LayerNorm after the FFN */
   FTX_STEP_QKV_ATTENTION = 9,   /* Q/K/V projection with the attention in its epilogue */
-  FTX_NUM_STEPS = 10
+  FTX_STEP_PREFETCH = 10,       /* read of W2 into the last-level cache (FTX_OPT_PREFETCH_WEIGHTS) */
+  FTX_NUM_STEPS = 11
 } ftx_step;
 
 /* Synchronize the events recorded since the last call and return, per step class, the

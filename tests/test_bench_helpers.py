@@ -49,6 +49,24 @@ def test_folded_layer_dispatches():
     assert roles[3] == "bias + residual + LayerNorm"
 
 
+PREFETCH = "_ZN3ftx17prefetch16_kernelEPK15HIP_vector_typeIjLj4EEm"
+LINEAR_128 = "_ZN3ftx11gemm_kernelIDF16_Li128ELi128ELi2ELi2ENS_9EpiLinearIDF16_Lb0EDF16_EELi2EEEvPKT_S5_iiiiiT4_"
+
+
+def test_prefetch_before_ffn_out():
+    """The W2 read ahead of the second FFN projection is its own step class, and the plain
+    projection after it is still FFN-out; the read moves W2's bytes once."""
+    layer = [QKV_ATTN, RES_STATS, NORM_IN, PREFETCH, LINEAR_128, LN_XN]
+    assert bench.classify_dispatches(layer * 2) == [
+        "qkv_attention", "attn_out_gemm", "ffn1_gemm", "weight_prefetch", "ffn2_gemm", "ln2"] * 2
+    role = next((v for k, v in bench.KERNEL_ROLES if k in PREFETCH), "")
+    assert "last-level cache" in role
+    import synthetic_inputs as si
+    sh = si.Shape(256, 32, 12, 64, 12, "fp16")
+    assert bench.step_work(sh, "weight_prefetch") == (0.0, sh.hidden * sh.ffn * 2)
+    assert bench.launches_per_layer({"qkv_attention": 12, "weight_prefetch": 12}, "weight_prefetch") == 1
+
+
 def test_unknown_kernels_are_not_classified():
     assert bench.classify_dispatches(["copy_kernel", LN]) == [None, "ln2"]
 

@@ -344,6 +344,39 @@ def test_layernorm_fold(shape):
           f"{shape} fold, new weights")
 
 
+@pytest.mark.parametrize("shape,auto", [
+    (si.Shape(256, 32, 12, 64, 2, "fp16"), True),   # 8192 rows: FFN-out on 384 128 x 128 tiles
+    (si.Shape(64, 32, 12, 64, 1, "bf16"), False),   # 2048 rows: 64 x 64 tiles, no prefetch
+    (si.Shape(20, 200, 12, 64, 1, "fp16"), False),  # 4480 rows (ragged lengths): 210 tiles
+])
+def test_weight_prefetch(shape, auto):
+    """FTX_OPT_PREFETCH_WEIGHTS: a kernel that reads W2 ahead of the second FFN projection on
+    the folded path.  Automatic (1): one launch per layer where that projection runs on
+    128 x 128 tiles with more tiles than CUs, else none; forced (2): one per layer; never (0):
+    none.  It writes nothing, so the three outputs are equal bit for bit, and they match the
+    oracle at the stack bar.  Modes outside 0..2 are refused."""
+    c = si.custom_case(shape, 57 + shape.batch, lens_range=(1, shape.seq_len), params="random_affine")
+    layers = list(c.layers())
+    enc = _encoder(shape, layers)
+    enc.set_option(ftx.FTX_OPT_KERNEL_TIMING, 1)
+    x, lens = to_dev(c.x, shape.dtype), dev_lens(c.lens)
+    outs = {}
+    for mode in (1, 2, 0):
+        enc.set_option(ftx.FTX_OPT_PREFETCH_WEIGHTS, mode)
+        outs[mode] = enc.forward(x, lens).clone()
+        t = enc.kernel_times()
+        assert t["ln1"][1] == 0, "the prefetch runs on the folded path"
+        want = shape.num_layers if mode == 2 or (mode == 1 and auto) else 0
+        assert t["weight_prefetch"][1] == want, (mode, t["weight_prefetch"])
+    with pytest.raises(ftx.FtxError):
+        enc.set_option(ftx.FTX_OPT_PREFETCH_WEIGHTS, 3)
+    enc.close()
+    assert torch.equal(outs[1], outs[0]) and torch.equal(outs[2], outs[0])
+    ref = oracle.encoder(c.x, layers, c.lens, shape.head_num)
+    tol = stack_tol(shape.dtype) if shape.num_layers > 1 else layer_tol(shape.dtype)
+    print("prefetch", check(to_f64(outs[1]), ref, shape.dtype, tol, f"{shape} prefetch"))
+
+
 @pytest.mark.parametrize("shape,with_lens", [
     (si.Shape(3, 100, 4, 32, 2, "fp16"), True),
     (si.Shape(2, 100, 4, 32, 2, "fp16"), False),   # no seq_lens: keys limited to 100

@@ -596,4 +596,33 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Read n16 16-byte vectors at p and discard them, so that the lines sit in the last-level
+// cache (and the reading XCD's L2) when the next kernel reads them.  Four independent loads
+// per thread per iteration; the XOR of everything read goes to an empty asm statement, which
+// keeps the loads without any store.
+__global__ __launch_bounds__(256) void prefetch16_kernel(const uint4* __restrict__ p, size_t n16) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  unsigned acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^
+           (d.x ^ d.y ^ d.z ^ d.w);
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = p[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  asm volatile("" ::"v"(acc));
+}
+
+hipError_t launch_prefetch(const void* p, size_t bytes, hipStream_t s) {
+  if (((uintptr_t)p & 15u) || (bytes & 15u)) return hipErrorInvalidValue;
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>((n16 + 255) / 256, 512);
+  prefetch16_kernel<<<(unsigned)blocks, 256, 0, s>>>((const uint4*)p, n16);
+  return hipGetLastError();
+}
+
 }  // namespace ftx

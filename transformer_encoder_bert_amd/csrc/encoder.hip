@@ -114,6 +114,8 @@ struct ftx_encoder {
   int fold = 1;             // FTX_OPT_FOLD_LAYERNORM
   int ln1_bn = 0, ln1_ntn = 0;  // attention-output tile width and tiles per row (fold)
   int ffn_rows = 0;             // rows per FFN chunk on the folded path (T: one chunk)
+  bool w2_prefetch_fits = false;  // FFN-out on 128x128 tiles, more tiles than CUs (folded path)
+  int prefetch = 1;             // FTX_OPT_PREFETCH_WEIGHTS
   int timing = 0;
   int graph_mode = 0;
   // graph of one whole forward, captured for the (input, seq_lens, output) it was made with
@@ -346,6 +348,12 @@ ftx_status enqueue_forward(ftx_encoder* e, const Workspace& ws, const void* inpu
                                        w.c1, st1, e->ln1_ntn, e->ln1_bn, true, ws.u, s);
         });
         if (st != FTX_OK) return st;
+        if (r0 == 0 && (e->prefetch == 2 || (e->prefetch == 1 && e->w2_prefetch_fits))) {
+          st = run_step(e, FTX_STEP_PREFETCH, s, [&] {
+            return launch_prefetch(w.w2_t, (size_t)H * F * e->es, s);
+          });
+          if (st != FTX_OK) return st;
+        }
         st = run_step(e, FTX_STEP_FFN2_GEMM, s, [&] {
           return launch_linear(dt, m, H, F, ws.u, w.w2_t, nullptr, false, (char*)ws.abuf + ro * eh,
                                s, f32res, ws.splitk, ws.splitk_elems);
@@ -566,6 +574,20 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
         plan_linear(dtype, rows, e->F, e->H, e->dev.cus, false, &tm2, &tn2, &sp2);
         if (sp2 == 1 && tm2 > 32 && linear_splits(dtype, rows, e->H, e->F, (size_t)1 << 40, true) == 1)
           e->ffn_rows = rows;
+      }
+      // The second FFN projection reads its weights cold: every layer's weights and
+      // activations pass through the last-level cache between two reads of a layer's W2.  On
+      // 128x128 tiles with more tiles than CUs (two blocks per CU, all resident at once, each
+      // with one slab in flight) the cold W2 slows it most: BERT-base 8192 rows 59 -> 44 us
+      // with W2 read just before it by a separate 5 us kernel; whole forwards (same box) S32
+      // B256 2.19 -> 2.05 ms, S128 B64 2.24 -> 2.10, BERT-large S128 B64 5.99 -> 5.79, S32
+      // B192 1.82 -> 1.79.  With fewer tiles (4096 rows) or 256-row tiles it loses by about
+      // the prefetch's own time.
+      {
+        int tm3, tn3, sp3;
+        plan_linear(dtype, e->ffn_rows, e->H, e->F, e->dev.cus, true, &tm3, &tn3, &sp3);
+        const int64_t tiles3 = (int64_t)((e->ffn_rows + tm3 - 1) / tm3) * ((e->H + tn3 - 1) / tn3);
+        e->w2_prefetch_fits = tm3 == 128 && tn3 == 128 && sp3 == 1 && tiles3 > e->dev.cus;
       }
     }
   }
@@ -801,6 +823,11 @@ ftx_status ftx_set_option(ftx_encoder* e, ftx_option option, int value) {
     case FTX_OPT_FOLD_LAYERNORM:
       if (e->fold != (value ? 1 : 0)) drop_graph(e);
       e->fold = value ? 1 : 0;
+      return FTX_OK;
+    case FTX_OPT_PREFETCH_WEIGHTS:
+      if (value < 0 || value > 2) return fail(FTX_ERR_INVALID_ARG, "weight prefetch mode is 0, 1 or 2");
+      if (e->prefetch != value) drop_graph(e);
+      e->prefetch = value;
       return FTX_OK;
   }
   return fail(FTX_ERR_INVALID_ARG, "unknown option");

@@ -186,6 +186,10 @@ hipError_t launch_transpose(ftx_dtype dt, int rows, int cols, const void* in, vo
 // Zero `bytes` bytes at p (16-byte aligned, a multiple of 16) with a kernel.
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
+// Read `bytes` bytes at p (16-byte aligned, a multiple of 16) and discard them: a prefetch
+// into the last-level cache ahead of a kernel that reads them.  Writes nothing.
+hipError_t launch_prefetch(const void* p, size_t bytes, hipStream_t s);
+
 // Largest LayerNorm row the library handles (4-element vectors, <= 16 per lane of a wave).
 constexpr int kMaxLayerNormCols = 4096;
 // largest inner dimension K of a projection: a 256-row panel of K elements stays below 2^31

@@ -23,8 +23,9 @@ FTX_OK, FTX_ERR_INVALID_ARG, FTX_ERR_UNSUPPORTED, FTX_ERR_OUT_OF_MEMORY, FTX_ERR
     FTX_ERR_NOT_READY = range(6)
 FTX_OPT_FUSED_EPILOGUES, FTX_OPT_KERNEL_TIMING, FTX_OPT_GRAPH, FTX_OPT_FUSED_ATTENTION = 0, 1, 2, 3
 FTX_OPT_FOLD_LAYERNORM = 4
+FTX_OPT_PREFETCH_WEIGHTS = 5
 STEP_NAMES = ("qkv_gemm", "bias_qkv_split", "attention", "attn_out_gemm", "ln1", "ffn1_gemm",
-              "bias_gelu", "ffn2_gemm", "ln2", "qkv_attention")
+              "bias_gelu", "ffn2_gemm", "ln2", "qkv_attention", "weight_prefetch")
 FTX_NUM_STEPS = len(STEP_NAMES)
 
 WEIGHT_FIELDS = ("w_q", "b_q", "w_k", "b_k", "w_v", "b_v", "w_o", "b_o", "ln1_gamma", "ln1_beta",
