@@ -188,8 +188,9 @@ const char *ftx_last_error(void);
  *     projection, so that the projection finds W2 in the last-level cache instead of HBM.
  *     1 = where that projection runs on 128 x 128 tiles with more tiles than the GPU has CUs
  *     (BERT-base from 6144 to 10240 rows, BERT-large at 8192); 2 = before every second FFN
- *     projection of the folded path; 0 = never.  Writes nothing: the result is the same
- *     bit for bit.  Values outside 0..2 -> FTX_ERR_INVALID_ARG.
+ *     projection of the folded path; 0 = never.  One launch per layer more where it runs.
+ *     Writes nothing: the result is the same bit for bit.  Values outside 0..2 ->
+ *     FTX_ERR_INVALID_ARG.
  * Unknown option -> FTX_ERR_INVALID_ARG. */
 typedef enum {
   FTX_OPT_FUSED_EPILOGUES = 0,
