@@ -307,6 +307,8 @@ def test_hidden_128_layernorm_in_the_projection(shape):
     si.Shape(16, 128, 16, 64, 2, "bf16"),  # bf16 (Z1 also in fp32), hidden 1024, 64 x 64 tiles
     si.Shape(10, 512, 16, 64, 1, "bf16"),  # S = 512, 5120 rows: 128 x 128 attention-output tiles
     si.Shape(32, 512, 16, 64, 1, "fp16"),  # fp16 hidden 1024 at 16384 rows: 256 x 256 tiles
+    si.Shape(128, 32, 12, 64, 1, "fp16"),  # 4096 rows: 128 x 96 attention-output tiles, 8 per row
+    si.Shape(32, 128, 12, 64, 1, "bf16"),  # the same tiling in bf16, ragged lengths
 ])
 def test_layernorm_fold(shape):
     """FTX_OPT_FOLD_LAYERNORM: the first LayerNorm folded into the FFN-in projection (gamma in

@@ -68,9 +68,11 @@ LINEAR_SHAPES = [
     (16384, 768, 3072),  # 256x192 tiles (BERT-base FFN-out at batch 512)
     (16416, 768, 3072),  # 256x256 tiles with a ragged M tail
     (4000, 4040, 2048),  # 256x256 tiles with ragged M and N tails
-    # 128x128 tiles with no more blocks than CUs and 12 slabs or more: three LDS stages
-    (4096, 768, 3072),   # BERT-base FFN-out at 4096 rows (192 tiles)
-    (4000, 776, 1576),   # ragged M, N and K tails (224 tiles)
+    # 128x128 tiles with no more blocks than CUs and 12 slabs or more: three LDS stages;
+    # where N is a multiple of 96 and that grid also fits the CUs, 128x96 tiles
+    (4096, 768, 3072),   # BERT-base FFN-out at 4096 rows (256 tiles of 128 x 96)
+    (3000, 768, 768),    # 128 x 96 with a ragged M tail (192 tiles)
+    (4000, 776, 1576),   # ragged M, N and K tails (224 tiles of 128 x 128)
     # 64x64 tiles with 12 slabs or more keep two slabs in flight (three LDS stages)
     (2048, 768, 768),    # BERT-base attention output at batch 64 (12 slabs)
     (2048, 768, 3072),   # BERT-base FFN-out at batch 64
@@ -110,7 +112,7 @@ def test_linear(dtype, M, N, K, epi):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("B,S,n,d", [(1, 32, 4, 32), (2, 64, 3, 64), (3, 128, 2, 32), (1, 512, 2, 64),
-                                     (64, 128, 12, 64)])
+                                     (64, 128, 12, 64), (32, 32, 12, 64)])
 def test_qkv_projection(dtype, B, S, n, d):
     H = n * d
     rng = np.random.default_rng(B + S + n + d)

@@ -267,7 +267,8 @@ template <typename T, typename TX, bool A_F32> struct EpiLinearLN {
 // column] -- the LayerNorm's own two-pass statistics, taken per tile; a consumer merges the
 // tiles' pairs (equal-count groups: mean of means, sum of M2 plus the spread of the means).
 // Whole-tile epilogue.  The residual tile comes into LDS by DMA (16-byte chunks,
-// row-contiguous; chunk c of tile row R at position c ^ (R & 7) of the row) while the
+// row-contiguous; chunk c of tile row R at position c ^ (R & SW) of the row, SW = 7 for rows of
+// a multiple of 8 chunks, 3 for 96-column tiles, 12 chunks) while the
 // accumulators take the bias; each lane adds its elements of x from LDS in the accumulator
 // layout and writes z back over them in place (no other lane touches those bytes), and the
 // block then stores z from LDS as 16-byte row-contiguous chunks.  The wave columns of a row
@@ -301,6 +302,8 @@ template <typename T> struct EpiLinearResStats {
     constexpr int NCH = BM * CPR;       // chunks in the tile
     static_assert(NCH % kWave == 0, "whole wave loads");
     constexpr int ROWB = BN * 2;        // LDS bytes per tile row
+    constexpr int SW = CPR % 8 == 0 ? 7 : 3;  // the chunk swizzle stays inside the row
+    static_assert(CPR % 4 == 0, "rows of a multiple of 4 chunks");
     static_assert(BM * ROWB <= 2 * (BM + BN) * 128, "the tile fits the two slab buffers");
     const int nth = blockDim.x;
     const int wm = wave / WN, wn = wave % WN, lr = lane % 32, g = lane / 32;
@@ -311,7 +314,7 @@ template <typename T> struct EpiLinearResStats {
         (void*)(x + (size_t)m0 * N), (short)0, min(BM, M - m0) * N * (int)sizeof(T), 0x00020000);
     for (int c0 = wave * kWave; c0 < NCH; c0 += nth) {
       const int c = c0 + lane, R = c / CPR, pos = c % CPR;
-      const int col = n0 + ((pos ^ (R & 7)) * 8);
+      const int col = n0 + ((pos ^ (R & SW)) * 8);
       const int voff = col < N ? (R * N + col) * (int)sizeof(T) : 0x7ffffff0;
       lds_dma16(rx, voff, smem + c0 * 16);
     }
@@ -329,7 +332,7 @@ template <typename T> struct EpiLinearResStats {
     // LDS byte address of this lane's 4 elements (row rl, columns 8 q + 4 g of column tile j)
     auto lds_at = [&](int rl, int j, int q) {
       const int chunk = (wn * TN + j) * 4 + q;
-      return rl * ROWB + ((chunk ^ (rl & 7)) * 16) + g * 8;
+      return rl * ROWB + ((chunk ^ (rl & SW)) * 16) + g * 8;
     };
     float mean[TM];
 #pragma unroll
@@ -391,7 +394,7 @@ template <typename T> struct EpiLinearResStats {
     for (int c = threadIdx.x; c < NCH; c += nth) {
       const int R = c / CPR, ch = c % CPR, col = n0 + ch * 8;
       if (m0 + R < M && col < N)
-        *(vec*)(z + (size_t)(m0 + R) * N + col) = *(const vec*)(smem + R * ROWB + ((ch ^ (R & 7)) * 16));
+        *(vec*)(z + (size_t)(m0 + R) * N + col) = *(const vec*)(smem + R * ROWB + ((ch ^ (R & SW)) * 16));
     }
     if (!zf) return;
     // fp32 copy: each 32 x 32 tile of the wave through its own LDS scratch (32 rows of 36
@@ -1344,18 +1347,21 @@ static int small_gemm_tm(int M, int N, int K, int cus) {
 // wins, so small batches get small tiles that still spread over every CU.  fp32 (twice the
 // register footprint per element) uses the table without its two largest tiles.
 
-enum TileCfg { TILE_256x256, TILE_256x192, TILE_256x128, TILE_128x128, TILE_64x64, TILE_32x32, TILE_COUNT };
-static const int kTileM[TILE_COUNT] = {256, 256, 256, 128, 64, 32};
-static const int kTileN[TILE_COUNT] = {256, 192, 128, 128, 64, 32};
+// TILE_128x96 (4 waves of 32 x 96) is not a candidate of the cost model: plan_gemm takes it in
+// place of 128x128 where both grids fit one block per CU (below).
+enum TileCfg { TILE_256x256, TILE_256x192, TILE_256x128, TILE_128x128, TILE_64x64, TILE_32x32,
+               TILE_128x96, TILE_COUNT };
+static const int kTileM[TILE_COUNT] = {256, 256, 256, 128, 64, 32, 128};
+static const int kTileN[TILE_COUNT] = {256, 192, 128, 128, 64, 32, 96};
 
 static TileCfg choose_tile(int M, int N, bool wide, int cus) {
   struct Cand { int bm, bn, per_cu; double eff; };
-  static const Cand cand[TILE_COUNT] = {{256, 256, 1, 0.37}, {256, 192, 1, 0.36}, {256, 128, 1, 0.34},
-                                        {128, 128, 2, 0.36}, {64, 64, 4, 0.25},   {32, 32, 8, 0.18}};
+  static const Cand cand[TILE_32x32 + 1] = {{256, 256, 1, 0.37}, {256, 192, 1, 0.36}, {256, 128, 1, 0.34},
+                                            {128, 128, 2, 0.36}, {64, 64, 4, 0.25},   {32, 32, 8, 0.18}};
   const long kCUs = std::max(cus, 1);
   int best = TILE_32x32;
   double best_t = 1e300;
-  for (int c = wide ? 0 : TILE_256x128; c < TILE_COUNT; ++c) {
+  for (int c = wide ? 0 : TILE_256x128; c <= TILE_32x32; ++c) {
     const Cand& x = cand[c];
     const long tiles = (long)((M + x.bm - 1) / x.bm) * ((N + x.bn - 1) / x.bn);
     const long rounds = (tiles + (long)kCUs * x.per_cu - 1) / ((long)kCUs * x.per_cu);
@@ -1401,6 +1407,7 @@ struct GemmPlan {
 };
 
 constexpr size_t kMaxPartialBytes = 16u << 20;
+constexpr int kSmallTileDeepSlabsPlan = 12;  // = kSmallTileDeepSlabs
 // A split finished by a reduction launch also pays that launch and the second read of the
 // partials: above 4 MiB of partials it lost in whole forwards (BERT-base B8, FFN-in at 256
 // rows cut in three, 9 MiB: 0.551 against 0.511 ms unsplit; S64 B4 0.563 against 0.523;
@@ -1415,7 +1422,7 @@ static GemmPlan plan_gemm(int M, int N, int K, int elem_bytes, bool sums_partial
   const int bk = 128 / elem_bytes;
   const long tiles = (long)((M + kTileM[p.cfg] - 1) / kTileM[p.cfg]) * ((N + kTileN[p.cfg] - 1) / kTileN[p.cfg]);
   const int nk = (K + bk - 1) / bk;
-  static const int waves[TILE_COUNT] = {8, 8, 8, 4, 4, 1};
+  static const int waves[TILE_COUNT] = {8, 8, 8, 4, 4, 1, 4};
   const bool fill_simds = sums_partials && N >= 256 && tiles * waves[p.cfg] < kSIMDs;
   if ((tiles < kCUs || fill_simds) && nk >= 4) {
     const size_t max_partial_bytes = sums_partials ? kMaxPartialBytes : kMaxReducedPartialBytes;
@@ -1429,6 +1436,14 @@ static GemmPlan plan_gemm(int M, int N, int K, int elem_bytes, bool sums_partial
       p.splits = (K + p.kchunk - 1) / p.kchunk;
     }
   }
+  // An unsplit 16-bit 128x128 grid within one block per CU, N a multiple of 96: 128x96 tiles
+  // cover the same rows with more blocks, still one per CU, each on three LDS stages from 12
+  // slabs.  BERT-base 4096 x 768 x 3072 alone: 27.9 -> 25.7 us (192 -> 256 tiles);
+  // 4096 x 768 x 768: 9.8 -> 8.9 us.
+  if (p.cfg == TILE_128x128 && p.splits == 1 && elem_bytes == 2 && N % 96 == 0 &&
+      nk >= kSmallTileDeepSlabsPlan && tiles <= kCUs &&
+      (long)((M + 127) / 128) * (N / 96) <= kCUs)
+    p.cfg = TILE_128x96;
   return p;
 }
 
@@ -1509,7 +1524,7 @@ static void gemm_kernel_launch(dim3 grid, int kchunk, int M, int N, int K, const
       return;
     }
   }
-  if constexpr (BM == 128 && BN == 128) {
+  if constexpr (BM == 128 && (BN == 128 || BN == 96)) {
     if ((kchunk + BK - 1) / BK >= kSmallTileDeepSlabs &&
         (int64_t)grid.x * grid.y <= device_info().cus) {
       gemm_kernel<T, BM, BN, WM, WN, Epi, 3><<<grid, WM * WN * kWave, 0, s>>>(
@@ -1597,6 +1612,9 @@ static hipError_t gemm_launch(int M, int N, int K, const void* a, const void* w_
     case TILE_128x128: return gemm_launch_cfg<T, 128, 128, 2, 2>(M, N, K, a, w_t, epi, plan, ws, di.xcds, s, reduce);
     case TILE_64x64: return gemm_launch_cfg<T, 64, 64, 2, 2>(M, N, K, a, w_t, epi, plan, ws, di.xcds, s, reduce);
     case TILE_32x32: return gemm_launch_cfg<T, 32, 32, 1, 1>(M, N, K, a, w_t, epi, plan, ws, di.xcds, s, reduce);
+    case TILE_128x96:
+      if constexpr (sizeof(T) == 2) return gemm_launch_cfg<T, 128, 96, 4, 1>(M, N, K, a, w_t, epi, plan, ws, di.xcds, s, reduce);
+      break;
     default: break;
   }
   return hipErrorInvalidValue;
@@ -1676,6 +1694,7 @@ static hipError_t gemm_launch_whole(int M, int N, int K, const void* a, const vo
     case TILE_256x192: if constexpr (sizeof(T) == 2) return run(TileShape<256, 192, 4, 2>{}); break;
     case TILE_256x128: return run(TileShape<256, 128, 4, 2>{});
     case TILE_128x128: return run(TileShape<128, 128, 2, 2>{});
+    case TILE_128x96: if constexpr (sizeof(T) == 2) return run(TileShape<128, 96, 4, 1>{}); break;
     case TILE_64x64: return run(TileShape<64, 64, 2, 2>{});
     default: break;  // 32x32 tiles: one wave holds a row's columns alone, not supported here
   }
