@@ -186,8 +186,8 @@ const char *ftx_last_error(void);
  *   FTX_OPT_PREFETCH_WEIGHTS (default 1): on the folded path, a kernel that only reads the
  *     layer's second FFN weight matrix (FTX_STEP_PREFETCH) runs just before the second FFN
  *     projection, so that the projection finds W2 in the last-level cache instead of HBM.
- *     1 = where that projection runs on 128 x 128 tiles with more tiles than the GPU has CUs
- *     (BERT-base from 6144 to 10240 rows, BERT-large at 8192); 2 = before every second FFN
+ *     1 = where that projection runs on 128-row tiles, at least 1.5 tiles per CU (BERT-base
+ *     from 6144 to 10240 rows, BERT-large at 8192); 2 = before every second FFN
  *     projection of the folded path; 0 = never.  One launch per layer more where it runs.
  *     Writes nothing: the result is the same bit for bit.  Values outside 0..2 ->
  *     FTX_ERR_INVALID_ARG.

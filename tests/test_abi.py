@@ -166,10 +166,12 @@ PLANS_256_CUS = [
     (("fp16", 16384, 768, 768, True), (256, 192, 1)),
     (("fp16", 16384, 3072, 768, False), (256, 256, 1)),
     (("fp16", 16384, 768, 3072, True), (256, 192, 1)),
-    (("fp16", 2048, 2304, 768, False), (128, 128, 1)),
+    (("fp16", 2048, 2304, 768, False), (128, 96, 1)),   # 384 tiles of 128 x 96, two per CU
     (("fp16", 2048, 768, 3072, True), (64, 64, 1)),
     (("fp16", 4096, 768, 3072, True), (128, 96, 1)),   # 256 tiles of 128 x 96, one per CU
     (("fp16", 4096, 768, 768, True), (128, 96, 1)),
+    (("fp16", 8192, 768, 3072, True), (128, 96, 1)),
+    (("fp16", 10240, 768, 3072, True), (128, 128, 1)),  # 128 x 96 would need 640 blocks
     (("bf16", 8192, 1024, 4096, True), (128, 128, 1)),
     (("fp16", 256, 3072, 768, False), (64, 64, 1)),
     (("fp16", 256, 768, 3072, True), (32, 32, 3)),

@@ -347,14 +347,14 @@ def test_layernorm_fold(shape):
 
 
 @pytest.mark.parametrize("shape,auto", [
-    (si.Shape(256, 32, 12, 64, 2, "fp16"), True),   # 8192 rows: FFN-out on 384 128 x 128 tiles
+    (si.Shape(256, 32, 12, 64, 2, "fp16"), True),   # 8192 rows: FFN-out on 512 128 x 96 tiles
     (si.Shape(64, 32, 12, 64, 1, "bf16"), False),   # 2048 rows: 64 x 64 tiles, no prefetch
-    (si.Shape(20, 200, 12, 64, 1, "fp16"), False),  # 4480 rows (ragged lengths): 210 tiles
+    (si.Shape(20, 200, 12, 64, 1, "fp16"), False),  # 4480 rows (ragged lengths): 280 tiles
 ])
 def test_weight_prefetch(shape, auto):
     """FTX_OPT_PREFETCH_WEIGHTS: a kernel that reads W2 ahead of the second FFN projection on
     the folded path.  Automatic (1): one launch per layer where that projection runs on
-    128 x 128 tiles with more tiles than CUs, else none; forced (2): one per layer; never (0):
+    128-row tiles, at least 1.5 per CU, else none; forced (2): one per layer; never (0):
     none.  It writes nothing, so the three outputs are equal bit for bit, and they match the
     oracle at the stack bar.  Modes outside 0..2 are refused."""
     c = si.custom_case(shape, 57 + shape.batch, lens_range=(1, shape.seq_len), params="random_affine")

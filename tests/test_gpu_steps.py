@@ -72,6 +72,7 @@ LINEAR_SHAPES = [
     # where N is a multiple of 96 and that grid also fits the CUs, 128x96 tiles
     (4096, 768, 3072),   # BERT-base FFN-out at 4096 rows (256 tiles of 128 x 96)
     (3000, 768, 768),    # 128 x 96 with a ragged M tail (192 tiles)
+    (6000, 768, 3072),   # 128 x 96, two blocks per CU (376 tiles), ragged M
     (4000, 776, 1576),   # ragged M, N and K tails (224 tiles of 128 x 128)
     # 64x64 tiles with 12 slabs or more keep two slabs in flight (three LDS stages)
     (2048, 768, 768),    # BERT-base attention output at batch 64 (12 slabs)

@@ -577,8 +577,8 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
       }
       // The second FFN projection reads its weights cold: every layer's weights and
       // activations pass through the last-level cache between two reads of a layer's W2.  On
-      // 128x128 tiles with more tiles than CUs (two blocks per CU, all resident at once, each
-      // with one slab in flight) the cold W2 slows it most: BERT-base 8192 rows 59 -> 44 us
+      // 128-row tiles with at least 1.5 tiles per CU (two blocks on most CUs, all resident at
+      // once, each with one slab in flight) the cold W2 slows it most: BERT-base 8192 rows 59 -> 44 us
       // with W2 read just before it by a separate 5 us kernel; whole forwards (same box) S32
       // B256 2.19 -> 2.05 ms, S128 B64 2.24 -> 2.10, BERT-large S128 B64 5.99 -> 5.79, S32
       // B192 1.82 -> 1.79.  With fewer tiles (4096 rows) or 256-row tiles it loses by about
@@ -587,7 +587,8 @@ ftx_status ftx_encoder_create(int batch_size, int seq_len, int head_num, int siz
         int tm3, tn3, sp3;
         plan_linear(dtype, e->ffn_rows, e->H, e->F, e->dev.cus, true, &tm3, &tn3, &sp3);
         const int64_t tiles3 = (int64_t)((e->ffn_rows + tm3 - 1) / tm3) * ((e->H + tn3 - 1) / tn3);
-        e->w2_prefetch_fits = tm3 == 128 && tn3 == 128 && sp3 == 1 && tiles3 > e->dev.cus;
+        e->w2_prefetch_fits = tm3 == 128 && (tn3 == 128 || tn3 == 96) && sp3 == 1 &&
+                              2 * tiles3 >= 3 * (int64_t)e->dev.cus;
       }
     }
   }

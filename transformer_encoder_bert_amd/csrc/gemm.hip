@@ -1348,7 +1348,7 @@ static int small_gemm_tm(int M, int N, int K, int cus) {
 // register footprint per element) uses the table without its two largest tiles.
 
 // TILE_128x96 (4 waves of 32 x 96) is not a candidate of the cost model: plan_gemm takes it in
-// place of 128x128 where both grids fit one block per CU (below).
+// place of 128x128 where its grid fits two blocks per CU (below).
 enum TileCfg { TILE_256x256, TILE_256x192, TILE_256x128, TILE_128x128, TILE_64x64, TILE_32x32,
                TILE_128x96, TILE_COUNT };
 static const int kTileM[TILE_COUNT] = {256, 256, 256, 128, 64, 32, 128};
@@ -1436,13 +1436,13 @@ static GemmPlan plan_gemm(int M, int N, int K, int elem_bytes, bool sums_partial
       p.splits = (K + p.kchunk - 1) / p.kchunk;
     }
   }
-  // An unsplit 16-bit 128x128 grid within one block per CU, N a multiple of 96: 128x96 tiles
-  // cover the same rows with more blocks, still one per CU, each on three LDS stages from 12
-  // slabs.  BERT-base 4096 x 768 x 3072 alone: 27.9 -> 25.7 us (192 -> 256 tiles);
-  // 4096 x 768 x 768: 9.8 -> 8.9 us.
+  // An unsplit 16-bit 128x128 grid, N a multiple of 96, whose 128x96 grid still fits two
+  // blocks per CU: 128x96 tiles cover the same rows with more blocks -- one per CU on three
+  // LDS stages from 12 slabs, or two per CU on two.  BERT-base 4096 x 768 x 3072 alone: 27.9
+  // -> 25.7 us (192 -> 256 tiles); 4096 x 768 x 768: 9.8 -> 8.9 us; 8192 x 768 x 3072: 44.5
+  // -> 41.8 us (384 -> 512); 6144 x 768 x 3072 39.5 -> 37.2, x 768 13.5 -> 12.2.
   if (p.cfg == TILE_128x128 && p.splits == 1 && elem_bytes == 2 && N % 96 == 0 &&
-      nk >= kSmallTileDeepSlabsPlan && tiles <= kCUs &&
-      (long)((M + 127) / 128) * (N / 96) <= kCUs)
+      nk >= kSmallTileDeepSlabsPlan && (long)((M + 127) / 128) * (N / 96) <= 2 * kCUs)
     p.cfg = TILE_128x96;
   return p;
 }
