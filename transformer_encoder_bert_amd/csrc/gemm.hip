@@ -1808,8 +1808,14 @@ static hipError_t qkv_attention_t(int B, int nh, const void* x, const void* w_t,
     // 128-row tiles of 4 waves while twice the tiles still fit one per CU (BERT-base S32
     // at batch 64 on 256 CUs: 96 tiles of 256 rows -> 192 of 128, 0.849 -> 0.806 ms; at
     // S64, 192 tiles of 256 rows would become 384 sharing CUs: 1.267 -> 1.287 ms, so they
-    // stay)
-    if (2 * tiles <= di.cus) {
+    // stay), and where the 256-row grid's last round would run at most half full: two
+    // 128-row blocks per CU then finish in the time of the full rounds, and each block's
+    // attention overlaps the other's K loop.  Alone on 256 CUs (S32, d 64, 12 heads):
+    // 6144 rows 38.2 -> 33.7 us, 8192 rows 40.7 -> 36.5, 12288 rows 62.8 -> 55.7; S128 8192
+    // rows 42.0 -> 40.5; against 240 tiles 22.7 -> 24.1, 480 tiles 43.5 -> 45.0 and 768
+    // tiles 67.9 -> 68.1, where the 256-row grid stays.
+    const int rem = tiles % di.cus;
+    if (2 * tiles <= di.cus || (tiles > di.cus && rem != 0 && 2 * rem <= di.cus)) {
       typedef EpiQKVAttn<T, SEQ, D, 128> Epi128;
       Epi128 epi{(T*)ctx, (const T*)bias, lens, M, N, s_valid, scale_log2e, causal};
       gemm_kernel<T, 128, 192, 2, 2, Epi128><<<((M + 127) / 128) * (N / 192), 4 * kWave, 0, s>>>(
