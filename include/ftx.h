@@ -169,7 +169,8 @@ const char *ftx_last_error(void);
  *     32 with an even head_num) and a 16-bit dtype, the Q/K/V projection and the attention
  *     run as one kernel that attends each 256 x 192 projection tile (256/S whole sequences,
  *     64/size_per_head heads; 128-row tiles when the 256-row grid has at most half as many
- *     tiles as the GPU has CUs) in its epilogue, so Q, K and V never reach memory
+ *     tiles as the GPU has CUs, or more tiles than CUs with its last round at most half
+ *     full) in its epilogue, so Q, K and V never reach memory
  *     (ftx_step_qkv_attention).  0 = never; 1 = when batch*S >= 256 and the 256-row grid
  *     has at least 64 tiles (ceil(batch*S/256) * 3*hidden/192), else the separate kernels;
  *     2 = whenever the shape fits.  Needs FTX_OPT_FUSED_EPILOGUES = 1.
