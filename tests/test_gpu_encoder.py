@@ -552,6 +552,7 @@ FULL = [
     ("bert_base_fp16_s128_varlen", 1, None),
     ("bert_large_bf16_s128", 256, [0, 200]),
     ("bert_large_bf16_s512", 32, [7, 31]),
+    ("bert_large_bf16_s512", 1, None),   # FFN-out partials on 64x64 tiles, 32x32 on three stages
 ]
 
 

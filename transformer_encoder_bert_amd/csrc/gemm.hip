@@ -1435,6 +1435,22 @@ static GemmPlan plan_gemm(int M, int N, int K, int elem_bytes, bool sums_partial
       p.kchunk = (nk + sp - 1) / sp * bk;
       p.splits = (K + p.kchunk - 1) / p.kchunk;
     }
+    // one-wave 32x32 blocks left with a K chain of 32 slabs or more: 64x64 blocks (4 waves
+    // sharing each slab), split again for their own grid (BERT-large S512 B1, FFN-out 512 x
+    // 1024 x 4096: 2 splits of 32 slabs -> 4 of 16; with the three-stage 32x32 rule, whole
+    // forwards 1.675 -> 1.476 ms on one box)
+    if (p.cfg == TILE_32x32 && fill_simds && p.kchunk / bk >= 32) {
+      const long t64 = (long)((M + 63) / 64) * ((N + 63) / 64);
+      const long f64 = t64 < kCUs ? (2 * kCUs + t64 - 1) / t64 : (kSIMDs + 4 * t64 - 1) / (4 * t64);
+      const int sp64 = (int)std::min<long>(std::min<long>(f64, nk / 2), std::min<long>(16, by_bytes));
+      p.cfg = TILE_64x64;
+      p.splits = 1;
+      p.kchunk = K;
+      if (sp64 > 1) {
+        p.kchunk = (nk + sp64 - 1) / sp64 * bk;
+        p.splits = (K + p.kchunk - 1) / p.kchunk;
+      }
+    }
   }
   // An unsplit 16-bit 128x128 grid, N a multiple of 96, whose 128x96 grid still fits two
   // blocks per CU: 128x96 tiles cover the same rows with more blocks -- one per CU on three
@@ -1533,6 +1549,14 @@ static void gemm_kernel_launch(dim3 grid, int kchunk, int M, int N, int K, const
     }
   }
   if constexpr (BM == 32 && BN == 32) {
+    // a one-wave block with a K chain of 12 slabs or more keeps two slabs in flight (three
+    // 8 KB stages), as the 64x64 tile does: BERT-large S512 B1 1.674 -> 1.549 ms, BERT-base
+    // B8 0.470 -> 0.444 (whole forwards, same box), B1 and B16 unchanged
+    if ((kchunk + BK - 1) / BK >= kSmallTileDeepSlabs) {
+      gemm_kernel<T, BM, BN, WM, WN, Epi, 3><<<grid, WM * WN * kWave, 0, s>>>(
+          (const T*)a, (const T*)w_t, M, N, K, kchunk, xcds, epi);
+      return;
+    }
     // a split-K block of at most three slabs loads them all before its first multiply (four
     // 8 KB stages): one memory round trip instead of one per slab
     if (grid.y > 1 && (kchunk + BK - 1) / BK <= 3) {
